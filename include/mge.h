@@ -1,0 +1,289 @@
+/*
+ * mge.h — C ABI of the MI355X (gfx950) grouped expert MLP library.
+ *
+ * The routed mixture-of-experts SwiGLU MLP, forward and backward, in BF16 and in
+ * MXFP8, as five stream-ordered calls plus helpers:
+ *
+ *   moe_route_permute   top-k routing, per-expert counts (split_sizes), stable
+ *                       permutation of the tokens by expert, gather of x
+ *                       (optionally quantized to MXFP8 on load)
+ *   mxfp8_quantize      16-bit master weights -> MXFP8 codes + E8M0 scales, in row
+ *                       and/or column orientation
+ *   grouped_mlp_fwd     grouped gate-up GEMM over all experts in one launch, fused
+ *                       SwiGLU x routing probability (+ MXFP8 quantize of h), grouped
+ *                       down GEMM
+ *   grouped_mlp_bwd     dy permute (+quantize), dh GEMM with fused SwiGLU backward and
+ *                       d_prob, dW_down, dX and dW_gate_up grouped GEMMs
+ *   unpermute_combine   out[t] = sum over the k slots of in[perm_pos[t][i]]
+ *
+ * Sources: "NVIDIA Shows an Efficient MoE Training Path for Biological Foundation
+ * Models" (sections "Grouped experts instead of a Python loop" and "Memory and
+ * quantization overhead"), the BioNeMo recipe report (sections "Fragmented Expert
+ * Kernels", "Quantization Overhead") and the ai4snews report (paragraphs on
+ * GroupedLinear, on FP8/MXFP8 and on the Sequential fusion).  MXFP8 follows the OCP
+ * Microscaling Formats v1.0 specification: E4M3 elements, one E8M0 (power of two)
+ * scale per 32 consecutive values along the reduction dimension.
+ *
+ * Conventions (all calls):
+ *   - Every pointer is a device pointer unless marked [host].  The caller allocates
+ *     and frees every buffer; the library never allocates device memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns; nothing synchronizes except
+ *     mge_check_device_errors.  split_sizes stays on the device.
+ *   - Arguments are checked on the host first; on a bad argument no kernel is
+ *     launched and an error code is returned (details in mge_last_error()).
+ *   - bf16 tensors are raw 16-bit patterns (uint16_t).  MXFP8 tensors are a pair:
+ *     uint8 E4M3 codes and uint8 E8M0 scales (value 2^(s-127)), one scale per 32
+ *     consecutive elements along the stated axis.
+ *   - Permuted layout: rows of all experts in expert order; expert e occupies rows
+ *     [group_offsets[e], group_offsets[e] + split_sizes[e]); group_offsets are
+ *     multiples of `align`; the rows in between are padding (perm_src = -1).  The
+ *     total row count is R = mge_perm_rows(T, k, E, align), a multiple of 32.
+ *   - "Column form" of a [rows][C] matrix is stored transposed, [C][R], with blocks
+ *     of 32 consecutive rows; rows of an expert's 32-row padding hold zeros.  With
+ *     align % 32 == 0 no block straddles two experts.  The column forms written by
+ *     the GEMM epilogues (h_col, dgu_col) cover rows [0, group_offsets[E]) only;
+ *     those written by moe_route_permute / the dy permute cover all R rows.
+ *   - Limits: 1 <= k <= min(E, 8); 1 <= E <= 256; H and F multiples of 32;
+ *     align a power of two in [1, 256]; column forms (training, backward) need
+ *     align % 32 == 0.
+ *     T = 0 is a no-op.  NaN/Inf inputs give undefined (but memory-safe) results.
+ *   - Calls are thread-safe and re-entrant; each is deterministic (no atomics on
+ *     the data path), so two identical calls give bit-identical outputs.
+ */
+#ifndef MGE_H
+#define MGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mge_status {
+  MGE_OK = 0,
+  MGE_ERR_INVALID_ARG = 1,   /* bad size, NULL pointer, misaligned pointer */
+  MGE_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement */
+  MGE_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the query says */
+  MGE_ERR_HIP = 4,           /* a HIP launch failed (hipGetLastError text in mge_last_error) */
+  MGE_ERR_DEVICE_CHECK = 5   /* a kernel flagged bad data (see mge_check_device_errors) */
+} mge_status;
+
+enum { MGE_PREC_BF16 = 0, MGE_PREC_MXFP8 = 1 };
+enum { MGE_DTYPE_BF16 = 0, MGE_DTYPE_F32 = 1 };
+enum { MGE_ORIENT_ROW = 1, MGE_ORIENT_COL = 2 };
+enum {
+  MGE_ROUTE_WANT_COL = 1,     /* also write the column form of the permuted x */
+  MGE_ROUTE_PROB_GIVEN = 2    /* topk_idx / topk_prob are inputs (router skipped) */
+};
+
+/* Rows of every permuted buffer: T*k + E*(align-1), rounded up to 32. */
+int64_t mge_perm_rows(int32_t T, int32_t k, int32_t E, int32_t align);
+
+/* ------------------------------------------------------------------------------
+ * moe_route_permute — top-k routing and the stable permutation by expert.
+ *
+ * Routing (each token is sent to a small number k of the E experts): per token the k
+ * largest fp32 logits, ordered by (logit descending, expert index ascending);
+ * topk_prob = softmax over the k selected logits (the full softmax renormalised over
+ * the top-k).  split_sizes[e] = number of (t, i) with topk_idx[t][i] == e (the
+ * per-expert counts the grouped call takes); group_offsets = exclusive prefix sum of
+ * split_sizes rounded up to align (E+1 entries).  The row of assignment (t, i) is
+ * group_offsets[e] + the number of assignments to e that come before (t, i) in
+ * (t, i) order (a stable counting sort, so indices are unique and bit-exact).
+ * perm_src[row] = t (-1 on padding), perm_pos[t][i] = row, prob_perm[row] = p (0 on
+ * padding).  If x != NULL the permuted x is written: prec BF16 -> x_perm bf16 [R][H];
+ * prec MXFP8 -> x_perm u8 codes [R][H] + x_perm_scale u8 [R][H/32] (blocks along H).
+ * With MGE_ROUTE_WANT_COL also the column form x_col ([H][R] bf16, or codes [H][R] +
+ * x_col_scale [H][R/32]); padding rows are zero in every permuted buffer.
+ * With MGE_ROUTE_PROB_GIVEN, logits is ignored and topk_idx/topk_prob are read; an
+ * index outside [0, E) sets the device error flag (read by mge_check_device_errors)
+ * and is clamped.
+ * Workspace: mge_route_workspace_bytes(T, E) bytes, 256-byte aligned.
+ * ---------------------------------------------------------------------------- */
+typedef struct mge_route_args {
+  uint32_t struct_size;      /* sizeof(mge_route_args) */
+  int32_t T, E, k, H, align;
+  int32_t prec;              /* format of x_perm / x_col */
+  uint32_t flags;
+  const float* logits;       /* [T][E] */
+  const uint16_t* x;         /* [T][H] bf16, or NULL (maps only) */
+  int32_t* topk_idx;         /* [T][k] */
+  float* topk_prob;          /* [T][k] */
+  int32_t* split_sizes;      /* [E] */
+  int32_t* group_offsets;    /* [E+1] */
+  int32_t* perm_src;         /* [R] */
+  int32_t* perm_pos;         /* [T][k] */
+  float* prob_perm;          /* [R] */
+  void* x_perm;              /* [R][H] bf16 or u8 */
+  uint8_t* x_perm_scale;     /* [R][H/32] (MXFP8) */
+  void* x_col;               /* [H][R] bf16 or u8 (MGE_ROUTE_WANT_COL) */
+  uint8_t* x_col_scale;      /* [H][R/32] (MXFP8, MGE_ROUTE_WANT_COL) */
+  void* workspace;
+  size_t workspace_bytes;
+} mge_route_args;
+
+size_t mge_route_workspace_bytes(int32_t T, int32_t E);
+mge_status moe_route_permute(const mge_route_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * mxfp8_quantize — BF16 -> MXFP8 (E4M3 + E8M0 per 32), the per-step quantization of
+ * the 16-bit master weights.
+ *
+ * in: `batch` matrices of [R][C] bf16; element (b, r, c) at in[b*in_batch_stride +
+ * r*in_row_stride + c] (strides in elements).  Per block of 32 values the shared
+ * exponent is e = floor(log2(amax)) - 8 clamped to [-127, 127] (all-zero block:
+ * -127); scale byte = e + 127; element = E4M3 round-to-nearest-even of v / 2^e,
+ * saturating at 448 (OCP MX v1.0).
+ * ROW: blocks along C: row_codes [b][R][C], row_scales [b][R][C/32].  Needs C % 32 == 0.
+ * COL: blocks along R, stored transposed and K-contiguous: col_codes [b][C][Rp],
+ * col_scales [b][C][Rp/32], Rp = R rounded up to 32 (zero padded) — by definition the
+ * ROW quantization of the transpose.
+ * ---------------------------------------------------------------------------- */
+typedef struct mge_quant_args {
+  uint32_t struct_size;
+  int32_t batch, R, C;
+  int64_t in_batch_stride, in_row_stride;
+  const uint16_t* in;
+  uint32_t orient;           /* MGE_ORIENT_ROW | MGE_ORIENT_COL */
+  uint8_t* row_codes;
+  uint8_t* row_scales;
+  uint8_t* col_codes;
+  uint8_t* col_scales;
+} mge_quant_args;
+
+mge_status mxfp8_quantize(const mge_quant_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * grouped_mlp_fwd — GroupedLinear(gate_up) -> ScaledSwiGLU -> GroupedLinear(down)
+ * over all experts, each projection one persistent grouped launch.
+ *
+ * Per expert e with rows X_e of the permuted x (split_sizes[e] rows, possibly 0):
+ *   [G U] = X_e W_gate_up[e]^T   (W_gate_up[e] is [2F][H]: gate rows 0..F-1, up rows F..2F-1)
+ *   h     = p * silu(G) * U      (p = prob_perm of the row; fp32, never stored unquantized)
+ *   Y_e   = h W_down[e]^T        (W_down[e] is [H][F])
+ * BF16: operands bf16, fp32 accumulate, h rounded to bf16.  MXFP8: x_perm, W_gate_up
+ * (blocks along H), h (blocks along F, quantized after the p scaling) and W_down
+ * (blocks along F) are MXFP8; fp32 accumulate on block-scaled MFMA.
+ * w_gate_up, w_down: [host] arrays of E device pointers (each expert keeps its own
+ * weight tensor); *_scale arrays only for MXFP8.
+ * Outputs: y_perm [R][H] (bf16 or f32, rows outside the groups untouched); h row form
+ * (bf16 [R][F], or codes [R][F] + h_scale [R][F/32]) — if h is NULL it lives in the
+ * workspace.  Training (saved_gu != NULL): saved_gu bf16 [R][2F] (G then U) and the
+ * column form of h (h_col [F][R] bf16, or codes + h_col_scale [F][R/32]) for dW_down.
+ * Workspace: mge_fwd_workspace_bytes(args).
+ * ---------------------------------------------------------------------------- */
+typedef struct mge_fwd_args {
+  uint32_t struct_size;
+  int32_t prec, E, H, F, T, k, align;
+  const int32_t* split_sizes;
+  const int32_t* group_offsets;
+  const float* prob_perm;
+  const void* x_perm;
+  const uint8_t* x_perm_scale;
+  const void* const* w_gate_up;          /* [host] E pointers */
+  const uint8_t* const* w_gate_up_scale; /* [host] E pointers (MXFP8) */
+  const void* const* w_down;             /* [host] E pointers */
+  const uint8_t* const* w_down_scale;    /* [host] E pointers (MXFP8) */
+  int32_t y_dtype;                       /* MGE_DTYPE_BF16 or MGE_DTYPE_F32 */
+  void* y_perm;
+  void* h;                               /* optional */
+  uint8_t* h_scale;                      /* optional (MXFP8) */
+  uint16_t* saved_gu;                    /* training: [R][2F] bf16, else NULL */
+  void* h_col;                           /* training */
+  uint8_t* h_col_scale;                  /* training, MXFP8 */
+  void* workspace;
+  size_t workspace_bytes;
+} mge_fwd_args;
+
+size_t mge_fwd_workspace_bytes(const mge_fwd_args* args);
+mge_status grouped_mlp_fwd(const mge_fwd_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * grouped_mlp_bwd — the matching backward of grouped_mlp_fwd, for L = <dy, y> with
+ * y = unpermute_combine(y_perm):
+ *   dY = dy gathered by perm_src; dh = dY W_down (K = H)
+ *   d_prob[t][i] = sum_f dh * silu(G) * U        (row perm_pos[t][i])
+ *   dU = dh * p * silu(G);  dG = dh * p * U * silu'(G)   (G, U from saved_gu)
+ *   dW_down[e]    = dY_e^T h_e          (K = the expert's tokens)
+ *   dX            = [dG dU] W_gate_up   (K = 2F) -> dx_perm; dx = combine(dx_perm)
+ *   dW_gate_up[e] = [dG dU]_e^T X_e     (K = the expert's tokens)
+ * MXFP8: dY is quantized along H (row form) and along tokens (column form, blocks
+ * start at each expert's first row); [dG dU] along 2F and along tokens; the weights
+ * come in column form (w_gate_up_col[e]: codes [H][2F] + scales [H][2F/32], i.e.
+ * mxfp8_quantize COL of W_gate_up[e]; w_down_col[e]: codes [F][H] + scales [F][H/32]);
+ * h_col and x_col are the column forms written by the forward and by
+ * moe_route_permute.  BF16: the weights are the bf16 masters (w_gate_up[e] [2F][H],
+ * w_down[e] [H][F]); h_col/x_col are the bf16 transposes.
+ * Outputs: dx_perm bf16 [R][H] (valid rows), dw_gate_up[e] [2F][H] and dw_down[e]
+ * [H][F] (fp32; accumulate != 0 adds to them instead of overwriting; experts with no
+ * tokens get zeros), d_prob f32 [T][k].  The intermediates (dY row/col, dGU row/col,
+ * d_prob partials) go to the optional buffers when given, else to the workspace.
+ * ---------------------------------------------------------------------------- */
+typedef struct mge_bwd_args {
+  uint32_t struct_size;
+  int32_t prec, E, H, F, T, k, align;
+  const uint16_t* dy;                    /* [T][H] bf16 */
+  const int32_t* split_sizes;
+  const int32_t* group_offsets;
+  const int32_t* perm_src;
+  const int32_t* perm_pos;
+  const float* prob_perm;
+  const uint16_t* saved_gu;              /* [R][2F] */
+  const void* h_col;  const uint8_t* h_col_scale;
+  const void* x_col;  const uint8_t* x_col_scale;
+  const void* const* w_gate_up;          /* [host] E: MXFP8 col codes [H][2F] / BF16 masters [2F][H] */
+  const uint8_t* const* w_gate_up_scale; /* [host] E: [H][2F/32] (MXFP8) */
+  const void* const* w_down;             /* [host] E: MXFP8 col codes [F][H] / BF16 masters [H][F] */
+  const uint8_t* const* w_down_scale;    /* [host] E: [F][H/32] (MXFP8) */
+  uint16_t* dx_perm;                     /* [R][H] bf16 */
+  float* const* dw_gate_up;              /* [host] E pointers, [2F][H] f32 */
+  float* const* dw_down;                 /* [host] E pointers, [H][F] f32 */
+  float* d_prob;                         /* [T][k] */
+  int32_t accumulate;
+  /* optional intermediates (NULL -> workspace) */
+  void* dy_row;  uint8_t* dy_row_scale;  /* [R][H] */
+  void* dy_col;  uint8_t* dy_col_scale;  /* [H][R] */
+  void* dgu_row; uint8_t* dgu_row_scale; /* [R][2F] */
+  void* dgu_col; uint8_t* dgu_col_scale; /* [2F][R] */
+  void* workspace;
+  size_t workspace_bytes;
+} mge_bwd_args;
+
+size_t mge_bwd_workspace_bytes(const mge_bwd_args* args);
+mge_status grouped_mlp_bwd(const mge_bwd_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * unpermute_combine — out[t][:] = sum_{i<k} w[t][i] * in[perm_pos[t][i]][:]
+ * (w = 1 when weights == NULL), summed in fp32 in slot order i = 0..k-1, no atomics.
+ * The probability is already applied inside the forward (before the down
+ * projection), so the forward's combine is unweighted.
+ * ---------------------------------------------------------------------------- */
+typedef struct mge_combine_args {
+  uint32_t struct_size;
+  int32_t T, k, H;
+  int32_t in_dtype, out_dtype;           /* MGE_DTYPE_* */
+  const void* in;                        /* [R][H] */
+  const int32_t* perm_pos;               /* [T][k] */
+  const float* weights;                  /* [T][k] or NULL */
+  void* out;                             /* [T][H] */
+} mge_combine_args;
+
+mge_status unpermute_combine(const mge_combine_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------ helpers */
+const char* mge_status_string(mge_status s);
+/* Detail of the last error on the calling thread ("" if none). */
+const char* mge_last_error(void);
+/* Synchronizes `stream`, then reads and clears the device error flag kept at the
+ * start of a moe_route_permute workspace.  Tests and debugging only. */
+mge_status mge_check_device_errors(void* route_workspace, void* stream);
+/* Library version, e.g. "0.1.0". */
+const char* mge_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MGE_H */

@@ -1,0 +1,415 @@
+"""ctypes binding of libmge.so (include/mge.h), with the same call names.
+
+Argument marshalling only: tensors are allocated with torch (device memory and the
+current stream are torch's), every step of the computation runs in the library's HIP
+kernels.  If the library is not built the first call raises — there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmge.so")
+
+MGE_OK, MGE_ERR_INVALID_ARG, MGE_ERR_UNSUPPORTED, MGE_ERR_WORKSPACE, MGE_ERR_HIP, MGE_ERR_DEVICE_CHECK = range(6)
+PREC = {"bf16": 0, "mxfp8": 1}
+DTYPE = {"bf16": 0, "f32": 1}
+ORIENT_ROW, ORIENT_COL = 1, 2
+ROUTE_WANT_COL, ROUTE_PROB_GIVEN = 1, 2
+
+vp = C.c_void_p
+i32 = C.c_int32
+u32 = C.c_uint32
+i64 = C.c_int64
+
+
+class RouteArgs(C.Structure):
+    _fields_ = [("struct_size", u32), ("T", i32), ("E", i32), ("k", i32), ("H", i32), ("align", i32),
+                ("prec", i32), ("flags", u32),
+                ("logits", vp), ("x", vp), ("topk_idx", vp), ("topk_prob", vp), ("split_sizes", vp),
+                ("group_offsets", vp), ("perm_src", vp), ("perm_pos", vp), ("prob_perm", vp),
+                ("x_perm", vp), ("x_perm_scale", vp), ("x_col", vp), ("x_col_scale", vp),
+                ("workspace", vp), ("workspace_bytes", C.c_size_t)]
+
+
+class QuantArgs(C.Structure):
+    _fields_ = [("struct_size", u32), ("batch", i32), ("R", i32), ("C", i32),
+                ("in_batch_stride", i64), ("in_row_stride", i64), ("in_", vp), ("orient", u32),
+                ("row_codes", vp), ("row_scales", vp), ("col_codes", vp), ("col_scales", vp)]
+
+
+class FwdArgs(C.Structure):
+    _fields_ = [("struct_size", u32), ("prec", i32), ("E", i32), ("H", i32), ("F", i32), ("T", i32),
+                ("k", i32), ("align", i32),
+                ("split_sizes", vp), ("group_offsets", vp), ("prob_perm", vp), ("x_perm", vp),
+                ("x_perm_scale", vp), ("w_gate_up", vp), ("w_gate_up_scale", vp), ("w_down", vp),
+                ("w_down_scale", vp), ("y_dtype", i32), ("y_perm", vp), ("h", vp), ("h_scale", vp),
+                ("saved_gu", vp), ("h_col", vp), ("h_col_scale", vp), ("workspace", vp),
+                ("workspace_bytes", C.c_size_t)]
+
+
+class BwdArgs(C.Structure):
+    _fields_ = [("struct_size", u32), ("prec", i32), ("E", i32), ("H", i32), ("F", i32), ("T", i32),
+                ("k", i32), ("align", i32),
+                ("dy", vp), ("split_sizes", vp), ("group_offsets", vp), ("perm_src", vp), ("perm_pos", vp),
+                ("prob_perm", vp), ("saved_gu", vp), ("h_col", vp), ("h_col_scale", vp), ("x_col", vp),
+                ("x_col_scale", vp), ("w_gate_up", vp), ("w_gate_up_scale", vp), ("w_down", vp),
+                ("w_down_scale", vp), ("dx_perm", vp), ("dw_gate_up", vp), ("dw_down", vp), ("d_prob", vp),
+                ("accumulate", i32),
+                ("dy_row", vp), ("dy_row_scale", vp), ("dy_col", vp), ("dy_col_scale", vp),
+                ("dgu_row", vp), ("dgu_row_scale", vp), ("dgu_col", vp), ("dgu_col_scale", vp),
+                ("workspace", vp), ("workspace_bytes", C.c_size_t)]
+
+
+class CombineArgs(C.Structure):
+    _fields_ = [("struct_size", u32), ("T", i32), ("k", i32), ("H", i32), ("in_dtype", i32), ("out_dtype", i32),
+                ("in_", vp), ("perm_pos", vp), ("weights", vp), ("out", vp)]
+
+
+_LIB = None
+EXPORTS = ["mge_perm_rows", "mge_route_workspace_bytes", "moe_route_permute", "mxfp8_quantize",
+           "mge_fwd_workspace_bytes", "grouped_mlp_fwd", "mge_bwd_workspace_bytes", "grouped_mlp_bwd",
+           "unpermute_combine", "mge_status_string", "mge_last_error", "mge_check_device_errors", "mge_version"]
+
+
+def lib():
+    """Loads libmge.so (raises if it is not built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m moe_grouped_expert_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        L.mge_perm_rows.restype = i64
+        L.mge_perm_rows.argtypes = [i32, i32, i32, i32]
+        L.mge_route_workspace_bytes.restype = C.c_size_t
+        L.mge_route_workspace_bytes.argtypes = [i32, i32]
+        L.mge_fwd_workspace_bytes.restype = C.c_size_t
+        L.mge_fwd_workspace_bytes.argtypes = [C.POINTER(FwdArgs)]
+        L.mge_bwd_workspace_bytes.restype = C.c_size_t
+        L.mge_bwd_workspace_bytes.argtypes = [C.POINTER(BwdArgs)]
+        for name, st in (("moe_route_permute", RouteArgs), ("mxfp8_quantize", QuantArgs),
+                         ("grouped_mlp_fwd", FwdArgs), ("grouped_mlp_bwd", BwdArgs),
+                         ("unpermute_combine", CombineArgs)):
+            f = getattr(L, name)
+            f.restype = C.c_int
+            f.argtypes = [C.POINTER(st), vp]
+        L.mge_status_string.restype = C.c_char_p
+        L.mge_status_string.argtypes = [C.c_int]
+        L.mge_last_error.restype = C.c_char_p
+        L.mge_last_error.argtypes = []
+        L.mge_check_device_errors.restype = C.c_int
+        L.mge_check_device_errors.argtypes = [vp, vp]
+        L.mge_version.restype = C.c_char_p
+        _LIB = L
+    return _LIB
+
+
+class MgeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        L = lib()
+        super().__init__(f"{where}: {L.mge_status_string(code).decode()}: {L.mge_last_error().decode()}")
+        self.code = code
+
+
+def _check(code: int, where: str):
+    if code != MGE_OK:
+        raise MgeError(code, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ptr_array(ts: Sequence[torch.Tensor]):
+    arr = (vp * len(ts))(*[t.data_ptr() for t in ts])
+    return arr
+
+
+def perm_rows(T: int, k: int, E: int, align: int) -> int:
+    return int(lib().mge_perm_rows(T, k, E, align))
+
+
+# ------------------------------------------------------------------------------ routing
+
+@dataclass
+class RouteOut:
+    T: int
+    E: int
+    k: int
+    H: int
+    align: int
+    prec: str
+    R: int
+    topk_idx: torch.Tensor
+    topk_prob: torch.Tensor
+    split_sizes: torch.Tensor
+    group_offsets: torch.Tensor
+    perm_src: torch.Tensor
+    perm_pos: torch.Tensor
+    prob_perm: torch.Tensor
+    x_perm: Optional[torch.Tensor] = None
+    x_perm_scale: Optional[torch.Tensor] = None
+    x_col: Optional[torch.Tensor] = None
+    x_col_scale: Optional[torch.Tensor] = None
+    workspace: Optional[torch.Tensor] = None
+
+
+def moe_route_permute(logits: Optional[torch.Tensor], x: Optional[torch.Tensor], k: int, E: Optional[int] = None,
+                      align: int = 32, prec: str = "bf16", want_col: bool = False,
+                      topk_idx: Optional[torch.Tensor] = None, topk_prob: Optional[torch.Tensor] = None,
+                      out: Optional[RouteOut] = None) -> RouteOut:
+    """Top-k routing + stable permutation by expert (+ gather / quantize of x)."""
+    given = topk_idx is not None
+    ref = logits if logits is not None else topk_idx
+    dev = ref.device
+    if logits is not None:
+        T, E = logits.shape
+        assert logits.dtype == torch.float32 and logits.is_contiguous()
+    else:
+        T = topk_idx.shape[0]
+        assert E is not None
+    H = x.shape[1] if x is not None else 32
+    if x is not None:
+        assert x.dtype == torch.bfloat16 and x.is_contiguous() and x.shape[0] == T
+    R = perm_rows(T, k, E, align)
+    if out is None:
+        i = dict(device=dev, dtype=torch.int32)
+        f = dict(device=dev, dtype=torch.float32)
+        o = RouteOut(T=T, E=E, k=k, H=H, align=align, prec=prec, R=R,
+                     topk_idx=topk_idx if given else torch.empty((T, k), **i),
+                     topk_prob=topk_prob if given else torch.empty((T, k), **f),
+                     split_sizes=torch.empty(E, **i), group_offsets=torch.empty(E + 1, **i),
+                     perm_src=torch.empty(R, **i), perm_pos=torch.empty((T, k), **i), prob_perm=torch.empty(R, **f))
+        if x is not None:
+            if prec == "mxfp8":
+                o.x_perm = torch.empty((R, H), device=dev, dtype=torch.uint8)
+                o.x_perm_scale = torch.empty((R, H // 32), device=dev, dtype=torch.uint8)
+                if want_col:
+                    o.x_col = torch.empty((H, R), device=dev, dtype=torch.uint8)
+                    o.x_col_scale = torch.empty((H, R // 32), device=dev, dtype=torch.uint8)
+            else:
+                o.x_perm = torch.empty((R, H), device=dev, dtype=torch.bfloat16)
+                if want_col:
+                    o.x_col = torch.empty((H, R), device=dev, dtype=torch.bfloat16)
+        nbytes = int(lib().mge_route_workspace_bytes(T, E))
+        o.workspace = torch.empty(max(nbytes, 256), device=dev, dtype=torch.uint8)
+    else:
+        o = out
+    a = RouteArgs()
+    a.struct_size = C.sizeof(RouteArgs)
+    a.T, a.E, a.k, a.H, a.align = T, E, k, H, align
+    a.prec = PREC[prec]
+    a.flags = (ROUTE_WANT_COL if want_col else 0) | (ROUTE_PROB_GIVEN if given else 0)
+    a.logits = _ptr(logits)
+    a.x = _ptr(x)
+    a.topk_idx, a.topk_prob = _ptr(o.topk_idx), _ptr(o.topk_prob)
+    a.split_sizes, a.group_offsets = _ptr(o.split_sizes), _ptr(o.group_offsets)
+    a.perm_src, a.perm_pos, a.prob_perm = _ptr(o.perm_src), _ptr(o.perm_pos), _ptr(o.prob_perm)
+    a.x_perm, a.x_perm_scale = _ptr(o.x_perm), _ptr(o.x_perm_scale)
+    a.x_col, a.x_col_scale = _ptr(o.x_col), _ptr(o.x_col_scale)
+    a.workspace, a.workspace_bytes = _ptr(o.workspace), o.workspace.numel()
+    _check(lib().moe_route_permute(C.byref(a), _stream(dev)), "moe_route_permute")
+    return o
+
+
+def check_device_errors(route: RouteOut) -> int:
+    return lib().mge_check_device_errors(_ptr(route.workspace), _stream(route.workspace.device))
+
+
+# ------------------------------------------------------------------------------ quantize
+
+def mxfp8_quantize(w: torch.Tensor, orient: str = "row", out=None):
+    """BF16 [..., R, C] -> (row_codes, row_scales, col_codes, col_scales) (absent ones None)."""
+    assert w.dtype == torch.bfloat16 and w.is_contiguous()
+    R, Cc = w.shape[-2], w.shape[-1]
+    lead = tuple(w.shape[:-2])
+    batch = 1
+    for d in lead:
+        batch *= d
+    Rp = (R + 31) // 32 * 32
+    want_row = orient in ("row", "both")
+    want_col = orient in ("col", "both")
+    dev = w.device
+    if out is None:
+        u8 = dict(device=dev, dtype=torch.uint8)
+        rc = torch.empty(lead + (R, Cc), **u8) if want_row else None
+        rs = torch.empty(lead + (R, Cc // 32), **u8) if want_row else None
+        cc = torch.empty(lead + (Cc, Rp), **u8) if want_col else None
+        cs = torch.empty(lead + (Cc, Rp // 32), **u8) if want_col else None
+    else:
+        rc, rs, cc, cs = out
+    a = QuantArgs()
+    a.struct_size = C.sizeof(QuantArgs)
+    a.batch, a.R, a.C = batch, R, Cc
+    a.in_batch_stride, a.in_row_stride = R * Cc, Cc
+    a.in_ = _ptr(w)
+    a.orient = (ORIENT_ROW if want_row else 0) | (ORIENT_COL if want_col else 0)
+    a.row_codes, a.row_scales, a.col_codes, a.col_scales = _ptr(rc), _ptr(rs), _ptr(cc), _ptr(cs)
+    _check(lib().mxfp8_quantize(C.byref(a), _stream(dev)), "mxfp8_quantize")
+    return rc, rs, cc, cs
+
+
+# ------------------------------------------------------------------------------ forward
+
+@dataclass
+class FwdOut:
+    y_perm: torch.Tensor
+    h: torch.Tensor
+    h_scale: Optional[torch.Tensor] = None
+    saved_gu: Optional[torch.Tensor] = None
+    h_col: Optional[torch.Tensor] = None
+    h_col_scale: Optional[torch.Tensor] = None
+    workspace: Optional[torch.Tensor] = None
+
+
+def _split(w, E):
+    if isinstance(w, torch.Tensor):
+        return [w[e] for e in range(E)]
+    return list(w)
+
+
+def grouped_mlp_fwd(rt: RouteOut, w_gate_up, w_down, w_gate_up_scale=None, w_down_scale=None,
+                    y_dtype: str = "bf16", train: bool = False, out: Optional[FwdOut] = None) -> FwdOut:
+    """Grouped gate-up GEMM -> SwiGLU x prob (+ quantize) -> grouped down GEMM."""
+    E, H, R = rt.E, rt.H, rt.R
+    wg = _split(w_gate_up, E)
+    wd = _split(w_down, E)
+    F = wg[0].shape[0] // 2
+    mx = rt.prec == "mxfp8"
+    dev = rt.x_perm.device
+    if out is None:
+        o = FwdOut(y_perm=torch.empty((R, H), device=dev, dtype=torch.bfloat16 if y_dtype == "bf16" else torch.float32),
+                   h=torch.empty((R, F), device=dev, dtype=torch.uint8 if mx else torch.bfloat16))
+        if mx:
+            o.h_scale = torch.empty((R, F // 32), device=dev, dtype=torch.uint8)
+        if train:
+            o.saved_gu = torch.empty((R, 2 * F), device=dev, dtype=torch.bfloat16)
+            o.h_col = torch.empty((F, R), device=dev, dtype=torch.uint8 if mx else torch.bfloat16)
+            if mx:
+                o.h_col_scale = torch.empty((F, R // 32), device=dev, dtype=torch.uint8)
+    else:
+        o = out
+    a = FwdArgs()
+    a.struct_size = C.sizeof(FwdArgs)
+    a.prec, a.E, a.H, a.F, a.T, a.k, a.align = PREC[rt.prec], E, H, F, rt.T, rt.k, rt.align
+    a.split_sizes, a.group_offsets, a.prob_perm = _ptr(rt.split_sizes), _ptr(rt.group_offsets), _ptr(rt.prob_perm)
+    a.x_perm, a.x_perm_scale = _ptr(rt.x_perm), _ptr(rt.x_perm_scale)
+    keep = [_ptr_array(wg), _ptr_array(wd)]
+    a.w_gate_up, a.w_down = C.cast(keep[0], vp), C.cast(keep[1], vp)
+    if mx:
+        keep += [_ptr_array(_split(w_gate_up_scale, E)), _ptr_array(_split(w_down_scale, E))]
+        a.w_gate_up_scale, a.w_down_scale = C.cast(keep[2], vp), C.cast(keep[3], vp)
+    a.y_dtype = DTYPE[y_dtype]
+    a.y_perm, a.h, a.h_scale = _ptr(o.y_perm), _ptr(o.h), _ptr(o.h_scale)
+    a.saved_gu, a.h_col, a.h_col_scale = _ptr(o.saved_gu), _ptr(o.h_col), _ptr(o.h_col_scale)
+    if o.workspace is None:
+        o.workspace = torch.empty(max(int(lib().mge_fwd_workspace_bytes(C.byref(a))), 256), device=dev,
+                                  dtype=torch.uint8)
+    a.workspace, a.workspace_bytes = _ptr(o.workspace), o.workspace.numel()
+    _check(lib().grouped_mlp_fwd(C.byref(a), _stream(dev)), "grouped_mlp_fwd")
+    return o
+
+
+# ------------------------------------------------------------------------------ backward
+
+@dataclass
+class BwdOut:
+    dx_perm: torch.Tensor
+    dw_gate_up: list
+    dw_down: list
+    d_prob: torch.Tensor
+    dy_row: Optional[torch.Tensor] = None
+    dy_row_scale: Optional[torch.Tensor] = None
+    dy_col: Optional[torch.Tensor] = None
+    dy_col_scale: Optional[torch.Tensor] = None
+    dgu_row: Optional[torch.Tensor] = None
+    dgu_row_scale: Optional[torch.Tensor] = None
+    dgu_col: Optional[torch.Tensor] = None
+    dgu_col_scale: Optional[torch.Tensor] = None
+    workspace: Optional[torch.Tensor] = None
+
+
+def grouped_mlp_bwd(dy: torch.Tensor, rt: RouteOut, fw: FwdOut, w_gate_up_k, w_down_k, w_gate_up_k_scale=None,
+                    w_down_k_scale=None, accumulate: bool = False, keep_intermediates: bool = False,
+                    out: Optional[BwdOut] = None) -> BwdOut:
+    """Backward of the grouped MLP.  Weights: MXFP8 column forms, or the bf16 masters."""
+    E, H, R, T, k = rt.E, rt.H, rt.R, rt.T, rt.k
+    mx = rt.prec == "mxfp8"
+    wg = _split(w_gate_up_k, E)
+    wd = _split(w_down_k, E)
+    F = fw.h.shape[1]
+    dev = dy.device
+    if out is None:
+        f32 = dict(device=dev, dtype=torch.float32)
+        o = BwdOut(dx_perm=torch.empty((R, H), device=dev, dtype=torch.bfloat16),
+                   dw_gate_up=[torch.empty((2 * F, H), **f32) for _ in range(E)],
+                   dw_down=[torch.empty((H, F), **f32) for _ in range(E)],
+                   d_prob=torch.empty((T, k), **f32))
+        if keep_intermediates:
+            cd = torch.uint8 if mx else torch.bfloat16
+            o.dy_row = torch.empty((R, H), device=dev, dtype=cd)
+            o.dy_col = torch.empty((H, R), device=dev, dtype=cd)
+            o.dgu_row = torch.empty((R, 2 * F), device=dev, dtype=cd)
+            o.dgu_col = torch.empty((2 * F, R), device=dev, dtype=cd)
+            if mx:
+                u8 = dict(device=dev, dtype=torch.uint8)
+                o.dy_row_scale = torch.empty((R, H // 32), **u8)
+                o.dy_col_scale = torch.empty((H, R // 32), **u8)
+                o.dgu_row_scale = torch.empty((R, 2 * F // 32), **u8)
+                o.dgu_col_scale = torch.empty((2 * F, R // 32), **u8)
+    else:
+        o = out
+    a = BwdArgs()
+    a.struct_size = C.sizeof(BwdArgs)
+    a.prec, a.E, a.H, a.F, a.T, a.k, a.align = PREC[rt.prec], E, H, F, T, k, rt.align
+    a.dy = _ptr(dy)
+    a.split_sizes, a.group_offsets = _ptr(rt.split_sizes), _ptr(rt.group_offsets)
+    a.perm_src, a.perm_pos, a.prob_perm = _ptr(rt.perm_src), _ptr(rt.perm_pos), _ptr(rt.prob_perm)
+    a.saved_gu = _ptr(fw.saved_gu)
+    a.h_col, a.h_col_scale = _ptr(fw.h_col), _ptr(fw.h_col_scale)
+    a.x_col, a.x_col_scale = _ptr(rt.x_col), _ptr(rt.x_col_scale)
+    keep = [_ptr_array(wg), _ptr_array(wd), _ptr_array(o.dw_gate_up), _ptr_array(o.dw_down)]
+    a.w_gate_up, a.w_down = C.cast(keep[0], vp), C.cast(keep[1], vp)
+    a.dw_gate_up, a.dw_down = C.cast(keep[2], vp), C.cast(keep[3], vp)
+    if mx:
+        keep += [_ptr_array(_split(w_gate_up_k_scale, E)), _ptr_array(_split(w_down_k_scale, E))]
+        a.w_gate_up_scale, a.w_down_scale = C.cast(keep[4], vp), C.cast(keep[5], vp)
+    a.dx_perm, a.d_prob = _ptr(o.dx_perm), _ptr(o.d_prob)
+    a.accumulate = 1 if accumulate else 0
+    a.dy_row, a.dy_row_scale, a.dy_col, a.dy_col_scale = _ptr(o.dy_row), _ptr(o.dy_row_scale), _ptr(o.dy_col), _ptr(o.dy_col_scale)
+    a.dgu_row, a.dgu_row_scale = _ptr(o.dgu_row), _ptr(o.dgu_row_scale)
+    a.dgu_col, a.dgu_col_scale = _ptr(o.dgu_col), _ptr(o.dgu_col_scale)
+    if o.workspace is None:
+        o.workspace = torch.empty(max(int(lib().mge_bwd_workspace_bytes(C.byref(a))), 256), device=dev,
+                                  dtype=torch.uint8)
+    a.workspace, a.workspace_bytes = _ptr(o.workspace), o.workspace.numel()
+    _check(lib().grouped_mlp_bwd(C.byref(a), _stream(dev)), "grouped_mlp_bwd")
+    return o
+
+
+# ------------------------------------------------------------------------------ combine
+
+def unpermute_combine(inp: torch.Tensor, perm_pos: torch.Tensor, weights: Optional[torch.Tensor] = None,
+                      out_dtype: str = "bf16", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    T, k = perm_pos.shape
+    H = inp.shape[1]
+    dev = inp.device
+    if out is None:
+        out = torch.empty((T, H), device=dev, dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32)
+    a = CombineArgs()
+    a.struct_size = C.sizeof(CombineArgs)
+    a.T, a.k, a.H = T, k, H
+    a.in_dtype = DTYPE["bf16"] if inp.dtype == torch.bfloat16 else DTYPE["f32"]
+    a.out_dtype = DTYPE["bf16"] if out.dtype == torch.bfloat16 else DTYPE["f32"]
+    a.in_, a.perm_pos, a.weights, a.out = _ptr(inp), _ptr(perm_pos), _ptr(weights), _ptr(out)
+    _check(lib().unpermute_combine(C.byref(a), _stream(dev)), "unpermute_combine")
+    return out

@@ -1,0 +1,516 @@
+// C ABI entry points: argument checks, workspace carving and the launch sequence of
+// each call.  Every check runs before the first launch; nothing here synchronizes
+// except mge_check_device_errors.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "mge_common.hpp"
+#include "mge_internal.hpp"
+
+namespace mge {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+mge_status hip_check(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("%s: %s", what, hipGetErrorString(e));
+    return MGE_ERR_HIP;
+  }
+  return MGE_OK;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+static bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+static size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Bump allocator over the caller's workspace.
+struct Carve {
+  uint8_t* base;
+  size_t used = 0;
+  explicit Carve(void* b) : base(static_cast<uint8_t*>(b)) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + used : nullptr;
+    used += up256(bytes);
+    return p;
+  }
+};
+
+static mge_status check_common(int T, int E, int k, int H, int align) {
+  MGE_REQUIRE(T >= 0, "T must be >= 0 (got %d)", T);
+  MGE_REQUIRE(E >= 1 && E <= 256, "E must be in [1, 256] (got %d)", E);
+  MGE_REQUIRE(k >= 1 && k <= 8 && k <= E, "k must be in [1, min(E, 8)] (got k=%d, E=%d)", k, E);
+  MGE_REQUIRE(H >= 32 && H % 32 == 0, "H must be a positive multiple of 32 (got %d)", H);
+  MGE_REQUIRE(pow2(align) && align <= 256, "align must be a power of two in [1, 256] (got %d)", align);
+  return MGE_OK;
+}
+
+}  // namespace mge
+
+using namespace mge;
+
+extern "C" {
+
+int64_t mge_perm_rows(int32_t T, int32_t k, int32_t E, int32_t align) {
+  int64_t n = int64_t(T) * k + int64_t(E) * (align - 1);
+  return (n + 31) / 32 * 32;
+}
+
+const char* mge_status_string(mge_status s) {
+  switch (s) {
+    case MGE_OK: return "MGE_OK";
+    case MGE_ERR_INVALID_ARG: return "MGE_ERR_INVALID_ARG";
+    case MGE_ERR_UNSUPPORTED: return "MGE_ERR_UNSUPPORTED";
+    case MGE_ERR_WORKSPACE: return "MGE_ERR_WORKSPACE";
+    case MGE_ERR_HIP: return "MGE_ERR_HIP";
+    case MGE_ERR_DEVICE_CHECK: return "MGE_ERR_DEVICE_CHECK";
+  }
+  return "MGE_ERR_UNKNOWN";
+}
+
+const char* mge_last_error(void) { return g_err; }
+
+const char* mge_version(void) { return "0.1.0"; }
+
+// ------------------------------------------------------------------ routing
+static int route_nblk(int T) { return (T + 255) / 256; }
+
+size_t mge_route_workspace_bytes(int32_t T, int32_t E) {
+  if (T < 0 || E < 1) return 0;
+  return up256(256) + up256(size_t(route_nblk(T)) * E * sizeof(int32_t));
+}
+
+mge_status moe_route_permute(const mge_route_args* a, void* stream) {
+  g_err[0] = 0;
+  MGE_REQUIRE(a != nullptr, "args is NULL");
+  MGE_REQUIRE(a->struct_size == sizeof(mge_route_args), "struct_size mismatch (%u vs %zu)", a->struct_size,
+              sizeof(mge_route_args));
+  mge_status st = check_common(a->T, a->E, a->k, a->H, a->align);
+  if (st != MGE_OK) return st;
+  MGE_REQUIRE(a->prec == MGE_PREC_BF16 || a->prec == MGE_PREC_MXFP8, "prec must be BF16 or MXFP8");
+  const bool given = (a->flags & MGE_ROUTE_PROB_GIVEN) != 0;
+  const bool want_col = (a->flags & MGE_ROUTE_WANT_COL) != 0;
+  MGE_REQUIRE((a->flags & ~uint32_t(MGE_ROUTE_PROB_GIVEN | MGE_ROUTE_WANT_COL)) == 0, "unknown flags 0x%x", a->flags);
+  MGE_REQUIRE(given || a->logits, "logits is NULL");
+  MGE_REQUIRE(a->topk_idx && a->topk_prob && a->split_sizes && a->group_offsets && a->perm_src && a->perm_pos &&
+                  a->prob_perm,
+              "an output map pointer is NULL");
+  if (a->x) {
+    MGE_REQUIRE(aligned16(a->x), "x must be 16-byte aligned");
+    MGE_REQUIRE(a->x_perm && aligned16(a->x_perm), "x_perm must be non-NULL and 16-byte aligned");
+    if (a->prec == MGE_PREC_MXFP8) MGE_REQUIRE(a->x_perm_scale, "x_perm_scale is NULL");
+    if (want_col) {
+      MGE_REQUIRE(a->x_col && aligned16(a->x_col), "x_col must be non-NULL and 16-byte aligned");
+      if (a->prec == MGE_PREC_MXFP8) {
+        MGE_REQUIRE(a->x_col_scale, "x_col_scale is NULL");
+        MGE_REQUIRE(a->align % 32 == 0, "the MXFP8 column form needs align %% 32 == 0 (got %d)", a->align);
+      }
+    }
+  }
+  const size_t need = mge_route_workspace_bytes(a->T, a->E);
+  if (!a->workspace || a->workspace_bytes < need) {
+    set_error("route workspace needs %zu bytes (got %zu)", need, a->workspace_bytes);
+    return MGE_ERR_WORKSPACE;
+  }
+  if (a->T == 0) return MGE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int R = int(mge_perm_rows(a->T, a->k, a->E, a->align));
+  Carve ws(a->workspace);
+  RouteParams p{};
+  p.T = a->T; p.E = a->E; p.k = a->k; p.align = a->align;
+  p.nblk = route_nblk(a->T);
+  int nb = 1;
+  while ((1 << nb) <= a->E) ++nb;   // bits to tell the E experts and the sentinel E apart
+  p.nbits = nb;
+  p.flags = a->flags;
+  p.logits = a->logits;
+  p.topk_idx = a->topk_idx; p.topk_prob = a->topk_prob;
+  p.split_sizes = a->split_sizes; p.group_offsets = a->group_offsets;
+  p.perm_src = a->perm_src; p.perm_pos = a->perm_pos; p.prob_perm = a->prob_perm;
+  p.err_flag = static_cast<int32_t*>(ws.take(256));
+  p.block_counts = static_cast<int32_t*>(ws.take(size_t(p.nblk) * a->E * 4));
+  p.R = R;
+  st = launch_route(p, s);
+  if (st != MGE_OK || !a->x) return st;
+  QuantTileParams q{};
+  q.in = a->x; q.in_batch_stride = 0; q.in_row_stride = a->H;
+  q.gather = a->perm_src;
+  q.batch = 1; q.R = R; q.C = a->H; q.Rp = R;
+  if (a->prec == MGE_PREC_MXFP8) {
+    q.row_codes = static_cast<uint8_t*>(a->x_perm);
+    q.row_scales = a->x_perm_scale;
+    if (want_col) { q.col_codes = static_cast<uint8_t*>(a->x_col); q.col_scales = a->x_col_scale; }
+  } else {
+    q.row_bf16 = static_cast<uint16_t*>(a->x_perm);
+    if (want_col) q.col_bf16 = static_cast<uint16_t*>(a->x_col);
+  }
+  return launch_quant_tile(q, a->prec == MGE_PREC_MXFP8, s);
+}
+
+// ------------------------------------------------------------------ quantize
+mge_status mxfp8_quantize(const mge_quant_args* a, void* stream) {
+  g_err[0] = 0;
+  MGE_REQUIRE(a != nullptr, "args is NULL");
+  MGE_REQUIRE(a->struct_size == sizeof(mge_quant_args), "struct_size mismatch");
+  MGE_REQUIRE(a->batch >= 0 && a->R >= 0 && a->C >= 0, "negative size");
+  MGE_REQUIRE(a->C % 32 == 0, "C must be a multiple of 32 (got %d)", a->C);
+  MGE_REQUIRE(a->orient != 0 && (a->orient & ~3u) == 0, "orient must be ROW, COL or ROW|COL");
+  MGE_REQUIRE(a->in && aligned16(a->in), "in must be non-NULL and 16-byte aligned");
+  MGE_REQUIRE(a->in_row_stride >= a->C && a->in_row_stride % 8 == 0, "in_row_stride must be >= C and a multiple of 8");
+  MGE_REQUIRE(a->batch <= 1 || (a->in_batch_stride % 8 == 0 && a->in_batch_stride >= int64_t(a->R) * a->in_row_stride),
+              "in_batch_stride too small or not a multiple of 8");
+  if (a->orient & MGE_ORIENT_ROW)
+    MGE_REQUIRE(a->row_codes && a->row_scales && aligned16(a->row_codes), "row outputs missing or misaligned");
+  if (a->orient & MGE_ORIENT_COL)
+    MGE_REQUIRE(a->col_codes && a->col_scales && aligned16(a->col_codes), "column outputs missing or misaligned");
+  if (a->batch == 0 || a->R == 0 || a->C == 0) return MGE_OK;
+  QuantTileParams q{};
+  q.in = a->in; q.in_batch_stride = a->in_batch_stride; q.in_row_stride = a->in_row_stride;
+  q.batch = a->batch; q.R = a->R; q.C = a->C; q.Rp = (a->R + 31) / 32 * 32;
+  if (a->orient & MGE_ORIENT_ROW) { q.row_codes = a->row_codes; q.row_scales = a->row_scales; }
+  if (a->orient & MGE_ORIENT_COL) { q.col_codes = a->col_codes; q.col_scales = a->col_scales; }
+  return launch_quant_tile(q, true, static_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------------------------ forward
+static mge_status check_mlp_dims(int prec, int E, int H, int F, int T, int k, int align) {
+  mge_status st = check_common(T, E, k, H, align);
+  if (st != MGE_OK) return st;
+  MGE_REQUIRE(prec == MGE_PREC_BF16 || prec == MGE_PREC_MXFP8, "prec must be BF16 or MXFP8");
+  MGE_REQUIRE(F >= 32 && F % 32 == 0, "F must be a positive multiple of 32 (got %d)", F);
+  return MGE_OK;
+}
+
+static size_t fwd_ws(const mge_fwd_args* a, int R) {
+  size_t n = up256(4 * size_t(a->E) * sizeof(void*));
+  if (!a->h) {
+    if (a->prec == MGE_PREC_MXFP8) n += up256(size_t(R) * a->F) + up256(size_t(R) * (a->F / 32));
+    else n += up256(size_t(R) * a->F * 2);
+  }
+  return n;
+}
+
+size_t mge_fwd_workspace_bytes(const mge_fwd_args* a) {
+  if (!a || a->E < 1 || a->T < 0 || a->k < 1 || a->align < 1) return 0;
+  return fwd_ws(a, int(mge_perm_rows(a->T, a->k, a->E, a->align)));
+}
+
+mge_status grouped_mlp_fwd(const mge_fwd_args* a, void* stream) {
+  g_err[0] = 0;
+  MGE_REQUIRE(a != nullptr, "args is NULL");
+  MGE_REQUIRE(a->struct_size == sizeof(mge_fwd_args), "struct_size mismatch");
+  mge_status st = check_mlp_dims(a->prec, a->E, a->H, a->F, a->T, a->k, a->align);
+  if (st != MGE_OK) return st;
+  const bool mx = a->prec == MGE_PREC_MXFP8;
+  const bool train = a->saved_gu != nullptr;
+  MGE_REQUIRE(a->split_sizes && a->group_offsets && a->prob_perm, "split_sizes / group_offsets / prob_perm NULL");
+  MGE_REQUIRE(a->x_perm && aligned16(a->x_perm), "x_perm must be non-NULL and 16-byte aligned");
+  MGE_REQUIRE(!mx || a->x_perm_scale, "x_perm_scale is NULL");
+  MGE_REQUIRE(a->w_gate_up && a->w_down, "weight pointer arrays are NULL");
+  MGE_REQUIRE(!mx || (a->w_gate_up_scale && a->w_down_scale), "weight scale pointer arrays are NULL");
+  for (int e = 0; e < a->E; ++e) {
+    MGE_REQUIRE(a->w_gate_up[e] && aligned16(a->w_gate_up[e]), "w_gate_up[%d] NULL or misaligned", e);
+    MGE_REQUIRE(a->w_down[e] && aligned16(a->w_down[e]), "w_down[%d] NULL or misaligned", e);
+    if (mx) MGE_REQUIRE(a->w_gate_up_scale[e] && a->w_down_scale[e], "weight scales of expert %d NULL", e);
+  }
+  MGE_REQUIRE(a->y_dtype == MGE_DTYPE_BF16 || a->y_dtype == MGE_DTYPE_F32, "y_dtype must be BF16 or F32");
+  MGE_REQUIRE(a->y_perm && aligned16(a->y_perm), "y_perm must be non-NULL and 16-byte aligned");
+  if (a->h) MGE_REQUIRE(aligned16(a->h) && (!mx || a->h_scale), "h misaligned or h_scale NULL");
+  if (train) {
+    MGE_REQUIRE(a->h_col && aligned16(a->h_col), "training needs h_col (16-byte aligned)");
+    MGE_REQUIRE(!mx || a->h_col_scale, "h_col_scale is NULL");
+    MGE_REQUIRE(a->align % 32 == 0, "training (column form of h) needs align %% 32 == 0 (got %d)", a->align);
+  }
+  const int R = int(mge_perm_rows(a->T, a->k, a->E, a->align));
+  const size_t need = fwd_ws(a, R);
+  if (!a->workspace || a->workspace_bytes < need) {
+    set_error("forward workspace needs %zu bytes (got %zu)", need, a->workspace_bytes);
+    return MGE_ERR_WORKSPACE;
+  }
+  if (a->T == 0) return MGE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carve ws(a->workspace);
+  void** tab = static_cast<void**>(ws.take(4 * size_t(a->E) * sizeof(void*)));
+  void* h = a->h;
+  uint8_t* hs = a->h_scale;
+  if (!h) {
+    if (mx) { h = ws.take(size_t(R) * a->F); hs = static_cast<uint8_t*>(ws.take(size_t(R) * (a->F / 32))); }
+    else h = ws.take(size_t(R) * a->F * 2);
+  }
+  const int E = a->E;
+  st = launch_upload_ptrs(reinterpret_cast<const void* const*>(a->w_gate_up), E, tab, s);
+  if (st != MGE_OK) return st;
+  st = launch_upload_ptrs(reinterpret_cast<const void* const*>(a->w_down), E, tab + E, s);
+  if (st != MGE_OK) return st;
+  if (mx) {
+    st = launch_upload_ptrs(reinterpret_cast<const void* const*>(a->w_gate_up_scale), E, tab + 2 * E, s);
+    if (st != MGE_OK) return st;
+    st = launch_upload_ptrs(reinterpret_cast<const void* const*>(a->w_down_scale), E, tab + 3 * E, s);
+    if (st != MGE_OK) return st;
+  }
+  const int64_t rows_bound = int64_t(a->T) * a->k;
+  const int elem = mx ? 1 : 2;
+
+  GemmParams g{};
+  g.mode = RAGGED_M; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
+  g.A = static_cast<const uint8_t*>(a->x_perm); g.lda = int64_t(a->H) * elem;
+  g.As = a->x_perm_scale; g.ldas = a->H / 32;
+  g.Bt = reinterpret_cast<const uint8_t* const*>(tab);
+  g.Bst = reinterpret_cast<const uint8_t* const*>(tab + 2 * E);
+  g.ldb = int64_t(a->H) * elem; g.ldbs = a->H / 32;
+  g.N = 2 * a->F; g.K = a->H; g.F = a->F;
+  g.prob = a->prob_perm;
+  if (mx) { g.h_codes = static_cast<uint8_t*>(h); g.h_scales = hs; }
+  else g.h_bf16 = static_cast<uint16_t*>(h);
+  if (train) {
+    g.saved_gu = a->saved_gu;
+    if (mx) { g.hc_codes = static_cast<uint8_t*>(a->h_col); g.hc_scales = a->h_col_scale; }
+    else g.hc_bf16 = static_cast<uint16_t*>(a->h_col);
+  }
+  g.Rp = R;
+  g.tiles_upper = gemm_tiles_upper(g, rows_bound);
+  st = launch_gemm(g, a->prec, EPI_SWIGLU, s);
+  if (st != MGE_OK) return st;
+
+  GemmParams d{};
+  d.mode = RAGGED_M; d.E = E; d.sizes = a->split_sizes; d.offs = a->group_offsets;
+  d.A = static_cast<const uint8_t*>(h); d.lda = int64_t(a->F) * elem;
+  d.As = hs; d.ldas = a->F / 32;
+  d.Bt = reinterpret_cast<const uint8_t* const*>(tab + E);
+  d.Bst = reinterpret_cast<const uint8_t* const*>(tab + 3 * E);
+  d.ldb = int64_t(a->F) * elem; d.ldbs = a->F / 32;
+  d.N = a->H; d.K = a->F;
+  d.out_dtype = a->y_dtype; d.C = a->y_perm; d.ldc = a->H;
+  d.tiles_upper = gemm_tiles_upper(d, rows_bound);
+  return launch_gemm(d, a->prec, EPI_STORE, s);
+}
+
+// ------------------------------------------------------------------ backward
+static size_t bwd_ws(const mge_bwd_args* a, int R, int nparts) {
+  const bool mx = a->prec == MGE_PREC_MXFP8;
+  const size_t H = a->H, F = a->F, E = a->E, F2 = 2 * F;
+  size_t n = up256(6 * E * sizeof(void*));
+  n += up256(size_t(R) * nparts * sizeof(float));
+  auto mat = [&](size_t rows, size_t cols) {
+    return mx ? up256(rows * cols) + up256(rows * (cols / 32)) : up256(rows * cols * 2);
+  };
+  if (!a->dy_row) n += mat(R, H);
+  if (!a->dy_col) n += mat(H, R);
+  if (!a->dgu_row) n += mat(R, F2);
+  if (!a->dgu_col) n += mat(F2, R);
+  if (!mx) n += E * (up256(F * H * 2) + up256(H * F2 * 2));   // bf16 transposed weights
+  return n;
+}
+
+size_t mge_bwd_workspace_bytes(const mge_bwd_args* a) {
+  if (!a || a->E < 1 || a->T < 0 || a->k < 1 || a->align < 1 || a->F < 32) return 0;
+  return bwd_ws(a, int(mge_perm_rows(a->T, a->k, a->E, a->align)), gemm_swiglu_bwd_nparts(a->F));
+}
+
+mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
+  g_err[0] = 0;
+  MGE_REQUIRE(a != nullptr, "args is NULL");
+  MGE_REQUIRE(a->struct_size == sizeof(mge_bwd_args), "struct_size mismatch");
+  mge_status st = check_mlp_dims(a->prec, a->E, a->H, a->F, a->T, a->k, a->align);
+  if (st != MGE_OK) return st;
+  const bool mx = a->prec == MGE_PREC_MXFP8;
+  MGE_REQUIRE(a->align % 32 == 0, "the backward (column forms along tokens) needs align %% 32 == 0 (got %d)",
+              a->align);
+  MGE_REQUIRE(a->dy && aligned16(a->dy), "dy must be non-NULL and 16-byte aligned");
+  MGE_REQUIRE(a->split_sizes && a->group_offsets && a->perm_src && a->perm_pos && a->prob_perm,
+              "routing maps are NULL");
+  MGE_REQUIRE(a->saved_gu, "saved_gu is NULL");
+  MGE_REQUIRE(a->h_col && aligned16(a->h_col) && a->x_col && aligned16(a->x_col), "h_col / x_col NULL or misaligned");
+  MGE_REQUIRE(!mx || (a->h_col_scale && a->x_col_scale), "h_col_scale / x_col_scale NULL");
+  MGE_REQUIRE(a->w_gate_up && a->w_down, "weight pointer arrays are NULL");
+  MGE_REQUIRE(!mx || (a->w_gate_up_scale && a->w_down_scale), "weight scale arrays are NULL");
+  MGE_REQUIRE(a->dw_gate_up && a->dw_down, "dW pointer arrays are NULL");
+  for (int e = 0; e < a->E; ++e) {
+    MGE_REQUIRE(a->w_gate_up[e] && aligned16(a->w_gate_up[e]), "w_gate_up[%d] NULL or misaligned", e);
+    MGE_REQUIRE(a->w_down[e] && aligned16(a->w_down[e]), "w_down[%d] NULL or misaligned", e);
+    if (mx) MGE_REQUIRE(a->w_gate_up_scale[e] && a->w_down_scale[e], "weight scales of expert %d NULL", e);
+    MGE_REQUIRE(a->dw_gate_up[e] && a->dw_down[e], "dW outputs of expert %d NULL", e);
+  }
+  MGE_REQUIRE(a->dx_perm && aligned16(a->dx_perm) && a->d_prob, "dx_perm / d_prob NULL or misaligned");
+  auto opt_ok = [&](void* c, uint8_t* s) { return !c || (aligned16(c) && (!mx || s)); };
+  MGE_REQUIRE(opt_ok(a->dy_row, a->dy_row_scale) && opt_ok(a->dy_col, a->dy_col_scale) &&
+                  opt_ok(a->dgu_row, a->dgu_row_scale) && opt_ok(a->dgu_col, a->dgu_col_scale),
+              "an optional intermediate is misaligned or lacks its scales");
+  const int R = int(mge_perm_rows(a->T, a->k, a->E, a->align));
+  const int nparts = gemm_swiglu_bwd_nparts(a->F);
+  const size_t need = bwd_ws(a, R, nparts);
+  if (!a->workspace || a->workspace_bytes < need) {
+    set_error("backward workspace needs %zu bytes (got %zu)", need, a->workspace_bytes);
+    return MGE_ERR_WORKSPACE;
+  }
+  if (a->T == 0) return MGE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int E = a->E, H = a->H, F = a->F, F2 = 2 * F;
+  const int elem = mx ? 1 : 2;
+  Carve ws(a->workspace);
+  void** tab = static_cast<void**>(ws.take(6 * size_t(E) * sizeof(void*)));
+  float* part = static_cast<float*>(ws.take(size_t(R) * nparts * sizeof(float)));
+  auto mat = [&](void* given, uint8_t* given_s, size_t rows, size_t cols, void** c, uint8_t** sc) {
+    if (given) { *c = given; *sc = given_s; return; }
+    if (mx) { *c = ws.take(rows * cols); *sc = static_cast<uint8_t*>(ws.take(rows * (cols / 32))); }
+    else { *c = ws.take(rows * cols * 2); *sc = nullptr; }
+  };
+  void *dyr, *dyc, *dgr, *dgc;
+  uint8_t *dyrs, *dycs, *dgrs, *dgcs;
+  mat(a->dy_row, a->dy_row_scale, R, H, &dyr, &dyrs);
+  mat(a->dy_col, a->dy_col_scale, H, R, &dyc, &dycs);
+  mat(a->dgu_row, a->dgu_row_scale, R, F2, &dgr, &dgrs);
+  mat(a->dgu_col, a->dgu_col_scale, F2, R, &dgc, &dgcs);
+
+  // weights in the K-contiguous orientation each GEMM reads
+  const void* const* wd_k;     // [F][H] per expert (dh GEMM)
+  const void* const* wgu_k;    // [H][2F] per expert (dX GEMM)
+  std::vector<const void*> wd_t, wgu_t;
+  if (mx) {
+    wd_k = a->w_down;
+    wgu_k = a->w_gate_up;
+  } else {
+    wd_t.resize(E); wgu_t.resize(E);
+    for (int e = 0; e < E; ++e) {
+      uint16_t* t1 = static_cast<uint16_t*>(ws.take(size_t(F) * H * 2));
+      uint16_t* t2 = static_cast<uint16_t*>(ws.take(size_t(H) * F2 * 2));
+      QuantTileParams q{};
+      q.in = static_cast<const uint16_t*>(a->w_down[e]); q.in_row_stride = F;
+      q.batch = 1; q.R = H; q.C = F; q.Rp = H; q.col_bf16 = t1;
+      st = launch_quant_tile(q, false, s);
+      if (st != MGE_OK) return st;
+      QuantTileParams q2{};
+      q2.in = static_cast<const uint16_t*>(a->w_gate_up[e]); q2.in_row_stride = H;
+      q2.batch = 1; q2.R = F2; q2.C = H; q2.Rp = F2; q2.col_bf16 = t2;
+      st = launch_quant_tile(q2, false, s);
+      if (st != MGE_OK) return st;
+      wd_t[e] = t1; wgu_t[e] = t2;
+    }
+    wd_k = wd_t.data();
+    wgu_k = wgu_t.data();
+  }
+  st = launch_upload_ptrs(wd_k, E, tab, s);
+  if (st == MGE_OK) st = launch_upload_ptrs(wgu_k, E, tab + E, s);
+  if (st == MGE_OK && mx) st = launch_upload_ptrs(reinterpret_cast<const void* const*>(a->w_down_scale), E, tab + 2 * E, s);
+  if (st == MGE_OK && mx) st = launch_upload_ptrs(reinterpret_cast<const void* const*>(a->w_gate_up_scale), E, tab + 3 * E, s);
+  if (st == MGE_OK) st = launch_upload_ptrs(reinterpret_cast<const void* const*>(a->dw_down), E, tab + 4 * E, s);
+  if (st == MGE_OK) st = launch_upload_ptrs(reinterpret_cast<const void* const*>(a->dw_gate_up), E, tab + 5 * E, s);
+  if (st != MGE_OK) return st;
+
+  // b1: dy gathered by perm_src, row form (along H) and column form (along tokens)
+  {
+    QuantTileParams q{};
+    q.in = a->dy; q.in_row_stride = H; q.gather = a->perm_src;
+    q.batch = 1; q.R = R; q.C = H; q.Rp = R;
+    if (mx) { q.row_codes = static_cast<uint8_t*>(dyr); q.row_scales = dyrs; q.col_codes = static_cast<uint8_t*>(dyc); q.col_scales = dycs; }
+    else { q.row_bf16 = static_cast<uint16_t*>(dyr); q.col_bf16 = static_cast<uint16_t*>(dyc); }
+    st = launch_quant_tile(q, mx, s);
+    if (st != MGE_OK) return st;
+  }
+  const int64_t rows_bound = int64_t(a->T) * a->k;
+  // b2: dh = dY W_down with the SwiGLU backward + d_prob partial epilogue
+  {
+    GemmParams g{};
+    g.mode = RAGGED_M; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
+    g.A = static_cast<const uint8_t*>(dyr); g.lda = int64_t(H) * elem; g.As = dyrs; g.ldas = H / 32;
+    g.Bt = reinterpret_cast<const uint8_t* const*>(tab);
+    g.Bst = reinterpret_cast<const uint8_t* const*>(tab + 2 * E);
+    g.ldb = int64_t(H) * elem; g.ldbs = H / 32;
+    g.N = F; g.K = H; g.F = F;
+    g.prob = a->prob_perm; g.gu = a->saved_gu;
+    if (mx) { g.dgu_codes = static_cast<uint8_t*>(dgr); g.dgu_scales = dgrs; g.dguc_codes = static_cast<uint8_t*>(dgc); g.dguc_scales = dgcs; }
+    else { g.dgu_bf16 = static_cast<uint16_t*>(dgr); g.dguc_bf16 = static_cast<uint16_t*>(dgc); }
+    g.dprob_part = part; g.nparts = nparts; g.Rp = R;
+    g.tiles_upper = gemm_tiles_upper(g, rows_bound);
+    st = launch_gemm(g, a->prec, EPI_SWIGLU_BWD, s);
+    if (st != MGE_OK) return st;
+  }
+  // b3: d_prob
+  st = launch_dprob_reduce(a->T, a->k, nparts, part, a->perm_pos, a->d_prob, s);
+  if (st != MGE_OK) return st;
+  // b4: dW_down[e] = dY_e^T h_e  (K = tokens of e)
+  {
+    GemmParams g{};
+    g.mode = RAGGED_K; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
+    g.A = static_cast<const uint8_t*>(dyc); g.lda = int64_t(R) * elem; g.As = dycs; g.ldas = R / 32;
+    g.B = static_cast<const uint8_t*>(a->h_col); g.Bs = a->h_col_scale; g.ldb = int64_t(R) * elem; g.ldbs = R / 32;
+    g.M = H; g.N = F;
+    g.out_dtype = MGE_DTYPE_F32; g.Ct = reinterpret_cast<void* const*>(tab + 4 * E); g.ldc = F;
+    g.accumulate = a->accumulate;
+    g.tiles_upper = gemm_tiles_upper(g, rows_bound);
+    st = launch_gemm(g, a->prec, EPI_STORE, s);
+    if (st != MGE_OK) return st;
+  }
+  // b5: dX = dGU W_gate_up  (K = 2F)
+  {
+    GemmParams g{};
+    g.mode = RAGGED_M; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
+    g.A = static_cast<const uint8_t*>(dgr); g.lda = int64_t(F2) * elem; g.As = dgrs; g.ldas = F2 / 32;
+    g.Bt = reinterpret_cast<const uint8_t* const*>(tab + E);
+    g.Bst = reinterpret_cast<const uint8_t* const*>(tab + 3 * E);
+    g.ldb = int64_t(F2) * elem; g.ldbs = F2 / 32;
+    g.N = H; g.K = F2;
+    g.out_dtype = MGE_DTYPE_BF16; g.C = a->dx_perm; g.ldc = H;
+    g.tiles_upper = gemm_tiles_upper(g, rows_bound);
+    st = launch_gemm(g, a->prec, EPI_STORE, s);
+    if (st != MGE_OK) return st;
+  }
+  // b6: dW_gate_up[e] = dGU_e^T X_e  (K = tokens of e)
+  {
+    GemmParams g{};
+    g.mode = RAGGED_K; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
+    g.A = static_cast<const uint8_t*>(dgc); g.lda = int64_t(R) * elem; g.As = dgcs; g.ldas = R / 32;
+    g.B = static_cast<const uint8_t*>(a->x_col); g.Bs = a->x_col_scale; g.ldb = int64_t(R) * elem; g.ldbs = R / 32;
+    g.M = F2; g.N = H;
+    g.out_dtype = MGE_DTYPE_F32; g.Ct = reinterpret_cast<void* const*>(tab + 5 * E); g.ldc = H;
+    g.accumulate = a->accumulate;
+    g.tiles_upper = gemm_tiles_upper(g, rows_bound);
+    st = launch_gemm(g, a->prec, EPI_STORE, s);
+  }
+  return st;
+}
+
+// ------------------------------------------------------------------ combine
+mge_status unpermute_combine(const mge_combine_args* a, void* stream) {
+  g_err[0] = 0;
+  MGE_REQUIRE(a != nullptr, "args is NULL");
+  MGE_REQUIRE(a->struct_size == sizeof(mge_combine_args), "struct_size mismatch");
+  MGE_REQUIRE(a->T >= 0 && a->k >= 1 && a->k <= 8, "T must be >= 0 and k in [1, 8]");
+  MGE_REQUIRE(a->H >= 32 && a->H % 32 == 0, "H must be a positive multiple of 32");
+  MGE_REQUIRE((a->in_dtype == MGE_DTYPE_BF16 || a->in_dtype == MGE_DTYPE_F32) &&
+                  (a->out_dtype == MGE_DTYPE_BF16 || a->out_dtype == MGE_DTYPE_F32),
+              "dtypes must be BF16 or F32");
+  MGE_REQUIRE(a->in && aligned16(a->in) && a->out && aligned16(a->out) && a->perm_pos,
+              "in / out / perm_pos NULL or misaligned");
+  return launch_combine(a->T, a->k, a->H, a->in_dtype, a->out_dtype, a->in, a->perm_pos, a->weights, a->out,
+                        static_cast<hipStream_t>(stream));
+}
+
+mge_status mge_check_device_errors(void* route_workspace, void* stream) {
+  g_err[0] = 0;
+  MGE_REQUIRE(route_workspace != nullptr, "workspace is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t flag = 0;
+  if (hipStreamSynchronize(s) != hipSuccess) return hip_check("hipStreamSynchronize");
+  if (hipMemcpy(&flag, route_workspace, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess)
+    return hip_check("hipMemcpy");
+  if (flag != 0) {
+    int32_t zero = 0;
+    hipMemcpy(route_workspace, &zero, sizeof(zero), hipMemcpyHostToDevice);
+    set_error("a kernel flagged invalid data (expert index outside [0, E))");
+    return MGE_ERR_DEVICE_CHECK;
+  }
+  return MGE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,622 @@
+// Persistent grouped GEMM for gfx950: C_e = A_e B_e^T for every expert in one launch.
+//
+// Both operands are K-contiguous ("NT"): row forms along K for the forward and dX
+// GEMMs, column forms (transposed, blocks along tokens) for the weight gradients.
+//   RAGGED_M: expert e owns rows [off[e], off[e] + sizes[e]) of a shared A and of the
+//             output; B is the expert's own weight (pointer table).  (gate-up, down,
+//             dh, dX)
+//   RAGGED_K: the reduction runs over expert e's tokens, the column span
+//             [off[e], off[e] + roundup32(sizes[e])) of shared A and B; the output is
+//             the expert's own [M][N] gradient.  (dW_down, dW_gate_up)
+// Tiles are 256 x 256 with 128-byte K slices (128 FP8 or 64 BF16 elements), 4 waves in
+// a 2 x 2 grid, each wave 128 x 128 built from 32 x 32 MFMA blocks:
+//   MXFP8: v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, one E8M0 scale per lane and
+//          32-element K block, applied by the matrix core — no dequantize pass)
+//   BF16:  v_mfma_f32_32x32x16_bf16
+// Operand tiles go HBM -> registers -> LDS (double-buffered, XOR-swizzled 16-byte
+// chunks so both the row-wise stores and the MFMA fragment reads are bank-conflict
+// free); the next K slice is fetched while the current one is multiplied.
+// A persistent grid walks the tiles (expert-major, then N, M fastest so that
+// consecutive tiles share the weight tile); virtual workgroup ids are remapped so
+// that the workgroups of one XCD (hardware dispatches round-robin over the 8 XCDs)
+// take consecutive tiles and share that XCD's L2.  Empty experts own no tiles (RAGGED_M)
+// or produce zero gradients (RAGGED_K).
+// Epilogues (fp32 accumulators never reach HBM):
+//   EPI_STORE       bf16 / f32 store (optionally accumulate), row masking
+//   EPI_SWIGLU      h = p * silu(G) * U with G, U of the same rows/columns in the same
+//                   lane; h quantized along F (MXFP8, amax over the 32 lanes that hold
+//                   one 32-column block) or rounded to bf16; training also stores G, U
+//                   (bf16) and the column form of h (blocks of 32 rows: 16 in a lane,
+//                   16 in its partner lane 32 apart)
+//   EPI_SWIGLU_BWD  dh -> dG, dU (with saved G, U, p) quantized row- and column-wise,
+//                   plus per-row partial sums of dh * silu(G) * U for d_prob
+#include "mge_common.hpp"
+#include "mge_internal.hpp"
+
+#include <type_traits>
+
+namespace mge {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int G_WAVES_M = 2;
+constexpr int G_WAVES_N = 2;
+constexpr int G_WMB = 4;   // 32-row MFMA blocks per wave (M)
+constexpr int G_WNB = 4;   // 32-col MFMA blocks per wave (N)
+constexpr int G_BM = G_WAVES_M * G_WMB * 32;
+constexpr int G_BN = G_WAVES_N * G_WNB * 32;
+constexpr int G_BKB = 128;                    // K bytes per slice
+constexpr int G_THREADS = 64 * G_WAVES_M * G_WAVES_N;
+constexpr int G_STAGE_BYTES = (G_BM + G_BN) * G_BKB;
+constexpr int G_LDS_BYTES = 2 * G_STAGE_BYTES;
+constexpr int G_MAXE = 256;
+
+static_assert(G_THREADS == 256, "loader assumes 256 threads");
+
+// Compile-time loop: the body sees its index as a constant expression, so register
+// arrays (the accumulators) are never indexed dynamically.
+template <int I, int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+  if constexpr (I < N) {
+    fn(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(fn);
+  }
+}
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * G_BKB + ((chunk ^ (row & 7)) << 4); }
+
+struct TileInfo {
+  int e, mt, nt;
+  int m_valid;          // rows of the tile's group (RAGGED_M) or M (RAGGED_K)
+  int row_off;          // first permuted row of the group (RAGGED_M) / K offset (RAGGED_K)
+  int k_len;            // reduction length in elements
+};
+
+template <bool MX, int EPI>
+__global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int32_t s_prefix[G_MAXE + 1];
+  __shared__ int32_t s_mtiles[G_MAXE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / G_WAVES_N;
+  const int wn = wave % G_WAVES_N;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  constexpr int ELEM = MX ? 1 : 2;           // bytes per element
+
+  // ---- tile table: tiles of expert e = mtiles(e) * ntiles
+  const int ncols_per_tile = (EPI == EPI_SWIGLU) ? G_BN / 2 : G_BN;
+  const int ncols = (EPI == EPI_SWIGLU) ? p.F : p.N;
+  const int ntiles = (ncols + ncols_per_tile - 1) / ncols_per_tile;
+  if (tid == 0) {
+    int acc = 0;
+    for (int e = 0; e < p.E; ++e) {
+      int mt = p.mode == RAGGED_M ? (p.sizes[e] + G_BM - 1) / G_BM : (p.M + G_BM - 1) / G_BM;
+      s_prefix[e] = acc;
+      s_mtiles[e] = mt;
+      acc += mt * ntiles;
+    }
+    s_prefix[p.E] = acc;
+  }
+  __syncthreads();
+  const int total = s_prefix[p.E];
+  const int nwg = gridDim.x;
+  int vid = blockIdx.x;
+  if ((nwg & 7) == 0) vid = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+
+  for (int tile = vid; tile < total; tile += nwg) {
+    // ---- decode the tile
+    int lo = 0, hi_ = p.E - 1;
+    while (lo < hi_) {
+      int mid = (lo + hi_ + 1) >> 1;
+      if (s_prefix[mid] <= tile) lo = mid; else hi_ = mid - 1;
+    }
+    const int e = lo;
+    const int local = tile - s_prefix[e];
+    const int mtn = s_mtiles[e];
+    const int mt = local % mtn;
+    const int nt = local / mtn;
+    const int off = p.offs[e];
+    const int m_valid = p.mode == RAGGED_M ? p.sizes[e] : p.M;
+    const int k_len = p.mode == RAGGED_M ? p.K : ((p.sizes[e] + 31) / 32) * 32;
+    const int m0 = mt * G_BM;
+    const int kbytes = k_len * ELEM;
+    const int nkt = (kbytes + G_BKB - 1) / G_BKB;
+
+    // ---- operand bases
+    const uint8_t* Abase;
+    const uint8_t* Asbase = nullptr;
+    const uint8_t* Bbase;
+    const uint8_t* Bsbase = nullptr;
+    if (p.mode == RAGGED_M) {
+      Abase = p.A + int64_t(off) * p.lda;
+      Bbase = p.Bt[e];
+      if (MX) { Asbase = p.As + int64_t(off) * p.ldas; Bsbase = p.Bst[e]; }
+    } else {
+      Abase = p.A + int64_t(off) * ELEM;
+      Bbase = p.B + int64_t(off) * ELEM;
+      if (MX) { Asbase = p.As + off / 32; Bsbase = p.Bs + off / 32; }
+    }
+
+    // ---- loader geometry: thread -> chunk (tid & 7), rows (tid >> 3) + 32 i
+    const int lchunk = tid & 7;
+    const int lrow = tid >> 3;
+    int64_t a_off[G_BM / 32];
+    int64_t b_off[G_BN / 32];
+#pragma unroll
+    for (int i = 0; i < G_BM / 32; ++i) {
+      int r = m0 + lrow + 32 * i;
+      int rmax = m_valid - 1;
+      r = r > rmax ? rmax : r;
+      r = r < 0 ? 0 : r;
+      a_off[i] = int64_t(r) * p.lda;
+    }
+#pragma unroll
+    for (int i = 0; i < G_BN / 32; ++i) {
+      int r = lrow + 32 * i;   // row of the B tile
+      int grow;
+      if (EPI == EPI_SWIGLU) {
+        int half = G_BN / 2;
+        int f = nt * half + (r % half);
+        f = f >= p.F ? p.F - 1 : f;
+        grow = r < half ? f : p.F + f;
+      } else {
+        grow = nt * G_BN + r;
+        grow = grow >= p.N ? p.N - 1 : grow;
+      }
+      b_off[i] = int64_t(grow) * p.ldb;
+    }
+
+    uint4 ra[G_BM / 32], rb[G_BN / 32];
+    auto gload = [&](int kt) {
+      const int kb = kt * G_BKB + lchunk * 16;
+      const bool ok = kb < kbytes;
+#pragma unroll
+      for (int i = 0; i < G_BM / 32; ++i)
+        ra[i] = ok ? *reinterpret_cast<const uint4*>(Abase + a_off[i] + kb) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < G_BN / 32; ++i)
+        rb[i] = ok ? *reinterpret_cast<const uint4*>(Bbase + b_off[i] + kb) : make_uint4(0, 0, 0, 0);
+    };
+    auto lstore = [&](int buf) {
+      uint8_t* sA = smem + buf * G_STAGE_BYTES;
+      uint8_t* sB = sA + G_BM * G_BKB;
+#pragma unroll
+      for (int i = 0; i < G_BM / 32; ++i) *reinterpret_cast<uint4*>(sA + swz(lrow + 32 * i, lchunk)) = ra[i];
+#pragma unroll
+      for (int i = 0; i < G_BN / 32; ++i) *reinterpret_cast<uint4*>(sB + swz(lrow + 32 * i, lchunk)) = rb[i];
+    };
+
+    // ---- MX scales for this lane's fragments (rows of the wave's M and N blocks)
+    int64_t sa_row[G_WMB], sb_row[G_WNB];
+    int brow_tile[G_WNB];
+#pragma unroll
+    for (int ni = 0; ni < G_WNB; ++ni) {
+      int r;
+      if (EPI == EPI_SWIGLU) {
+        constexpr int hb = G_WNB / 2;
+        r = ni < hb ? (wn * hb + ni) * 32 : G_BN / 2 + (wn * hb + ni - hb) * 32;
+      } else {
+        r = (wn * G_WNB + ni) * 32;
+      }
+      brow_tile[ni] = r;
+    }
+    if (MX) {
+#pragma unroll
+      for (int mi = 0; mi < G_WMB; ++mi) {
+        int r = m0 + (wm * G_WMB + mi) * 32 + l32;
+        r = r >= m_valid ? m_valid - 1 : r;
+        r = r < 0 ? 0 : r;
+        sa_row[mi] = int64_t(r) * p.ldas;
+      }
+#pragma unroll
+      for (int ni = 0; ni < G_WNB; ++ni) {
+        int r = brow_tile[ni] + l32;
+        int grow;
+        if (EPI == EPI_SWIGLU) {
+          int half = G_BN / 2;
+          int f = nt * half + (r % half);
+          f = f >= p.F ? p.F - 1 : f;
+          grow = r < half ? f : p.F + f;
+        } else {
+          grow = nt * G_BN + r;
+          grow = grow >= p.N ? p.N - 1 : grow;
+        }
+        sb_row[ni] = int64_t(grow) * p.ldbs;
+      }
+    }
+    uint32_t sa[G_WMB], sb[G_WNB];
+    uint32_t nsa[G_WMB], nsb[G_WNB];
+    const int kblocks = k_len / 32;
+    auto sload = [&](int kt, uint32_t* da, uint32_t* db) {
+      // 4 scale bytes (one per 32-element block) of this K slice; blocks past the end
+      // read as 127 (scale 1) — their codes are zero.
+#pragma unroll
+      for (int mi = 0; mi < G_WMB; ++mi) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          int kb = kt * 4 + j;
+          uint32_t v = kb < kblocks ? uint32_t(Asbase[sa_row[mi] + kb]) : 127u;
+          w |= v << (8 * j);
+        }
+        da[mi] = w >> (8 * hi);
+      }
+#pragma unroll
+      for (int ni = 0; ni < G_WNB; ++ni) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          int kb = kt * 4 + j;
+          uint32_t v = kb < kblocks ? uint32_t(Bsbase[sb_row[ni] + kb]) : 127u;
+          w |= v << (8 * j);
+        }
+        db[ni] = w >> (8 * hi);
+      }
+    };
+
+    f32x16 acc[G_WMB][G_WNB];
+#pragma unroll
+    for (int mi = 0; mi < G_WMB; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < G_WNB; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+    __syncthreads();   // previous tile's LDS readers (epilogue) are done
+    if (nkt > 0) {
+      gload(0);
+      if (MX) sload(0, sa, sb);
+      lstore(0);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int buf = kt & 1;
+      const bool more = kt + 1 < nkt;
+      if (more) {
+        gload(kt + 1);
+        if (MX) sload(kt + 1, nsa, nsb);
+      }
+      const uint8_t* sA = smem + buf * G_STAGE_BYTES;
+      const uint8_t* sB = sA + G_BM * G_BKB;
+      if (MX) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          i32x8 af[G_WMB], bfr[G_WNB];
+#pragma unroll
+          for (int mi = 0; mi < G_WMB; ++mi) {
+            int row = (wm * G_WMB + mi) * 32 + l32;
+            int c = s * 4 + hi * 2;
+            uint4 x0 = *reinterpret_cast<const uint4*>(sA + swz(row, c));
+            uint4 x1 = *reinterpret_cast<const uint4*>(sA + swz(row, c + 1));
+            af[mi] = i32x8{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
+          }
+#pragma unroll
+          for (int ni = 0; ni < G_WNB; ++ni) {
+            int row = brow_tile[ni] + l32;
+            int c = s * 4 + hi * 2;
+            uint4 x0 = *reinterpret_cast<const uint4*>(sB + swz(row, c));
+            uint4 x1 = *reinterpret_cast<const uint4*>(sB + swz(row, c + 1));
+            bfr[ni] = i32x8{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
+          }
+#pragma unroll
+          for (int mi = 0; mi < G_WMB; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < G_WNB; ++ni) {
+              if (s == 0)
+                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0,
+                                                                              int(sa[mi]), 0, int(sb[ni]));
+              else
+                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bfr[ni], acc[mi][ni], 0, 0, 2,
+                                                                              int(sa[mi]), 2, int(sb[ni]));
+            }
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          bf16x8 af[G_WMB], bfr[G_WNB];
+#pragma unroll
+          for (int mi = 0; mi < G_WMB; ++mi) {
+            int row = (wm * G_WMB + mi) * 32 + l32;
+            af[mi] = *reinterpret_cast<const bf16x8*>(sA + swz(row, s * 2 + hi));
+          }
+#pragma unroll
+          for (int ni = 0; ni < G_WNB; ++ni) {
+            int row = brow_tile[ni] + l32;
+            bfr[ni] = *reinterpret_cast<const bf16x8*>(sB + swz(row, s * 2 + hi));
+          }
+#pragma unroll
+          for (int mi = 0; mi < G_WMB; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < G_WNB; ++ni)
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+        }
+      }
+      if (more) {
+        lstore(buf ^ 1);
+        if (MX) {
+#pragma unroll
+          for (int mi = 0; mi < G_WMB; ++mi) sa[mi] = nsa[mi];
+#pragma unroll
+          for (int ni = 0; ni < G_WNB; ++ni) sb[ni] = nsb[ni];
+        }
+      }
+      __syncthreads();
+    }
+
+    // ---------------------------------------------------------------- epilogues
+    // Accumulator element r of block (mi, ni) is row 8*(r/4) + 4*hi + (r%4) and column
+    // l32 of that 32 x 32 block.
+    const int wrow0 = m0 + wm * G_WMB * 32;   // wave's first row (group-local)
+    if constexpr (EPI == EPI_STORE) {
+      static_for<0, G_WMB>([&](auto mic) {
+        constexpr int mi = decltype(mic)::value;
+        static_for<0, G_WNB>([&](auto nic) {
+          constexpr int ni = decltype(nic)::value;
+          const int col = nt * G_BN + brow_tile[ni] + l32;
+          const bool cok = col < p.N;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = wrow0 + mi * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            float v = acc[mi][ni][r];
+            if (cok && row < m_valid) {
+              if (p.mode == RAGGED_M) {
+                int64_t idx = int64_t(off + row) * p.ldc + col;
+                if (p.out_dtype == MGE_DTYPE_BF16) reinterpret_cast<uint16_t*>(p.C)[idx] = f32_to_bf16(v);
+                else reinterpret_cast<float*>(p.C)[idx] = v;
+              } else {
+                int64_t idx = int64_t(row) * p.ldc + col;
+                if (p.out_dtype == MGE_DTYPE_BF16) {
+                  uint16_t* o = reinterpret_cast<uint16_t*>(p.Ct[e]);
+                  if (p.accumulate) v += bf16_to_f32(o[idx]);
+                  o[idx] = f32_to_bf16(v);
+                } else {
+                  float* o = reinterpret_cast<float*>(p.Ct[e]);
+                  if (p.accumulate) v += o[idx];
+                  o[idx] = v;
+                }
+              }
+            }
+          }
+        });
+      });
+    } else if constexpr (EPI == EPI_SWIGLU) {
+      constexpr int hb = G_WNB / 2;
+      const int F = p.F;
+      const int F2 = 2 * F;
+      const int m_pad = (m_valid + 31) / 32 * 32;
+      static_for<0, G_WMB>([&](auto mic) {
+        constexpr int mi = decltype(mic)::value;
+        float pr[16];
+        const int rbase = wrow0 + mi * 32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rbase + 8 * (r >> 2) + 4 * hi + (r & 3);
+          pr[r] = row < m_valid ? p.prob[off + row] : 0.f;
+        }
+        static_for<0, hb>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          const int f = nt * (G_BN / 2) + (wn * hb + j) * 32 + l32;
+          const bool fok = f < F;
+          float h[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = rbase + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const bool ok = fok && row < m_valid;
+            const float G = acc[mi][j][r];
+            const float U = acc[mi][j + hb][r];
+            h[r] = ok ? pr[r] * silu_f(G) * U : 0.f;
+            if (p.saved_gu && ok) {
+              int64_t o = int64_t(off + row) * F2 + f;
+              p.saved_gu[o] = f32_to_bf16(G);
+              p.saved_gu[o + F] = f32_to_bf16(U);
+            }
+          }
+          // row form of h (blocks of 32 along F = the 32 lanes of this half-wave)
+          if (MX) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = rbase + 8 * (r >> 2) + 4 * hi + (r & 3);
+              float amax = wave_max_xor(fabsf(h[r]), 32);
+              uint32_t s = mx_scale_byte(amax);
+              uint32_t code = e4m3_rne(h[r] * mx_inv_scale(s));
+              if (row < m_valid && fok) {
+                int64_t o = int64_t(off + row) * F + f;
+                p.h_codes[o] = uint8_t(code);
+                if (l32 == 0) p.h_scales[int64_t(off + row) * (F / 32) + f / 32] = uint8_t(s);
+              }
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = rbase + 8 * (r >> 2) + 4 * hi + (r & 3);
+              if (row < m_valid && fok) p.h_bf16[int64_t(off + row) * F + f] = f32_to_bf16(h[r]);
+            }
+          }
+          // column form of h (training): this 32-row block of column f
+          if ((p.hc_codes || p.hc_bf16) && fok && rbase < m_pad) {
+            if (MX) {
+              float amax = 0.f;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(h[r]));
+              amax = fmaxf(amax, __shfl_xor(amax, 32));
+              uint32_t s = mx_scale_byte(amax);
+              float inv = mx_inv_scale(s);
+              uint8_t* dst = p.hc_codes + int64_t(f) * p.Rp + off + rbase + 4 * hi;
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                uint32_t w = e4m3_rne(h[4 * g] * inv) | (e4m3_rne(h[4 * g + 1] * inv) << 8) |
+                             (e4m3_rne(h[4 * g + 2] * inv) << 16) | (e4m3_rne(h[4 * g + 3] * inv) << 24);
+                *reinterpret_cast<uint32_t*>(dst + 8 * g) = w;
+              }
+              if (hi == 0) p.hc_scales[int64_t(f) * (p.Rp / 32) + (off + rbase) / 32] = uint8_t(s);
+            } else {
+              uint16_t* dst = p.hc_bf16 + int64_t(f) * p.Rp + off + rbase + 4 * hi;
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                uint2 w;
+                w.x = uint32_t(f32_to_bf16(h[4 * g])) | (uint32_t(f32_to_bf16(h[4 * g + 1])) << 16);
+                w.y = uint32_t(f32_to_bf16(h[4 * g + 2])) | (uint32_t(f32_to_bf16(h[4 * g + 3])) << 16);
+                *reinterpret_cast<uint2*>(dst + 8 * g) = w;
+              }
+            }
+          }
+        });
+      });
+    } else {  // EPI_SWIGLU_BWD: columns are f, the accumulator is dh
+      const int F = p.F;
+      const int F2 = 2 * F;
+      const int m_pad = (m_valid + 31) / 32 * 32;
+      const int part = nt * G_WAVES_N + wn;
+      static_for<0, G_WMB>([&](auto mic) {
+        constexpr int mi = decltype(mic)::value;
+        float pr[16], dps[16];
+        const int rbase = wrow0 + mi * 32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rbase + 8 * (r >> 2) + 4 * hi + (r & 3);
+          pr[r] = row < m_valid ? p.prob[off + row] : 0.f;
+          dps[r] = 0.f;
+        }
+        static_for<0, G_WNB>([&](auto nic) {
+          constexpr int ni = decltype(nic)::value;
+          const int f = nt * G_BN + (wn * G_WNB + ni) * 32 + l32;
+          const bool fok = f < F;
+          float dG[16], dU[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = rbase + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const bool ok = fok && row < m_valid;
+            float G = 0.f, U = 0.f;
+            if (ok) {
+              int64_t o = int64_t(off + row) * F2 + f;
+              G = bf16_to_f32(p.gu[o]);
+              U = bf16_to_f32(p.gu[o + F]);
+            }
+            const float dh = acc[mi][ni][r];
+            const float sg = sigmoid_f(G);
+            const float sl = G * sg;
+            dps[r] += ok ? dh * sl * U : 0.f;
+            dU[r] = ok ? dh * pr[r] * sl : 0.f;
+            dG[r] = ok ? dh * pr[r] * U * sg * (1.f + G * (1.f - sg)) : 0.f;
+          }
+          // row form [R][2F]: dG at column f, dU at column F + f
+          static_for<0, 2>([&](auto halfc) {
+            constexpr int half = decltype(halfc)::value;
+            float* v = half == 0 ? dG : dU;
+            const int col = half * F + f;
+            if (MX) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int row = rbase + 8 * (r >> 2) + 4 * hi + (r & 3);
+                float amax = wave_max_xor(fabsf(v[r]), 32);
+                uint32_t s = mx_scale_byte(amax);
+                uint32_t code = e4m3_rne(v[r] * mx_inv_scale(s));
+                if (row < m_valid && fok) {
+                  p.dgu_codes[int64_t(off + row) * F2 + col] = uint8_t(code);
+                  if (l32 == 0) p.dgu_scales[int64_t(off + row) * (F2 / 32) + col / 32] = uint8_t(s);
+                }
+              }
+            } else {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int row = rbase + 8 * (r >> 2) + 4 * hi + (r & 3);
+                if (row < m_valid && fok) p.dgu_bf16[int64_t(off + row) * F2 + col] = f32_to_bf16(v[r]);
+              }
+            }
+            // column form [2F][Rp]
+            if ((p.dguc_codes || p.dguc_bf16) && fok && rbase < m_pad) {
+              if (MX) {
+                float amax = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(v[r]));
+                amax = fmaxf(amax, __shfl_xor(amax, 32));
+                uint32_t s = mx_scale_byte(amax);
+                float inv = mx_inv_scale(s);
+                uint8_t* dst = p.dguc_codes + int64_t(col) * p.Rp + off + rbase + 4 * hi;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                  uint32_t w = e4m3_rne(v[4 * g] * inv) | (e4m3_rne(v[4 * g + 1] * inv) << 8) |
+                               (e4m3_rne(v[4 * g + 2] * inv) << 16) | (e4m3_rne(v[4 * g + 3] * inv) << 24);
+                  *reinterpret_cast<uint32_t*>(dst + 8 * g) = w;
+                }
+                if (hi == 0) p.dguc_scales[int64_t(col) * (p.Rp / 32) + (off + rbase) / 32] = uint8_t(s);
+              } else {
+                uint16_t* dst = p.dguc_bf16 + int64_t(col) * p.Rp + off + rbase + 4 * hi;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                  uint2 w;
+                  w.x = uint32_t(f32_to_bf16(v[4 * g])) | (uint32_t(f32_to_bf16(v[4 * g + 1])) << 16);
+                  w.y = uint32_t(f32_to_bf16(v[4 * g + 2])) | (uint32_t(f32_to_bf16(v[4 * g + 3])) << 16);
+                  *reinterpret_cast<uint2*>(dst + 8 * g) = w;
+                }
+              }
+            }
+          });
+        });
+        // d_prob partial of each row over this wave's columns (fixed xor-tree order)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = wave_sum_xor(dps[r], 32);
+          const int row = rbase + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (l32 == 0 && row < m_valid) p.dprob_part[int64_t(off + row) * p.nparts + part] = v;
+        }
+      });
+    }
+  }
+}
+
+int gemm_swiglu_bwd_nparts(int F) { return ((F + G_BN - 1) / G_BN) * G_WAVES_N; }
+
+int gemm_tiles_upper(const GemmParams& p, int64_t total_rows_bound) {
+  const int ncols_per_tile = G_BN;
+  int64_t nt = (int64_t(p.N) + ncols_per_tile - 1) / ncols_per_tile;
+  if (p.mode == RAGGED_M) {
+    int64_t mt = (total_rows_bound + G_BM - 1) / G_BM + p.E;
+    return int(mt * nt);
+  }
+  int64_t mt = (int64_t(p.M) + G_BM - 1) / G_BM;
+  return int(mt * nt * p.E);
+}
+
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  hipGetDevice(&dev);
+  if (dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] == 0) {
+    int v = 0;
+    hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    cus[dev] = v > 0 ? v : 256;
+  }
+  return cus[dev];
+}
+
+template <bool MX, int EPI>
+static mge_status launch_one(const GemmParams& p, hipStream_t s) {
+  hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_kernel<MX, EPI>),
+                      hipFuncAttributeMaxDynamicSharedMemorySize, G_LDS_BYTES);
+  int grid = device_cus();
+  if (p.tiles_upper < grid) grid = p.tiles_upper;
+  if (grid <= 0) return MGE_OK;
+  hipLaunchKernelGGL((grouped_gemm_kernel<MX, EPI>), dim3(grid), dim3(G_THREADS), G_LDS_BYTES, s, p);
+  return hip_check("grouped_gemm_kernel");
+}
+
+mge_status launch_gemm(const GemmParams& p, int prec, int epi, hipStream_t s) {
+  const bool mx = prec == MGE_PREC_MXFP8;
+  switch (epi) {
+    case EPI_STORE: return mx ? launch_one<true, EPI_STORE>(p, s) : launch_one<false, EPI_STORE>(p, s);
+    case EPI_SWIGLU: return mx ? launch_one<true, EPI_SWIGLU>(p, s) : launch_one<false, EPI_SWIGLU>(p, s);
+    case EPI_SWIGLU_BWD:
+      return mx ? launch_one<true, EPI_SWIGLU_BWD>(p, s) : launch_one<false, EPI_SWIGLU_BWD>(p, s);
+  }
+  return MGE_ERR_INVALID_ARG;
+}
+
+}  // namespace mge

@@ -1,0 +1,136 @@
+// MXFP8 block quantization (E4M3 + E8M0 per 32) of bf16 matrices, row and column
+// orientation, with an optional row gather (the permuted x / dy of the grouped MLP).
+//
+// One workgroup owns a 64-row x 128-column tile.  Row form: each thread quantizes
+// the 32-value block it loaded itself (no LDS).  Column form: the tile is staged in
+// LDS and each thread quantizes 32 consecutive rows of one column, writing the
+// transposed, K-contiguous layout the weight-gradient GEMMs read.  The bf16 variant
+// of the same kernel writes a plain (gathered) copy and the bf16 transpose.
+// HBM-bound: 2 B read + (1 + 1/32) B written per element and orientation.
+#include "mge_common.hpp"
+#include "mge_internal.hpp"
+
+namespace mge {
+
+constexpr int QT_ROWS = 64;
+constexpr int QT_COLS = 128;
+constexpr int QT_LDS_STRIDE = QT_COLS + 8;   // bf16 elements per LDS row
+
+template <bool MX>
+__global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileParams p) {
+  __shared__ uint16_t tile[QT_ROWS * QT_LDS_STRIDE];
+  const int tid = threadIdx.x;
+  const int c0 = blockIdx.x * QT_COLS;
+  const int r0 = blockIdx.y * QT_ROWS;
+  const int b = blockIdx.z;
+  const uint16_t* in = p.in + int64_t(b) * p.in_batch_stride;
+
+  // ---- load: thread -> (row r0 + tid/4, columns c0 + (tid%4)*32 .. +32)
+  const int rl = tid >> 2;
+  const int cl = (tid & 3) * 32;
+  const int r = r0 + rl;
+  const int c = c0 + cl;
+  uint4 v[4];
+  bool have = false;
+  if (r < p.R && c < p.C) {
+    int64_t src = r;
+    if (p.gather) src = p.gather[r];
+    if (src >= 0) {
+      const uint4* g = reinterpret_cast<const uint4*>(in + src * p.in_row_stride + c);
+      v[0] = g[0]; v[1] = g[1]; v[2] = g[2]; v[3] = g[3];
+      have = true;
+    }
+  }
+  if (!have) {
+    for (int i = 0; i < 4; ++i) v[i] = make_uint4(0, 0, 0, 0);
+  }
+
+  // ---- row form
+  if (r < p.R && c < p.C && (p.row_codes || p.row_bf16)) {
+    if (MX) {
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(v);
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        amax = fmaxf(amax, fabsf(__uint_as_float(w[i] << 16)));
+        amax = fmaxf(amax, fabsf(__uint_as_float(w[i] & 0xffff0000u)));
+      }
+      uint32_t s = mx_scale_byte(amax);
+      float inv = mx_inv_scale(s);
+      uint32_t out[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t q0 = e4m3_rne(__uint_as_float(w[2 * i] << 16) * inv);
+        uint32_t q1 = e4m3_rne(__uint_as_float(w[2 * i] & 0xffff0000u) * inv);
+        uint32_t q2 = e4m3_rne(__uint_as_float(w[2 * i + 1] << 16) * inv);
+        uint32_t q3 = e4m3_rne(__uint_as_float(w[2 * i + 1] & 0xffff0000u) * inv);
+        out[i] = q0 | (q1 << 8) | (q2 << 16) | (q3 << 24);
+      }
+      int64_t ob = int64_t(b) * p.R + r;
+      uint4* dst = reinterpret_cast<uint4*>(p.row_codes + ob * p.C + c);
+      dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+      dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+      p.row_scales[ob * (p.C / 32) + c / 32] = uint8_t(s);
+    } else {
+      int64_t ob = int64_t(b) * p.R + r;
+      uint4* dst = reinterpret_cast<uint4*>(p.row_bf16 + ob * p.C + c);
+      dst[0] = v[0]; dst[1] = v[1]; dst[2] = v[2]; dst[3] = v[3];
+    }
+  }
+
+  if (!(p.col_codes || p.col_bf16)) return;
+
+  // ---- column form: stage the tile, then thread -> (column tid%128, rows (tid/128)*32..+32)
+  {
+    uint4* t4 = reinterpret_cast<uint4*>(tile + rl * QT_LDS_STRIDE + cl);
+    t4[0] = v[0]; t4[1] = v[1]; t4[2] = v[2]; t4[3] = v[3];
+  }
+  __syncthreads();
+  const int cc = tid & 127;
+  const int rb = tid >> 7;
+  const int col = c0 + cc;
+  const int rowb = r0 + rb * 32;
+  if (col >= p.C || rowb >= p.Rp) return;
+  float f[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) f[j] = bf16_to_f32(tile[(rb * 32 + j) * QT_LDS_STRIDE + cc]);
+  const int64_t ocol = int64_t(b) * p.C + col;
+  if (MX) {
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(f[j]));
+    uint32_t s = mx_scale_byte(amax);
+    float inv = mx_inv_scale(s);
+    uint32_t out[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      out[i] = e4m3_rne(f[4 * i] * inv) | (e4m3_rne(f[4 * i + 1] * inv) << 8) |
+               (e4m3_rne(f[4 * i + 2] * inv) << 16) | (e4m3_rne(f[4 * i + 3] * inv) << 24);
+    uint4* dst = reinterpret_cast<uint4*>(p.col_codes + ocol * p.Rp + rowb);
+    dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+    dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+    p.col_scales[ocol * (p.Rp / 32) + rowb / 32] = uint8_t(s);
+  } else {
+    uint32_t out[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      out[i] = uint32_t(tile[(rb * 32 + 2 * i) * QT_LDS_STRIDE + cc]) |
+               (uint32_t(tile[(rb * 32 + 2 * i + 1) * QT_LDS_STRIDE + cc]) << 16);
+    uint4* dst = reinterpret_cast<uint4*>(p.col_bf16 + ocol * p.Rp + rowb);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+  }
+}
+
+mge_status launch_quant_tile(const QuantTileParams& p, bool mx, hipStream_t s) {
+  if (p.R <= 0 || p.C <= 0 || p.batch <= 0) return MGE_OK;
+  int rows_cover = p.Rp > p.R ? p.Rp : p.R;
+  dim3 grid((p.C + QT_COLS - 1) / QT_COLS, (rows_cover + QT_ROWS - 1) / QT_ROWS, p.batch);
+  if (mx)
+    hipLaunchKernelGGL(quant_tile_kernel<true>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(quant_tile_kernel<false>, grid, dim3(256), 0, s, p);
+  return hip_check("quant_tile_kernel");
+}
+
+}  // namespace mge

@@ -17,7 +17,7 @@ Two tiers:
     call does, and use one fp64 matmul per expert and projection.
 
 The backward is the gradient of L = <dy, y> with respect to x, W_gate_up, W_down and
-p (the pages only say the fused forward has "a matching backward"):
+p (the pages only say that the fused forward comes with a fused backward):
     dY = gather(dy), dh = dY W_down, dp = sum_f dh * silu(G) * U,
     dU = dh * p * silu(G), dG = dh * p * U * sig(G) * (1 + G (1 - sig(G))),
     dW_down = dY^T h, dW_gate_up = [dG dU]^T X, dX = [dG dU] W_gate_up, dx = combine(dX).

@@ -1,9 +1,9 @@
 """Top-k routing and the token permutation by expert — oracle, test infrastructure only.
 
-The pages say the router activates only a few experts per token ([P1] intro), that
-the grouped call gathers the tokens of every expert and takes the per-expert token
-counts as an extra ``split_sizes`` argument ([P1] "Grouped experts instead of a
-Python loop"; [P4] paragraph on GroupedLinear), and that the SwiGLU output is
+Per the pages, each token is sent to a small number of experts ([P1] intro), and the
+grouped call collects every expert's tokens and is told how many each expert has
+through a separate ``split_sizes`` argument ([P1] "Grouped experts instead of a
+Python loop"; [P4] paragraph on GroupedLinear); the SwiGLU output is
 scaled by the routing probability ([P4] paragraph on the Sequential fusion).
 
 Readings where the pages are silent:

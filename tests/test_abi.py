@@ -1,0 +1,134 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every function
+include/mge.h declares, the Python structs match the C layout (a size mismatch is
+rejected before anything else), and bad arguments are rejected on the host with the
+documented codes before any launch."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mge.h")
+
+from moe_grouped_expert_amd import _binding as b  # noqa: E402
+
+pytestmark = pytest.mark.skipif(not os.path.exists(b.LIB_PATH), reason="libmge.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol():
+    L = b.lib()
+    names = declared_functions()
+    assert len(names) >= 13, names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(b.EXPORTS) <= set(names)
+
+
+def test_version_and_status_strings():
+    L = b.lib()
+    assert L.mge_version().decode().count(".") == 2
+    for code in range(6):
+        assert L.mge_status_string(code).decode().startswith("MGE_")
+
+
+def test_perm_rows():
+    # T*k + E*(align-1), rounded up to 32
+    assert b.perm_rows(256, 2, 4, 32) == 640
+    assert b.perm_rows(16384, 2, 8, 32) == 32768 + 256
+    assert b.perm_rows(3, 1, 1, 1) == 32
+    assert b.perm_rows(0, 2, 8, 32) == 256
+
+
+def _call(fn, st, **fields):
+    a = st()
+    a.struct_size = C.sizeof(st)
+    for k, v in fields.items():
+        setattr(a, k, v)
+    L = b.lib()
+    r = getattr(L, fn)(C.byref(a), None)
+    return r, L.mge_last_error().decode()
+
+
+def test_struct_size_checked():
+    a = b.RouteArgs()
+    a.struct_size = C.sizeof(b.RouteArgs) - 8
+    L = b.lib()
+    assert L.moe_route_permute(C.byref(a), None) == b.MGE_ERR_INVALID_ARG
+    assert "struct_size" in L.mge_last_error().decode()
+    assert L.moe_route_permute(None, None) == b.MGE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("fields,msg", [
+    (dict(T=-1, E=4, k=2, H=64, align=32), "T must"),
+    (dict(T=8, E=0, k=1, H=64, align=32), "E must"),
+    (dict(T=8, E=300, k=1, H=64, align=32), "E must"),
+    (dict(T=8, E=4, k=5, H=64, align=32), "k must"),
+    (dict(T=8, E=16, k=9, H=64, align=32), "k must"),
+    (dict(T=8, E=4, k=2, H=48, align=32), "H must"),
+    (dict(T=8, E=4, k=2, H=64, align=24), "align must"),
+    (dict(T=8, E=4, k=2, H=64, align=32, prec=3), "prec"),
+])
+def test_route_rejects_bad_sizes(fields, msg):
+    r, err = _call("moe_route_permute", b.RouteArgs, **fields)
+    assert r == b.MGE_ERR_INVALID_ARG and msg in err, err
+
+
+def test_route_rejects_null_outputs_and_small_workspace():
+    base = dict(T=8, E=4, k=2, H=64, align=32, logits=64)
+    r, err = _call("moe_route_permute", b.RouteArgs, **base)
+    assert r == b.MGE_ERR_INVALID_ARG and "NULL" in err
+    ptrs = {n: 256 * (i + 1) for i, n in enumerate(
+        ["topk_idx", "topk_prob", "split_sizes", "group_offsets", "perm_src", "perm_pos", "prob_perm"])}
+    r, err = _call("moe_route_permute", b.RouteArgs, **base, **ptrs, workspace=4096, workspace_bytes=16)
+    assert r == b.MGE_ERR_WORKSPACE and "workspace" in err
+    r, err = _call("moe_route_permute", b.RouteArgs, **base, **ptrs, x=4096 + 8, x_perm=8192)
+    assert r == b.MGE_ERR_INVALID_ARG and "aligned" in err
+    # MXFP8 column form needs align % 32 == 0
+    r, err = _call("moe_route_permute", b.RouteArgs, **{**base, "align": 16}, **ptrs, prec=1, x=4096, x_perm=8192,
+                   x_perm_scale=16384, flags=b.ROUTE_WANT_COL, x_col=32768, x_col_scale=65536)
+    assert r == b.MGE_ERR_INVALID_ARG and "align" in err
+
+
+def test_route_workspace_query():
+    L = b.lib()
+    assert L.mge_route_workspace_bytes(256, 4) >= 256 + 4 * 4
+    assert L.mge_route_workspace_bytes(32768, 8) >= 128 * 8 * 4
+
+
+def test_quantize_rejects():
+    r, err = _call("mxfp8_quantize", b.QuantArgs, batch=1, R=64, C=48, orient=1, in_=4096, in_row_stride=48)
+    assert r == b.MGE_ERR_INVALID_ARG and "multiple of 32" in err
+    r, err = _call("mxfp8_quantize", b.QuantArgs, batch=1, R=64, C=64, orient=1, in_=4096, in_row_stride=64)
+    assert r == b.MGE_ERR_INVALID_ARG and "row outputs" in err
+    r, err = _call("mxfp8_quantize", b.QuantArgs, batch=1, R=64, C=64, orient=4, in_=4096, in_row_stride=64)
+    assert r == b.MGE_ERR_INVALID_ARG and "orient" in err
+    # empty input is a valid no-op
+    r, err = _call("mxfp8_quantize", b.QuantArgs, batch=1, R=0, C=64, orient=1, in_=4096, in_row_stride=64,
+                   row_codes=8192, row_scales=16384)
+    assert r == b.MGE_OK, err
+
+
+def test_fwd_bwd_combine_reject():
+    r, err = _call("grouped_mlp_fwd", b.FwdArgs, prec=1, E=4, H=64, F=100, T=8, k=2, align=32)
+    assert r == b.MGE_ERR_INVALID_ARG and "F must" in err
+    r, err = _call("grouped_mlp_fwd", b.FwdArgs, prec=1, E=4, H=64, F=128, T=8, k=2, align=32)
+    assert r == b.MGE_ERR_INVALID_ARG and "NULL" in err
+    r, err = _call("grouped_mlp_bwd", b.BwdArgs, prec=0, E=4, H=64, F=128, T=8, k=2, align=8)
+    assert r == b.MGE_ERR_INVALID_ARG and "align" in err
+    r, err = _call("unpermute_combine", b.CombineArgs, T=4, k=9, H=64)
+    assert r == b.MGE_ERR_INVALID_ARG
+    r, err = _call("unpermute_combine", b.CombineArgs, T=4, k=2, H=64, in_dtype=2)
+    assert r == b.MGE_ERR_INVALID_ARG and "dtype" in err
+
+
+def test_check_device_errors_rejects_null():
+    L = b.lib()
+    assert L.mge_check_device_errors(None, None) == b.MGE_ERR_INVALID_ARG
