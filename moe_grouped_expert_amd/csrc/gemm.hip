@@ -11,7 +11,12 @@
 // Tiles are 256 x 256 with 128-byte K slices (128 FP8 or 64 BF16 elements), 4 waves in
 // a 2 x 2 grid, each wave 128 x 128 built from 32 x 32 MFMA blocks:
 //   MXFP8: v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, one E8M0 scale per lane and
-//          32-element K block, applied by the matrix core — no dequantize pass)
+//          32-element K block, applied by the matrix core — no dequantize pass).
+//          Operand layout (measured on gfx950): lane l = 32h + i feeds row/column i;
+//          its register bytes 0..15 are K elements 16h..16h+15 and bytes 16..31 are
+//          32+16h..32+16h+15 of the 64-element step, so K block h (elements
+//          32h..32h+31) is scaled by the scale register of the lanes with that h, the
+//          byte chosen by op_sel.
 //   BF16:  v_mfma_f32_32x32x16_bf16
 // Operand tiles go HBM -> registers -> LDS (double-buffered, XOR-swizzled 16-byte
 // chunks so both the row-wise stores and the MFMA fragment reads are bank-conflict
@@ -291,17 +296,17 @@ __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmParams p
 #pragma unroll
           for (int mi = 0; mi < G_WMB; ++mi) {
             int row = (wm * G_WMB + mi) * 32 + l32;
-            int c = s * 4 + hi * 2;
+            int c = s * 4 + hi;
             uint4 x0 = *reinterpret_cast<const uint4*>(sA + swz(row, c));
-            uint4 x1 = *reinterpret_cast<const uint4*>(sA + swz(row, c + 1));
+            uint4 x1 = *reinterpret_cast<const uint4*>(sA + swz(row, c + 2));
             af[mi] = i32x8{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
           }
 #pragma unroll
           for (int ni = 0; ni < G_WNB; ++ni) {
             int row = brow_tile[ni] + l32;
-            int c = s * 4 + hi * 2;
+            int c = s * 4 + hi;
             uint4 x0 = *reinterpret_cast<const uint4*>(sB + swz(row, c));
-            uint4 x1 = *reinterpret_cast<const uint4*>(sB + swz(row, c + 1));
+            uint4 x1 = *reinterpret_cast<const uint4*>(sB + swz(row, c + 2));
             bfr[ni] = i32x8{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
           }
 #pragma unroll

@@ -34,8 +34,8 @@ def sweep_blocks():
         pad[: others.size] = others
         rows.append(np.concatenate([np.full((nb, 1), amax), pad.reshape(nb, 31)], axis=1))
     blk = np.concatenate(rows)                 # [nblocks][32], each row one block
-    nb = blk.shape[0] // 8 * 8
-    return blk[:nb].reshape(nb // 8, 256).astype(np.float32)   # 8 blocks per row
+    nb = blk.shape[0] // 256 * 256           # rows of 8 blocks, a multiple of 32 rows
+    return blk[:nb].reshape(nb // 8, 256).astype(np.float32)
 
 
 def test_quantize_exhaustive_bitexact(m):
