@@ -1,0 +1,370 @@
+#!/usr/bin/env python3
+"""Throughput of the grouped expert MLP hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input, every
+stage in the library's HIP kernels through the C ABI:
+  moe_route_permute (top-k routing, split_sizes, stable permutation, x gathered and
+  MXFP8-quantized row- and column-wise) -> mxfp8_quantize of the 16-bit master
+  weights (row and column forms, as every training step re-quantizes them) ->
+  grouped_mlp_fwd (gate-up GEMM + SwiGLU x prob + quantize-h epilogue, down GEMM) ->
+  unpermute_combine -> grouped_mlp_bwd (dy permute + quantize, dh GEMM + SwiGLU
+  backward, d_prob, dW_down, dX, dW_gate_up) -> unpermute_combine of dx.
+
+Default workload: the Mixtral-8x7B-shaped expert layer (8 experts, hidden 4096,
+ffn 14336, top-2) training step in MXFP8 with 16-bit master weights, 8192 tokens.
+Inputs are seeded synthetic tensors, resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is algorithmic TFLOP/s of the step (6*M*H*F forward +
+12*M*H*F backward, M = tokens * top-k; no padding, no recompute); tokens/s beside it.
+`roofline` is for the kernel with the largest share of the step time, from HIP
+events recorded around each kernel launch on its own stream during the timed
+steps.  `cpu_baseline` is the fp64 CPU oracle timed on a bounded sample of the same
+workload (rank 0, one GPU only).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "grouped-MLP fwd/bwd TFLOP/s + tokens/s, Mixtral-8x7B expert layer, MXFP8"
+
+# Published dense MFMA peaks of the MI355X (TFLOP/s) and its HBM3E bandwidth (GB/s).
+PEAK_TFLOPS = {"mxfp8": 5000.0, "bf16": 2500.0}
+PEAK_HBM_GBS = 8000.0
+
+WORKLOADS = {
+    # name: (synth workload id, training step?)
+    "train_mxfp8": (4, True),
+    "fwd_bf16": (1, False),
+    "fwd_mxfp8": (2, False),
+    "fwd_mxfp8_skew": (3, False),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------------------ inputs
+
+def make_inputs(w, dev):
+    """Seeded inputs: routing logits from numpy (fixes split_sizes), the large tensors
+    drawn on the device with torch's seeded generator, same distributions."""
+    import torch
+
+    import synth
+    logits = torch.from_numpy(synth.logits(w)).to(dev)
+    x = synth.torch_normal_bf16((w.T, w.H), 1.0, 1000 * w.cfg_id + synth.TID_X, dev)
+    wg = synth.torch_normal_bf16((w.E, w.F, w.H), w.weight_std, 1000 * w.cfg_id + synth.TID_WGATE, dev)
+    wu = synth.torch_normal_bf16((w.E, w.F, w.H), w.weight_std, 1000 * w.cfg_id + synth.TID_WUP, dev)
+    wgu = torch.cat([wg, wu], dim=1).contiguous()
+    del wg, wu
+    wd = synth.torch_normal_bf16((w.E, w.H, w.F), w.weight_std, 1000 * w.cfg_id + synth.TID_WDOWN, dev)
+    dy = synth.torch_normal_bf16((w.T, w.H), 1.0, 1000 * w.cfg_id + synth.TID_DY, dev) if w.backward else None
+    return dict(logits=logits, x=x, wgu=wgu, wd=wd, dy=dy)
+
+
+# ------------------------------------------------------------------------------ step
+
+class Step:
+    """The hot path with every output buffer allocated once (allocation stays outside
+    the timed region; the library itself never allocates)."""
+
+    def __init__(self, m, w, inp, train):
+        self.m, self.w, self.inp, self.train = m, w, inp, train
+        self.prec = w.prec
+        self.g = None
+        self.wq = self.dq = None
+        self.f = self.b = None
+        self.y = self.dx = None
+
+    def __call__(self):
+        m, w, inp = self.m, self.w, self.inp
+        mx = self.prec == "mxfp8"
+        self.g = m.moe_route_permute(inp["logits"], inp["x"], w.k, align=32, prec=self.prec, want_col=self.train,
+                                     out=self.g)
+        if mx:
+            orient = "both" if self.train else "row"
+            self.wq = m.mxfp8_quantize(inp["wgu"], orient, out=self.wq)
+            self.dq = m.mxfp8_quantize(inp["wd"], orient, out=self.dq)
+            self.f = m.grouped_mlp_fwd(self.g, self.wq[0], self.dq[0], self.wq[1], self.dq[1], train=self.train,
+                                       out=self.f)
+        else:
+            self.f = m.grouped_mlp_fwd(self.g, inp["wgu"], inp["wd"], train=self.train, out=self.f)
+        self.y = m.unpermute_combine(self.f.y_perm, self.g.perm_pos, out=self.y)
+        if self.train:
+            if mx:
+                self.b = m.grouped_mlp_bwd(inp["dy"], self.g, self.f, self.wq[2], self.dq[2], self.wq[3], self.dq[3],
+                                           out=self.b)
+            else:
+                self.b = m.grouped_mlp_bwd(inp["dy"], self.g, self.f, inp["wgu"], inp["wd"], out=self.b)
+            self.dx = m.unpermute_combine(self.b.dx_perm, self.g.perm_pos, out=self.dx)
+
+
+# ------------------------------------------------------------------------------ per-kernel work
+
+def kernel_work(name, w, R):
+    """Algorithmic work of one launch of a library kernel: ("flop", n) or ("byte", n).
+
+    GEMMs: the method's flops on the M = T*k real rows (no padding rows).  HBM-bound
+    kernels: bytes that must cross HBM once (inputs read, outputs written)."""
+    M, H, F, T, k, E = w.M, w.H, w.F, w.T, w.k, w.E
+    mhf = float(M) * H * F
+    gemm = {"gemm_gateup_swiglu": 4 * mhf, "gemm_down": 2 * mhf, "gemm_dh_swiglu_bwd": 2 * mhf,
+            "gemm_dx": 4 * mhf, "gemm_dw_down": 2 * mhf, "gemm_dw_gateup": 4 * mhf}
+    for key, v in gemm.items():
+        if name.startswith(key + "_"):
+            return "flop", v
+    mxb = 1.0 + 1.0 / 32.0            # bytes per MXFP8 element (code + scale share)
+    if name == "permute_quant_mx":
+        # x or dy gathered (bf16 read once per token) -> row and (training) column forms
+        forms = 2 if w.backward else 1
+        return "byte", 2.0 * T * H + forms * mxb * M * H + 4.0 * R
+    if name == "permute_bf16":
+        return "byte", 2.0 * T * H + (2 if w.backward else 1) * 2.0 * M * H + 4.0 * R
+    if name == "quant_mx":
+        return None                    # per-tensor size varies (W_gate_up vs W_down): see weight_quant_bytes
+    if name == "combine":
+        return "byte", 2.0 * k * T * H + 2.0 * T * H + 4.0 * T * k
+    if name in ("route_topk", "route_scatter"):
+        return "byte", 4.0 * T * E + 8.0 * T * k if name == "route_topk" else 4.0 * T * k * 4
+    return None
+
+
+def summarize_kernels(records, steps, w, R, prec):
+    """Aggregates the per-launch event timings into per-kernel statistics."""
+    agg = {}
+    for name, ms in records:
+        if ms < 0:
+            continue
+        a = agg.setdefault(name, dict(launches=0, total_ms=0.0))
+        a["launches"] += 1
+        a["total_ms"] += ms
+    total = sum(a["total_ms"] for a in agg.values())
+    out = {}
+    for name, a in sorted(agg.items(), key=lambda kv: -kv[1]["total_ms"]):
+        avg = a["total_ms"] / a["launches"]
+        d = dict(launches_per_step=a["launches"] / steps, avg_ms=round(avg, 5),
+                 share=round(a["total_ms"] / total, 4) if total > 0 else None)
+        wk = kernel_work(name, w, R)
+        if wk is not None:
+            kind, n = wk
+            if kind == "flop":
+                tf = n / (avg * 1e-3) / 1e12
+                d.update(tflops=round(tf, 1), frac_of_peak=round(tf / PEAK_TFLOPS[prec], 4))
+            else:
+                gbs = n / (avg * 1e-3) / 1e9
+                d.update(gbs=round(gbs, 1), frac_of_hbm=round(gbs / PEAK_HBM_GBS, 4))
+        out[name] = d
+    return out, total / steps
+
+
+# ------------------------------------------------------------------------------ traffic (rocprofv3 counters)
+
+def kernel_source_digest():
+    """Digest of the GEMM kernel sources: counter-derived traffic is only reported while
+    the kernels are the ones the counters were taken on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "moe_grouped_expert_amd", "csrc")
+    for f in ("gemm_impl.hpp", "gemm_mx.hip", "gemm_bf16.hip", "mge_common.hpp", "mge_internal.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch of `kernel` from profiles/traffic.json (FETCH_SIZE + WRITE_SIZE
+    per dispatch, scaled by the copy-kernel calibration), or None when absent or stale."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_digest") != kernel_source_digest():
+        return None
+    e = d.get("kernels", {}).get(workload, {}).get(kernel)
+    return None if e is None else e.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(w, max_rows=32, f_cols=3072):
+    """The fp64 CPU oracle, as it stands, on a bounded sample of the workload.
+
+    Sample: expert 0 of the workload, the first `max_rows` assignments routed to it
+    (their tokens and routing probabilities from the oracle's own routing of the
+    workload's logits), the full hidden size and the first `f_cols` of the expert's
+    ffn columns (gate, up and down weights restricted to them), through the whole
+    MXFP8 training step (or forward) as the oracle defines it: quantize the weights
+    (row and column forms), permute and quantize x, gate-up GEMM + SwiGLU x prob,
+    quantize h, down GEMM, combine; backward: dy permute/quantize, dh + SwiGLU
+    backward, d_prob, dW_down, dX, dW_gate_up.  Rate = the sample's algorithmic flops
+    (the same 6 + 12 flops per assignment, hidden and ffn column) / wall time."""
+    import numpy as np
+
+    import synth
+    from oracle import mlp, mx
+    from oracle import route as rt
+
+    cores = len(os.sched_getaffinity(0))
+    l = synth.logits(w)[:4096]
+    idx, p = rt.route(l, w.k)
+    hit = np.argwhere(idx == 0)[:max_rows]
+    toks, slots = hit[:, 0], hit[:, 1]
+    n = len(toks)
+    fs = min(f_cols, w.F)
+    std = np.float32(w.weight_std)
+    # expert 0's weights from the workload's numpy streams (the first rows of each stream
+    # are expert 0), restricted to the sampled ffn columns
+    wg0 = synth.to_bf16_values(synth.rng(w.cfg_id, synth.TID_WGATE).standard_normal((fs, w.H), dtype=np.float32) * std)
+    wu0 = synth.to_bf16_values(synth.rng(w.cfg_id, synth.TID_WUP).standard_normal((fs, w.H), dtype=np.float32) * std)
+    wd0 = synth.to_bf16_values(
+        synth.rng(w.cfg_id, synth.TID_WDOWN).standard_normal((w.H, w.F), dtype=np.float32)[:, :fs] * std)
+    wgu0 = np.concatenate([wg0, wu0], axis=0)
+    xs = synth.x(w)[toks]
+    dys = synth.dy(w)[toks] if w.backward else None
+    t0 = time.perf_counter()
+    lay = mlp.Layout(np.zeros((n, 1), np.int32), p[toks, slots][:, None], 1, 32)
+    wq = mx.quantize_rows(wgu0)
+    dq = mx.quantize_rows(wd0)
+    X = lay.gather(xs)
+    xq, xsc = mx.quantize_rows(X)
+    G, U, h = mlp.mx_gateup_stage(xq, xsc, [wq[0]], [wq[1]], lay)
+    hq, hs = mx.quantize_rows(h)
+    Y = mlp.mx_down_stage(hq, hs, [dq[0]], [dq[1]], lay)
+    lay.combine(Y)
+    flops = 6.0 * n * w.H * fs
+    if w.backward:
+        wqc = mx.quantize_cols(wgu0)
+        dqc = mx.quantize_cols(wd0)
+        xc = mx.quantize_cols(X)
+        hc = mx.quantize_cols(h)
+        DY = lay.gather(dys)
+        dyq, dysc = mx.quantize_rows(DY)
+        dyc = mx.quantize_cols(DY)
+        dG, dU, dp = mlp.mx_dh_stage(dyq, dysc, [dqc[0]], [dqc[1]], G, U, lay)
+        dGU = np.concatenate([dG, dU], axis=1)
+        gq, gs = mx.quantize_rows(dGU)
+        gc = mx.quantize_cols(dGU)
+        mlp.mx_dw_stage(dyc[0], dyc[1], hc[0], hc[1], lay)
+        dX = mlp.mx_dx_stage(gq, gs, [wqc[0]], [wqc[1]], lay)
+        mlp.mx_dw_stage(gc[0], gc[1], xc[0], xc[1], lay)
+        lay.combine(dX)
+        flops += 12.0 * n * w.H * fs
+    dt = time.perf_counter() - t0
+    # token-equivalents: assignments / k, scaled by the fraction of the ffn width done
+    tok = n / w.k * fs / w.F
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": (f"expert 0 of the {w.name} workload: its first {n} routed assignments, full H={w.H}, "
+                       f"ffn columns 0..{fs - 1} of F={w.F}; whole MXFP8 "
+                       f"{'training step (fwd+bwd)' if w.backward else 'forward'} incl. that weight slice's "
+                       f"quantization; fp64 numpy, {dt:.1f} s wall"),
+            "seconds": round(dt, 2), "tokens_per_s": round(tok / dt, 4)}
+
+
+# ------------------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="train_mxfp8", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=32, help="assignments in the CPU oracle sample")
+    ap.add_argument("--cpu-fcols", type=int, default=3072, help="ffn columns in the CPU oracle sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import moe_grouped_expert_amd as m
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    m.lib()   # raises when the HIP library is not built: there is no other path
+    dev = torch.device("cuda:0")
+    wid, train = WORKLOADS[args.workload]
+    w = synth.WORKLOADS[wid]
+    log(f"[bench] workload {w.name}: T={w.T} E={w.E} H={w.H} F={w.F} k={w.k} prec={w.prec} train={train}")
+    inp = make_inputs(w, dev)
+    torch.cuda.synchronize()
+    step = Step(m, w, inp, train)
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {i + 1}/{args.warmup} done")
+    R = step.g.R
+    sizes = step.g.split_sizes.cpu().tolist()
+
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    m.profile_start()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    records = m.profile_stop()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] {args.steps} timed steps: {ms:.3f} ms/step")
+
+    flops = w.flops_fwd() + (w.flops_bwd() if train else 0.0)
+    tflops = flops / (ms * 1e-3) / 1e12
+    tok_s = w.T / (ms * 1e-3)
+    kernels, kern_ms = summarize_kernels(records, args.steps, w, R, w.prec)
+    dom = next(iter(kernels))
+    dk = kernels[dom]
+    wk = kernel_work(dom, w, R)
+    if wk and wk[0] == "flop":
+        ach = wk[1] / (dk["avg_ms"] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_TFLOPS[w.prec],
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS[w.prec], 4),
+                "traffic": traffic_for(dom, args.workload), "avg_launch_ms": dk["avg_ms"],
+                "algorithmic_flop_per_launch": wk[1]}
+    else:
+        nb = wk[1] if wk else None
+        ach = nb / (dk["avg_ms"] * 1e-3) / 1e9 if nb else None
+        roof = {"kernel": dom, "bound": "hbm", "achieved": ach and round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": ach and round(ach / PEAK_HBM_GBS, 4),
+                "traffic": traffic_for(dom, args.workload), "avg_launch_ms": dk["avg_ms"]}
+    gemm_ms = sum(v["avg_ms"] * v["launches_per_step"] for k, v in kernels.items() if k.startswith("gemm_"))
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.prec, "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "E": w.E, "H": w.H, "F": w.F, "k": w.k, "prec": w.prec,
+                   "passes": "fwd+bwd" if train else "fwd", "align": 32, "split_sizes": sizes,
+                   "parallelism": "single GPU"},
+        "tokens_per_s": round(tok_s, 1),
+        "algorithmic_tflop_per_step": round(flops / 1e12, 4),
+        "gemm_only": {"ms_per_step": round(gemm_ms, 4),
+                      "tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms > 0 else None},
+        "kernel_ms_per_step": round(kern_ms, 4),
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows, args.cpu_fcols)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

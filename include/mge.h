@@ -282,6 +282,26 @@ mge_status mge_check_device_errors(void* route_workspace, void* stream);
 /* Library version, e.g. "0.1.0". */
 const char* mge_version(void);
 
+/* ------------------------------------------------------------------------------
+ * Per-kernel timing — a measuring aid, not part of the computation (the pages give
+ * no per-operator breakdown of the grouped MLP; this provides one).
+ * Between mge_profile_start() and mge_profile_stop(), every kernel the library
+ * launches, from any thread and on any stream, is bracketed by two HIP events
+ * recorded on its own stream.  mge_profile_stop() ends recording, waits for the
+ * recorded events, writes up to max_records records (launch order: kernel name and
+ * elapsed milliseconds; -1 if an event could not be read, detail in
+ * mge_last_error) to out (may be NULL), and returns the number of launches recorded.
+ * The events are created once and reused; no device memory is allocated.  Starting
+ * again discards the previous records.
+ * ---------------------------------------------------------------------------- */
+typedef struct mge_kernel_time {
+  char name[56];
+  float ms;
+} mge_kernel_time;
+
+mge_status mge_profile_start(void);
+int32_t mge_profile_stop(mge_kernel_time* out, int32_t max_records);
+
 #ifdef __cplusplus
 }
 #endif

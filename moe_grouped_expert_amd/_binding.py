@@ -74,7 +74,12 @@ class CombineArgs(C.Structure):
 _LIB = None
 EXPORTS = ["mge_perm_rows", "mge_route_workspace_bytes", "moe_route_permute", "mxfp8_quantize",
            "mge_fwd_workspace_bytes", "grouped_mlp_fwd", "mge_bwd_workspace_bytes", "grouped_mlp_bwd",
-           "unpermute_combine", "mge_status_string", "mge_last_error", "mge_check_device_errors", "mge_version"]
+           "unpermute_combine", "mge_status_string", "mge_last_error", "mge_check_device_errors", "mge_version",
+           "mge_profile_start", "mge_profile_stop"]
+
+
+class KernelTime(C.Structure):
+    _fields_ = [("name", C.c_char * 56), ("ms", C.c_float)]
 
 
 def lib():
@@ -105,6 +110,10 @@ def lib():
         L.mge_check_device_errors.restype = C.c_int
         L.mge_check_device_errors.argtypes = [vp, vp]
         L.mge_version.restype = C.c_char_p
+        L.mge_profile_start.restype = C.c_int
+        L.mge_profile_start.argtypes = []
+        L.mge_profile_stop.restype = i32
+        L.mge_profile_stop.argtypes = [C.c_void_p, i32]
         _LIB = L
     return _LIB
 
@@ -394,6 +403,23 @@ def grouped_mlp_bwd(dy: torch.Tensor, rt: RouteOut, fw: FwdOut, w_gate_up_k, w_d
     a.workspace, a.workspace_bytes = _ptr(o.workspace), o.workspace.numel()
     _check(lib().grouped_mlp_bwd(C.byref(a), _stream(dev)), "grouped_mlp_bwd")
     return o
+
+
+# ------------------------------------------------------------------------------ timing
+
+def profile_start() -> None:
+    """Start recording a HIP event pair around every kernel the library launches."""
+    _check(lib().mge_profile_start(), "mge_profile_start")
+
+
+def profile_stop() -> list:
+    """Stop recording; returns [(kernel name, milliseconds)] in launch order."""
+    L = lib()
+    n = int(L.mge_profile_stop(None, 0))
+    buf = (KernelTime * max(n, 1))()
+    # records are kept until the next start, so a second read returns the same list
+    L.mge_profile_stop(C.cast(buf, C.c_void_p), n)
+    return [(buf[i].name.decode(), float(buf[i].ms)) for i in range(n)]
 
 
 # ------------------------------------------------------------------------------ combine

@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "mge_common.hpp"
@@ -28,6 +30,43 @@ mge_status hip_check(const char* what) {
     return MGE_ERR_HIP;
   }
   return MGE_OK;
+}
+
+// ------------------------------------------------------------------ per-kernel timing
+struct ProfRecord {
+  const char* name;
+  hipEvent_t start, stop;
+};
+static std::atomic<bool> g_prof_on{false};
+static std::mutex g_prof_mu;
+static std::vector<ProfRecord> g_prof_rec;     // this session's launches, in order
+static std::vector<hipEvent_t> g_prof_pool;    // events kept for reuse across sessions
+
+static hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+ProfScope::ProfScope(hipStream_t s, const char* name) : stream(s), slot(-1) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfRecord r{name, prof_event(), prof_event()};
+  if (!r.start || !r.stop) return;
+  hipEventRecord(r.start, s);
+  slot = int(g_prof_rec.size());
+  g_prof_rec.push_back(r);
+}
+
+ProfScope::~ProfScope() {
+  if (slot < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (slot < int(g_prof_rec.size())) hipEventRecord(g_prof_rec[slot].stop, stream);
 }
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -81,6 +120,38 @@ const char* mge_status_string(mge_status s) {
 const char* mge_last_error(void) { return g_err; }
 
 const char* mge_version(void) { return "0.1.0"; }
+
+mge_status mge_profile_start(void) {
+  g_err[0] = 0;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_prof_rec) {
+    g_prof_pool.push_back(r.start);
+    g_prof_pool.push_back(r.stop);
+  }
+  g_prof_rec.clear();
+  g_prof_on.store(true);
+  return MGE_OK;
+}
+
+int32_t mge_profile_stop(mge_kernel_time* out, int32_t max_records) {
+  g_err[0] = 0;
+  g_prof_on.store(false);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  const int32_t n = int32_t(g_prof_rec.size());
+  for (int32_t i = 0; i < n; ++i) {
+    ProfRecord& r = g_prof_rec[i];
+    float ms = -1.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) {
+      set_error("reading the events of launch %d (%s) failed", i, r.name);
+      ms = -1.f;
+    }
+    if (out && i < max_records) {
+      snprintf(out[i].name, sizeof(out[i].name), "%s", r.name);
+      out[i].ms = ms;
+    }
+  }
+  return n;
+}
 
 // ------------------------------------------------------------------ routing
 static int route_nblk(int T) { return (T + 255) / 256; }
@@ -191,13 +262,31 @@ static mge_status check_mlp_dims(int prec, int E, int H, int F, int T, int k, in
   return MGE_OK;
 }
 
+// Bytes of a packed scale matrix (launch_scale_pack) of `batch` x [rows][kb].
+static size_t packed_bytes(int batch, int rows, int kb) { return up256(size_t(batch) * scale_pack_dwords(rows, kb) * 4); }
+
 static size_t fwd_ws(const mge_fwd_args* a, int R) {
   size_t n = up256(4 * size_t(a->E) * sizeof(void*));
+  const bool mx = a->prec == MGE_PREC_MXFP8;
   if (!a->h) {
-    if (a->prec == MGE_PREC_MXFP8) n += up256(size_t(R) * a->F) + up256(size_t(R) * (a->F / 32));
+    if (mx) n += up256(size_t(R) * a->F) + up256(size_t(R) * (a->F / 32));
     else n += up256(size_t(R) * a->F * 2);
   }
+  if (mx) {
+    n += packed_bytes(1, R, a->H / 32) + packed_bytes(a->E, 2 * a->F, a->H / 32);
+    n += packed_bytes(1, R, a->F / 32) + packed_bytes(a->E, a->H, a->F / 32);
+  }
   return n;
+}
+
+// Every operand the GEMMs address with 32-bit buffer offsets must stay below 2^31 bytes.
+static mge_status check_offsets(int R, int H, int F, int elem) {
+  const int64_t lim = int64_t(1) << 31;
+  const int64_t big = int64_t(R) * 2 * F * elem;            // [R][2F] and [2F][R] forms
+  const int64_t w = int64_t(2) * F * H * elem;               // one expert's W_gate_up
+  MGE_REQUIRE(big < lim && w < lim && int64_t(R) * H * elem < lim,
+              "operand too large for 32-bit offsets (R=%d H=%d F=%d)", R, H, F);
+  return MGE_OK;
 }
 
 size_t mge_fwd_workspace_bytes(const mge_fwd_args* a) {
@@ -260,14 +349,38 @@ mge_status grouped_mlp_fwd(const mge_fwd_args* a, void* stream) {
   }
   const int64_t rows_bound = int64_t(a->T) * a->k;
   const int elem = mx ? 1 : 2;
+  st = check_offsets(R, a->H, a->F, elem);
+  if (st != MGE_OK) return st;
+  const int H = a->H, F = a->F;
+  uint32_t *xs_p = nullptr, *wgu_p = nullptr, *hs_p = nullptr, *wd_p = nullptr;
+  if (mx) {
+    xs_p = static_cast<uint32_t*>(ws.take(packed_bytes(1, R, H / 32)));
+    wgu_p = static_cast<uint32_t*>(ws.take(packed_bytes(E, 2 * F, H / 32)));
+    hs_p = static_cast<uint32_t*>(ws.take(packed_bytes(1, R, F / 32)));
+    wd_p = static_cast<uint32_t*>(ws.take(packed_bytes(E, H, F / 32)));
+    ScalePackParams q{};
+    q.src = a->x_perm_scale; q.ld = H / 32; q.batch = 1; q.rows = R; q.kb = H / 32; q.dst = xs_p;
+    st = launch_scale_pack(q, s);
+    if (st != MGE_OK) return st;
+    ScalePackParams w{};
+    w.src_tab = reinterpret_cast<const uint8_t* const*>(tab + 2 * E); w.ld = H / 32;
+    w.batch = E; w.rows = 2 * F; w.kb = H / 32; w.dst = wgu_p;
+    st = launch_scale_pack(w, s);
+    if (st != MGE_OK) return st;
+    ScalePackParams d{};
+    d.src_tab = reinterpret_cast<const uint8_t* const*>(tab + 3 * E); d.ld = F / 32;
+    d.batch = E; d.rows = H; d.kb = F / 32; d.dst = wd_p;
+    st = launch_scale_pack(d, s);
+    if (st != MGE_OK) return st;
+  }
 
   GemmParams g{};
   g.mode = RAGGED_M; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
   g.A = static_cast<const uint8_t*>(a->x_perm); g.lda = int64_t(a->H) * elem;
-  g.As = a->x_perm_scale; g.ldas = a->H / 32;
+  g.Asp = xs_p; g.asp_ld = R;
   g.Bt = reinterpret_cast<const uint8_t* const*>(tab);
-  g.Bst = reinterpret_cast<const uint8_t* const*>(tab + 2 * E);
-  g.ldb = int64_t(a->H) * elem; g.ldbs = a->H / 32;
+  g.Bsp = wgu_p; g.bsp_ld = 2 * F; g.bsp_estride = scale_pack_dwords(2 * F, H / 32);
+  g.ldb = int64_t(a->H) * elem;
   g.N = 2 * a->F; g.K = a->H; g.F = a->F;
   g.prob = a->prob_perm;
   if (mx) { g.h_codes = static_cast<uint8_t*>(h); g.h_scales = hs; }
@@ -279,20 +392,28 @@ mge_status grouped_mlp_fwd(const mge_fwd_args* a, void* stream) {
   }
   g.Rp = R;
   g.tiles_upper = gemm_tiles_upper(g, rows_bound);
-  st = launch_gemm(g, a->prec, EPI_SWIGLU, s);
+  g.role = GEMM_GATEUP;
+  st = launch_gemm(g, a->prec, s);
   if (st != MGE_OK) return st;
+  if (mx) {
+    ScalePackParams q{};
+    q.src = hs; q.ld = F / 32; q.batch = 1; q.rows = R; q.kb = F / 32; q.dst = hs_p;
+    st = launch_scale_pack(q, s);
+    if (st != MGE_OK) return st;
+  }
 
   GemmParams d{};
   d.mode = RAGGED_M; d.E = E; d.sizes = a->split_sizes; d.offs = a->group_offsets;
   d.A = static_cast<const uint8_t*>(h); d.lda = int64_t(a->F) * elem;
-  d.As = hs; d.ldas = a->F / 32;
+  d.Asp = hs_p; d.asp_ld = R;
   d.Bt = reinterpret_cast<const uint8_t* const*>(tab + E);
-  d.Bst = reinterpret_cast<const uint8_t* const*>(tab + 3 * E);
-  d.ldb = int64_t(a->F) * elem; d.ldbs = a->F / 32;
+  d.Bsp = wd_p; d.bsp_ld = H; d.bsp_estride = scale_pack_dwords(H, F / 32);
+  d.ldb = int64_t(a->F) * elem;
   d.N = a->H; d.K = a->F;
   d.out_dtype = a->y_dtype; d.C = a->y_perm; d.ldc = a->H;
   d.tiles_upper = gemm_tiles_upper(d, rows_bound);
-  return launch_gemm(d, a->prec, EPI_STORE, s);
+  d.role = GEMM_DOWN;
+  return launch_gemm(d, a->prec, s);
 }
 
 // ------------------------------------------------------------------ backward
@@ -309,6 +430,13 @@ static size_t bwd_ws(const mge_bwd_args* a, int R, int nparts) {
   if (!a->dgu_row) n += mat(R, F2);
   if (!a->dgu_col) n += mat(F2, R);
   if (!mx) n += E * (up256(F * H * 2) + up256(H * F2 * 2));   // bf16 transposed weights
+  if (mx) {
+    const int r = R, h = int(H), f = int(F), f2 = int(F2), e = int(E);
+    n += packed_bytes(1, r, h / 32) + packed_bytes(e, f, h / 32);      // dh GEMM: dY row, W_down col
+    n += packed_bytes(1, h, r / 32) + packed_bytes(1, f, r / 32);      // dW_down: dY col, h col
+    n += packed_bytes(1, r, f2 / 32) + packed_bytes(e, h, f2 / 32);    // dX: dGU row, W_gate_up col
+    n += packed_bytes(1, f2, r / 32) + packed_bytes(1, h, r / 32);     // dW_gate_up: dGU col, x col
+  }
   return n;
 }
 
@@ -418,21 +546,57 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
     if (st != MGE_OK) return st;
   }
   const int64_t rows_bound = int64_t(a->T) * a->k;
+  st = check_offsets(R, H, F, elem);
+  if (st != MGE_OK) return st;
+  // packed scales of every MX operand (the GEMMs read one dword per row and K slice)
+  uint32_t *dyr_p = nullptr, *wdc_p = nullptr, *dyc_p = nullptr, *hc_p = nullptr;
+  uint32_t *dgr_p = nullptr, *wguc_p = nullptr, *dgc_p = nullptr, *xc_p = nullptr;
+  auto pack = [&](const uint8_t* src, const uint8_t* const* src_tab, int batch, int rows, int kb,
+                  const int32_t* kb_valid, uint32_t* dst) {
+    ScalePackParams q{};
+    q.src = src; q.src_tab = src_tab; q.ld = kb; q.batch = batch; q.rows = rows; q.kb = kb;
+    q.kb_valid = kb_valid; q.dst = dst;
+    return launch_scale_pack(q, s);
+  };
+  const int32_t* rows_written = a->group_offsets + E;   // column forms from epilogues end here
+  if (mx) {
+    dyr_p = static_cast<uint32_t*>(ws.take(packed_bytes(1, R, H / 32)));
+    wdc_p = static_cast<uint32_t*>(ws.take(packed_bytes(E, F, H / 32)));
+    dyc_p = static_cast<uint32_t*>(ws.take(packed_bytes(1, H, R / 32)));
+    hc_p = static_cast<uint32_t*>(ws.take(packed_bytes(1, F, R / 32)));
+    dgr_p = static_cast<uint32_t*>(ws.take(packed_bytes(1, R, F2 / 32)));
+    wguc_p = static_cast<uint32_t*>(ws.take(packed_bytes(E, H, F2 / 32)));
+    dgc_p = static_cast<uint32_t*>(ws.take(packed_bytes(1, F2, R / 32)));
+    xc_p = static_cast<uint32_t*>(ws.take(packed_bytes(1, H, R / 32)));
+    st = pack(dyrs, nullptr, 1, R, H / 32, nullptr, dyr_p);
+    if (st == MGE_OK) st = pack(nullptr, reinterpret_cast<const uint8_t* const*>(tab + 2 * E), E, F, H / 32, nullptr, wdc_p);
+    if (st == MGE_OK) st = pack(dycs, nullptr, 1, H, R / 32, nullptr, dyc_p);
+    if (st == MGE_OK) st = pack(a->h_col_scale, nullptr, 1, F, R / 32, rows_written, hc_p);
+    if (st == MGE_OK) st = pack(nullptr, reinterpret_cast<const uint8_t* const*>(tab + 3 * E), E, H, F2 / 32, nullptr, wguc_p);
+    if (st == MGE_OK) st = pack(a->x_col_scale, nullptr, 1, H, R / 32, nullptr, xc_p);
+    if (st != MGE_OK) return st;
+  }
   // b2: dh = dY W_down with the SwiGLU backward + d_prob partial epilogue
   {
     GemmParams g{};
     g.mode = RAGGED_M; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
-    g.A = static_cast<const uint8_t*>(dyr); g.lda = int64_t(H) * elem; g.As = dyrs; g.ldas = H / 32;
+    g.A = static_cast<const uint8_t*>(dyr); g.lda = int64_t(H) * elem; g.Asp = dyr_p; g.asp_ld = R;
     g.Bt = reinterpret_cast<const uint8_t* const*>(tab);
-    g.Bst = reinterpret_cast<const uint8_t* const*>(tab + 2 * E);
-    g.ldb = int64_t(H) * elem; g.ldbs = H / 32;
+    g.Bsp = wdc_p; g.bsp_ld = F; g.bsp_estride = scale_pack_dwords(F, H / 32);
+    g.ldb = int64_t(H) * elem;
     g.N = F; g.K = H; g.F = F;
     g.prob = a->prob_perm; g.gu = a->saved_gu;
     if (mx) { g.dgu_codes = static_cast<uint8_t*>(dgr); g.dgu_scales = dgrs; g.dguc_codes = static_cast<uint8_t*>(dgc); g.dguc_scales = dgcs; }
     else { g.dgu_bf16 = static_cast<uint16_t*>(dgr); g.dguc_bf16 = static_cast<uint16_t*>(dgc); }
     g.dprob_part = part; g.nparts = nparts; g.Rp = R;
     g.tiles_upper = gemm_tiles_upper(g, rows_bound);
-    st = launch_gemm(g, a->prec, EPI_SWIGLU_BWD, s);
+    g.role = GEMM_DH;
+    st = launch_gemm(g, a->prec, s);
+    if (st != MGE_OK) return st;
+  }
+  if (mx) {
+    st = pack(dgrs, nullptr, 1, R, F2 / 32, nullptr, dgr_p);
+    if (st == MGE_OK) st = pack(dgcs, nullptr, 1, F2, R / 32, rows_written, dgc_p);
     if (st != MGE_OK) return st;
   }
   // b3: d_prob
@@ -442,40 +606,43 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
   {
     GemmParams g{};
     g.mode = RAGGED_K; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
-    g.A = static_cast<const uint8_t*>(dyc); g.lda = int64_t(R) * elem; g.As = dycs; g.ldas = R / 32;
-    g.B = static_cast<const uint8_t*>(a->h_col); g.Bs = a->h_col_scale; g.ldb = int64_t(R) * elem; g.ldbs = R / 32;
+    g.A = static_cast<const uint8_t*>(dyc); g.lda = int64_t(R) * elem; g.Asp = dyc_p; g.asp_ld = H;
+    g.B = static_cast<const uint8_t*>(a->h_col); g.ldb = int64_t(R) * elem; g.Bsp = hc_p; g.bsp_ld = F;
     g.M = H; g.N = F;
     g.out_dtype = MGE_DTYPE_F32; g.Ct = reinterpret_cast<void* const*>(tab + 4 * E); g.ldc = F;
     g.accumulate = a->accumulate;
     g.tiles_upper = gemm_tiles_upper(g, rows_bound);
-    st = launch_gemm(g, a->prec, EPI_STORE, s);
+    g.role = GEMM_DW_DOWN;
+    st = launch_gemm(g, a->prec, s);
     if (st != MGE_OK) return st;
   }
   // b5: dX = dGU W_gate_up  (K = 2F)
   {
     GemmParams g{};
     g.mode = RAGGED_M; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
-    g.A = static_cast<const uint8_t*>(dgr); g.lda = int64_t(F2) * elem; g.As = dgrs; g.ldas = F2 / 32;
+    g.A = static_cast<const uint8_t*>(dgr); g.lda = int64_t(F2) * elem; g.Asp = dgr_p; g.asp_ld = R;
     g.Bt = reinterpret_cast<const uint8_t* const*>(tab + E);
-    g.Bst = reinterpret_cast<const uint8_t* const*>(tab + 3 * E);
-    g.ldb = int64_t(F2) * elem; g.ldbs = F2 / 32;
+    g.Bsp = wguc_p; g.bsp_ld = H; g.bsp_estride = scale_pack_dwords(H, F2 / 32);
+    g.ldb = int64_t(F2) * elem;
     g.N = H; g.K = F2;
     g.out_dtype = MGE_DTYPE_BF16; g.C = a->dx_perm; g.ldc = H;
     g.tiles_upper = gemm_tiles_upper(g, rows_bound);
-    st = launch_gemm(g, a->prec, EPI_STORE, s);
+    g.role = GEMM_DX;
+    st = launch_gemm(g, a->prec, s);
     if (st != MGE_OK) return st;
   }
   // b6: dW_gate_up[e] = dGU_e^T X_e  (K = tokens of e)
   {
     GemmParams g{};
     g.mode = RAGGED_K; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
-    g.A = static_cast<const uint8_t*>(dgc); g.lda = int64_t(R) * elem; g.As = dgcs; g.ldas = R / 32;
-    g.B = static_cast<const uint8_t*>(a->x_col); g.Bs = a->x_col_scale; g.ldb = int64_t(R) * elem; g.ldbs = R / 32;
+    g.A = static_cast<const uint8_t*>(dgc); g.lda = int64_t(R) * elem; g.Asp = dgc_p; g.asp_ld = F2;
+    g.B = static_cast<const uint8_t*>(a->x_col); g.ldb = int64_t(R) * elem; g.Bsp = xc_p; g.bsp_ld = H;
     g.M = F2; g.N = H;
     g.out_dtype = MGE_DTYPE_F32; g.Ct = reinterpret_cast<void* const*>(tab + 5 * E); g.ldc = H;
     g.accumulate = a->accumulate;
     g.tiles_upper = gemm_tiles_upper(g, rows_bound);
-    st = launch_gemm(g, a->prec, EPI_STORE, s);
+    g.role = GEMM_DW_GATEUP;
+    st = launch_gemm(g, a->prec, s);
   }
   return st;
 }

@@ -70,6 +70,7 @@ mge_status launch_combine(int T, int k, int H, int in_dtype, int out_dtype, cons
                           const int32_t* perm_pos, const float* weights, void* out, hipStream_t s) {
   if (T <= 0) return MGE_OK;
   dim3 g(T), b(CB_THREADS);
+  ProfScope prof(s, "combine");
   if (in_dtype == MGE_DTYPE_BF16 && out_dtype == MGE_DTYPE_BF16)
     hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t>), g, b, 0, s, k, H, (const uint16_t*)in, perm_pos,
                        weights, (uint16_t*)out);
@@ -100,6 +101,7 @@ mge_status launch_dprob_reduce(int T, int k, int nparts, const float* partial, c
                                float* d_prob, hipStream_t s) {
   int n = T * k;
   if (n <= 0) return MGE_OK;
+  ProfScope prof(s, "dprob_reduce");
   hipLaunchKernelGGL(dprob_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, s, n, nparts, partial, perm_pos,
                      d_prob);
   return hip_check("dprob_reduce_kernel");
@@ -125,6 +127,7 @@ mge_status launch_upload_ptrs(const void* const* host_ptrs, int n, void** dev_ta
     c.dst = dev_table + base;
     c.n = (n - base) < UP_CHUNK ? (n - base) : UP_CHUNK;
     for (int i = 0; i < c.n; ++i) c.p[i] = host_ptrs[base + i];
+    ProfScope prof(s, "upload_ptrs");
     hipLaunchKernelGGL(upload_ptrs_kernel, dim3(1), dim3(UP_CHUNK), 0, s, c);
   }
   return hip_check("upload_ptrs_kernel");

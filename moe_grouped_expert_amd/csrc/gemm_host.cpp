@@ -1,0 +1,31 @@
+// Host side of the grouped GEMM: tile-count bounds for grid sizing, the number of
+// d_prob partial sums, and the dispatch to the per-precision kernel sets.
+#include "gemm_impl.hpp"
+
+namespace mge {
+
+mge_status launch_gemm_mx(const GemmParams& p, hipStream_t s);
+mge_status launch_gemm_bf16(const GemmParams& p, hipStream_t s);
+
+int gemm_swiglu_bwd_nparts(int F) { return ((F + G_BN - 1) / G_BN) * G_WAVES_N; }
+
+int gemm_tiles_upper(const GemmParams& p, int64_t total_rows_bound) {
+  int64_t nt = (int64_t(p.N) + G_BN - 1) / G_BN;
+  if (p.mode == RAGGED_M) {
+    int64_t mt = (total_rows_bound + G_BM - 1) / G_BM + p.E;
+    return int(mt * nt);
+  }
+  int64_t mt = (int64_t(p.M) + G_BM - 1) / G_BM;
+  return int(mt * nt * p.E);
+}
+
+mge_status launch_gemm(const GemmParams& p, int prec, hipStream_t s) {
+  const bool k_mode = p.role == GEMM_DW_DOWN || p.role == GEMM_DW_GATEUP;
+  if ((p.mode == RAGGED_K) != k_mode) {
+    set_error("GEMM role %d does not match mode %d", p.role, p.mode);
+    return MGE_ERR_INVALID_ARG;
+  }
+  return prec == MGE_PREC_MXFP8 ? launch_gemm_mx(p, s) : launch_gemm_bf16(p, s);
+}
+
+}  // namespace mge

@@ -35,6 +35,8 @@
 //                   16 in its partner lane 32 apart)
 //   EPI_SWIGLU_BWD  dh -> dG, dU (with saved G, U, p) quantized row- and column-wise,
 //                   plus per-row partial sums of dh * silu(G) * U for d_prob
+#pragma once
+
 #include "mge_common.hpp"
 #include "mge_internal.hpp"
 
@@ -45,6 +47,7 @@ namespace mge {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int G_WAVES_M = 2;
 constexpr int G_WAVES_N = 2;
@@ -57,6 +60,11 @@ constexpr int G_THREADS = 64 * G_WAVES_M * G_WAVES_N;
 constexpr int G_STAGE_BYTES = (G_BM + G_BN) * G_BKB;
 constexpr int G_LDS_BYTES = 2 * G_STAGE_BYTES;
 constexpr int G_MAXE = 256;
+// Buffer-resource word 3 of the gfx9 family (raw buffer, 32-bit dwords), the record
+// bound, and the offset that lies beyond it (such a lane loads zeros).
+constexpr int kRsrcFlags = 0x00020000;
+constexpr int kRsrcRecords = 0x7fffffff;
+constexpr uint32_t kInvalid = 0x80000000u;   // OR-ed into an offset: the lane reads zeros
 
 static_assert(G_THREADS == 256, "loader assumes 256 threads");
 
@@ -70,6 +78,17 @@ __device__ __forceinline__ void static_for(Fn&& fn) {
   }
 }
 
+// Values that are the same in every lane, moved to scalar registers so that buffer
+// resources and LDS-DMA destinations need no per-lane handling.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<const T*>((uint64_t(hi) << 32) | lo);
+}
+
 __device__ __forceinline__ int swz(int row, int chunk) { return row * G_BKB + ((chunk ^ (row & 7)) << 4); }
 
 struct TileInfo {
@@ -79,15 +98,32 @@ struct TileInfo {
   int k_len;            // reduction length in elements
 };
 
-template <bool MX, int EPI>
-__global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmParams p) {
+// Raw buffer resource over `base` (gfx9 word 3, full 31-bit range).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base) {
+  const uint64_t v = reinterpret_cast<uint64_t>(base);
+  return i32x4{int(uint32_t(v)), int(uint32_t(v >> 32) & 0xffff), kRsrcRecords, kRsrcFlags};
+}
+
+// 16 bytes per lane from buffer offset `voff` straight into LDS at lds_addr + 16*lane
+// (buffer_load_dwordx4 ... lds; M0 holds the wave's LDS destination).  Written as asm
+// so the compiler neither waits on it before unrelated LDS reads nor reorders LDS
+// accesses across it; the caller waits (vmcnt) and synchronizes before reading.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+template <bool MX, int EPI, int MODE>
+__device__ __forceinline__ void gemm_body(const GemmParams& p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // LDS byte address of the dynamic shared block (the low half of its generic address)
+  const uint32_t lds_base = uniform(int(uint32_t(reinterpret_cast<uintptr_t>(smem))));
   __shared__ int32_t s_prefix[G_MAXE + 1];
   __shared__ int32_t s_mtiles[G_MAXE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = uniform(tid >> 6);
   const int wm = wave / G_WAVES_N;
   const int wn = wave % G_WAVES_N;
   const int l32 = lane & 31;
@@ -101,7 +137,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmParams p
   if (tid == 0) {
     int acc = 0;
     for (int e = 0; e < p.E; ++e) {
-      int mt = p.mode == RAGGED_M ? (p.sizes[e] + G_BM - 1) / G_BM : (p.M + G_BM - 1) / G_BM;
+      int mt = MODE == RAGGED_M ? (p.sizes[e] + G_BM - 1) / G_BM : (p.M + G_BM - 1) / G_BM;
       s_prefix[e] = acc;
       s_mtiles[e] = mt;
       acc += mt * ntiles;
@@ -109,7 +145,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmParams p
     s_prefix[p.E] = acc;
   }
   __syncthreads();
-  const int total = s_prefix[p.E];
+  const int total = uniform(s_prefix[p.E]);
   const int nwg = gridDim.x;
   int vid = blockIdx.x;
   if ((nwg & 7) == 0) vid = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
@@ -121,110 +157,121 @@ __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmParams p
       int mid = (lo + hi_ + 1) >> 1;
       if (s_prefix[mid] <= tile) lo = mid; else hi_ = mid - 1;
     }
-    const int e = lo;
-    const int local = tile - s_prefix[e];
-    const int mtn = s_mtiles[e];
+    // every tile quantity is wave-uniform: keep it in scalar registers
+    const int e = uniform(lo);
+    const int local = tile - uniform(s_prefix[e]);
+    const int mtn = uniform(s_mtiles[e]);
     const int mt = local % mtn;
     const int nt = local / mtn;
-    const int off = p.offs[e];
-    const int m_valid = p.mode == RAGGED_M ? p.sizes[e] : p.M;
-    const int k_len = p.mode == RAGGED_M ? p.K : ((p.sizes[e] + 31) / 32) * 32;
+    const int off = uniform(p.offs[e]);
+    const int m_valid = MODE == RAGGED_M ? uniform(p.sizes[e]) : p.M;
     const int m0 = mt * G_BM;
-    const int kbytes = k_len * ELEM;
-    const int nkt = (kbytes + G_BKB - 1) / G_BKB;
-
-    // ---- operand bases
-    const uint8_t* Abase;
-    const uint8_t* Asbase = nullptr;
-    const uint8_t* Bbase;
-    const uint8_t* Bsbase = nullptr;
-    if (p.mode == RAGGED_M) {
-      Abase = p.A + int64_t(off) * p.lda;
-      Bbase = p.Bt[e];
-      if (MX) { Asbase = p.As + int64_t(off) * p.ldas; Bsbase = p.Bst[e]; }
+    // K range in bytes.  RAGGED_M: [0, K).  RAGGED_K: the expert's token span
+    // [off, off + roundup32(size)) of the column forms; the loop starts at the slice
+    // boundary below it and the chunks outside the span load as zeros.
+    int kbase, klo, khi;
+    if constexpr (MODE == RAGGED_M) {
+      kbase = 0; klo = 0; khi = p.K * ELEM;
     } else {
-      Abase = p.A + int64_t(off) * ELEM;
-      Bbase = p.B + int64_t(off) * ELEM;
-      if (MX) { Asbase = p.As + off / 32; Bsbase = p.Bs + off / 32; }
+      const int span = ((uniform(p.sizes[e]) + 31) / 32) * 32;
+      klo = off * ELEM;
+      khi = (off + span) * ELEM;
+      kbase = span > 0 ? (klo / G_BKB) * G_BKB : klo;
     }
+    const int nkt = (khi - kbase + G_BKB - 1) / G_BKB;
 
-    // ---- loader geometry: thread -> chunk (tid & 7), rows (tid >> 3) + 32 i
-    const int lchunk = tid & 7;
-    const int lrow = tid >> 3;
-    int64_t a_off[G_BM / 32];
-    int64_t b_off[G_BN / 32];
-#pragma unroll
-    for (int i = 0; i < G_BM / 32; ++i) {
-      int r = m0 + lrow + 32 * i;
-      int rmax = m_valid - 1;
-      r = r > rmax ? rmax : r;
-      r = r < 0 ? 0 : r;
-      a_off[i] = int64_t(r) * p.lda;
+    // ---- operands as buffer resources: a lane whose offset is kInvalid reads zeros
+    // (rows past the group, chunks outside the K range), so tails need no extra path.
+    const uint8_t* Abase;
+    const uint8_t* Bbase;
+    if constexpr (MODE == RAGGED_M) {
+      Abase = p.A + int64_t(off) * p.lda;
+      Bbase = uniform_ptr(p.Bt[e]);
+    } else {
+      Abase = p.A;
+      Bbase = p.B;
     }
+    const i32x4 rsrcA = make_rsrc(Abase);
+    const i32x4 rsrcB = make_rsrc(Bbase);
+
+    // ---- loader geometry: wave instruction i fills LDS rows [(wave*8+i)*8, +8) of a
+    // 256-row operand tile, 1 KB contiguous (lane l -> row +l/8, LDS chunk l%8).  The
+    // lane loads the global chunk that the XOR swizzle maps to that LDS chunk.
+    const int lchunk = (lane & 7) ^ (lane >> 3);
+    uint32_t a_off[8], b_off[8];
 #pragma unroll
-    for (int i = 0; i < G_BN / 32; ++i) {
-      int r = lrow + 32 * i;   // row of the B tile
+    for (int i = 0; i < 8; ++i) {
+      const int r = wave * 64 + i * 8 + (lane >> 3);   // row within the tile
+      const int ra = m0 + r;
+      a_off[i] = ra < m_valid ? uint32_t(ra) * uint32_t(p.lda) + lchunk * 16 : kInvalid;
       int grow;
-      if (EPI == EPI_SWIGLU) {
-        int half = G_BN / 2;
-        int f = nt * half + (r % half);
-        f = f >= p.F ? p.F - 1 : f;
-        grow = r < half ? f : p.F + f;
+      if constexpr (EPI == EPI_SWIGLU) {
+        constexpr int half = G_BN / 2;
+        const int f = nt * half + (r % half);
+        grow = f < p.F ? (r < half ? f : p.F + f) : -1;
       } else {
         grow = nt * G_BN + r;
-        grow = grow >= p.N ? p.N - 1 : grow;
+        grow = grow < p.N ? grow : -1;
       }
-      b_off[i] = int64_t(grow) * p.ldb;
+      b_off[i] = grow >= 0 ? uint32_t(grow) * uint32_t(p.ldb) + lchunk * 16 : kInvalid;
     }
-
-    uint4 ra[G_BM / 32], rb[G_BN / 32];
-    auto gload = [&](int kt) {
-      const int kb = kt * G_BKB + lchunk * 16;
-      const bool ok = kb < kbytes;
+    auto issue_loads = [&](int kt, int buf) {
+      // chunks outside [klo, khi) get the top offset bit set (-> zeros); arithmetic
+      // rather than a select so the loads stay straight-line code
+      const int kslice = kbase + kt * G_BKB;          // first byte of the slice
+      const int kb = kslice + lchunk * 16;             // this lane's chunk (a_off/b_off hold the chunk term)
+      const uint32_t out = ((uint32_t(kb - klo) | uint32_t(khi - 1 - kb)) >> 31) << 31;
+      const uint32_t kadd = uint32_t(kslice);
+      const uint32_t la = lds_base + buf * G_STAGE_BYTES + wave * 8 * 1024;
+      const uint32_t lb = la + G_BM * G_BKB;
 #pragma unroll
-      for (int i = 0; i < G_BM / 32; ++i)
-        ra[i] = ok ? *reinterpret_cast<const uint4*>(Abase + a_off[i] + kb) : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < 8; ++i) dma16(rsrcA, la + i * 1024, (a_off[i] + kadd) | out);
 #pragma unroll
-      for (int i = 0; i < G_BN / 32; ++i)
-        rb[i] = ok ? *reinterpret_cast<const uint4*>(Bbase + b_off[i] + kb) : make_uint4(0, 0, 0, 0);
-    };
-    auto lstore = [&](int buf) {
-      uint8_t* sA = smem + buf * G_STAGE_BYTES;
-      uint8_t* sB = sA + G_BM * G_BKB;
-#pragma unroll
-      for (int i = 0; i < G_BM / 32; ++i) *reinterpret_cast<uint4*>(sA + swz(lrow + 32 * i, lchunk)) = ra[i];
-#pragma unroll
-      for (int i = 0; i < G_BN / 32; ++i) *reinterpret_cast<uint4*>(sB + swz(lrow + 32 * i, lchunk)) = rb[i];
+      for (int i = 0; i < 8; ++i) dma16(rsrcB, lb + i * 1024, (b_off[i] + kadd) | out);
     };
 
-    // ---- MX scales for this lane's fragments (rows of the wave's M and N blocks)
-    int64_t sa_row[G_WMB], sb_row[G_WNB];
+    // ---- MX scales: packed as one dword per (row, 128-element slice) holding the 4
+    // E8M0 bytes of that slice, rows contiguous, so the 32 lanes of a block read 128
+    // consecutive bytes.
     int brow_tile[G_WNB];
 #pragma unroll
     for (int ni = 0; ni < G_WNB; ++ni) {
-      int r;
-      if (EPI == EPI_SWIGLU) {
+      if constexpr (EPI == EPI_SWIGLU) {
         constexpr int hb = G_WNB / 2;
-        r = ni < hb ? (wn * hb + ni) * 32 : G_BN / 2 + (wn * hb + ni - hb) * 32;
+        brow_tile[ni] = ni < hb ? (wn * hb + ni) * 32 : G_BN / 2 + (wn * hb + ni - hb) * 32;
       } else {
-        r = (wn * G_WNB + ni) * 32;
+        brow_tile[ni] = (wn * G_WNB + ni) * 32;
       }
-      brow_tile[ni] = r;
     }
-    if (MX) {
+    const uint32_t* sa_ptr[G_WMB];
+    const uint32_t* sb_ptr[G_WNB];
+    int64_t sa_step = 0, sb_step = 0;
+    if constexpr (MX) {
+      int64_t j0 = MODE == RAGGED_M ? 0 : kbase / 128;   // first packed slice
+      const uint32_t* Ap;
+      const uint32_t* Bp;
+      if constexpr (MODE == RAGGED_M) {
+        Ap = p.Asp + off;
+        Bp = p.Bsp + int64_t(e) * p.bsp_estride;
+      } else {
+        Ap = p.Asp;
+        Bp = p.Bsp;
+      }
+      sa_step = p.asp_ld;
+      sb_step = p.bsp_ld;
 #pragma unroll
       for (int mi = 0; mi < G_WMB; ++mi) {
         int r = m0 + (wm * G_WMB + mi) * 32 + l32;
         r = r >= m_valid ? m_valid - 1 : r;
         r = r < 0 ? 0 : r;
-        sa_row[mi] = int64_t(r) * p.ldas;
+        sa_ptr[mi] = Ap + j0 * sa_step + r;
       }
 #pragma unroll
       for (int ni = 0; ni < G_WNB; ++ni) {
-        int r = brow_tile[ni] + l32;
+        const int r = brow_tile[ni] + l32;
         int grow;
-        if (EPI == EPI_SWIGLU) {
-          int half = G_BN / 2;
+        if constexpr (EPI == EPI_SWIGLU) {
+          constexpr int half = G_BN / 2;
           int f = nt * half + (r % half);
           f = f >= p.F ? p.F - 1 : f;
           grow = r < half ? f : p.F + f;
@@ -232,37 +279,19 @@ __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmParams p
           grow = nt * G_BN + r;
           grow = grow >= p.N ? p.N - 1 : grow;
         }
-        sb_row[ni] = int64_t(grow) * p.ldbs;
+        sb_ptr[ni] = Bp + j0 * sb_step + grow;
       }
     }
+    // raw packed dwords; the lane's byte (block 4kt + hi, and + 2 for the second
+    // 64-element step) is selected at the MFMA by shift + op_sel, so a load is only
+    // waited for where it is used
     uint32_t sa[G_WMB], sb[G_WNB];
     uint32_t nsa[G_WMB], nsb[G_WNB];
-    const int kblocks = k_len / 32;
     auto sload = [&](int kt, uint32_t* da, uint32_t* db) {
-      // 4 scale bytes (one per 32-element block) of this K slice; blocks past the end
-      // read as 127 (scale 1) — their codes are zero.
 #pragma unroll
-      for (int mi = 0; mi < G_WMB; ++mi) {
-        uint32_t w = 0;
+      for (int mi = 0; mi < G_WMB; ++mi) da[mi] = sa_ptr[mi][kt * sa_step];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          int kb = kt * 4 + j;
-          uint32_t v = kb < kblocks ? uint32_t(Asbase[sa_row[mi] + kb]) : 127u;
-          w |= v << (8 * j);
-        }
-        da[mi] = w >> (8 * hi);
-      }
-#pragma unroll
-      for (int ni = 0; ni < G_WNB; ++ni) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          int kb = kt * 4 + j;
-          uint32_t v = kb < kblocks ? uint32_t(Bsbase[sb_row[ni] + kb]) : 127u;
-          w |= v << (8 * j);
-        }
-        db[ni] = w >> (8 * hi);
-      }
+      for (int ni = 0; ni < G_WNB; ++ni) db[ni] = sb_ptr[ni][kt * sb_step];
     };
 
     f32x16 acc[G_WMB][G_WNB];
@@ -273,85 +302,92 @@ __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmParams p
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
-    __syncthreads();   // previous tile's LDS readers (epilogue) are done
+    // MFMA operand fragments of one K step, read from the swizzled LDS tile:
+    //   MX  : 64-element step s of the slice; lane (hi, l32) takes 16-byte chunks
+    //         4s + hi and 4s + hi + 2 of its row
+    //   BF16: 16-element step s; lane takes chunk 2s + hi
+    typedef typename std::conditional<MX, i32x8, bf16x8>::type frag_t;
+    constexpr int NSTEP = MX ? 2 : 4;
+    auto read_frags = [&](const uint8_t* sA, const uint8_t* sB, int s, frag_t* af, frag_t* bfr) {
+#pragma unroll
+      for (int mi = 0; mi < G_WMB; ++mi) {
+        const int row = (wm * G_WMB + mi) * 32 + l32;
+        if constexpr (MX) {
+          const int c = s * 4 + hi;
+          const uint4 x0 = *reinterpret_cast<const uint4*>(sA + swz(row, c));
+          const uint4 x1 = *reinterpret_cast<const uint4*>(sA + swz(row, c + 2));
+          af[mi] = i32x8{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
+        } else {
+          af[mi] = *reinterpret_cast<const bf16x8*>(sA + swz(row, s * 2 + hi));
+        }
+      }
+#pragma unroll
+      for (int ni = 0; ni < G_WNB; ++ni) {
+        const int row = brow_tile[ni] + l32;
+        if constexpr (MX) {
+          const int c = s * 4 + hi;
+          const uint4 x0 = *reinterpret_cast<const uint4*>(sB + swz(row, c));
+          const uint4 x1 = *reinterpret_cast<const uint4*>(sB + swz(row, c + 2));
+          bfr[ni] = i32x8{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
+        } else {
+          bfr[ni] = *reinterpret_cast<const bf16x8*>(sB + swz(row, s * 2 + hi));
+        }
+      }
+    };
+    auto mfma_step = [&](int s, const frag_t* af, const frag_t* bfr) {
+#pragma unroll
+      for (int mi = 0; mi < G_WMB; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < G_WNB; ++ni) {
+          if constexpr (MX) {
+            const int xa = int(sa[mi] >> (8 * hi));
+            const int xb = int(sb[ni] >> (8 * hi));
+            if (s == 0)
+              acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0, xa, 0,
+                                                                            xb);
+            else
+              acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bfr[ni], acc[mi][ni], 0, 0, 2, xa, 2,
+                                                                            xb);
+          } else {
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+          }
+        }
+    };
+
+    __syncthreads();   // previous tile's LDS readers are done
     if (nkt > 0) {
-      gload(0);
-      if (MX) sload(0, sa, sb);
-      lstore(0);
+      issue_loads(0, 0);
+      if constexpr (MX) sload(0, sa, sb);
     }
+    __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) lgkmcnt(0): the LDS copies have landed
     __syncthreads();
     for (int kt = 0; kt < nkt; ++kt) {
       const int buf = kt & 1;
-      const bool more = kt + 1 < nkt;
-      if (more) {
-        gload(kt + 1);
-        if (MX) sload(kt + 1, nsa, nsb);
-      }
+      // 1. the next slice streams into the other LDS buffer while this one is used
+      //    (past the last slice every chunk is out of range and loads zeros: no branch)
+      issue_loads(kt + 1, buf ^ 1);
+      if constexpr (MX) sload(kt + 1 < nkt ? kt + 1 : kt, nsa, nsb);
+      __builtin_amdgcn_sched_barrier(0);
+      // 2. MFMAs on this slice; the fragments of step s+1 are read while step s runs
       const uint8_t* sA = smem + buf * G_STAGE_BYTES;
       const uint8_t* sB = sA + G_BM * G_BKB;
-      if (MX) {
+      frag_t af[2][G_WMB], bfr[2][G_WNB];
+      read_frags(sA, sB, 0, af[0], bfr[0]);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          i32x8 af[G_WMB], bfr[G_WNB];
-#pragma unroll
-          for (int mi = 0; mi < G_WMB; ++mi) {
-            int row = (wm * G_WMB + mi) * 32 + l32;
-            int c = s * 4 + hi;
-            uint4 x0 = *reinterpret_cast<const uint4*>(sA + swz(row, c));
-            uint4 x1 = *reinterpret_cast<const uint4*>(sA + swz(row, c + 2));
-            af[mi] = i32x8{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
-          }
-#pragma unroll
-          for (int ni = 0; ni < G_WNB; ++ni) {
-            int row = brow_tile[ni] + l32;
-            int c = s * 4 + hi;
-            uint4 x0 = *reinterpret_cast<const uint4*>(sB + swz(row, c));
-            uint4 x1 = *reinterpret_cast<const uint4*>(sB + swz(row, c + 2));
-            bfr[ni] = i32x8{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
-          }
-#pragma unroll
-          for (int mi = 0; mi < G_WMB; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < G_WNB; ++ni) {
-              if (s == 0)
-                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0,
-                                                                              int(sa[mi]), 0, int(sb[ni]));
-              else
-                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bfr[ni], acc[mi][ni], 0, 0, 2,
-                                                                              int(sa[mi]), 2, int(sb[ni]));
-            }
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          bf16x8 af[G_WMB], bfr[G_WNB];
-#pragma unroll
-          for (int mi = 0; mi < G_WMB; ++mi) {
-            int row = (wm * G_WMB + mi) * 32 + l32;
-            af[mi] = *reinterpret_cast<const bf16x8*>(sA + swz(row, s * 2 + hi));
-          }
-#pragma unroll
-          for (int ni = 0; ni < G_WNB; ++ni) {
-            int row = brow_tile[ni] + l32;
-            bfr[ni] = *reinterpret_cast<const bf16x8*>(sB + swz(row, s * 2 + hi));
-          }
-#pragma unroll
-          for (int mi = 0; mi < G_WMB; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < G_WNB; ++ni)
-              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
-        }
+      for (int s = 0; s < NSTEP; ++s) {
+        if (s + 1 < NSTEP) read_frags(sA, sB, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
+        mfma_step(s, af[s & 1], bfr[s & 1]);
       }
-      if (more) {
-        lstore(buf ^ 1);
-        if (MX) {
-#pragma unroll
-          for (int mi = 0; mi < G_WMB; ++mi) sa[mi] = nsa[mi];
-#pragma unroll
-          for (int ni = 0; ni < G_WNB; ++ni) sb[ni] = nsb[ni];
-        }
-      }
+      __builtin_amdgcn_sched_barrier(0);
+      // 3. the next slice is resident and every wave is done with this one
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+      if constexpr (MX) {
+#pragma unroll
+        for (int mi = 0; mi < G_WMB; ++mi) sa[mi] = nsa[mi];
+#pragma unroll
+        for (int ni = 0; ni < G_WNB; ++ni) sb[ni] = nsb[ni];
+      }
     }
 
     // ---------------------------------------------------------------- epilogues
@@ -370,7 +406,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmParams p
             const int row = wrow0 + mi * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
             float v = acc[mi][ni][r];
             if (cok && row < m_valid) {
-              if (p.mode == RAGGED_M) {
+              if constexpr (MODE == RAGGED_M) {
                 int64_t idx = int64_t(off + row) * p.ldc + col;
                 if (p.out_dtype == MGE_DTYPE_BF16) reinterpret_cast<uint16_t*>(p.C)[idx] = f32_to_bf16(v);
                 else reinterpret_cast<float*>(p.C)[idx] = v;
@@ -576,20 +612,8 @@ __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmParams p
   }
 }
 
-int gemm_swiglu_bwd_nparts(int F) { return ((F + G_BN - 1) / G_BN) * G_WAVES_N; }
-
-int gemm_tiles_upper(const GemmParams& p, int64_t total_rows_bound) {
-  const int ncols_per_tile = G_BN;
-  int64_t nt = (int64_t(p.N) + ncols_per_tile - 1) / ncols_per_tile;
-  if (p.mode == RAGGED_M) {
-    int64_t mt = (total_rows_bound + G_BM - 1) / G_BM + p.E;
-    return int(mt * nt);
-  }
-  int64_t mt = (int64_t(p.M) + G_BM - 1) / G_BM;
-  return int(mt * nt * p.E);
-}
-
-static int device_cus() {
+// ---------------------------------------------------------------- host-side launch
+static inline int device_cus() {
   static int cus[64] = {0};
   int dev = 0;
   hipGetDevice(&dev);
@@ -602,26 +626,17 @@ static int device_cus() {
   return cus[dev];
 }
 
-template <bool MX, int EPI>
-static mge_status launch_one(const GemmParams& p, hipStream_t s) {
-  hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_kernel<MX, EPI>),
-                      hipFuncAttributeMaxDynamicSharedMemorySize, G_LDS_BYTES);
+// Persistent launch: one workgroup per CU (the kernel holds one workgroup per CU by its
+// LDS use), fewer when the tile count is smaller.
+template <typename Kern>
+static mge_status launch_gemm_kernel(Kern kern, const char* name, const GemmParams& p, hipStream_t s) {
+  hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, G_LDS_BYTES);
   int grid = device_cus();
   if (p.tiles_upper < grid) grid = p.tiles_upper;
   if (grid <= 0) return MGE_OK;
-  hipLaunchKernelGGL((grouped_gemm_kernel<MX, EPI>), dim3(grid), dim3(G_THREADS), G_LDS_BYTES, s, p);
-  return hip_check("grouped_gemm_kernel");
-}
-
-mge_status launch_gemm(const GemmParams& p, int prec, int epi, hipStream_t s) {
-  const bool mx = prec == MGE_PREC_MXFP8;
-  switch (epi) {
-    case EPI_STORE: return mx ? launch_one<true, EPI_STORE>(p, s) : launch_one<false, EPI_STORE>(p, s);
-    case EPI_SWIGLU: return mx ? launch_one<true, EPI_SWIGLU>(p, s) : launch_one<false, EPI_SWIGLU>(p, s);
-    case EPI_SWIGLU_BWD:
-      return mx ? launch_one<true, EPI_SWIGLU_BWD>(p, s) : launch_one<false, EPI_SWIGLU_BWD>(p, s);
-  }
-  return MGE_ERR_INVALID_ARG;
+  ProfScope prof(s, name);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(G_THREADS), G_LDS_BYTES, s, p);
+  return hip_check(name);
 }
 
 }  // namespace mge

@@ -8,6 +8,20 @@
 
 namespace mge {
 
+// ------------------------------------------------------------ per-kernel timing
+// While mge_profile_start() is in effect, a ProfScope records a HIP event on the
+// launch stream when it is constructed and another when it is destroyed, so each
+// kernel launched inside the scope gets its own start/stop pair.  Otherwise it does
+// nothing (one relaxed atomic load).
+struct ProfScope {
+  ProfScope(hipStream_t s, const char* name);
+  ~ProfScope();
+  ProfScope(const ProfScope&) = delete;
+  ProfScope& operator=(const ProfScope&) = delete;
+  hipStream_t stream;
+  int slot;
+};
+
 // ------------------------------------------------------------ block quantize / gather
 struct QuantTileParams {
   const uint16_t* in;
@@ -20,6 +34,21 @@ struct QuantTileParams {
   uint16_t* col_bf16;                        // bf16 transpose [b][C][Rp]
 };
 mge_status launch_quant_tile(const QuantTileParams& p, bool mx, hipStream_t s);
+
+// E8M0 scales [rows][kb] (kb bytes per row, row stride ld bytes) -> the packed layout
+// the GEMM reads: dst[b][j][r] = bytes 4j..4j+3 of row r as one dword (j < ceil(kb/4)).
+// Bytes at block index >= kb, or >= *kb_valid/32 when kb_valid is given (a device
+// count of valid rows along K: blocks past it hold no data), become 127 (scale 1).
+struct ScalePackParams {
+  const uint8_t* src;             // batch b at src + b * src_bstride ...
+  const uint8_t* const* src_tab;  // ... or at src_tab[b] (device table) when non-NULL
+  int64_t src_bstride, ld;
+  int batch, rows, kb;
+  const int32_t* kb_valid;        // optional
+  uint32_t* dst;                  // [batch][ceil(kb/4)][rows]
+};
+mge_status launch_scale_pack(const ScalePackParams& p, hipStream_t s);
+inline int64_t scale_pack_dwords(int rows, int kb) { return int64_t(rows) * ((kb + 3) / 4); }
 
 // ------------------------------------------------------------ routing / permutation
 struct RouteParams {
@@ -49,19 +78,36 @@ mge_status launch_upload_ptrs(const void* const* host_ptrs, int n, void** dev_ta
 // ------------------------------------------------------------ grouped GEMM
 enum GemmMode { RAGGED_M = 0, RAGGED_K = 1 };
 enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_BWD = 2 };
+// The six GEMMs of the layer; each is its own kernel symbol (traces, per-kernel timing).
+enum GemmRole {
+  GEMM_GATEUP = 0,      // [G U] = X W_gate_up^T, SwiGLU x p epilogue       (RAGGED_M)
+  GEMM_DOWN = 1,        // Y = h W_down^T                                   (RAGGED_M)
+  GEMM_DH = 2,          // dh = dY W_down, SwiGLU backward + d_prob epilogue (RAGGED_M)
+  GEMM_DX = 3,          // dX = dGU W_gate_up                               (RAGGED_M)
+  GEMM_DW_DOWN = 4,     // dW_down = dY^T h                                 (RAGGED_K)
+  GEMM_DW_GATEUP = 5    // dW_gate_up = dGU^T X                             (RAGGED_K)
+};
 
 struct GemmParams {
+  int role;              // GemmRole
   int mode;              // RAGGED_M: group e = rows [off[e], off[e]+sizes[e]) of A; RAGGED_K: K span of group e
   int E;
   const int32_t* sizes;
   const int32_t* offs;
   // A: RAGGED_M -> shared [R][K] (row stride lda bytes); RAGGED_K -> shared [M][R] (row stride lda bytes)
   const uint8_t* A;  int64_t lda;
-  const uint8_t* As; int64_t ldas;        // MX scales of A (bytes per row)
-  // B: RAGGED_M -> per-expert tables Bt[e] ([N][K], row stride ldb bytes); RAGGED_K -> shared [N][R]
-  const uint8_t* const* Bt; const uint8_t* const* Bst;
-  const uint8_t* B;  const uint8_t* Bs;
-  int64_t ldb, ldbs;
+  // B: RAGGED_M -> per-expert table Bt[e] ([N][K], row stride ldb bytes); RAGGED_K -> shared [N][R]
+  const uint8_t* const* Bt;
+  const uint8_t* B;
+  int64_t ldb;
+  // MX scales, packed (launch_scale_pack): dword j of a row holds the E8M0 bytes of K
+  // blocks 4j..4j+3; the dwords of one j are contiguous over rows.
+  //   A: RAGGED_M -> [K/128][R] over the permuted rows (asp_ld = R);
+  //      RAGGED_K -> [R/128][M] (asp_ld = M)
+  //   B: RAGGED_M -> expert e at Bsp + e*bsp_estride, [K/128][N] (bsp_ld = N);
+  //      RAGGED_K -> [R/128][N] (bsp_ld = N)
+  const uint32_t* Asp; int64_t asp_ld;
+  const uint32_t* Bsp; int64_t bsp_ld, bsp_estride;
   int M, N, K;           // M used in RAGGED_K; K used in RAGGED_M (elements)
   // outputs
   int out_dtype;         // MGE_DTYPE_*
@@ -91,6 +137,6 @@ struct GemmParams {
 int gemm_swiglu_bwd_nparts(int F);
 // Upper bound of tiles for a RAGGED_M GEMM (host-side, from T*k and E).
 int gemm_tiles_upper(const GemmParams& p, int64_t total_rows_bound);
-mge_status launch_gemm(const GemmParams& p, int prec, int epi, hipStream_t s);
+mge_status launch_gemm(const GemmParams& p, int prec, hipStream_t s);
 
 }  // namespace mge

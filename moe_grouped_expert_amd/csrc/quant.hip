@@ -122,10 +122,56 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileParams p) {
   }
 }
 
+// ---------------------------------------------------------------- scale packing
+// A 64-row x 64-byte tile of a scale matrix goes through LDS: rows are read with
+// consecutive threads on consecutive bytes, the packed dwords are written with
+// consecutive threads on consecutive rows.
+constexpr int SP_ROWS = 64;
+constexpr int SP_BYTES = 64;
+
+__global__ __launch_bounds__(256) void scale_pack_kernel(ScalePackParams p) {
+  __shared__ uint8_t tile[SP_ROWS][SP_BYTES + 4];
+  const int tid = threadIdx.x;
+  const int c0 = blockIdx.x * SP_BYTES;
+  const int r0 = blockIdx.y * SP_ROWS;
+  const int b = blockIdx.z;
+  const uint8_t* src = p.src_tab ? p.src_tab[b] : p.src + int64_t(b) * p.src_bstride;
+  const int kb_lim = p.kb_valid ? min(p.kb, p.kb_valid[0] / 32) : p.kb;
+  for (int i = tid; i < SP_ROWS * SP_BYTES; i += 256) {
+    const int rr = i / SP_BYTES, cc = i % SP_BYTES;
+    const int r = r0 + rr, c = c0 + cc;
+    uint8_t v = 127;
+    if (r < p.rows && c < kb_lim) v = src[int64_t(r) * p.ld + c];
+    tile[rr][cc] = v;
+  }
+  __syncthreads();
+  const int kb4 = (p.kb + 3) / 4;
+  uint32_t* dst = p.dst + int64_t(b) * kb4 * p.rows;
+  for (int i = tid; i < SP_ROWS * (SP_BYTES / 4); i += 256) {
+    const int jj = i / SP_ROWS, rr = i % SP_ROWS;
+    const int j = c0 / 4 + jj, r = r0 + rr;
+    if (r < p.rows && j < kb4) {
+      const uint32_t w = uint32_t(tile[rr][4 * jj]) | (uint32_t(tile[rr][4 * jj + 1]) << 8) |
+                         (uint32_t(tile[rr][4 * jj + 2]) << 16) | (uint32_t(tile[rr][4 * jj + 3]) << 24);
+      dst[int64_t(j) * p.rows + r] = w;
+    }
+  }
+}
+
+mge_status launch_scale_pack(const ScalePackParams& p, hipStream_t s) {
+  if (p.rows <= 0 || p.kb <= 0 || p.batch <= 0) return MGE_OK;
+  dim3 grid((p.kb + SP_BYTES - 1) / SP_BYTES, (p.rows + SP_ROWS - 1) / SP_ROWS, p.batch);
+  ProfScope prof(s, "scale_pack");
+  hipLaunchKernelGGL(scale_pack_kernel, grid, dim3(256), 0, s, p);
+  return hip_check("scale_pack_kernel");
+}
+
 mge_status launch_quant_tile(const QuantTileParams& p, bool mx, hipStream_t s) {
   if (p.R <= 0 || p.C <= 0 || p.batch <= 0) return MGE_OK;
   int rows_cover = p.Rp > p.R ? p.Rp : p.R;
   dim3 grid((p.C + QT_COLS - 1) / QT_COLS, (rows_cover + QT_ROWS - 1) / QT_ROWS, p.batch);
+  const char* name = mx ? (p.gather ? "permute_quant_mx" : "quant_mx") : (p.gather ? "permute_bf16" : "transpose_bf16");
+  ProfScope prof(s, name);
   if (mx)
     hipLaunchKernelGGL(quant_tile_kernel<true>, grid, dim3(256), 0, s, p);
   else

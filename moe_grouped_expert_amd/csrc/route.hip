@@ -207,10 +207,22 @@ __global__ __launch_bounds__(RT_THREADS) void route_scatter_kernel(RouteParams p
 }
 
 mge_status launch_route(const RouteParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(route_clear_kernel, dim3(1), dim3(64), 0, s, p.err_flag);
-  hipLaunchKernelGGL(route_topk_kernel, dim3(p.nblk), dim3(RT_THREADS), 0, s, p);
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(RT_THREADS), 0, s, p);
-  hipLaunchKernelGGL(route_scatter_kernel, dim3(p.nblk), dim3(RT_THREADS), 0, s, p);
+  {
+    ProfScope prof(s, "route_clear");
+    hipLaunchKernelGGL(route_clear_kernel, dim3(1), dim3(64), 0, s, p.err_flag);
+  }
+  {
+    ProfScope prof(s, "route_topk");
+    hipLaunchKernelGGL(route_topk_kernel, dim3(p.nblk), dim3(RT_THREADS), 0, s, p);
+  }
+  {
+    ProfScope prof(s, "route_scan");
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(RT_THREADS), 0, s, p);
+  }
+  {
+    ProfScope prof(s, "route_scatter");
+    hipLaunchKernelGGL(route_scatter_kernel, dim3(p.nblk), dim3(RT_THREADS), 0, s, p);
+  }
   return hip_check("route kernels");
 }
 
