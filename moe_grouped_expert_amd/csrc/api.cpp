@@ -262,8 +262,10 @@ static mge_status check_mlp_dims(int prec, int E, int H, int F, int T, int k, in
   return MGE_OK;
 }
 
-// Bytes of a packed scale matrix (launch_scale_pack) of `batch` x [rows][kb].
-static size_t packed_bytes(int batch, int rows, int kb) { return up256(size_t(batch) * scale_pack_dwords(rows, kb) * 4); }
+// Bytes of a packed scale matrix (launch_scale_pack) of `batch` x [rows][kb]: exact, and
+// rounded up for carving the workspace.
+static uint32_t packed_exact(int batch, int rows, int kb) { return uint32_t(int64_t(batch) * scale_pack_dwords(rows, kb) * 4); }
+static size_t packed_bytes(int batch, int rows, int kb) { return up256(packed_exact(batch, rows, kb)); }
 
 static size_t fwd_ws(const mge_fwd_args* a, int R) {
   size_t n = up256(4 * size_t(a->E) * sizeof(void*));
@@ -377,9 +379,10 @@ mge_status grouped_mlp_fwd(const mge_fwd_args* a, void* stream) {
   GemmParams g{};
   g.mode = RAGGED_M; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
   g.A = static_cast<const uint8_t*>(a->x_perm); g.lda = int64_t(a->H) * elem;
-  g.Asp = xs_p; g.asp_ld = R;
+  g.Asp = xs_p; g.asp_ld = R; g.asp_bytes = packed_exact(1, R, H / 32);
   g.Bt = reinterpret_cast<const uint8_t* const*>(tab);
   g.Bsp = wgu_p; g.bsp_ld = 2 * F; g.bsp_estride = scale_pack_dwords(2 * F, H / 32);
+  g.bsp_bytes = packed_exact(E, 2 * F, H / 32);
   g.ldb = int64_t(a->H) * elem;
   g.N = 2 * a->F; g.K = a->H; g.F = a->F;
   g.prob = a->prob_perm;
@@ -405,9 +408,10 @@ mge_status grouped_mlp_fwd(const mge_fwd_args* a, void* stream) {
   GemmParams d{};
   d.mode = RAGGED_M; d.E = E; d.sizes = a->split_sizes; d.offs = a->group_offsets;
   d.A = static_cast<const uint8_t*>(h); d.lda = int64_t(a->F) * elem;
-  d.Asp = hs_p; d.asp_ld = R;
+  d.Asp = hs_p; d.asp_ld = R; d.asp_bytes = packed_exact(1, R, F / 32);
   d.Bt = reinterpret_cast<const uint8_t* const*>(tab + E);
   d.Bsp = wd_p; d.bsp_ld = H; d.bsp_estride = scale_pack_dwords(H, F / 32);
+  d.bsp_bytes = packed_exact(E, H, F / 32);
   d.ldb = int64_t(a->F) * elem;
   d.N = a->H; d.K = a->F;
   d.out_dtype = a->y_dtype; d.C = a->y_perm; d.ldc = a->H;
@@ -417,11 +421,12 @@ mge_status grouped_mlp_fwd(const mge_fwd_args* a, void* stream) {
 }
 
 // ------------------------------------------------------------------ backward
-static size_t bwd_ws(const mge_bwd_args* a, int R, int nparts) {
+static size_t bwd_ws(const mge_bwd_args* a, int R) {
   const bool mx = a->prec == MGE_PREC_MXFP8;
   const size_t H = a->H, F = a->F, E = a->E, F2 = 2 * F;
   size_t n = up256(6 * E * sizeof(void*));
-  n += up256(size_t(R) * nparts * sizeof(float));
+  n += up256(size_t(R) * sizeof(float));                 // d_prob per permuted row
+  n += up256(size_t(R) * F * sizeof(float));             // dh (fp32)
   auto mat = [&](size_t rows, size_t cols) {
     return mx ? up256(rows * cols) + up256(rows * (cols / 32)) : up256(rows * cols * 2);
   };
@@ -442,7 +447,7 @@ static size_t bwd_ws(const mge_bwd_args* a, int R, int nparts) {
 
 size_t mge_bwd_workspace_bytes(const mge_bwd_args* a) {
   if (!a || a->E < 1 || a->T < 0 || a->k < 1 || a->align < 1 || a->F < 32) return 0;
-  return bwd_ws(a, int(mge_perm_rows(a->T, a->k, a->E, a->align)), gemm_swiglu_bwd_nparts(a->F));
+  return bwd_ws(a, int(mge_perm_rows(a->T, a->k, a->E, a->align)));
 }
 
 mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
@@ -475,8 +480,7 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
                   opt_ok(a->dgu_row, a->dgu_row_scale) && opt_ok(a->dgu_col, a->dgu_col_scale),
               "an optional intermediate is misaligned or lacks its scales");
   const int R = int(mge_perm_rows(a->T, a->k, a->E, a->align));
-  const int nparts = gemm_swiglu_bwd_nparts(a->F);
-  const size_t need = bwd_ws(a, R, nparts);
+  const size_t need = bwd_ws(a, R);
   if (!a->workspace || a->workspace_bytes < need) {
     set_error("backward workspace needs %zu bytes (got %zu)", need, a->workspace_bytes);
     return MGE_ERR_WORKSPACE;
@@ -487,7 +491,8 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
   const int elem = mx ? 1 : 2;
   Carve ws(a->workspace);
   void** tab = static_cast<void**>(ws.take(6 * size_t(E) * sizeof(void*)));
-  float* part = static_cast<float*>(ws.take(size_t(R) * nparts * sizeof(float)));
+  float* dprob_row = static_cast<float*>(ws.take(size_t(R) * sizeof(float)));
+  float* dh = static_cast<float*>(ws.take(size_t(R) * F * sizeof(float)));
   auto mat = [&](void* given, uint8_t* given_s, size_t rows, size_t cols, void** c, uint8_t** sc) {
     if (given) { *c = given; *sc = given_s; return; }
     if (mx) { *c = ws.take(rows * cols); *sc = static_cast<uint8_t*>(ws.take(rows * (cols / 32))); }
@@ -576,38 +581,45 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
     if (st == MGE_OK) st = pack(a->x_col_scale, nullptr, 1, H, R / 32, nullptr, xc_p);
     if (st != MGE_OK) return st;
   }
-  // b2: dh = dY W_down with the SwiGLU backward + d_prob partial epilogue
+  // b2: dh = dY W_down (fp32), then the SwiGLU backward with the saved G, U and p:
+  // dGU in row and column forms and the d_prob row sums
   {
     GemmParams g{};
     g.mode = RAGGED_M; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
-    g.A = static_cast<const uint8_t*>(dyr); g.lda = int64_t(H) * elem; g.Asp = dyr_p; g.asp_ld = R;
+    g.A = static_cast<const uint8_t*>(dyr); g.lda = int64_t(H) * elem; g.Asp = dyr_p; g.asp_ld = R; g.asp_bytes = packed_exact(1, R, H / 32);
     g.Bt = reinterpret_cast<const uint8_t* const*>(tab);
     g.Bsp = wdc_p; g.bsp_ld = F; g.bsp_estride = scale_pack_dwords(F, H / 32);
+    g.bsp_bytes = packed_exact(E, F, H / 32);
     g.ldb = int64_t(H) * elem;
     g.N = F; g.K = H; g.F = F;
-    g.prob = a->prob_perm; g.gu = a->saved_gu;
-    if (mx) { g.dgu_codes = static_cast<uint8_t*>(dgr); g.dgu_scales = dgrs; g.dguc_codes = static_cast<uint8_t*>(dgc); g.dguc_scales = dgcs; }
-    else { g.dgu_bf16 = static_cast<uint16_t*>(dgr); g.dguc_bf16 = static_cast<uint16_t*>(dgc); }
-    g.dprob_part = part; g.nparts = nparts; g.Rp = R;
+    g.out_dtype = MGE_DTYPE_F32; g.C = dh; g.ldc = F;
     g.tiles_upper = gemm_tiles_upper(g, rows_bound);
     g.role = GEMM_DH;
     st = launch_gemm(g, a->prec, s);
     if (st != MGE_OK) return st;
+    SwigluBwdParams q{};
+    q.R = R; q.F = F; q.Rp = R;
+    q.dh = dh; q.gu = a->saved_gu; q.prob = a->prob_perm; q.perm_src = a->perm_src;
+    if (mx) { q.row_codes = static_cast<uint8_t*>(dgr); q.row_scales = dgrs; q.col_codes = static_cast<uint8_t*>(dgc); q.col_scales = dgcs; }
+    else { q.row_bf16 = static_cast<uint16_t*>(dgr); q.col_bf16 = static_cast<uint16_t*>(dgc); }
+    q.dprob_row = dprob_row;
+    st = launch_swiglu_bwd(q, mx, s);
+    if (st != MGE_OK) return st;
   }
   if (mx) {
     st = pack(dgrs, nullptr, 1, R, F2 / 32, nullptr, dgr_p);
-    if (st == MGE_OK) st = pack(dgcs, nullptr, 1, F2, R / 32, rows_written, dgc_p);
+    if (st == MGE_OK) st = pack(dgcs, nullptr, 1, F2, R / 32, nullptr, dgc_p);
     if (st != MGE_OK) return st;
   }
-  // b3: d_prob
-  st = launch_dprob_reduce(a->T, a->k, nparts, part, a->perm_pos, a->d_prob, s);
+  // b3: d_prob[t][i] = the row sum of the assignment's permuted row
+  st = launch_dprob_reduce(a->T, a->k, 1, dprob_row, a->perm_pos, a->d_prob, s);
   if (st != MGE_OK) return st;
   // b4: dW_down[e] = dY_e^T h_e  (K = tokens of e)
   {
     GemmParams g{};
     g.mode = RAGGED_K; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
-    g.A = static_cast<const uint8_t*>(dyc); g.lda = int64_t(R) * elem; g.Asp = dyc_p; g.asp_ld = H;
-    g.B = static_cast<const uint8_t*>(a->h_col); g.ldb = int64_t(R) * elem; g.Bsp = hc_p; g.bsp_ld = F;
+    g.A = static_cast<const uint8_t*>(dyc); g.lda = int64_t(R) * elem; g.Asp = dyc_p; g.asp_ld = H; g.asp_bytes = packed_exact(1, H, R / 32);
+    g.B = static_cast<const uint8_t*>(a->h_col); g.ldb = int64_t(R) * elem; g.Bsp = hc_p; g.bsp_ld = F; g.bsp_bytes = packed_exact(1, F, R / 32);
     g.M = H; g.N = F;
     g.out_dtype = MGE_DTYPE_F32; g.Ct = reinterpret_cast<void* const*>(tab + 4 * E); g.ldc = F;
     g.accumulate = a->accumulate;
@@ -620,9 +632,10 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
   {
     GemmParams g{};
     g.mode = RAGGED_M; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
-    g.A = static_cast<const uint8_t*>(dgr); g.lda = int64_t(F2) * elem; g.Asp = dgr_p; g.asp_ld = R;
+    g.A = static_cast<const uint8_t*>(dgr); g.lda = int64_t(F2) * elem; g.Asp = dgr_p; g.asp_ld = R; g.asp_bytes = packed_exact(1, R, F2 / 32);
     g.Bt = reinterpret_cast<const uint8_t* const*>(tab + E);
     g.Bsp = wguc_p; g.bsp_ld = H; g.bsp_estride = scale_pack_dwords(H, F2 / 32);
+    g.bsp_bytes = packed_exact(E, H, F2 / 32);
     g.ldb = int64_t(F2) * elem;
     g.N = H; g.K = F2;
     g.out_dtype = MGE_DTYPE_BF16; g.C = a->dx_perm; g.ldc = H;
@@ -635,8 +648,8 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
   {
     GemmParams g{};
     g.mode = RAGGED_K; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
-    g.A = static_cast<const uint8_t*>(dgc); g.lda = int64_t(R) * elem; g.Asp = dgc_p; g.asp_ld = F2;
-    g.B = static_cast<const uint8_t*>(a->x_col); g.ldb = int64_t(R) * elem; g.Bsp = xc_p; g.bsp_ld = H;
+    g.A = static_cast<const uint8_t*>(dgc); g.lda = int64_t(R) * elem; g.Asp = dgc_p; g.asp_ld = F2; g.asp_bytes = packed_exact(1, F2, R / 32);
+    g.B = static_cast<const uint8_t*>(a->x_col); g.ldb = int64_t(R) * elem; g.Bsp = xc_p; g.bsp_ld = H; g.bsp_bytes = packed_exact(1, H, R / 32);
     g.M = F2; g.N = H;
     g.out_dtype = MGE_DTYPE_F32; g.Ct = reinterpret_cast<void* const*>(tab + 5 * E); g.ldc = H;
     g.accumulate = a->accumulate;

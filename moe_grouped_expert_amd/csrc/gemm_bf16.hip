@@ -9,7 +9,7 @@ namespace mge {
 
 MGE_GEMM_KERNEL(gemm_gateup_swiglu_bf16, EPI_SWIGLU, RAGGED_M)
 MGE_GEMM_KERNEL(gemm_down_bf16, EPI_STORE, RAGGED_M)
-MGE_GEMM_KERNEL(gemm_dh_swiglu_bwd_bf16, EPI_SWIGLU_BWD, RAGGED_M)
+MGE_GEMM_KERNEL(gemm_dh_bf16, EPI_STORE, RAGGED_M)
 MGE_GEMM_KERNEL(gemm_dx_bf16, EPI_STORE, RAGGED_M)
 MGE_GEMM_KERNEL(gemm_dw_down_bf16, EPI_STORE, RAGGED_K)
 MGE_GEMM_KERNEL(gemm_dw_gateup_bf16, EPI_STORE, RAGGED_K)
@@ -20,7 +20,7 @@ mge_status launch_gemm_bf16(const GemmParams& p, hipStream_t s) {
   switch (p.role) {
     case GEMM_GATEUP: return launch_gemm_kernel(gemm_gateup_swiglu_bf16, "gemm_gateup_swiglu_bf16", p, s);
     case GEMM_DOWN: return launch_gemm_kernel(gemm_down_bf16, "gemm_down_bf16", p, s);
-    case GEMM_DH: return launch_gemm_kernel(gemm_dh_swiglu_bwd_bf16, "gemm_dh_swiglu_bwd_bf16", p, s);
+    case GEMM_DH: return launch_gemm_kernel(gemm_dh_bf16, "gemm_dh_bf16", p, s);
     case GEMM_DX: return launch_gemm_kernel(gemm_dx_bf16, "gemm_dx_bf16", p, s);
     case GEMM_DW_DOWN: return launch_gemm_kernel(gemm_dw_down_bf16, "gemm_dw_down_bf16", p, s);
     case GEMM_DW_GATEUP: return launch_gemm_kernel(gemm_dw_gateup_bf16, "gemm_dw_gateup_bf16", p, s);

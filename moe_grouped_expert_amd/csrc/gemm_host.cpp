@@ -7,8 +7,6 @@ namespace mge {
 mge_status launch_gemm_mx(const GemmParams& p, hipStream_t s);
 mge_status launch_gemm_bf16(const GemmParams& p, hipStream_t s);
 
-int gemm_swiglu_bwd_nparts(int F) { return ((F + G_BN - 1) / G_BN) * G_WAVES_N; }
-
 int gemm_tiles_upper(const GemmParams& p, int64_t total_rows_bound) {
   int64_t nt = (int64_t(p.N) + G_BN - 1) / G_BN;
   if (p.mode == RAGGED_M) {

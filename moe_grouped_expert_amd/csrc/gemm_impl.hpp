@@ -33,8 +33,6 @@
 //                   one 32-column block) or rounded to bf16; training also stores G, U
 //                   (bf16) and the column form of h (blocks of 32 rows: 16 in a lane,
 //                   16 in its partner lane 32 apart)
-//   EPI_SWIGLU_BWD  dh -> dG, dU (with saved G, U, p) quantized row- and column-wise,
-//                   plus per-row partial sums of dh * silu(G) * U for d_prob
 #pragma once
 
 #include "mge_common.hpp"
@@ -55,10 +53,10 @@ constexpr int G_WMB = 4;   // 32-row MFMA blocks per wave (M)
 constexpr int G_WNB = 4;   // 32-col MFMA blocks per wave (N)
 constexpr int G_BM = G_WAVES_M * G_WMB * 32;
 constexpr int G_BN = G_WAVES_N * G_WNB * 32;
-constexpr int G_BKB = 128;                    // K bytes per slice
+constexpr int G_BKB = 64;                     // K bytes per slice (one MXFP8 MFMA step)
+constexpr int G_STAGES = 4;                   // LDS ring depth: 3 slices in flight
 constexpr int G_THREADS = 64 * G_WAVES_M * G_WAVES_N;
-constexpr int G_STAGE_BYTES = (G_BM + G_BN) * G_BKB;
-constexpr int G_LDS_BYTES = 2 * G_STAGE_BYTES;
+constexpr int G_STAGE_BYTES = (G_BM + G_BN) * G_BKB;   // 32 KB
 constexpr int G_MAXE = 256;
 // Buffer-resource word 3 of the gfx9 family (raw buffer, 32-bit dwords), the record
 // bound, and the offset that lies beyond it (such a lane loads zeros).
@@ -89,29 +87,58 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
   return reinterpret_cast<const T*>((uint64_t(hi) << 32) | lo);
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * G_BKB + ((chunk ^ (row & 7)) << 4); }
+// Byte offset of 16-byte chunk `chunk` (0..3) of tile row `row` in LDS.  The LDS of
+// gfx950 has 64 four-byte banks and serves a ds_read_b128 16 lanes at a time; a 64-byte
+// row covers a quarter of the banks, so four consecutive rows fill one bank row and the
+// chunk is XOR-ed with (row / 4) mod 4: the 16 rows a fragment read touches at once fall
+// on 16 distinct (bank quarter, chunk) pairs.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * G_BKB + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
-struct TileInfo {
-  int e, mt, nt;
-  int m_valid;          // rows of the tile's group (RAGGED_M) or M (RAGGED_K)
-  int row_off;          // first permuted row of the group (RAGGED_M) / K offset (RAGGED_K)
-  int k_len;            // reduction length in elements
-};
-
-// Raw buffer resource over `base` (gfx9 word 3, full 31-bit range).
+// Raw buffer resource over `base` (gfx9 word 3, full 31-bit range) ...
 __device__ __forceinline__ i32x4 make_rsrc(const void* base) {
   const uint64_t v = reinterpret_cast<uint64_t>(base);
   return i32x4{int(uint32_t(v)), int(uint32_t(v >> 32) & 0xffff), kRsrcRecords, kRsrcFlags};
 }
+// ... and one bounded to `bytes` (reads past it return zeros).
+__device__ __forceinline__ i32x4 make_rsrc_n(const void* base, uint32_t bytes) {
+  const uint64_t v = reinterpret_cast<uint64_t>(base);
+  return i32x4{int(uint32_t(v)), int(uint32_t(v >> 32) & 0xffff), int(bytes), kRsrcFlags};
+}
+
+// s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory and `lgkm`
+// LDS/scalar operations are outstanding (export counter not waited on).
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 0xf) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
 // 16 bytes per lane from buffer offset `voff` straight into LDS at lds_addr + 16*lane
 // (buffer_load_dwordx4 ... lds; M0 holds the wave's LDS destination).  Written as asm
-// so the compiler neither waits on it before unrelated LDS reads nor reorders LDS
-// accesses across it; the caller waits (vmcnt) and synchronizes before reading.
+// so the compiler neither waits on it before unrelated LDS reads nor moves LDS accesses
+// across it; every VMEM operation of the K loop is one of these, and the loop waits for
+// them with explicit vmcnt values.  An s_nop separates the M0 write from the DMA that
+// reads it.
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_addr), "v"(voff), "s"(rsrc)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_addr), "v"(voff),
+               "s"(rsrc)
                : "memory", "m0");
 }
+
+// A decoded tile: which expert and block it is, its K range and operand bases.
+struct Tile {
+  int valid;
+  int e, nt, off, m_valid, m0;
+  int kbase, klo, khi, nkt;   // K range in bytes; slices of G_BKB from kbase
+  const uint8_t* A;           // operand bases of the buffer resources
+  const uint8_t* B;
+  int64_t sa_rows, sb_rows;   // MX: packed-scale dword of the tile's first A / B row at group 0
+};
+
+// LDS map (bytes from the start of the dynamic block):
+//   [0, G_STAGES*G_STAGE_BYTES)   operand tiles, G_STAGES x (A 256 x 64 B, B 256 x 64 B)
+//   then G_STAGES x 4 KB          E8M0 scales: four 1 KB slots per stage, slot w filled
+//                                 by wave w (A rows 0-127, 128-255, B rows 0-127,
+//                                 128-255; 512 B used per slot)
+constexpr int G_SCALE_STAGE = 4096;
+constexpr int G_SCALE_BASE = G_STAGES * G_STAGE_BYTES;
+constexpr int G_DYN_LDS = G_SCALE_BASE + G_STAGES * G_SCALE_STAGE;
 
 template <bool MX, int EPI, int MODE>
 __device__ __forceinline__ void gemm_body(const GemmParams& p) {
@@ -150,149 +177,181 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
   int vid = blockIdx.x;
   if ((nwg & 7) == 0) vid = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
 
-  for (int tile = vid; tile < total; tile += nwg) {
-    // ---- decode the tile
+  // every tile quantity is wave-uniform: kept in scalar registers
+  auto decode = [&](int tile) {
+    Tile t{};
+    t.valid = tile < total;
+    if (!t.valid) return t;
     int lo = 0, hi_ = p.E - 1;
     while (lo < hi_) {
       int mid = (lo + hi_ + 1) >> 1;
       if (s_prefix[mid] <= tile) lo = mid; else hi_ = mid - 1;
     }
-    // every tile quantity is wave-uniform: keep it in scalar registers
-    const int e = uniform(lo);
-    const int local = tile - uniform(s_prefix[e]);
-    const int mtn = uniform(s_mtiles[e]);
+    t.e = uniform(lo);
+    const int local = tile - uniform(s_prefix[t.e]);
+    const int mtn = uniform(s_mtiles[t.e]);
     const int mt = local % mtn;
-    const int nt = local / mtn;
-    const int off = uniform(p.offs[e]);
-    const int m_valid = MODE == RAGGED_M ? uniform(p.sizes[e]) : p.M;
-    const int m0 = mt * G_BM;
+    t.nt = local / mtn;
+    t.off = uniform(p.offs[t.e]);
+    t.m_valid = MODE == RAGGED_M ? uniform(p.sizes[t.e]) : p.M;
+    t.m0 = mt * G_BM;
     // K range in bytes.  RAGGED_M: [0, K).  RAGGED_K: the expert's token span
     // [off, off + roundup32(size)) of the column forms; the loop starts at the slice
     // boundary below it and the chunks outside the span load as zeros.
-    int kbase, klo, khi;
     if constexpr (MODE == RAGGED_M) {
-      kbase = 0; klo = 0; khi = p.K * ELEM;
+      t.kbase = 0; t.klo = 0; t.khi = p.K * ELEM;
+      t.A = p.A + int64_t(t.off) * p.lda;
+      t.B = uniform_ptr(p.Bt[t.e]);
     } else {
-      const int span = ((uniform(p.sizes[e]) + 31) / 32) * 32;
-      klo = off * ELEM;
-      khi = (off + span) * ELEM;
-      kbase = span > 0 ? (klo / G_BKB) * G_BKB : klo;
+      const int span = ((uniform(p.sizes[t.e]) + 31) / 32) * 32;
+      t.klo = t.off * ELEM;
+      t.khi = (t.off + span) * ELEM;
+      t.kbase = span > 0 ? (t.klo / G_BKB) * G_BKB : t.klo;
+      t.A = p.A;
+      t.B = p.B;
     }
-    const int nkt = (khi - kbase + G_BKB - 1) / G_BKB;
-
-    // ---- operands as buffer resources: a lane whose offset is kInvalid reads zeros
-    // (rows past the group, chunks outside the K range), so tails need no extra path.
-    const uint8_t* Abase;
-    const uint8_t* Bbase;
-    if constexpr (MODE == RAGGED_M) {
-      Abase = p.A + int64_t(off) * p.lda;
-      Bbase = uniform_ptr(p.Bt[e]);
-    } else {
-      Abase = p.A;
-      Bbase = p.B;
-    }
-    const i32x4 rsrcA = make_rsrc(Abase);
-    const i32x4 rsrcB = make_rsrc(Bbase);
-
-    // ---- loader geometry: wave instruction i fills LDS rows [(wave*8+i)*8, +8) of a
-    // 256-row operand tile, 1 KB contiguous (lane l -> row +l/8, LDS chunk l%8).  The
-    // lane loads the global chunk that the XOR swizzle maps to that LDS chunk.
-    const int lchunk = (lane & 7) ^ (lane >> 3);
-    uint32_t a_off[8], b_off[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = wave * 64 + i * 8 + (lane >> 3);   // row within the tile
-      const int ra = m0 + r;
-      a_off[i] = ra < m_valid ? uint32_t(ra) * uint32_t(p.lda) + lchunk * 16 : kInvalid;
-      int grow;
-      if constexpr (EPI == EPI_SWIGLU) {
-        constexpr int half = G_BN / 2;
-        const int f = nt * half + (r % half);
-        grow = f < p.F ? (r < half ? f : p.F + f) : -1;
+    t.nkt = (t.khi - t.kbase + G_BKB - 1) / G_BKB;
+    if constexpr (MX) {
+      // packed scales: dword (j, row) at row + j * ld holds the 4 blocks of K elements
+      // [128j, 128j + 128); slice kt covers bytes kbase + 64kt.. = group (kbase/64+kt)/2
+      if constexpr (MODE == RAGGED_M) {
+        t.sa_rows = t.off + t.m0;
+        t.sb_rows = int64_t(t.e) * p.bsp_estride;
       } else {
-        grow = nt * G_BN + r;
-        grow = grow < p.N ? grow : -1;
+        t.sa_rows = t.m0;
+        t.sb_rows = 0;
       }
-      b_off[i] = grow >= 0 ? uint32_t(grow) * uint32_t(p.ldb) + lchunk * 16 : kInvalid;
     }
-    auto issue_loads = [&](int kt, int buf) {
-      // chunks outside [klo, khi) get the top offset bit set (-> zeros); arithmetic
-      // rather than a select so the loads stay straight-line code
-      const int kslice = kbase + kt * G_BKB;          // first byte of the slice
-      const int kb = kslice + lchunk * 16;             // this lane's chunk (a_off/b_off hold the chunk term)
-      const uint32_t out = ((uint32_t(kb - klo) | uint32_t(khi - 1 - kb)) >> 31) << 31;
-      const uint32_t kadd = uint32_t(kslice);
-      const uint32_t la = lds_base + buf * G_STAGE_BYTES + wave * 8 * 1024;
-      const uint32_t lb = la + G_BM * G_BKB;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dma16(rsrcA, la + i * 1024, (a_off[i] + kadd) | out);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dma16(rsrcB, lb + i * 1024, (b_off[i] + kadd) | out);
-    };
+    return t;
+  };
 
-    // ---- MX scales: packed as one dword per (row, 128-element slice) holding the 4
-    // E8M0 bytes of that slice, rows contiguous, so the 32 lanes of a block read 128
-    // consecutive bytes.
-    int brow_tile[G_WNB];
+  // operand row of B-tile row r (0..255), or -1 past the end
+  auto b_row = [&](const Tile& t, int r) {
+    if constexpr (EPI == EPI_SWIGLU) {
+      constexpr int half = G_BN / 2;
+      const int f = t.nt * half + (r % half);
+      return f < p.F ? (r < half ? f : p.F + f) : -1;
+    } else {
+      const int g = t.nt * G_BN + r;
+      return g < p.N ? g : -1;
+    }
+  };
+
+  // ---- loader geometry: wave instruction i (0..3) fills LDS rows [(wave*4+i)*16, +16)
+  // of a 256-row operand tile, 1 KB contiguous (lane l -> row +l/4, LDS chunk l%4).  The
+  // lane loads the global chunk that the swizzle maps to that LDS chunk: with row =
+  // 16q + l/4, (row/4) mod 4 = (l/16) mod 4.  Lanes whose offset has the top bit set
+  // read zeros (rows past the group, chunks outside the K range), so tails need no
+  // extra path.
+  const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  uint32_t a_off[4], b_off[4];
+  auto lane_offs = [&](const Tile& t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (wave * 4 + i) * 16 + (lane >> 2);   // row within the tile
+      const int ra = t.m0 + r;
+      a_off[i] = ra < t.m_valid ? uint32_t(ra) * uint32_t(p.lda) + lchunk * 16 : kInvalid;
+      const int g = b_row(t, r);
+      b_off[i] = g >= 0 ? uint32_t(g) * uint32_t(p.ldb) + lchunk * 16 : kInvalid;
+    }
+  };
+
+  // one K slice of tile t into LDS stage `stage` (operands and, MX, its scales); past
+  // the last slice every lane is out of range and loads zeros
+  constexpr int DMA_PER_SLICE = 8 + (MX ? 1 : 0);   // VMEM operations of one issue_slice
+  auto issue_slice = [&](const Tile& t, int kt, int stage) {
+    const i32x4 rA = make_rsrc(t.A);
+    const i32x4 rB = make_rsrc(t.B);
+    const int kslice = t.kbase + kt * G_BKB;         // first byte of the slice
+    // this lane's chunk (a_off/b_off hold the chunk term); outside [klo, khi) the top
+    // offset bit is set
+    const int kb = kslice + lchunk * 16;
+    const uint32_t out = ((uint32_t(kb - t.klo) | uint32_t(t.khi - 1 - kb)) >> 31) << 31;
+    const uint32_t kadd = uint32_t(kslice);
+    const uint32_t la = lds_base + stage * G_STAGE_BYTES + wave * 4 * 1024;
+    const uint32_t lb = la + G_BM * G_BKB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(rA, la + i * 1024, (a_off[i] + kadd) | out);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(rB, lb + i * 1024, (b_off[i] + kadd) | out);
+    if constexpr (MX) {
+      // wave w brings 128 rows of scale dwords (lanes 0..31, 16 B = 4 rows each):
+      // A rows (w&1)*128.. for w < 2, B rows for w >= 2; the dwords of the slice's
+      // 128-element group (both 64-byte halves of a group read the same dwords)
+      const bool slice_ok = kt < t.nkt;
+      const int half = wave & 1;
+      const int64_t j = (t.kbase / G_BKB + kt) >> 1;
+      int64_t dw;             // first dword of the 128 rows
+      const uint32_t* base;
+      uint32_t bytes;
+      if (wave < 2) {
+        dw = t.sa_rows + j * p.asp_ld + half * 128;
+        base = p.Asp;
+        bytes = p.asp_bytes;
+      } else {
+        int r0;
+        if constexpr (EPI == EPI_SWIGLU) r0 = half == 0 ? t.nt * (G_BN / 2) : p.F + t.nt * (G_BN / 2);
+        else r0 = t.nt * G_BN + half * 128;
+        dw = t.sb_rows + j * p.bsp_ld + r0;
+        base = p.Bsp;
+        bytes = p.bsp_bytes;
+      }
+      const i32x4 rS = make_rsrc_n(base, bytes);
+      const uint32_t so = (slice_ok && lane < 32) ? uint32_t(dw * 4) + lane * 16 : kInvalid;
+      dma16(rS, lds_base + G_SCALE_BASE + stage * G_SCALE_STAGE + wave * 1024, so);
+    }
+  };
+
+  int brow_tile[G_WNB];
+#pragma unroll
+  for (int ni = 0; ni < G_WNB; ++ni) {
+    if constexpr (EPI == EPI_SWIGLU) {
+      constexpr int hb = G_WNB / 2;
+      brow_tile[ni] = ni < hb ? (wn * hb + ni) * 32 : G_BN / 2 + (wn * hb + ni - hb) * 32;
+    } else {
+      brow_tile[ni] = (wn * G_WNB + ni) * 32;
+    }
+  }
+
+  // MFMA operand fragments of one K step, read from the swizzled LDS tile:
+  //   MX  : the slice is one 64-element step; lane (hi, l32) takes 16-byte chunks hi and
+  //         hi + 2 of its row
+  //   BF16: 16-element step s (of 2); lane takes chunk 2s + hi
+  typedef typename std::conditional<MX, i32x8, bf16x8>::type frag_t;
+  constexpr int NSTEP = MX ? 1 : 2;
+  auto read_frags = [&](const uint8_t* sA, const uint8_t* sB, int s, frag_t* af, frag_t* bfr) {
+#pragma unroll
+    for (int mi = 0; mi < G_WMB; ++mi) {
+      const int row = (wm * G_WMB + mi) * 32 + l32;
+      if constexpr (MX) {
+        const int c = hi;
+        const uint4 x0 = *reinterpret_cast<const uint4*>(sA + swz(row, c));
+        const uint4 x1 = *reinterpret_cast<const uint4*>(sA + swz(row, c + 2));
+        af[mi] = i32x8{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
+      } else {
+        af[mi] = *reinterpret_cast<const bf16x8*>(sA + swz(row, s * 2 + hi));
+      }
+    }
 #pragma unroll
     for (int ni = 0; ni < G_WNB; ++ni) {
-      if constexpr (EPI == EPI_SWIGLU) {
-        constexpr int hb = G_WNB / 2;
-        brow_tile[ni] = ni < hb ? (wn * hb + ni) * 32 : G_BN / 2 + (wn * hb + ni - hb) * 32;
+      const int row = brow_tile[ni] + l32;
+      if constexpr (MX) {
+        const int c = hi;
+        const uint4 x0 = *reinterpret_cast<const uint4*>(sB + swz(row, c));
+        const uint4 x1 = *reinterpret_cast<const uint4*>(sB + swz(row, c + 2));
+        bfr[ni] = i32x8{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
       } else {
-        brow_tile[ni] = (wn * G_WNB + ni) * 32;
+        bfr[ni] = *reinterpret_cast<const bf16x8*>(sB + swz(row, s * 2 + hi));
       }
     }
-    const uint32_t* sa_ptr[G_WMB];
-    const uint32_t* sb_ptr[G_WNB];
-    int64_t sa_step = 0, sb_step = 0;
-    if constexpr (MX) {
-      int64_t j0 = MODE == RAGGED_M ? 0 : kbase / 128;   // first packed slice
-      const uint32_t* Ap;
-      const uint32_t* Bp;
-      if constexpr (MODE == RAGGED_M) {
-        Ap = p.Asp + off;
-        Bp = p.Bsp + int64_t(e) * p.bsp_estride;
-      } else {
-        Ap = p.Asp;
-        Bp = p.Bsp;
-      }
-      sa_step = p.asp_ld;
-      sb_step = p.bsp_ld;
-#pragma unroll
-      for (int mi = 0; mi < G_WMB; ++mi) {
-        int r = m0 + (wm * G_WMB + mi) * 32 + l32;
-        r = r >= m_valid ? m_valid - 1 : r;
-        r = r < 0 ? 0 : r;
-        sa_ptr[mi] = Ap + j0 * sa_step + r;
-      }
-#pragma unroll
-      for (int ni = 0; ni < G_WNB; ++ni) {
-        const int r = brow_tile[ni] + l32;
-        int grow;
-        if constexpr (EPI == EPI_SWIGLU) {
-          constexpr int half = G_BN / 2;
-          int f = nt * half + (r % half);
-          f = f >= p.F ? p.F - 1 : f;
-          grow = r < half ? f : p.F + f;
-        } else {
-          grow = nt * G_BN + r;
-          grow = grow >= p.N ? p.N - 1 : grow;
-        }
-        sb_ptr[ni] = Bp + j0 * sb_step + grow;
-      }
-    }
-    // raw packed dwords; the lane's byte (block 4kt + hi, and + 2 for the second
-    // 64-element step) is selected at the MFMA by shift + op_sel, so a load is only
-    // waited for where it is used
-    uint32_t sa[G_WMB], sb[G_WNB];
-    uint32_t nsa[G_WMB], nsb[G_WNB];
-    auto sload = [&](int kt, uint32_t* da, uint32_t* db) {
-#pragma unroll
-      for (int mi = 0; mi < G_WMB; ++mi) da[mi] = sa_ptr[mi][kt * sa_step];
-#pragma unroll
-      for (int ni = 0; ni < G_WNB; ++ni) db[ni] = sb_ptr[ni][kt * sb_step];
-    };
+  };
+
+  Tile cur = decode(vid);
+  bool cur_issued = false;   // slice 0 of `cur` already on its way into stage 0
+  for (int tile = vid; tile < total; tile += nwg) {
+    const Tile nxt = decode(tile + nwg);
+    const int e = cur.e, nt = cur.nt, off = cur.off, m_valid = cur.m_valid, m0 = cur.m0, nkt = cur.nkt;
+    lane_offs(cur);
 
     f32x16 acc[G_WMB][G_WNB];
 #pragma unroll
@@ -302,91 +361,78 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
-    // MFMA operand fragments of one K step, read from the swizzled LDS tile:
-    //   MX  : 64-element step s of the slice; lane (hi, l32) takes 16-byte chunks
-    //         4s + hi and 4s + hi + 2 of its row
-    //   BF16: 16-element step s; lane takes chunk 2s + hi
-    typedef typename std::conditional<MX, i32x8, bf16x8>::type frag_t;
-    constexpr int NSTEP = MX ? 2 : 4;
-    auto read_frags = [&](const uint8_t* sA, const uint8_t* sB, int s, frag_t* af, frag_t* bfr) {
-#pragma unroll
-      for (int mi = 0; mi < G_WMB; ++mi) {
-        const int row = (wm * G_WMB + mi) * 32 + l32;
-        if constexpr (MX) {
-          const int c = s * 4 + hi;
-          const uint4 x0 = *reinterpret_cast<const uint4*>(sA + swz(row, c));
-          const uint4 x1 = *reinterpret_cast<const uint4*>(sA + swz(row, c + 2));
-          af[mi] = i32x8{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
-        } else {
-          af[mi] = *reinterpret_cast<const bf16x8*>(sA + swz(row, s * 2 + hi));
-        }
-      }
-#pragma unroll
-      for (int ni = 0; ni < G_WNB; ++ni) {
-        const int row = brow_tile[ni] + l32;
-        if constexpr (MX) {
-          const int c = s * 4 + hi;
-          const uint4 x0 = *reinterpret_cast<const uint4*>(sB + swz(row, c));
-          const uint4 x1 = *reinterpret_cast<const uint4*>(sB + swz(row, c + 2));
-          bfr[ni] = i32x8{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
-        } else {
-          bfr[ni] = *reinterpret_cast<const bf16x8*>(sB + swz(row, s * 2 + hi));
-        }
-      }
-    };
-    auto mfma_step = [&](int s, const frag_t* af, const frag_t* bfr) {
+    // MX: lane hi scales K block 2*gh + hi of the slice's 128-element group (gh = which
+    // 64-byte half of the group the slice is), byte 0 of the shifted dword (op_sel 0)
+    auto mfma_step = [&](int s, int gh, const frag_t* af, const frag_t* bfr, const uint32_t* sa, const uint32_t* sb) {
+      const int sh = 8 * (2 * gh + hi);
 #pragma unroll
       for (int mi = 0; mi < G_WMB; ++mi)
 #pragma unroll
         for (int ni = 0; ni < G_WNB; ++ni) {
           if constexpr (MX) {
-            const int xa = int(sa[mi] >> (8 * hi));
-            const int xb = int(sb[ni] >> (8 * hi));
-            if (s == 0)
-              acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0, xa, 0,
-                                                                            xb);
-            else
-              acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bfr[ni], acc[mi][ni], 0, 0, 2, xa, 2,
-                                                                            xb);
+            const int xa = int(sa[mi] >> sh);
+            const int xb = int(sb[ni] >> sh);
+            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0, xa, 0, xb);
           } else {
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
           }
         }
     };
 
-    __syncthreads();   // previous tile's LDS readers are done
-    if (nkt > 0) {
-      issue_loads(0, 0);
-      if constexpr (MX) sload(0, sa, sb);
+    // ---- K loop: a ring of G_STAGES LDS stages; slice kt+3 streams in while slice kt is
+    // multiplied, so three slices are always in flight
+    if (!cur_issued) {
+      __syncthreads();   // LDS stages are free
+#pragma unroll
+      for (int q = 0; q < G_STAGES - 1; ++q) issue_slice(cur, q, q);
     }
-    __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) lgkmcnt(0): the LDS copies have landed
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((G_STAGES - 2) * DMA_PER_SLICE, 0));   // slice 0 resident
     __syncthreads();
     for (int kt = 0; kt < nkt; ++kt) {
-      const int buf = kt & 1;
-      // 1. the next slice streams into the other LDS buffer while this one is used
-      //    (past the last slice every chunk is out of range and loads zeros: no branch)
-      issue_loads(kt + 1, buf ^ 1);
-      if constexpr (MX) sload(kt + 1 < nkt ? kt + 1 : kt, nsa, nsb);
+      const int stage = kt & (G_STAGES - 1);
+      issue_slice(cur, kt + G_STAGES - 1, (kt + G_STAGES - 1) & (G_STAGES - 1));
       __builtin_amdgcn_sched_barrier(0);
-      // 2. MFMAs on this slice; the fragments of step s+1 are read while step s runs
-      const uint8_t* sA = smem + buf * G_STAGE_BYTES;
+      const uint8_t* sA = smem + stage * G_STAGE_BYTES;
       const uint8_t* sB = sA + G_BM * G_BKB;
+      uint32_t sa[G_WMB], sb[G_WNB];
+      int gh = 0;
+      if constexpr (MX) {
+        gh = (cur.kbase / G_BKB + kt) & 1;
+        const uint8_t* sS = smem + G_SCALE_BASE + stage * G_SCALE_STAGE;
+#pragma unroll
+        for (int mi = 0; mi < G_WMB; ++mi) {
+          const int r = (wm * G_WMB + mi) * 32 + l32;
+          sa[mi] = *reinterpret_cast<const uint32_t*>(sS + (r >> 7) * 1024 + (r & 127) * 4);
+        }
+#pragma unroll
+        for (int ni = 0; ni < G_WNB; ++ni) {
+          const int r = brow_tile[ni] + l32;
+          sb[ni] = *reinterpret_cast<const uint32_t*>(sS + 2048 + (r >> 7) * 1024 + (r & 127) * 4);
+        }
+      }
       frag_t af[2][G_WMB], bfr[2][G_WNB];
       read_frags(sA, sB, 0, af[0], bfr[0]);
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s) {
         if (s + 1 < NSTEP) read_frags(sA, sB, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
-        mfma_step(s, af[s & 1], bfr[s & 1]);
+        mfma_step(s, gh, af[s & 1], bfr[s & 1], sa, sb);
       }
       __builtin_amdgcn_sched_barrier(0);
-      // 3. the next slice is resident and every wave is done with this one
-      __builtin_amdgcn_s_waitcnt(0);
+      // slice kt+1 resident (slices kt+2, kt+3 may still be in flight) and every wave is
+      // done with stage kt before it is refilled
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm((G_STAGES - 2) * DMA_PER_SLICE, 0));
       __syncthreads();
-      if constexpr (MX) {
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // the past-the-end (all-zero) slices have landed
+    // all stages are free: with a plain store epilogue, start the next tile's first
+    // slices now so their latency hides behind the stores
+    cur_issued = false;
+    if constexpr (EPI == EPI_STORE) {
+      if (nxt.valid && nxt.nkt > 0 && !p.accumulate) {
+        lane_offs(nxt);
 #pragma unroll
-        for (int mi = 0; mi < G_WMB; ++mi) sa[mi] = nsa[mi];
-#pragma unroll
-        for (int ni = 0; ni < G_WNB; ++ni) sb[ni] = nsb[ni];
+        for (int q = 0; q < G_STAGES - 1; ++q) issue_slice(nxt, q, q);
+        cur_issued = true;
       }
     }
 
@@ -395,37 +441,50 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
     // l32 of that 32 x 32 block.
     const int wrow0 = m0 + wm * G_WMB * 32;   // wave's first row (group-local)
     if constexpr (EPI == EPI_STORE) {
-      static_for<0, G_WMB>([&](auto mic) {
-        constexpr int mi = decltype(mic)::value;
-        static_for<0, G_WNB>([&](auto nic) {
-          constexpr int ni = decltype(nic)::value;
-          const int col = nt * G_BN + brow_tile[ni] + l32;
-          const bool cok = col < p.N;
+      // accumulator row r of a block is 8*(r/4) + 4*hi + (r%4); lanes 0..31 hold 32
+      // consecutive columns, so each store instruction writes two contiguous row pieces
+      auto store_tile = [&](auto* __restrict__ out, int64_t row0, bool accum) {
+        static_for<0, G_WMB>([&](auto mic) {
+          constexpr int mi = decltype(mic)::value;
+          static_for<0, G_WNB>([&](auto nic) {
+            constexpr int ni = decltype(nic)::value;
+            const int col = nt * G_BN + brow_tile[ni] + l32;
+            const bool cok = col < p.N;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = wrow0 + mi * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            float v = acc[mi][ni][r];
-            if (cok && row < m_valid) {
-              if constexpr (MODE == RAGGED_M) {
-                int64_t idx = int64_t(off + row) * p.ldc + col;
-                if (p.out_dtype == MGE_DTYPE_BF16) reinterpret_cast<uint16_t*>(p.C)[idx] = f32_to_bf16(v);
-                else reinterpret_cast<float*>(p.C)[idx] = v;
-              } else {
-                int64_t idx = int64_t(row) * p.ldc + col;
-                if (p.out_dtype == MGE_DTYPE_BF16) {
-                  uint16_t* o = reinterpret_cast<uint16_t*>(p.Ct[e]);
-                  if (p.accumulate) v += bf16_to_f32(o[idx]);
-                  o[idx] = f32_to_bf16(v);
+            for (int r = 0; r < 16; ++r) {
+              const int row = wrow0 + mi * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+              if (cok && row < m_valid) {
+                const int64_t idx = (row0 + row) * p.ldc + col;
+                float v = acc[mi][ni][r];
+                if constexpr (sizeof(*out) == 2) {
+                  if (accum) v += bf16_to_f32(out[idx]);
+                  out[idx] = f32_to_bf16(v);
                 } else {
-                  float* o = reinterpret_cast<float*>(p.Ct[e]);
-                  if (p.accumulate) v += o[idx];
-                  o[idx] = v;
+                  if (accum) v += out[idx];
+                  out[idx] = v;
                 }
               }
             }
-          }
+          });
         });
-      });
+      };
+      const bool accum = MODE == RAGGED_K && p.accumulate;
+      void* dst;
+      int64_t row0;
+      if constexpr (MODE == RAGGED_M) {
+        dst = p.C;
+        row0 = off;
+      } else {
+        dst = const_cast<void*>(uniform_ptr(const_cast<const void*>(p.Ct[e])));
+        row0 = 0;
+      }
+      if (p.out_dtype == MGE_DTYPE_BF16) {
+        if (accum) store_tile(reinterpret_cast<uint16_t*>(dst), row0, true);
+        else store_tile(reinterpret_cast<uint16_t*>(dst), row0, false);
+      } else {
+        if (accum) store_tile(reinterpret_cast<float*>(dst), row0, true);
+        else store_tile(reinterpret_cast<float*>(dst), row0, false);
+      }
     } else if constexpr (EPI == EPI_SWIGLU) {
       constexpr int hb = G_WNB / 2;
       const int F = p.F;
@@ -509,107 +568,10 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
           }
         });
       });
-    } else {  // EPI_SWIGLU_BWD: columns are f, the accumulator is dh
-      const int F = p.F;
-      const int F2 = 2 * F;
-      const int m_pad = (m_valid + 31) / 32 * 32;
-      const int part = nt * G_WAVES_N + wn;
-      static_for<0, G_WMB>([&](auto mic) {
-        constexpr int mi = decltype(mic)::value;
-        float pr[16], dps[16];
-        const int rbase = wrow0 + mi * 32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rbase + 8 * (r >> 2) + 4 * hi + (r & 3);
-          pr[r] = row < m_valid ? p.prob[off + row] : 0.f;
-          dps[r] = 0.f;
-        }
-        static_for<0, G_WNB>([&](auto nic) {
-          constexpr int ni = decltype(nic)::value;
-          const int f = nt * G_BN + (wn * G_WNB + ni) * 32 + l32;
-          const bool fok = f < F;
-          float dG[16], dU[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = rbase + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const bool ok = fok && row < m_valid;
-            float G = 0.f, U = 0.f;
-            if (ok) {
-              int64_t o = int64_t(off + row) * F2 + f;
-              G = bf16_to_f32(p.gu[o]);
-              U = bf16_to_f32(p.gu[o + F]);
-            }
-            const float dh = acc[mi][ni][r];
-            const float sg = sigmoid_f(G);
-            const float sl = G * sg;
-            dps[r] += ok ? dh * sl * U : 0.f;
-            dU[r] = ok ? dh * pr[r] * sl : 0.f;
-            dG[r] = ok ? dh * pr[r] * U * sg * (1.f + G * (1.f - sg)) : 0.f;
-          }
-          // row form [R][2F]: dG at column f, dU at column F + f
-          static_for<0, 2>([&](auto halfc) {
-            constexpr int half = decltype(halfc)::value;
-            float* v = half == 0 ? dG : dU;
-            const int col = half * F + f;
-            if (MX) {
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int row = rbase + 8 * (r >> 2) + 4 * hi + (r & 3);
-                float amax = wave_max_xor(fabsf(v[r]), 32);
-                uint32_t s = mx_scale_byte(amax);
-                uint32_t code = e4m3_rne(v[r] * mx_inv_scale(s));
-                if (row < m_valid && fok) {
-                  p.dgu_codes[int64_t(off + row) * F2 + col] = uint8_t(code);
-                  if (l32 == 0) p.dgu_scales[int64_t(off + row) * (F2 / 32) + col / 32] = uint8_t(s);
-                }
-              }
-            } else {
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int row = rbase + 8 * (r >> 2) + 4 * hi + (r & 3);
-                if (row < m_valid && fok) p.dgu_bf16[int64_t(off + row) * F2 + col] = f32_to_bf16(v[r]);
-              }
-            }
-            // column form [2F][Rp]
-            if ((p.dguc_codes || p.dguc_bf16) && fok && rbase < m_pad) {
-              if (MX) {
-                float amax = 0.f;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(v[r]));
-                amax = fmaxf(amax, __shfl_xor(amax, 32));
-                uint32_t s = mx_scale_byte(amax);
-                float inv = mx_inv_scale(s);
-                uint8_t* dst = p.dguc_codes + int64_t(col) * p.Rp + off + rbase + 4 * hi;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                  uint32_t w = e4m3_rne(v[4 * g] * inv) | (e4m3_rne(v[4 * g + 1] * inv) << 8) |
-                               (e4m3_rne(v[4 * g + 2] * inv) << 16) | (e4m3_rne(v[4 * g + 3] * inv) << 24);
-                  *reinterpret_cast<uint32_t*>(dst + 8 * g) = w;
-                }
-                if (hi == 0) p.dguc_scales[int64_t(col) * (p.Rp / 32) + (off + rbase) / 32] = uint8_t(s);
-              } else {
-                uint16_t* dst = p.dguc_bf16 + int64_t(col) * p.Rp + off + rbase + 4 * hi;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                  uint2 w;
-                  w.x = uint32_t(f32_to_bf16(v[4 * g])) | (uint32_t(f32_to_bf16(v[4 * g + 1])) << 16);
-                  w.y = uint32_t(f32_to_bf16(v[4 * g + 2])) | (uint32_t(f32_to_bf16(v[4 * g + 3])) << 16);
-                  *reinterpret_cast<uint2*>(dst + 8 * g) = w;
-                }
-              }
-            }
-          });
-        });
-        // d_prob partial of each row over this wave's columns (fixed xor-tree order)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = wave_sum_xor(dps[r], 32);
-          const int row = rbase + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (l32 == 0 && row < m_valid) p.dprob_part[int64_t(off + row) * p.nparts + part] = v;
-        }
-      });
     }
+    cur = nxt;
   }
+  __builtin_amdgcn_s_waitcnt(0);   // no LDS DMA outlives the workgroup
 }
 
 // ---------------------------------------------------------------- host-side launch
@@ -630,12 +592,12 @@ static inline int device_cus() {
 // LDS use), fewer when the tile count is smaller.
 template <typename Kern>
 static mge_status launch_gemm_kernel(Kern kern, const char* name, const GemmParams& p, hipStream_t s) {
-  hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, G_LDS_BYTES);
+  hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, G_DYN_LDS);
   int grid = device_cus();
   if (p.tiles_upper < grid) grid = p.tiles_upper;
   if (grid <= 0) return MGE_OK;
   ProfScope prof(s, name);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(G_THREADS), G_LDS_BYTES, s, p);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(G_THREADS), G_DYN_LDS, s, p);
   return hip_check(name);
 }
 

@@ -9,7 +9,7 @@ namespace mge {
 
 MGE_GEMM_KERNEL(gemm_gateup_swiglu_mx, EPI_SWIGLU, RAGGED_M)
 MGE_GEMM_KERNEL(gemm_down_mx, EPI_STORE, RAGGED_M)
-MGE_GEMM_KERNEL(gemm_dh_swiglu_bwd_mx, EPI_SWIGLU_BWD, RAGGED_M)
+MGE_GEMM_KERNEL(gemm_dh_mx, EPI_STORE, RAGGED_M)
 MGE_GEMM_KERNEL(gemm_dx_mx, EPI_STORE, RAGGED_M)
 MGE_GEMM_KERNEL(gemm_dw_down_mx, EPI_STORE, RAGGED_K)
 MGE_GEMM_KERNEL(gemm_dw_gateup_mx, EPI_STORE, RAGGED_K)
@@ -20,7 +20,7 @@ mge_status launch_gemm_mx(const GemmParams& p, hipStream_t s) {
   switch (p.role) {
     case GEMM_GATEUP: return launch_gemm_kernel(gemm_gateup_swiglu_mx, "gemm_gateup_swiglu_mx", p, s);
     case GEMM_DOWN: return launch_gemm_kernel(gemm_down_mx, "gemm_down_mx", p, s);
-    case GEMM_DH: return launch_gemm_kernel(gemm_dh_swiglu_bwd_mx, "gemm_dh_swiglu_bwd_mx", p, s);
+    case GEMM_DH: return launch_gemm_kernel(gemm_dh_mx, "gemm_dh_mx", p, s);
     case GEMM_DX: return launch_gemm_kernel(gemm_dx_mx, "gemm_dx_mx", p, s);
     case GEMM_DW_DOWN: return launch_gemm_kernel(gemm_dw_down_mx, "gemm_dw_down_mx", p, s);
     case GEMM_DW_GATEUP: return launch_gemm_kernel(gemm_dw_gateup_mx, "gemm_dw_gateup_mx", p, s);

@@ -71,18 +71,33 @@ mge_status launch_route(const RouteParams& p, hipStream_t s);
 // ------------------------------------------------------------ combine / reductions
 mge_status launch_combine(int T, int k, int H, int in_dtype, int out_dtype, const void* in,
                           const int32_t* perm_pos, const float* weights, void* out, hipStream_t s);
+// ------------------------------------------------------------ SwiGLU backward (elementwise)
+struct SwigluBwdParams {
+  int R, F, Rp;                          // permuted rows, ffn width, rows of the column form
+  const float* dh;                       // [R][F] fp32 (dY W_down)
+  const uint16_t* gu;                    // saved [R][2F] bf16 (G then U)
+  const float* prob;                     // prob_perm [R]
+  const int32_t* perm_src;               // [R], -1 on padding rows
+  uint8_t* row_codes; uint8_t* row_scales;  // MX dGU row [R][2F], [R][2F/32]
+  uint16_t* row_bf16;                    // bf16 dGU row [R][2F]
+  uint8_t* col_codes; uint8_t* col_scales;  // MX dGU column [2F][Rp], [2F][Rp/32]
+  uint16_t* col_bf16;                    // bf16 dGU transpose [2F][Rp]
+  float* dprob_row;                      // [R]: sum_f dh * silu(G) * U (valid rows)
+};
+mge_status launch_swiglu_bwd(const SwigluBwdParams& p, bool mx, hipStream_t s);
+
 mge_status launch_dprob_reduce(int T, int k, int nparts, const float* partial, const int32_t* perm_pos,
                                float* d_prob, hipStream_t s);
 mge_status launch_upload_ptrs(const void* const* host_ptrs, int n, void** dev_table, hipStream_t s);
 
 // ------------------------------------------------------------ grouped GEMM
 enum GemmMode { RAGGED_M = 0, RAGGED_K = 1 };
-enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_BWD = 2 };
+enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1 };
 // The six GEMMs of the layer; each is its own kernel symbol (traces, per-kernel timing).
 enum GemmRole {
   GEMM_GATEUP = 0,      // [G U] = X W_gate_up^T, SwiGLU x p epilogue       (RAGGED_M)
   GEMM_DOWN = 1,        // Y = h W_down^T                                   (RAGGED_M)
-  GEMM_DH = 2,          // dh = dY W_down, SwiGLU backward + d_prob epilogue (RAGGED_M)
+  GEMM_DH = 2,          // dh = dY W_down (fp32; the SwiGLU backward runs after it)  (RAGGED_M)
   GEMM_DX = 3,          // dX = dGU W_gate_up                               (RAGGED_M)
   GEMM_DW_DOWN = 4,     // dW_down = dY^T h                                 (RAGGED_K)
   GEMM_DW_GATEUP = 5    // dW_gate_up = dGU^T X                             (RAGGED_K)
@@ -106,8 +121,8 @@ struct GemmParams {
   //      RAGGED_K -> [R/128][M] (asp_ld = M)
   //   B: RAGGED_M -> expert e at Bsp + e*bsp_estride, [K/128][N] (bsp_ld = N);
   //      RAGGED_K -> [R/128][N] (bsp_ld = N)
-  const uint32_t* Asp; int64_t asp_ld;
-  const uint32_t* Bsp; int64_t bsp_ld, bsp_estride;
+  const uint32_t* Asp; int64_t asp_ld; uint32_t asp_bytes;
+  const uint32_t* Bsp; int64_t bsp_ld, bsp_estride; uint32_t bsp_bytes;
   int M, N, K;           // M used in RAGGED_K; K used in RAGGED_M (elements)
   // outputs
   int out_dtype;         // MGE_DTYPE_*
@@ -123,18 +138,9 @@ struct GemmParams {
   uint8_t* hc_codes; uint8_t* hc_scales;   // MX h column [F][Rp], [F][Rp/32] (training)
   uint16_t* hc_bf16;                       // bf16 h transpose [F][Rp] (training)
   int Rp;
-  // SwiGLU backward epilogue: N is F
-  const uint16_t* gu;                      // saved [R][2F]
-  uint8_t* dgu_codes; uint8_t* dgu_scales; // MX dGU row [R][2F], [R][2F/32]
-  uint16_t* dgu_bf16;                      // bf16 dGU row [R][2F]
-  uint8_t* dguc_codes; uint8_t* dguc_scales;  // MX dGU column [2F][Rp], [2F][Rp/32]
-  uint16_t* dguc_bf16;                     // bf16 dGU transpose [2F][Rp]
-  float* dprob_part; int nparts;           // [R][nparts]
   int tiles_upper;                         // host bound on the number of tiles (grid sizing)
 };
 
-// Number of d_prob partial sums per row written by the SwiGLU-backward epilogue.
-int gemm_swiglu_bwd_nparts(int F);
 // Upper bound of tiles for a RAGGED_M GEMM (host-side, from T*k and E).
 int gemm_tiles_upper(const GemmParams& p, int64_t total_rows_bound);
 mge_status launch_gemm(const GemmParams& p, int prec, hipStream_t s);
