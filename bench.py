@@ -118,7 +118,7 @@ def kernel_work(name, w, R):
     kernels: bytes that must cross HBM once (inputs read, outputs written)."""
     M, H, F, T, k, E = w.M, w.H, w.F, w.T, w.k, w.E
     mhf = float(M) * H * F
-    gemm = {"gemm_gateup_swiglu": 4 * mhf, "gemm_down": 2 * mhf, "gemm_dh_swiglu_bwd": 2 * mhf,
+    gemm = {"gemm_gateup_swiglu": 4 * mhf, "gemm_down": 2 * mhf, "gemm_dh": 2 * mhf,
             "gemm_dx": 4 * mhf, "gemm_dw_down": 2 * mhf, "gemm_dw_gateup": 4 * mhf}
     for key, v in gemm.items():
         if name.startswith(key + "_"):
@@ -131,7 +131,15 @@ def kernel_work(name, w, R):
     if name == "permute_bf16":
         return "byte", 2.0 * T * H + (2 if w.backward else 1) * 2.0 * M * H + 4.0 * R
     if name == "quant_mx":
-        return None                    # per-tensor size varies (W_gate_up vs W_down): see weight_quant_bytes
+        # the step's two weight quantizations (W_gate_up: 2FH, W_down: HF per expert),
+        # averaged per launch: bf16 read, row and (training) column forms written
+        forms = 2 if w.backward else 1
+        return "byte", 1.5 * E * H * F * (2.0 + forms * mxb)
+    if name in ("swiglu_bwd_mx", "swiglu_bwd_bf16"):
+        # per real (row, ffn column): dh f32 and G, U bf16 read; dG, dU written in row
+        # and column forms (MXFP8 codes + scale share, or bf16)
+        out = 2 * 2 * (mxb if name.endswith("_mx") else 2.0)
+        return "byte", float(M) * F * (4.0 + 4.0 + out) + 8.0 * R
     if name == "combine":
         return "byte", 2.0 * k * T * H + 2.0 * T * H + 4.0 * T * k
     if name in ("route_topk", "route_scatter"):
@@ -197,7 +205,7 @@ def traffic_for(kernel, workload):
 
 # ------------------------------------------------------------------------------ CPU baseline
 
-def cpu_baseline(w, max_rows=32, f_cols=3072):
+def cpu_baseline(w, max_rows=32, f_cols=None):
     """The fp64 CPU oracle, as it stands, on a bounded sample of the workload.
 
     Sample: expert 0 of the workload, the first `max_rows` assignments routed to it
@@ -221,7 +229,7 @@ def cpu_baseline(w, max_rows=32, f_cols=3072):
     hit = np.argwhere(idx == 0)[:max_rows]
     toks, slots = hit[:, 0], hit[:, 1]
     n = len(toks)
-    fs = min(f_cols, w.F)
+    fs = w.F if f_cols is None else min(f_cols, w.F)
     std = np.float32(w.weight_std)
     # expert 0's weights from the workload's numpy streams (the first rows of each stream
     # are expert 0), restricted to the sampled ffn columns
@@ -281,7 +289,7 @@ def main():
     ap.add_argument("--workload", default="train_mxfp8", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=32, help="assignments in the CPU oracle sample")
-    ap.add_argument("--cpu-fcols", type=int, default=3072, help="ffn columns in the CPU oracle sample")
+    ap.add_argument("--cpu-fcols", type=int, default=None, help="ffn columns in the CPU oracle sample (default: all)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",

@@ -1,5 +1,5 @@
-// Host side of the grouped GEMM: tile-count bounds for grid sizing, the number of
-// d_prob partial sums, and the dispatch to the per-precision kernel sets.
+// Host side of the grouped GEMM: tile-count bounds for grid sizing, the checks of a
+// role's mode and output form, and the dispatch to the per-precision kernel sets.
 #include "gemm_impl.hpp"
 
 namespace mge {
@@ -21,6 +21,23 @@ mge_status launch_gemm(const GemmParams& p, int prec, hipStream_t s) {
   const bool k_mode = p.role == GEMM_DW_DOWN || p.role == GEMM_DW_GATEUP;
   if ((p.mode == RAGGED_K) != k_mode) {
     set_error("GEMM role %d does not match mode %d", p.role, p.mode);
+    return MGE_ERR_INVALID_ARG;
+  }
+  if (p.role != GEMM_GATEUP) {
+    const bool ok = p.role == GEMM_DOWN ? (p.out_dtype == MGE_DTYPE_BF16 || p.out_dtype == MGE_DTYPE_F32)
+                    : p.role == GEMM_DX ? p.out_dtype == MGE_DTYPE_BF16
+                                        : p.out_dtype == MGE_DTYPE_F32;
+    if (!ok || (p.accumulate && !k_mode)) {
+      set_error("GEMM role %d: output dtype %d / accumulate %d not supported", p.role, p.out_dtype, p.accumulate);
+      return MGE_ERR_INVALID_ARG;
+    }
+    // the store epilogue addresses a wave's 128 output rows with 32-bit offsets
+    if (int64_t(p.ldc) * 4 * G_BM >= (int64_t(1) << 31)) {
+      set_error("GEMM output row stride %lld too large", static_cast<long long>(p.ldc));
+      return MGE_ERR_INVALID_ARG;
+    }
+  } else if (int64_t(p.F) * 4 * 2 * G_BM >= (int64_t(1) << 31)) {
+    set_error("F = %d too large for the SwiGLU epilogue", p.F);
     return MGE_ERR_INVALID_ARG;
   }
   return prec == MGE_PREC_MXFP8 ? launch_gemm_mx(p, s) : launch_gemm_bf16(p, s);

@@ -8,8 +8,8 @@
 //   RAGGED_K: the reduction runs over expert e's tokens, the column span
 //             [off[e], off[e] + roundup32(sizes[e])) of shared A and B; the output is
 //             the expert's own [M][N] gradient.  (dW_down, dW_gate_up)
-// Tiles are 256 x 256 with 128-byte K slices (128 FP8 or 64 BF16 elements), 4 waves in
-// a 2 x 2 grid, each wave 128 x 128 built from 32 x 32 MFMA blocks:
+// Tiles are 256 x 256, 4 waves in a 2 x 2 grid, each wave 128 x 128 built from 32 x 32
+// MFMA blocks whose fp32 accumulators stay in AGPRs:
 //   MXFP8: v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, one E8M0 scale per lane and
 //          32-element K block, applied by the matrix core — no dequantize pass).
 //          Operand layout (measured on gfx950): lane l = 32h + i feeds row/column i;
@@ -18,16 +18,22 @@
 //          32h..32h+31) is scaled by the scale register of the lanes with that h, the
 //          byte chosen by op_sel.
 //   BF16:  v_mfma_f32_32x32x16_bf16
-// Operand tiles go HBM -> registers -> LDS (double-buffered, XOR-swizzled 16-byte
-// chunks so both the row-wise stores and the MFMA fragment reads are bank-conflict
-// free); the next K slice is fetched while the current one is multiplied.
+// Operands stream HBM -> LDS directly (buffer_load ... lds, no register staging) in
+// 64-byte K slices (64 FP8 or 32 BF16 elements) through a ring of 4 LDS stages, three
+// slices in flight while one is multiplied.  LDS rows are 64 bytes with the 16-byte
+// chunks XOR-swizzled by row so the MFMA fragment reads spread over the 64 banks.  The
+// MX scales of a slice ride along into LDS (packed: one dword = 4 blocks of a row).
 // A persistent grid walks the tiles (expert-major, then N, M fastest so that
 // consecutive tiles share the weight tile); virtual workgroup ids are remapped so
 // that the workgroups of one XCD (hardware dispatches round-robin over the 8 XCDs)
 // take consecutive tiles and share that XCD's L2.  Empty experts own no tiles (RAGGED_M)
-// or produce zero gradients (RAGGED_K).
-// Epilogues (fp32 accumulators never reach HBM):
-//   EPI_STORE       bf16 / f32 store (optionally accumulate), row masking
+// or produce zero gradients (RAGGED_K).  The next tile's first slices are issued
+// before the epilogue, so their latency hides behind it.
+// Epilogues (fp32 accumulators never reach HBM; no per-element branches: stores go
+// through buffer resources whose record bound ends at the last valid row, so the
+// hardware range check drops rows past the group, and columns past N get an offset
+// beyond every bound):
+//   EPI_STORE       bf16 / f32 store, or f32 added to the output (OutForm)
 //   EPI_SWIGLU      h = p * silu(G) * U with G, U of the same rows/columns in the same
 //                   lane; h quantized along F (MXFP8, amax over the 32 lanes that hold
 //                   one 32-column block) or rounded to bf16; training also stores G, U
@@ -79,6 +85,15 @@ __device__ __forceinline__ void static_for(Fn&& fn) {
 // Values that are the same in every lane, moved to scalar registers so that buffer
 // resources and LDS-DMA destinations need no per-lane handling.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// Element i (wave-uniform) of a table the kernel never writes (sizes, offsets, pointer
+// tables), read through the constant address space: the compiler then emits a scalar
+// load, counted by lgkmcnt.  A vector load would be counted by vmcnt, and waiting for
+// it would also wait for every operand DMA and epilogue store issued before it.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* base, int i) {
+  typedef const __attribute__((address_space(4))) T const_t;
+  return reinterpret_cast<const_t*>(reinterpret_cast<uintptr_t>(base))[i];
+}
 template <typename T>
 __device__ __forceinline__ const T* uniform_ptr(const T* p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
@@ -103,6 +118,22 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base) {
 __device__ __forceinline__ i32x4 make_rsrc_n(const void* base, uint32_t bytes) {
   const uint64_t v = reinterpret_cast<uint64_t>(base);
   return i32x4{int(uint32_t(v)), int(uint32_t(v >> 32) & 0xffff), int(bytes), kRsrcFlags};
+}
+
+// One accumulator element into a VGPR.  The explicit read (an AGPR operand) keeps the
+// accumulator tile in AGPRs until the epilogue reaches its block; left to itself the
+// compiler copies all 256 accumulators into VGPRs at the end of the K loop and spills.
+// The MFMA -> read hazard is covered by the wait states issued after the K loop
+// (acc_settle), which the compiler cannot see through the asm.
+__device__ __forceinline__ float acc_read(float x) {
+  float y;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(y) : "a"(x));
+  return y;
+}
+// 64 wait states: more than the longest MFMA result latency of gfx950 (a 16-pass XDL
+// op needs 18 before a VALU may read its result)
+__device__ __forceinline__ void acc_settle() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
 // s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory and `lgkm`
@@ -140,13 +171,14 @@ constexpr int G_SCALE_STAGE = 4096;
 constexpr int G_SCALE_BASE = G_STAGES * G_STAGE_BYTES;
 constexpr int G_DYN_LDS = G_SCALE_BASE + G_STAGES * G_SCALE_STAGE;
 
-template <bool MX, int EPI, int MODE>
+template <bool MX, int EPI, int MODE, int OUT>
 __device__ __forceinline__ void gemm_body(const GemmParams& p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   // LDS byte address of the dynamic shared block (the low half of its generic address)
   const uint32_t lds_base = uniform(int(uint32_t(reinterpret_cast<uintptr_t>(smem))));
   __shared__ int32_t s_prefix[G_MAXE + 1];
   __shared__ int32_t s_mtiles[G_MAXE];
+  __shared__ __attribute__((aligned(16))) float s_prob[G_BM];   // SwiGLU: routing probability of each tile row
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -192,8 +224,8 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
     const int mtn = uniform(s_mtiles[t.e]);
     const int mt = local % mtn;
     t.nt = local / mtn;
-    t.off = uniform(p.offs[t.e]);
-    t.m_valid = MODE == RAGGED_M ? uniform(p.sizes[t.e]) : p.M;
+    t.off = ld_uniform(p.offs, t.e);
+    t.m_valid = MODE == RAGGED_M ? ld_uniform(p.sizes, t.e) : p.M;
     t.m0 = mt * G_BM;
     // K range in bytes.  RAGGED_M: [0, K).  RAGGED_K: the expert's token span
     // [off, off + roundup32(size)) of the column forms; the loop starts at the slice
@@ -201,9 +233,9 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
     if constexpr (MODE == RAGGED_M) {
       t.kbase = 0; t.klo = 0; t.khi = p.K * ELEM;
       t.A = p.A + int64_t(t.off) * p.lda;
-      t.B = uniform_ptr(p.Bt[t.e]);
+      t.B = ld_uniform(p.Bt, t.e);
     } else {
-      const int span = ((uniform(p.sizes[t.e]) + 31) / 32) * 32;
+      const int span = ((ld_uniform(p.sizes, t.e) + 31) / 32) * 32;
       t.klo = t.off * ELEM;
       t.khi = (t.off + span) * ELEM;
       t.kbase = span > 0 ? (t.klo / G_BKB) * G_BKB : t.klo;
@@ -352,6 +384,12 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
     const Tile nxt = decode(tile + nwg);
     const int e = cur.e, nt = cur.nt, off = cur.off, m_valid = cur.m_valid, m0 = cur.m0, nkt = cur.nkt;
     lane_offs(cur);
+    // SwiGLU: the probability of tile row tid, loaded now so that its latency hides
+    // behind the K loop (it is staged in LDS for the epilogue)
+    float my_prob = 0.f;
+    if constexpr (EPI == EPI_SWIGLU) {
+      if (m0 + tid < m_valid) my_prob = p.prob[off + m0 + tid];
+    }
 
     f32x16 acc[G_WMB][G_WNB];
 #pragma unroll
@@ -424,11 +462,13 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
       __syncthreads();
     }
     __builtin_amdgcn_s_waitcnt(0);   // the past-the-end (all-zero) slices have landed
-    // all stages are free: with a plain store epilogue, start the next tile's first
-    // slices now so their latency hides behind the stores
+    acc_settle();                    // the last MFMA results are readable
+    // all stages are free: start the next tile's first slices now so their latency hides
+    // behind the epilogue (which uses no stage memory).  Not when the epilogue reads the
+    // output back: those loads would queue behind the slices.
     cur_issued = false;
-    if constexpr (EPI == EPI_STORE) {
-      if (nxt.valid && nxt.nkt > 0 && !p.accumulate) {
+    {
+      if (nxt.valid && nxt.nkt > 0 && OUT != OUT_F32_ACC) {
         lane_offs(nxt);
 #pragma unroll
         for (int q = 0; q < G_STAGES - 1; ++q) issue_slice(nxt, q, q);
@@ -441,131 +481,166 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
     // l32 of that 32 x 32 block.
     const int wrow0 = m0 + wm * G_WMB * 32;   // wave's first row (group-local)
     if constexpr (EPI == EPI_STORE) {
-      // accumulator row r of a block is 8*(r/4) + 4*hi + (r%4); lanes 0..31 hold 32
-      // consecutive columns, so each store instruction writes two contiguous row pieces
-      auto store_tile = [&](auto* __restrict__ out, int64_t row0, bool accum) {
-        static_for<0, G_WMB>([&](auto mic) {
-          constexpr int mi = decltype(mic)::value;
-          static_for<0, G_WNB>([&](auto nic) {
-            constexpr int ni = decltype(nic)::value;
-            const int col = nt * G_BN + brow_tile[ni] + l32;
-            const bool cok = col < p.N;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int row = wrow0 + mi * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-              if (cok && row < m_valid) {
-                const int64_t idx = (row0 + row) * p.ldc + col;
-                float v = acc[mi][ni][r];
-                if constexpr (sizeof(*out) == 2) {
-                  if (accum) v += bf16_to_f32(out[idx]);
-                  out[idx] = f32_to_bf16(v);
-                } else {
-                  if (accum) v += out[idx];
-                  out[idx] = v;
-                }
-              }
-            }
-          });
-        });
-      };
-      const bool accum = MODE == RAGGED_K && p.accumulate;
-      void* dst;
-      int64_t row0;
+      // Lane (hi, l32) stores column l32 of each 32 x 32 block, rows 8*(r/4) + 4*hi +
+      // r%4; the record bound of the resource ends at the last valid row of the wave's
+      // 128-row span and lanes whose column is past N get an offset beyond every bound.
+      constexpr int ESZ = OUT == OUT_BF16 ? 2 : 4;
+      int vr = m_valid - wrow0;
+      vr = uniform(vr < 0 ? 0 : (vr > G_WMB * 32 ? G_WMB * 32 : vr));
+      uint8_t* cbase;
       if constexpr (MODE == RAGGED_M) {
-        dst = p.C;
-        row0 = off;
+        cbase = static_cast<uint8_t*>(p.C) + (int64_t(off) + wrow0) * p.ldc * ESZ;
       } else {
-        dst = const_cast<void*>(uniform_ptr(const_cast<const void*>(p.Ct[e])));
-        row0 = 0;
+        cbase = static_cast<uint8_t*>(ld_uniform(p.Ct, e)) +
+                int64_t(wrow0) * p.ldc * ESZ;
       }
-      if (p.out_dtype == MGE_DTYPE_BF16) {
-        if (accum) store_tile(reinterpret_cast<uint16_t*>(dst), row0, true);
-        else store_tile(reinterpret_cast<uint16_t*>(dst), row0, false);
-      } else {
-        if (accum) store_tile(reinterpret_cast<float*>(dst), row0, true);
-        else store_tile(reinterpret_cast<float*>(dst), row0, false);
-      }
-    } else if constexpr (EPI == EPI_SWIGLU) {
-      constexpr int hb = G_WNB / 2;
-      const int F = p.F;
-      const int F2 = 2 * F;
-      const int m_pad = (m_valid + 31) / 32 * 32;
+      const uint32_t rowb = uint32_t(p.ldc) * ESZ;
+      const __amdgpu_buffer_rsrc_t rC = __builtin_amdgcn_make_buffer_rsrc(cbase, 0, int(uint32_t(vr) * rowb), kRsrcFlags);
       static_for<0, G_WMB>([&](auto mic) {
         constexpr int mi = decltype(mic)::value;
-        float pr[16];
-        const int rbase = wrow0 + mi * 32;
+        if (wrow0 + mi * 32 >= m_valid) return;
+        static_for<0, G_WNB>([&](auto nic) {
+          constexpr int ni = decltype(nic)::value;
+          const int col = nt * G_BN + brow_tile[ni] + l32;
+          const uint32_t lo = col < p.N ? uint32_t(col) * ESZ + uint32_t(4 * hi) * rowb : kInvalid;
+          if constexpr (OUT == OUT_F32_ACC) {
+            uint32_t old[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rbase + 8 * (r >> 2) + 4 * hi + (r & 3);
-          pr[r] = row < m_valid ? p.prob[off + row] : 0.f;
-        }
-        static_for<0, hb>([&](auto jc) {
-          constexpr int j = decltype(jc)::value;
-          const int f = nt * (G_BN / 2) + (wn * hb + j) * 32 + l32;
-          const bool fok = f < F;
-          float h[16];
+            for (int r = 0; r < 16; ++r)
+              old[r] = __builtin_amdgcn_raw_buffer_load_b32(rC, int(lo + uint32_t(mi * 32 + 8 * (r >> 2) + (r & 3)) * rowb), 0, 0);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = rbase + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const bool ok = fok && row < m_valid;
-            const float G = acc[mi][j][r];
-            const float U = acc[mi][j + hb][r];
-            h[r] = ok ? pr[r] * silu_f(G) * U : 0.f;
-            if (p.saved_gu && ok) {
-              int64_t o = int64_t(off + row) * F2 + f;
-              p.saved_gu[o] = f32_to_bf16(G);
-              p.saved_gu[o + F] = f32_to_bf16(U);
-            }
-          }
-          // row form of h (blocks of 32 along F = the 32 lanes of this half-wave)
-          if (MX) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int row = rbase + 8 * (r >> 2) + 4 * hi + (r & 3);
-              float amax = wave_max_xor(fabsf(h[r]), 32);
-              uint32_t s = mx_scale_byte(amax);
-              uint32_t code = e4m3_rne(h[r] * mx_inv_scale(s));
-              if (row < m_valid && fok) {
-                int64_t o = int64_t(off + row) * F + f;
-                p.h_codes[o] = uint8_t(code);
-                if (l32 == 0) p.h_scales[int64_t(off + row) * (F / 32) + f / 32] = uint8_t(s);
-              }
-            }
+            for (int r = 0; r < 16; ++r)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc_read(acc[mi][ni][r]) + __uint_as_float(old[r])), rC,
+                                                    int(lo + uint32_t(mi * 32 + 8 * (r >> 2) + (r & 3)) * rowb), 0, 0);
           } else {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int row = rbase + 8 * (r >> 2) + 4 * hi + (r & 3);
-              if (row < m_valid && fok) p.h_bf16[int64_t(off + row) * F + f] = f32_to_bf16(h[r]);
+              const int o = int(lo + uint32_t(mi * 32 + 8 * (r >> 2) + (r & 3)) * rowb);
+              if constexpr (OUT == OUT_BF16)
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc_read(acc[mi][ni][r])), rC, o, 0, 0);
+              else
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[mi][ni][r]), rC, o, 0, 0);
             }
           }
-          // column form of h (training): this 32-row block of column f
-          if ((p.hc_codes || p.hc_bf16) && fok && rbase < m_pad) {
-            if (MX) {
-              float amax = 0.f;
+          __builtin_amdgcn_sched_barrier(0);   // one block at a time (register peak)
+        });
+      });
+    } else if constexpr (EPI == EPI_SWIGLU) {
+      // h = p * silu(G) * U over the wave's 128 rows x 64 ffn columns, written as the row
+      // form (blocks of 32 along F) and, in training, the column form (blocks of 32 rows)
+      // plus G and U in bf16.  Lanes 0..31 of a half-wave hold 32 consecutive columns of
+      // one row, so a row block's amax is a half-wave all-reduce; a lane holds 16 rows of
+      // one column and the two half-waves together a column's 32-row block.  Row-form
+      // stores go through buffer resources whose record bound ends at the group's last
+      // row, so rows past it are dropped by the hardware range check; 32-row blocks past
+      // the group and 32-column blocks past F are skipped whole (wave-uniform).
+      s_prob[tid] = my_prob;
+      __syncthreads();
+      constexpr int hb = G_WNB / 2;
+      const int F = p.F;
+      const int F2 = 2 * F;
+      const bool train = p.saved_gu != nullptr;
+      int vr = m_valid - wrow0;                         // valid rows of the wave's span
+      vr = uniform(vr < 0 ? 0 : (vr > G_WMB * 32 ? G_WMB * 32 : vr));
+      const int64_t grow0 = int64_t(off) + wrow0;       // permuted row of span row 0
+      auto rsrc = [](const void* base, uint32_t bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kRsrcFlags);
+      };
+      __amdgpu_buffer_rsrc_t rH, rHs, rGU;
+      if constexpr (MX) {
+        rH = rsrc(p.h_codes + grow0 * F, uint32_t(vr) * F);
+        rHs = rsrc(p.h_scales + grow0 * (F / 32), uint32_t(vr) * (F / 32));
+      } else {
+        rH = rsrc(p.h_bf16 + grow0 * F, uint32_t(vr) * F * 2);
+        rHs = rH;
+      }
+      rGU = rsrc(train ? p.saved_gu + grow0 * F2 : p.saved_gu, train ? uint32_t(vr) * F2 * 2 : 0u);
+      static_for<0, G_WMB>([&](auto mic) {
+        constexpr int mi = decltype(mic)::value;
+        const int rb = mi * 32;                          // block row within the span
+        if (wrow0 + rb >= m_valid) return;               // past the group and its padding
+        // rows of this lane's 16 values within the span: rb + 8*(r/4) + 4*hi + r%4
+        float pr[16];
 #pragma unroll
-              for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(h[r]));
-              amax = fmaxf(amax, __shfl_xor(amax, 32));
-              uint32_t s = mx_scale_byte(amax);
-              float inv = mx_inv_scale(s);
-              uint8_t* dst = p.hc_codes + int64_t(f) * p.Rp + off + rbase + 4 * hi;
+        for (int g = 0; g < 4; ++g) {
+          const float4 q = *reinterpret_cast<const float4*>(&s_prob[wm * G_WMB * 32 + rb + 8 * g + 4 * hi]);
+          pr[4 * g] = q.x; pr[4 * g + 1] = q.y; pr[4 * g + 2] = q.z; pr[4 * g + 3] = q.w;
+        }
+        static_for<0, hb>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          const int fb0 = nt * (G_BN / 2) + (wn * hb + j) * 32;   // first column of the block
+          if (fb0 >= F) return;
+          const int f = fb0 + l32;
+          float h[16], Gv[16], Uv[16];
 #pragma unroll
-              for (int g = 0; g < 4; ++g) {
-                uint32_t w = e4m3_rne(h[4 * g] * inv) | (e4m3_rne(h[4 * g + 1] * inv) << 8) |
-                             (e4m3_rne(h[4 * g + 2] * inv) << 16) | (e4m3_rne(h[4 * g + 3] * inv) << 24);
-                *reinterpret_cast<uint32_t*>(dst + 8 * g) = w;
-              }
-              if (hi == 0) p.hc_scales[int64_t(f) * (p.Rp / 32) + (off + rbase) / 32] = uint8_t(s);
+          for (int r = 0; r < 16; ++r) {
+            Gv[r] = acc_read(acc[mi][j][r]);
+            Uv[r] = acc_read(acc[mi][j + hb][r]);
+            h[r] = pr[r] * (Gv[r] * __builtin_amdgcn_rcpf(1.f + __expf(-Gv[r]))) * Uv[r];
+          }
+          auto lrow = [&](int r) { return rb + 8 * (r >> 2) + 4 * hi + (r & 3); };
+          if (train) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int o = (lrow(r) * F2 + f) * 2;
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(Gv[r]), rGU, o, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(Uv[r]), rGU, o + 2 * F, 0, 0);
+            }
+          }
+          if constexpr (MX) {
+            // row form: one scale per (row, 32-column block), shared by the half-wave
+            uint32_t sc = 0;
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+              const uint32_t s0 = mx_scale_byte(max_half_wave(fabsf(h[r])));
+              const uint32_t s1 = mx_scale_byte(max_half_wave(fabsf(h[r + 1])));
+              const uint32_t c = e4m3x2(h[r] * mx_inv_scale(s0), h[r + 1] * mx_inv_scale(s1));
+              __builtin_amdgcn_raw_buffer_store_b8(uint8_t(c), rH, lrow(r) * F + f, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b8(uint8_t(c >> 8), rH, lrow(r + 1) * F + f, 0, 0);
+              sc = l32 == r ? s0 : sc;
+              sc = l32 == r + 1 ? s1 : sc;
+            }
+            // lane l32 < 16 writes the scale of its row l32
+            const uint32_t so = l32 < 16 ? uint32_t(lrow(l32) * (F / 32) + fb0 / 32) : kInvalid;
+            __builtin_amdgcn_raw_buffer_store_b8(uint8_t(sc), rHs, so, 0, 0);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(h[r]), rH, (lrow(r) * F + f) * 2, 0, 0);
+          }
+          if (train) {
+            // column form of column f, rows [rb, rb + 32): after the half-wave swaps,
+            // lane hi holds rows 16*hi .. 16*hi + 15 in order
+            const int64_t cbase = int64_t(f) * p.Rp + grow0 + rb + 16 * hi;   // element index
+            if constexpr (MX) {
+              float cmax = 0.f;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) cmax = fmaxf(cmax, fabsf(h[r]));
+              cmax = max_xor32(cmax);
+              const uint32_t s = mx_scale_byte(cmax);
+              const float inv = mx_inv_scale(s);
+              uint32_t c[4];
+#pragma unroll
+              for (int g = 0; g < 4; ++g) c[g] = e4m3x4(h[4 * g] * inv, h[4 * g + 1] * inv, h[4 * g + 2] * inv, h[4 * g + 3] * inv);
+              const U32Pair x02 = permlane32_swap(c[0], c[2]);
+              const U32Pair x13 = permlane32_swap(c[1], c[3]);
+              *reinterpret_cast<uint4*>(p.hc_codes + cbase) = make_uint4(x02.a, x02.b, x13.a, x13.b);
+              if (hi == 0) p.hc_scales[int64_t(f) * (p.Rp / 32) + (grow0 + rb) / 32] = uint8_t(s);
             } else {
-              uint16_t* dst = p.hc_bf16 + int64_t(f) * p.Rp + off + rbase + 4 * hi;
+              uint32_t c[8];
 #pragma unroll
               for (int g = 0; g < 4; ++g) {
-                uint2 w;
-                w.x = uint32_t(f32_to_bf16(h[4 * g])) | (uint32_t(f32_to_bf16(h[4 * g + 1])) << 16);
-                w.y = uint32_t(f32_to_bf16(h[4 * g + 2])) | (uint32_t(f32_to_bf16(h[4 * g + 3])) << 16);
-                *reinterpret_cast<uint2*>(dst + 8 * g) = w;
+                c[2 * g] = bf16x2(h[4 * g], h[4 * g + 1]);
+                c[2 * g + 1] = bf16x2(h[4 * g + 2], h[4 * g + 3]);
               }
+              const U32Pair a0 = permlane32_swap(c[0], c[4]), a1 = permlane32_swap(c[1], c[5]);
+              const U32Pair b0 = permlane32_swap(c[2], c[6]), b1 = permlane32_swap(c[3], c[7]);
+              uint4* dst = reinterpret_cast<uint4*>(p.hc_bf16 + cbase);
+              dst[0] = make_uint4(a0.a, a1.a, a0.b, a1.b);
+              dst[1] = make_uint4(b0.a, b1.a, b0.b, b1.b);
             }
           }
+          __builtin_amdgcn_sched_barrier(0);   // one block at a time (register peak)
         });
       });
     }

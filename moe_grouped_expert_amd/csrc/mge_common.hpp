@@ -19,12 +19,14 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-// fp32 -> bf16 round-to-nearest-even (finite inputs; NaN keeps a quiet NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+// fp32 -> bf16 round-to-nearest-even (NaN stays NaN): gfx950's v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
+
+// Two bf16 in one dword: lo in bits 0..15, hi in bits 16..31 (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // E8M0 scale byte of a block from its amax (|values| max as fp32):
@@ -40,27 +42,59 @@ __device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
 // 2^-e for the scale byte s (e = s - 127): fp32 with exponent field 254 - s.
 __device__ __forceinline__ float mx_inv_scale(uint32_t s) { return __uint_as_float((254u - s) << 23); }
 
-// E4M3 code of w (already divided by the block scale), round-to-nearest-even,
-// saturating at 448, signed zero kept.  Works on the fp32 bit pattern: the spacing of
-// E4M3 values in the binade b = max(floor(log2|w|), -6) is 2^(b-3); the 24-bit
-// significand is shifted right to that spacing with ties to even; the code is then
-// 8*(b+7) + (multiple - 8), which also covers subnormals and the carry into the next
-// binade.
+// E4M3 codes of values already divided by their block scale: round to the nearest
+// E4M3 value, ties to even, saturating at +-448, signed zero kept.  gfx950's
+// v_cvt_pk_fp8_f32 rounds to nearest even into the OCP E4M3 format; clamping the input
+// to +-448 first makes it saturate (448 is the largest finite E4M3 value and every
+// |w| in (448, 464) rounds to it anyway).  Over all 2^32 fp32 inputs this equals the
+// bit-level definition: the spacing of E4M3 values in binade b = max(floor(log2|w|), -6)
+// is 2^(b-3), the significand is rounded to that spacing with ties to even, and results
+// beyond 448 become 448.
+__device__ __forceinline__ float e4m3_clamp(float w) { return __builtin_amdgcn_fmed3f(w, -448.f, 448.f); }
+
+// codes of a, b in bytes 0, 1
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false)) & 0xffffu;
+}
+
+// codes of a, b, c, d in bytes 0..3
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), v, true);
+  return uint32_t(v);
+}
+
 __device__ __forceinline__ uint32_t e4m3_rne(float w) {
-  uint32_t b = __float_as_uint(w);
-  uint32_t sign = (b >> 24) & 0x80u;
-  uint32_t a = b & 0x7fffffffu;
-  if (a >= 0x43e00000u) return sign | 0x7eu;   // |w| >= 448
-  if (a <= 0x3a800000u) return sign;           // |w| <= 2^-10 rounds to zero
-  int E = int(a >> 23) - 127;                  // >= -10 here
-  int bin = E < -6 ? -6 : E;
-  uint32_t sig = (a & 0x7fffffu) | 0x800000u;
-  int sh = bin - E + 20;                       // 20..24
-  uint32_t q = sig >> sh;
-  uint32_t rem = sig & ((1u << sh) - 1u);
-  uint32_t half = 1u << (sh - 1);
-  q += (rem > half) | ((rem == half) & (q & 1u));
-  return sign | uint32_t(8 * (bin + 7) + int(q) - 8);
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(w), 0.f, 0, false)) & 0xffu;
+}
+
+// Max over the 32 lanes of each half-wave, returned in every lane: DPP exchanges
+// within 16-lane rows (xor 1, xor 2, mirror in 8, mirror in 16), then a swizzle that
+// swaps the two 16-lane rows of each half.  Needs all 64 lanes active.
+__device__ __forceinline__ float max_half_wave(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false)));    // quad_perm 1,0,3,2
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false)));    // quad_perm 2,3,0,1
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, false)));   // row_half_mirror
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xf, 0xf, false)));   // row_mirror
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));                // swap 16-lane rows
+  return v;
+}
+
+// v_permlane32_swap_b32: lanes 32..63 of a trade places with lanes 0..31 of b.  Returns
+// the new (a, b): lane i < 32 then holds (a[i], a[i + 32]) and lane i + 32 holds
+// (b[i], b[i + 32]).
+struct U32Pair {
+  uint32_t a, b;
+};
+__device__ __forceinline__ U32Pair permlane32_swap(uint32_t a, uint32_t b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  return U32Pair{uint32_t(r[0]), uint32_t(r[1])};
+}
+
+// max of v over lanes i and i ^ 32
+__device__ __forceinline__ float max_xor32(float v) {
+  const U32Pair r = permlane32_swap(__float_as_uint(v), __float_as_uint(v));
+  return fmaxf(__uint_as_float(r.a), __uint_as_float(r.b));
 }
 
 __device__ __forceinline__ float wave_max_xor(float v, int lanes) {

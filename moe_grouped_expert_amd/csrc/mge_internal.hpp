@@ -93,6 +93,9 @@ mge_status launch_upload_ptrs(const void* const* host_ptrs, int n, void** dev_ta
 // ------------------------------------------------------------ grouped GEMM
 enum GemmMode { RAGGED_M = 0, RAGGED_K = 1 };
 enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1 };
+// What a plain-store epilogue writes (a kernel template parameter, so that each kernel
+// carries one store path): none (SwiGLU), bf16, f32, or f32 added to the output.
+enum OutForm { OUT_NONE = 0, OUT_BF16 = 1, OUT_F32 = 2, OUT_F32_ACC = 3 };
 // The six GEMMs of the layer; each is its own kernel symbol (traces, per-kernel timing).
 enum GemmRole {
   GEMM_GATEUP = 0,      // [G U] = X W_gate_up^T, SwiGLU x p epilogue       (RAGGED_M)
