@@ -59,10 +59,10 @@ constexpr int G_WMB = 4;   // 32-row MFMA blocks per wave (M)
 constexpr int G_WNB = 4;   // 32-col MFMA blocks per wave (N)
 constexpr int G_BM = G_WAVES_M * G_WMB * 32;
 constexpr int G_BN = G_WAVES_N * G_WNB * 32;
-constexpr int G_BKB = 64;                     // K bytes per slice (one MXFP8 MFMA step)
-constexpr int G_STAGES = 4;                   // LDS ring depth: 3 slices in flight
+constexpr int G_BKB = 128;                    // K bytes per slice: one whole 128-byte line per operand row
+constexpr int G_STAGES = 2;                   // LDS stages: one slice in flight while the other is multiplied
 constexpr int G_THREADS = 64 * G_WAVES_M * G_WAVES_N;
-constexpr int G_STAGE_BYTES = (G_BM + G_BN) * G_BKB;   // 32 KB
+constexpr int G_STAGE_BYTES = (G_BM + G_BN) * G_BKB;   // 64 KB
 constexpr int G_MAXE = 256;
 // Buffer-resource word 3 of the gfx9 family (raw buffer, 32-bit dwords), the record
 // bound, and the offset that lies beyond it (such a lane loads zeros).
@@ -102,12 +102,12 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
   return reinterpret_cast<const T*>((uint64_t(hi) << 32) | lo);
 }
 
-// Byte offset of 16-byte chunk `chunk` (0..3) of tile row `row` in LDS.  The LDS of
-// gfx950 has 64 four-byte banks and serves a ds_read_b128 16 lanes at a time; a 64-byte
-// row covers a quarter of the banks, so four consecutive rows fill one bank row and the
-// chunk is XOR-ed with (row / 4) mod 4: the 16 rows a fragment read touches at once fall
-// on 16 distinct (bank quarter, chunk) pairs.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * G_BKB + ((chunk ^ ((row >> 2) & 3)) << 4); }
+// Byte offset of 16-byte chunk `chunk` (0..7) of tile row `row` in LDS.  The LDS of
+// gfx950 has 64 four-byte banks and serves a ds_read_b128 16 lanes at a time; a fragment
+// read has 16 consecutive rows read the same chunk.  A 128-byte row covers half of the
+// banks (even rows one half, odd rows the other), so the chunk is XOR-ed with
+// (row / 2) mod 8: the 8 rows of each parity land on 8 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * G_BKB + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 // Raw buffer resource over `base` (gfx9 word 3, full 31-bit range) ...
 __device__ __forceinline__ i32x4 make_rsrc(const void* base) {
@@ -115,9 +115,11 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base) {
   return i32x4{int(uint32_t(v)), int(uint32_t(v >> 32) & 0xffff), kRsrcRecords, kRsrcFlags};
 }
 // ... and one bounded to `bytes` (reads past it return zeros).
+// The words go through readfirstlane: the inline-asm users take the resource in SGPRs and
+// the compiler keeps some uniform values (clamps) in VGPRs.
 __device__ __forceinline__ i32x4 make_rsrc_n(const void* base, uint32_t bytes) {
   const uint64_t v = reinterpret_cast<uint64_t>(base);
-  return i32x4{int(uint32_t(v)), int(uint32_t(v >> 32) & 0xffff), int(bytes), kRsrcFlags};
+  return i32x4{uniform(int(uint32_t(v))), uniform(int(uint32_t(v >> 32) & 0xffff)), uniform(int(bytes)), kRsrcFlags};
 }
 
 // One accumulator element into a VGPR.  The explicit read (an AGPR operand) keeps the
@@ -157,13 +159,17 @@ struct Tile {
   int valid;
   int e, nt, off, m_valid, m0;
   int kbase, klo, khi, nkt;   // K range in bytes; slices of G_BKB from kbase
-  const uint8_t* A;           // operand bases of the buffer resources
+  // operand buffer resources: A starts at the tile's first row and B at its first weight
+  // row (SwiGLU: the gate half; the up half is F rows further); the record bounds end at
+  // the last valid row, so the hardware range check zeroes rows past the group / N / F
+  const uint8_t* A;
   const uint8_t* B;
+  uint32_t arec, brec;
   int64_t sa_rows, sb_rows;   // MX: packed-scale dword of the tile's first A / B row at group 0
 };
 
 // LDS map (bytes from the start of the dynamic block):
-//   [0, G_STAGES*G_STAGE_BYTES)   operand tiles, G_STAGES x (A 256 x 64 B, B 256 x 64 B)
+//   [0, G_STAGES*G_STAGE_BYTES)   operand tiles, G_STAGES x (A 256 x 128 B, B 256 x 128 B)
 //   then G_STAGES x 4 KB          E8M0 scales: four 1 KB slots per stage, slot w filled
 //                                 by wave w (A rows 0-127, 128-255, B rows 0-127,
 //                                 128-255; 512 B used per slot)
@@ -185,8 +191,18 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
   const int wave = uniform(tid >> 6);
   const int wm = wave / G_WAVES_N;
   const int wn = wave % G_WAVES_N;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
+  // l32 / hi are re-derived from an opaque copy of the lane id at the top of every tile
+  // and again after its K loop: the per-lane addresses of the K loop (LDS fragments) and
+  // of the epilogue (stores) are then computed in their own phase instead of being
+  // hoisted to kernel start, where together they would stay live and spill.
+  int l32 = lane & 31;
+  int hi = lane >> 5;
+  auto rederive_lane = [&]() {
+    int v = lane;
+    asm volatile("" : "+v"(v));
+    l32 = v & 31;
+    hi = v >> 5;
+  };
   constexpr int ELEM = MX ? 1 : 2;           // bytes per element
 
   // ---- tile table: tiles of expert e = mtiles(e) * ntiles
@@ -230,22 +246,32 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
     // K range in bytes.  RAGGED_M: [0, K).  RAGGED_K: the expert's token span
     // [off, off + roundup32(size)) of the column forms; the loop starts at the slice
     // boundary below it and the chunks outside the span load as zeros.
+    auto rows_left = [](int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); };
+    const uint8_t* bmat;
     if constexpr (MODE == RAGGED_M) {
       t.kbase = 0; t.klo = 0; t.khi = p.K * ELEM;
-      t.A = p.A + int64_t(t.off) * p.lda;
-      t.B = ld_uniform(p.Bt, t.e);
+      t.A = p.A + (int64_t(t.off) + t.m0) * p.lda;
+      bmat = ld_uniform(p.Bt, t.e);
     } else {
       const int span = ((ld_uniform(p.sizes, t.e) + 31) / 32) * 32;
       t.klo = t.off * ELEM;
       t.khi = (t.off + span) * ELEM;
       t.kbase = span > 0 ? (t.klo / G_BKB) * G_BKB : t.klo;
-      t.A = p.A;
-      t.B = p.B;
+      t.A = p.A + int64_t(t.m0) * p.lda;
+      bmat = p.B;
+    }
+    t.arec = uint32_t(rows_left(t.m_valid - t.m0, G_BM)) * uint32_t(p.lda);
+    if constexpr (EPI == EPI_SWIGLU) {
+      t.B = bmat + int64_t(t.nt) * (G_BN / 2) * p.ldb;
+      t.brec = uint32_t(rows_left(p.F - t.nt * (G_BN / 2), G_BN / 2)) * uint32_t(p.ldb);
+    } else {
+      t.B = bmat + int64_t(t.nt) * G_BN * p.ldb;
+      t.brec = uint32_t(rows_left(p.N - t.nt * G_BN, G_BN)) * uint32_t(p.ldb);
     }
     t.nkt = (t.khi - t.kbase + G_BKB - 1) / G_BKB;
     if constexpr (MX) {
       // packed scales: dword (j, row) at row + j * ld holds the 4 blocks of K elements
-      // [128j, 128j + 128); slice kt covers bytes kbase + 64kt.. = group (kbase/64+kt)/2
+      // [128j, 128j + 128); slice kt is group kbase/128 + kt
       if constexpr (MODE == RAGGED_M) {
         t.sa_rows = t.off + t.m0;
         t.sb_rows = int64_t(t.e) * p.bsp_estride;
@@ -257,62 +283,57 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
     return t;
   };
 
-  // operand row of B-tile row r (0..255), or -1 past the end
-  auto b_row = [&](const Tile& t, int r) {
-    if constexpr (EPI == EPI_SWIGLU) {
-      constexpr int half = G_BN / 2;
-      const int f = t.nt * half + (r % half);
-      return f < p.F ? (r < half ? f : p.F + f) : -1;
-    } else {
-      const int g = t.nt * G_BN + r;
-      return g < p.N ? g : -1;
-    }
-  };
 
-  // ---- loader geometry: wave instruction i (0..3) fills LDS rows [(wave*4+i)*16, +16)
-  // of a 256-row operand tile, 1 KB contiguous (lane l -> row +l/4, LDS chunk l%4).  The
-  // lane loads the global chunk that the swizzle maps to that LDS chunk: with row =
-  // 16q + l/4, (row/4) mod 4 = (l/16) mod 4.  Lanes whose offset has the top bit set
-  // read zeros (rows past the group, chunks outside the K range), so tails need no
-  // extra path.
-  const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
-  uint32_t a_off[4], b_off[4];
-  auto lane_offs = [&](const Tile& t) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (wave * 4 + i) * 16 + (lane >> 2);   // row within the tile
-      const int ra = t.m0 + r;
-      a_off[i] = ra < t.m_valid ? uint32_t(ra) * uint32_t(p.lda) + lchunk * 16 : kInvalid;
-      const int g = b_row(t, r);
-      b_off[i] = g >= 0 ? uint32_t(g) * uint32_t(p.ldb) + lchunk * 16 : kInvalid;
-    }
-  };
+  // ---- loader geometry: wave instruction i (0..7) fills LDS rows [(wave*8+i)*8, +8) of
+  // a 256-row operand tile, 1 KB contiguous (lane l -> row +l/8, LDS chunk l%8), so every
+  // lane group of 8 reads one whole 128-byte line.  The lane loads the global chunk that
+  // the swizzle maps to that LDS chunk: with row = 8q + l/8, (row/2) mod 8 =
+  // 4*(q mod 2) + l/16, i.e. chunk (l%8) ^ (l/16) for even i and that ^ 4 for odd i.
+  // Rows past the valid ones fall outside the resource's record bound and chunks
+  // outside the K range get the top offset bit: both read zeros, so tails need no extra
+  // path.  Lane offsets (row start + chunk) relative to the tile's first row, for even
+  // and odd instructions; instruction i adds i*8 rows.
+  const int lchunk0 = (lane & 7) ^ (lane >> 4);
+  const int arow0 = wave * 64 + (lane >> 3);
+  const int brow0 = (EPI == EPI_SWIGLU ? (wave & 1) * 64 : wave * 64) + (lane >> 3);
+  const uint32_t a_lane[2] = {uint32_t(arow0) * uint32_t(p.lda) + lchunk0 * 16,
+                              uint32_t(arow0) * uint32_t(p.lda) + (lchunk0 ^ 4) * 16};
+  const uint32_t b_lane[2] = {uint32_t(brow0) * uint32_t(p.ldb) + lchunk0 * 16,
+                              uint32_t(brow0) * uint32_t(p.ldb) + (lchunk0 ^ 4) * 16};
+  const uint32_t lda8 = uniform(int(8 * p.lda)), ldb8 = uniform(int(8 * p.ldb));
 
   // one K slice of tile t into LDS stage `stage` (operands and, MX, its scales); past
   // the last slice every lane is out of range and loads zeros
-  constexpr int DMA_PER_SLICE = 8 + (MX ? 1 : 0);   // VMEM operations of one issue_slice
+  constexpr int DMA_PER_SLICE = 16 + (MX ? 1 : 0);   // VMEM operations of one issue_slice
   auto issue_slice = [&](const Tile& t, int kt, int stage) {
-    const i32x4 rA = make_rsrc(t.A);
-    const i32x4 rB = make_rsrc(t.B);
+    const i32x4 rA = make_rsrc_n(t.A, t.arec);
+    // SwiGLU: waves 0, 1 load the gate rows, waves 2, 3 the up rows (F rows further)
+    const uint8_t* bb = t.B;
+    if constexpr (EPI == EPI_SWIGLU) {
+      if (wave >= 2) bb += int64_t(p.F) * p.ldb;
+    }
+    const i32x4 rB = make_rsrc_n(bb, t.brec);
     const int kslice = t.kbase + kt * G_BKB;         // first byte of the slice
-    // this lane's chunk (a_off/b_off hold the chunk term); outside [klo, khi) the top
-    // offset bit is set
-    const int kb = kslice + lchunk * 16;
-    const uint32_t out = ((uint32_t(kb - t.klo) | uint32_t(t.khi - 1 - kb)) >> 31) << 31;
+    // this lane's chunk for even and odd instructions (the lane offsets hold the chunk
+    // term); outside [klo, khi) the top offset bit is set
+    const int kb0 = kslice + lchunk0 * 16;
+    const int kb1 = kslice + (lchunk0 ^ 4) * 16;
+    const uint32_t out0 = ((uint32_t(kb0 - t.klo) | uint32_t(t.khi - 1 - kb0)) >> 31) << 31;
+    const uint32_t out1 = ((uint32_t(kb1 - t.klo) | uint32_t(t.khi - 1 - kb1)) >> 31) << 31;
     const uint32_t kadd = uint32_t(kslice);
-    const uint32_t la = lds_base + stage * G_STAGE_BYTES + wave * 4 * 1024;
+    const uint32_t la = lds_base + stage * G_STAGE_BYTES + wave * 8 * 1024;
     const uint32_t lb = la + G_BM * G_BKB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(rA, la + i * 1024, (a_off[i] + kadd) | out);
+    for (int i = 0; i < 8; ++i) dma16(rA, la + i * 1024, (a_lane[i & 1] + i * lda8 + kadd) | ((i & 1) ? out1 : out0));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(rB, lb + i * 1024, (b_off[i] + kadd) | out);
+    for (int i = 0; i < 8; ++i) dma16(rB, lb + i * 1024, (b_lane[i & 1] + i * ldb8 + kadd) | ((i & 1) ? out1 : out0));
     if constexpr (MX) {
       // wave w brings 128 rows of scale dwords (lanes 0..31, 16 B = 4 rows each):
       // A rows (w&1)*128.. for w < 2, B rows for w >= 2; the dwords of the slice's
-      // 128-element group (both 64-byte halves of a group read the same dwords)
+      // 128-element group (a slice is exactly one group)
       const bool slice_ok = kt < t.nkt;
       const int half = wave & 1;
-      const int64_t j = (t.kbase / G_BKB + kt) >> 1;
+      const int64_t j = t.kbase / G_BKB + kt;
       int64_t dw;             // first dword of the 128 rows
       const uint32_t* base;
       uint32_t bytes;
@@ -346,17 +367,17 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
   }
 
   // MFMA operand fragments of one K step, read from the swizzled LDS tile:
-  //   MX  : the slice is one 64-element step; lane (hi, l32) takes 16-byte chunks hi and
-  //         hi + 2 of its row
-  //   BF16: 16-element step s (of 2); lane takes chunk 2s + hi
+  //   MX  : 64-element step s (of 2); lane (hi, l32) takes 16-byte chunks 4s + hi and
+  //         4s + hi + 2 of its row
+  //   BF16: 16-element step s (of 4); lane takes chunk 2s + hi
   typedef typename std::conditional<MX, i32x8, bf16x8>::type frag_t;
-  constexpr int NSTEP = MX ? 1 : 2;
+  constexpr int NSTEP = MX ? 2 : 4;
   auto read_frags = [&](const uint8_t* sA, const uint8_t* sB, int s, frag_t* af, frag_t* bfr) {
 #pragma unroll
     for (int mi = 0; mi < G_WMB; ++mi) {
       const int row = (wm * G_WMB + mi) * 32 + l32;
       if constexpr (MX) {
-        const int c = hi;
+        const int c = 4 * s + hi;
         const uint4 x0 = *reinterpret_cast<const uint4*>(sA + swz(row, c));
         const uint4 x1 = *reinterpret_cast<const uint4*>(sA + swz(row, c + 2));
         af[mi] = i32x8{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
@@ -368,7 +389,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
     for (int ni = 0; ni < G_WNB; ++ni) {
       const int row = brow_tile[ni] + l32;
       if constexpr (MX) {
-        const int c = hi;
+        const int c = 4 * s + hi;
         const uint4 x0 = *reinterpret_cast<const uint4*>(sB + swz(row, c));
         const uint4 x1 = *reinterpret_cast<const uint4*>(sB + swz(row, c + 2));
         bfr[ni] = i32x8{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
@@ -381,9 +402,9 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
   Tile cur = decode(vid);
   bool cur_issued = false;   // slice 0 of `cur` already on its way into stage 0
   for (int tile = vid; tile < total; tile += nwg) {
+    rederive_lane();
     const Tile nxt = decode(tile + nwg);
     const int e = cur.e, nt = cur.nt, off = cur.off, m_valid = cur.m_valid, m0 = cur.m0, nkt = cur.nkt;
-    lane_offs(cur);
     // SwiGLU: the probability of tile row tid, loaded now so that its latency hides
     // behind the K loop (it is staged in LDS for the epilogue)
     float my_prob = 0.f;
@@ -399,10 +420,11 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
-    // MX: lane hi scales K block 2*gh + hi of the slice's 128-element group (gh = which
-    // 64-byte half of the group the slice is), byte 0 of the shifted dword (op_sel 0)
-    auto mfma_step = [&](int s, int gh, const frag_t* af, const frag_t* bfr, const uint32_t* sa, const uint32_t* sb) {
-      const int sh = 8 * (2 * gh + hi);
+    // MX: in K step s (elements 64s..64s+63 of the slice's 128-element group) lane hi
+    // scales K block 2s + hi: byte 2s + hi of the group's dword, shifted down to byte 0
+    // (op_sel 0)
+    auto mfma_step = [&](int s, const frag_t* af, const frag_t* bfr, const uint32_t* sa, const uint32_t* sb) {
+      const int sh = 8 * (2 * s + hi);
 #pragma unroll
       for (int mi = 0; mi < G_WMB; ++mi)
 #pragma unroll
@@ -417,8 +439,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
         }
     };
 
-    // ---- K loop: a ring of G_STAGES LDS stages; slice kt+3 streams in while slice kt is
-    // multiplied, so three slices are always in flight
+    // ---- K loop: G_STAGES LDS stages; slice kt+1 streams in while slice kt is multiplied
     if (!cur_issued) {
       __syncthreads();   // LDS stages are free
 #pragma unroll
@@ -433,9 +454,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
       const uint8_t* sA = smem + stage * G_STAGE_BYTES;
       const uint8_t* sB = sA + G_BM * G_BKB;
       uint32_t sa[G_WMB], sb[G_WNB];
-      int gh = 0;
       if constexpr (MX) {
-        gh = (cur.kbase / G_BKB + kt) & 1;
         const uint8_t* sS = smem + G_SCALE_BASE + stage * G_SCALE_STAGE;
 #pragma unroll
         for (int mi = 0; mi < G_WMB; ++mi) {
@@ -453,23 +472,22 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s) {
         if (s + 1 < NSTEP) read_frags(sA, sB, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
-        mfma_step(s, gh, af[s & 1], bfr[s & 1], sa, sb);
+        mfma_step(s, af[s & 1], bfr[s & 1], sa, sb);
       }
       __builtin_amdgcn_sched_barrier(0);
-      // slice kt+1 resident (slices kt+2, kt+3 may still be in flight) and every wave is
-      // done with stage kt before it is refilled
+      // slice kt+1 resident and every wave done with stage kt before it is refilled
       __builtin_amdgcn_s_waitcnt(waitcnt_imm((G_STAGES - 2) * DMA_PER_SLICE, 0));
       __syncthreads();
     }
     __builtin_amdgcn_s_waitcnt(0);   // the past-the-end (all-zero) slices have landed
     acc_settle();                    // the last MFMA results are readable
+    rederive_lane();
     // all stages are free: start the next tile's first slices now so their latency hides
     // behind the epilogue (which uses no stage memory).  Not when the epilogue reads the
     // output back: those loads would queue behind the slices.
     cur_issued = false;
     {
       if (nxt.valid && nxt.nkt > 0 && OUT != OUT_F32_ACC) {
-        lane_offs(nxt);
 #pragma unroll
         for (int q = 0; q < G_STAGES - 1; ++q) issue_slice(nxt, q, q);
         cur_issued = true;
@@ -571,21 +589,18 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
           const int fb0 = nt * (G_BN / 2) + (wn * hb + j) * 32;   // first column of the block
           if (fb0 >= F) return;
           const int f = fb0 + l32;
-          float h[16], Gv[16], Uv[16];
+          auto lrow = [&](int r) { return rb + 8 * (r >> 2) + 4 * hi + (r & 3); };
+          float h[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            Gv[r] = acc_read(acc[mi][j][r]);
-            Uv[r] = acc_read(acc[mi][j + hb][r]);
-            h[r] = pr[r] * (Gv[r] * __builtin_amdgcn_rcpf(1.f + __expf(-Gv[r]))) * Uv[r];
-          }
-          auto lrow = [&](int r) { return rb + 8 * (r >> 2) + 4 * hi + (r & 3); };
-          if (train) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
+            const float G = acc_read(acc[mi][j][r]);
+            const float U = acc_read(acc[mi][j + hb][r]);
+            if (train) {
               const int o = (lrow(r) * F2 + f) * 2;
-              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(Gv[r]), rGU, o, 0, 0);
-              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(Uv[r]), rGU, o + 2 * F, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(G), rGU, o, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(U), rGU, o + 2 * F, 0, 0);
             }
+            h[r] = pr[r] * (G * __builtin_amdgcn_rcpf(1.f + __expf(-G))) * U;
           }
           if constexpr (MX) {
             // row form: one scale per (row, 32-column block), shared by the half-wave
