@@ -23,8 +23,9 @@
 // slices in flight while one is multiplied.  LDS rows are 64 bytes with the 16-byte
 // chunks XOR-swizzled by row so the MFMA fragment reads spread over the 64 banks.  The
 // MX scales of a slice ride along into LDS (packed: one dword = 4 blocks of a row).
-// A persistent grid walks the tiles (expert-major, then N, M fastest so that
-// consecutive tiles share the weight tile); virtual workgroup ids are remapped so
+// A persistent grid walks the tiles (expert-major, then bands of 8 M-tiles walked across
+// N with M fastest, so that the 32 tiles an XCD runs at once are an 8 x 4 block sharing
+// A and B tiles in its L2); virtual workgroup ids are remapped so
 // that the workgroups of one XCD (hardware dispatches round-robin over the 8 XCDs)
 // take consecutive tiles and share that XCD's L2.  Empty experts own no tiles (RAGGED_M)
 // or produce zero gradients (RAGGED_K).  The next tile's first slices are issued
@@ -64,6 +65,7 @@ constexpr int G_STAGES = 2;                   // LDS stages: one slice in flight
 constexpr int G_THREADS = 64 * G_WAVES_M * G_WAVES_N;
 constexpr int G_STAGE_BYTES = (G_BM + G_BN) * G_BKB;   // 64 KB
 constexpr int G_MAXE = 256;
+constexpr int G_GROUP_M = 8;                  // M-tiles per band of the tile raster
 // Buffer-resource word 3 of the gfx9 family (raw buffer, 32-bit dwords), the record
 // bound, and the offset that lies beyond it (such a lane loads zeros).
 constexpr int kRsrcFlags = 0x00020000;
@@ -238,8 +240,14 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
     t.e = uniform(lo);
     const int local = tile - uniform(s_prefix[t.e]);
     const int mtn = uniform(s_mtiles[t.e]);
-    const int mt = local % mtn;
-    t.nt = local / mtn;
+    // grouped raster: bands of G_GROUP_M M-tiles, each band walked across all N-tiles
+    // with M fastest, so that any G_GROUP_M x 4 consecutive tiles (the 32 workgroups of
+    // an XCD) share 8 A tiles and 4 B tiles in that XCD's L2
+    const int band = local / (G_GROUP_M * ntiles);
+    const int within = local - band * G_GROUP_M * ntiles;
+    const int gm = min(G_GROUP_M, mtn - band * G_GROUP_M);
+    const int mt = band * G_GROUP_M + within % gm;
+    t.nt = within / gm;
     t.off = ld_uniform(p.offs, t.e);
     t.m_valid = MODE == RAGGED_M ? ld_uniform(p.sizes, t.e) : p.M;
     t.m0 = mt * G_BM;
@@ -302,31 +310,34 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
                               uint32_t(brow0) * uint32_t(p.ldb) + (lchunk0 ^ 4) * 16};
   const uint32_t lda8 = uniform(int(8 * p.lda)), ldb8 = uniform(int(8 * p.ldb));
 
-  // one K slice of tile t into LDS stage `stage` (operands and, MX, its scales); past
-  // the last slice every lane is out of range and loads zeros
-  constexpr int DMA_PER_SLICE = 16 + (MX ? 1 : 0);   // VMEM operations of one issue_slice
-  auto issue_slice = [&](const Tile& t, int kt, int stage) {
-    const i32x4 rA = make_rsrc_n(t.A, t.arec);
+  // One K slice of tile t into LDS stage `stage` (operands and, MX, its scales); past
+  // the last slice every lane is out of range and loads zeros.  prep_slice computes the
+  // slice's resources and offsets; dma_operand(i) issues operand instruction i (0..7 A,
+  // 8..15 B) so that the K loop can spread them between its MFMAs.
+  constexpr int DMA_PER_SLICE = 16 + (MX ? 1 : 0);   // VMEM operations of one slice
+  struct SliceDma {
+    i32x4 rA, rB, rS;
+    uint32_t kadd, out0, out1, la, lb, ls, so;
+  };
+  auto prep_slice = [&](const Tile& t, int kt, int stage) {
+    SliceDma c;
+    c.rA = make_rsrc_n(t.A, t.arec);
     // SwiGLU: waves 0, 1 load the gate rows, waves 2, 3 the up rows (F rows further)
     const uint8_t* bb = t.B;
     if constexpr (EPI == EPI_SWIGLU) {
       if (wave >= 2) bb += int64_t(p.F) * p.ldb;
     }
-    const i32x4 rB = make_rsrc_n(bb, t.brec);
+    c.rB = make_rsrc_n(bb, t.brec);
     const int kslice = t.kbase + kt * G_BKB;         // first byte of the slice
     // this lane's chunk for even and odd instructions (the lane offsets hold the chunk
     // term); outside [klo, khi) the top offset bit is set
     const int kb0 = kslice + lchunk0 * 16;
     const int kb1 = kslice + (lchunk0 ^ 4) * 16;
-    const uint32_t out0 = ((uint32_t(kb0 - t.klo) | uint32_t(t.khi - 1 - kb0)) >> 31) << 31;
-    const uint32_t out1 = ((uint32_t(kb1 - t.klo) | uint32_t(t.khi - 1 - kb1)) >> 31) << 31;
-    const uint32_t kadd = uint32_t(kslice);
-    const uint32_t la = lds_base + stage * G_STAGE_BYTES + wave * 8 * 1024;
-    const uint32_t lb = la + G_BM * G_BKB;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(rA, la + i * 1024, (a_lane[i & 1] + i * lda8 + kadd) | ((i & 1) ? out1 : out0));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(rB, lb + i * 1024, (b_lane[i & 1] + i * ldb8 + kadd) | ((i & 1) ? out1 : out0));
+    c.out0 = ((uint32_t(kb0 - t.klo) | uint32_t(t.khi - 1 - kb0)) >> 31) << 31;
+    c.out1 = ((uint32_t(kb1 - t.klo) | uint32_t(t.khi - 1 - kb1)) >> 31) << 31;
+    c.kadd = uint32_t(kslice);
+    c.la = lds_base + stage * G_STAGE_BYTES + wave * 8 * 1024;
+    c.lb = c.la + G_BM * G_BKB;
     if constexpr (MX) {
       // wave w brings 128 rows of scale dwords (lanes 0..31, 16 B = 4 rows each):
       // A rows (w&1)*128.. for w < 2, B rows for w >= 2; the dwords of the slice's
@@ -349,10 +360,25 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
         base = p.Bsp;
         bytes = p.bsp_bytes;
       }
-      const i32x4 rS = make_rsrc_n(base, bytes);
-      const uint32_t so = (slice_ok && lane < 32) ? uint32_t(dw * 4) + lane * 16 : kInvalid;
-      dma16(rS, lds_base + G_SCALE_BASE + stage * G_SCALE_STAGE + wave * 1024, so);
+      c.rS = make_rsrc_n(base, bytes);
+      c.so = (slice_ok && lane < 32) ? uint32_t(dw * 4) + lane * 16 : kInvalid;
+      c.ls = lds_base + G_SCALE_BASE + stage * G_SCALE_STAGE + wave * 1024;
     }
+    return c;
+  };
+  auto dma_operand = [&](const SliceDma& c, int i) {
+    const uint32_t out = (i & 1) ? c.out1 : c.out0;
+    if (i < 8) dma16(c.rA, c.la + i * 1024, (a_lane[i & 1] + i * lda8 + c.kadd) | out);
+    else dma16(c.rB, c.lb + (i - 8) * 1024, (b_lane[i & 1] + (i - 8) * ldb8 + c.kadd) | out);
+  };
+  auto dma_scale = [&](const SliceDma& c) {
+    if constexpr (MX) dma16(c.rS, c.ls, c.so);
+  };
+  auto issue_slice = [&](const Tile& t, int kt, int stage) {
+    const SliceDma c = prep_slice(t, kt, stage);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dma_operand(c, i);
+    dma_scale(c);
   };
 
   int brow_tile[G_WNB];
@@ -423,7 +449,12 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
     // MX: in K step s (elements 64s..64s+63 of the slice's 128-element group) lane hi
     // scales K block 2s + hi: byte 2s + hi of the group's dword, shifted down to byte 0
     // (op_sel 0)
-    auto mfma_step = [&](int s, const frag_t* af, const frag_t* bfr, const uint32_t* sa, const uint32_t* sb) {
+    // The next slice's 16 operand DMAs go out two after each of the first 8 MFMAs of the
+    // slice: issued back to back before the MFMAs they hold the in-order wave at the
+    // memory pipeline, spread over the whole slice the last ones have too little time
+    // left to land (measured on MI355X, both slower).
+    auto mfma_step = [&](int s, const frag_t* af, const frag_t* bfr, const uint32_t* sa, const uint32_t* sb,
+                         const SliceDma& nx) {
       const int sh = 8 * (2 * s + hi);
 #pragma unroll
       for (int mi = 0; mi < G_WMB; ++mi)
@@ -435,6 +466,13 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
             acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0, xa, 0, xb);
           } else {
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+          }
+          const int q = mi * G_WNB + ni;
+          if (s == 0 && q < 8) {
+            __builtin_amdgcn_sched_barrier(0);
+            dma_operand(nx, 2 * q);
+            dma_operand(nx, 2 * q + 1);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
     };
@@ -449,7 +487,8 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
     __syncthreads();
     for (int kt = 0; kt < nkt; ++kt) {
       const int stage = kt & (G_STAGES - 1);
-      issue_slice(cur, kt + G_STAGES - 1, (kt + G_STAGES - 1) & (G_STAGES - 1));
+      const SliceDma nx = prep_slice(cur, kt + G_STAGES - 1, (kt + G_STAGES - 1) & (G_STAGES - 1));
+      dma_scale(nx);
       __builtin_amdgcn_sched_barrier(0);
       const uint8_t* sA = smem + stage * G_STAGE_BYTES;
       const uint8_t* sB = sA + G_BM * G_BKB;
@@ -472,7 +511,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s) {
         if (s + 1 < NSTEP) read_frags(sA, sB, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
-        mfma_step(s, af[s & 1], bfr[s & 1], sa, sb);
+        mfma_step(s, af[s & 1], bfr[s & 1], sa, sb, nx);
       }
       __builtin_amdgcn_sched_barrier(0);
       // slice kt+1 resident and every wave done with stage kt before it is refilled
