@@ -425,7 +425,7 @@ static size_t bwd_ws(const mge_bwd_args* a, int R) {
   const bool mx = a->prec == MGE_PREC_MXFP8;
   const size_t H = a->H, F = a->F, E = a->E, F2 = 2 * F;
   size_t n = up256(6 * E * sizeof(void*));
-  n += up256(size_t(R) * sizeof(float));                 // d_prob per permuted row
+  n += up256(size_t(R) * swiglu_bwd_nparts(int(F)) * sizeof(float));   // d_prob partials per permuted row
   n += up256(size_t(R) * F * sizeof(float));             // dh (fp32)
   auto mat = [&](size_t rows, size_t cols) {
     return mx ? up256(rows * cols) + up256(rows * (cols / 32)) : up256(rows * cols * 2);
@@ -491,7 +491,8 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
   const int elem = mx ? 1 : 2;
   Carve ws(a->workspace);
   void** tab = static_cast<void**>(ws.take(6 * size_t(E) * sizeof(void*)));
-  float* dprob_row = static_cast<float*>(ws.take(size_t(R) * sizeof(float)));
+  const int nparts = swiglu_bwd_nparts(a->F);
+  float* dprob_part = static_cast<float*>(ws.take(size_t(R) * nparts * sizeof(float)));
   float* dh = static_cast<float*>(ws.take(size_t(R) * F * sizeof(float)));
   auto mat = [&](void* given, uint8_t* given_s, size_t rows, size_t cols, void** c, uint8_t** sc) {
     if (given) { *c = given; *sc = given_s; return; }
@@ -602,7 +603,8 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
     q.dh = dh; q.gu = a->saved_gu; q.prob = a->prob_perm; q.perm_src = a->perm_src;
     if (mx) { q.row_codes = static_cast<uint8_t*>(dgr); q.row_scales = dgrs; q.col_codes = static_cast<uint8_t*>(dgc); q.col_scales = dgcs; }
     else { q.row_bf16 = static_cast<uint16_t*>(dgr); q.col_bf16 = static_cast<uint16_t*>(dgc); }
-    q.dprob_row = dprob_row;
+    q.dprob_part = dprob_part;
+    q.nparts = nparts;
     st = launch_swiglu_bwd(q, mx, s);
     if (st != MGE_OK) return st;
   }
@@ -612,7 +614,7 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
     if (st != MGE_OK) return st;
   }
   // b3: d_prob[t][i] = the row sum of the assignment's permuted row
-  st = launch_dprob_reduce(a->T, a->k, 1, dprob_row, a->perm_pos, a->d_prob, s);
+  st = launch_dprob_reduce(a->T, a->k, nparts, dprob_part, a->perm_pos, a->d_prob, s);
   if (st != MGE_OK) return st;
   // b4: dW_down[e] = dY_e^T h_e  (K = tokens of e)
   {

@@ -82,8 +82,11 @@ struct SwigluBwdParams {
   uint16_t* row_bf16;                    // bf16 dGU row [R][2F]
   uint8_t* col_codes; uint8_t* col_scales;  // MX dGU column [2F][Rp], [2F][Rp/32]
   uint16_t* col_bf16;                    // bf16 dGU transpose [2F][Rp]
-  float* dprob_row;                      // [R]: sum_f dh * silu(G) * U (valid rows)
+  // [R][nparts]: sum of dh * silu(G) * U over ffn column group j (256 columns) of row m
+  float* dprob_part;
+  int nparts;                            // swiglu_bwd_nparts(F)
 };
+int swiglu_bwd_nparts(int F);
 mge_status launch_swiglu_bwd(const SwigluBwdParams& p, bool mx, hipStream_t s);
 
 mge_status launch_dprob_reduce(int T, int k, int nparts, const float* partial, const int32_t* perm_pos,
