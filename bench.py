@@ -178,14 +178,87 @@ def summarize_kernels(records, steps, w, R, prec):
 # ------------------------------------------------------------------------------ traffic (rocprofv3 counters)
 
 def kernel_source_digest():
-    """Digest of the GEMM kernel sources: counter-derived traffic is only reported while
-    the kernels are the ones the counters were taken on."""
+    """Digest of the kernel sources: counter-derived traffic is only reported while the
+    kernels are the ones the counters were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "moe_grouped_expert_amd", "csrc")
-    for f in ("gemm_impl.hpp", "gemm_mx.hip", "gemm_bf16.hip", "mge_common.hpp", "mge_internal.hpp"):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
+
+
+COPY_CAL_BYTES = 1 << 30   # the plain device-to-device copy the counters are calibrated on
+
+
+def calibrate_copy():
+    """A plain 1 GiB device-to-device copy (three launches): under rocprofv3 --pmc its
+    FETCH_SIZE / WRITE_SIZE readings give the factor from counter units to HBM bytes."""
+    import torch
+
+    src = torch.ones(COPY_CAL_BYTES, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_CAL_BYTES, "launches": 3}))
+
+
+def _short_kernel(name):
+    """'mge::gemm_dx_mx(mge::GemmParams)' -> 'gemm_dx_mx'; 'void mge::k<true>(...)' -> 'k<true>'."""
+    if name.startswith("void "):
+        name = name[5:]
+    depth, cut = 0, len(name)
+    for i, ch in enumerate(name):   # the parameter list starts at the first '(' outside <...>
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    name = name[:cut]
+    return name[5:] if name.startswith("mge::") else name
+
+
+def _counter_values(path):
+    import csv
+
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, workload):
+    """profiles/traffic.json from four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE, in
+    KiB per dispatch, over one training step and over the 1 GiB copy): per library kernel,
+    the mean per dispatch of each counter scaled by copy_bytes / (copy's reading)."""
+    def cal(path):
+        vals = [v for n, vs in _counter_values(path).items() if "copyBuffer" in n or "copy" in n.lower() for v in vs]
+        return COPY_CAL_BYTES / (max(vals) * 1024.0)
+
+    f_scale, w_scale = cal(cal_fetch_csv), cal(cal_write_csv)
+    fetch, write = _counter_values(fetch_csv), _counter_values(write_csv)
+    kernels = {}
+    for name, fv in fetch.items():
+        if "mge::" not in name or name not in write:
+            continue
+        wv = write[name]
+        fb = sum(fv) / len(fv) * 1024.0 * f_scale
+        wb = sum(wv) / len(wv) * 1024.0 * w_scale
+        kernels[_short_kernel(name)] = {"dispatches": len(fv), "fetch_bytes": round(fb), "write_bytes": round(wb),
+                                        "hbm_bytes_per_launch": round(fb + wb)}
+    out = {"source_digest": kernel_source_digest(),
+           "calibration": {"copy_bytes": COPY_CAL_BYTES, "fetch_factor": round(f_scale, 5),
+                           "write_factor": round(w_scale, 5)},
+           "kernels": {workload: kernels}}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    print(f"wrote {path}: {len(kernels)} kernels, fetch x{f_scale:.4f}, write x{w_scale:.4f}")
 
 
 def traffic_for(kernel, workload):
@@ -290,7 +363,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=32, help="assignments in the CPU oracle sample")
     ap.add_argument("--cpu-fcols", type=int, default=None, help="ffn columns in the CPU oracle sample (default: all)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only the 1 GiB copy the traffic counters are calibrated on")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
+                    help="write profiles/traffic.json from rocprofv3 counter_collection.csv files (no GPU)")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.workload)
+        return
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
