@@ -41,9 +41,10 @@
  *     total row count is R = mge_perm_rows(T, k, E, align), a multiple of 32.
  *   - "Column form" of a [rows][C] matrix is stored transposed, [C][R], with blocks
  *     of 32 consecutive rows; rows of an expert's 32-row padding hold zeros.  With
- *     align % 32 == 0 no block straddles two experts.  The column forms written by
- *     the GEMM epilogues (h_col, dgu_col) cover rows [0, group_offsets[E]) only;
- *     those written by moe_route_permute / the dy permute cover all R rows.
+ *     align % 32 == 0 no block straddles two experts.  The column form of h written
+ *     by the forward's gate-up epilogue covers rows [0, group_offsets[E]) only; those
+ *     written by moe_route_permute, the dy permute and the SwiGLU backward (dgu_col)
+ *     cover all R rows.
  *   - Limits: 1 <= k <= min(E, 8); 1 <= E <= 256; H and F multiples of 32;
  *     align a power of two in [1, 256]; column forms (training, backward) need
  *     align % 32 == 0.
@@ -218,8 +219,10 @@ mge_status grouped_mlp_fwd(const mge_fwd_args* args, void* stream);
  * w_down[e] [H][F]); h_col/x_col are the bf16 transposes.
  * Outputs: dx_perm bf16 [R][H] (valid rows), dw_gate_up[e] [2F][H] and dw_down[e]
  * [H][F] (fp32; accumulate != 0 adds to them instead of overwriting; experts with no
- * tokens get zeros), d_prob f32 [T][k].  The intermediates (dY row/col, dGU row/col,
- * d_prob partials) go to the optional buffers when given, else to the workspace.
+ * tokens get zeros), d_prob f32 [T][k].  The intermediates (dY row/col, dGU row/col)
+ * go to the optional buffers when given, else to the workspace; dh (fp32 [R][F]) and
+ * the d_prob partial sums (one per row and 256-column group of F, summed in a fixed
+ * order) always live in the workspace.
  * ---------------------------------------------------------------------------- */
 typedef struct mge_bwd_args {
   uint32_t struct_size;
