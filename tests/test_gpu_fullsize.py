@@ -191,3 +191,73 @@ def test_mixtral_mxfp8_train_step_sampled():
     for key, v in errs.items():
         tol = TOL_REQ if key in ("dx_perm", "dw_gate_up") else TOL
         assert v <= tol, (key, v)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_mixtral_forward_sampled(cfg):
+    """The three forward-only workloads at full size (BF16 and MXFP8 with 16384 tokens,
+    MXFP8 with 32768 tokens and a Zipf-skewed router whose experts 2 and 5 get no
+    tokens), through bench.Step: sampled rows of the largest and the smallest non-empty
+    expert.  BF16: h and y_perm end to end against fp64 on the same bf16 inputs
+    (rel_F 1e-2).  MXFP8: x codes bit-exact, h from the GPU's x and weight codes and
+    y_perm from the GPU's h codes (rel_F 2e-3)."""
+    import bench
+    import moe_grouped_expert_amd as m
+    from tests.gpu_helpers import layout_from_gpu, npy, say
+
+    w = synth.WORKLOADS[cfg]
+    assert not w.backward and w.H == 4096 and w.F == 14336
+    dev = torch.device("cuda:0")
+    say("[gpu] full-size forward", w.name)
+    inp = bench.make_inputs(w, dev)
+    step = bench.Step(m, w, inp, train=False)
+    step()
+    torch.cuda.synchronize()
+    g, f = step.g, step.f
+    E, H, F, k = w.E, w.H, w.F, w.k
+    mx8 = w.prec == "mxfp8"
+    rng = np.random.default_rng(5050 + cfg)
+    lay = layout_from_gpu(g, E, 32)
+    idx, _ = rt.route(synth.logits(w), k)
+    np.testing.assert_array_equal(lay.topk_idx, idx)
+    np.testing.assert_array_equal(npy(g.split_sizes), lay.sizes)
+    if w.skew:
+        assert lay.sizes[2] == 0 and lay.sizes[5] == 0
+    perm_src = npy(g.perm_src)
+    prob = npy(g.prob_perm).astype(np.float64)
+    x = _bf16_np(inp["x"])
+    nonempty = [e for e in range(E) if lay.sizes[e] > 0]
+    experts = sorted({max(nonempty, key=lambda e: lay.sizes[e]), min(nonempty, key=lambda e: lay.sizes[e])})
+    got = {"h": [[], []], "y_perm": [[], []]}
+    for e in experts:
+        r = lay.rows(e)
+        rows = np.array(sorted({r.start, r.stop - 1, min(r.start + 256, r.stop - 1)} |
+                               set(int(v) for v in rng.integers(r.start, r.stop, 3))))
+        if mx8:
+            q, s = mx.quantize_rows(x[perm_src[rows]])
+            np.testing.assert_array_equal(npy(_take(g.x_perm, rows)), q)
+            np.testing.assert_array_equal(npy(_take(g.x_perm_scale, rows)), s)
+            xd = _deq(npy(_take(g.x_perm, rows)), npy(_take(g.x_perm_scale, rows)))
+            wgu_d = _deq(npy(step.wq[0][e]), npy(step.wq[1][e]))
+            GU = xd @ wgu_d.T
+            del wgu_d
+            h = prob[rows][:, None] * mlp.silu(GU[:, :F]) * GU[:, F:]
+            hq, hs = mx.quantize_rows(h)
+            hg = _deq(npy(_take(f.h, rows)), npy(_take(f.h_scale, rows)))
+            got["h"][0].append(hg)
+            got["h"][1].append(_deq(hq, hs))
+            Y = hg @ _deq(npy(step.dq[0][e]), npy(step.dq[1][e])).T
+        else:
+            GU = x[perm_src[rows]] @ _bf16_np(inp["wgu"][e]).T
+            h = prob[rows][:, None] * mlp.silu(GU[:, :F]) * GU[:, F:]
+            got["h"][0].append(_bf16_np(_take(f.h, rows)))
+            got["h"][1].append(h)
+            Y = h @ _bf16_np(inp["wd"][e]).T
+        got["y_perm"][0].append(_bf16_np(_take(f.y_perm, rows)))
+        got["y_perm"][1].append(Y)
+    errs = {key: rel_f(np.concatenate(a), np.concatenate(ref)) for key, (a, ref) in got.items()}
+    say("[gpu] full-size forward", w.name, "experts", experts, "sizes", [int(lay.sizes[e]) for e in experts],
+        {kk: f"{v:.2e}" for kk, v in errs.items()})
+    tol = TOL if mx8 else 1e-2
+    for key, v in errs.items():
+        assert v <= tol, (key, v)
