@@ -360,19 +360,13 @@ mge_status grouped_mlp_fwd(const mge_fwd_args* a, void* stream) {
     wgu_p = static_cast<uint32_t*>(ws.take(packed_bytes(E, 2 * F, H / 32)));
     hs_p = static_cast<uint32_t*>(ws.take(packed_bytes(1, R, F / 32)));
     wd_p = static_cast<uint32_t*>(ws.take(packed_bytes(E, H, F / 32)));
-    ScalePackParams q{};
-    q.src = a->x_perm_scale; q.ld = H / 32; q.batch = 1; q.rows = R; q.kb = H / 32; q.dst = xs_p;
-    st = launch_scale_pack(q, s);
-    if (st != MGE_OK) return st;
-    ScalePackParams w{};
-    w.src_tab = reinterpret_cast<const uint8_t* const*>(tab + 2 * E); w.ld = H / 32;
-    w.batch = E; w.rows = 2 * F; w.kb = H / 32; w.dst = wgu_p;
-    st = launch_scale_pack(w, s);
-    if (st != MGE_OK) return st;
-    ScalePackParams d{};
-    d.src_tab = reinterpret_cast<const uint8_t* const*>(tab + 3 * E); d.ld = F / 32;
-    d.batch = E; d.rows = H; d.kb = F / 32; d.dst = wd_p;
-    st = launch_scale_pack(d, s);
+    ScalePackParams pk[3] = {};
+    pk[0].src = a->x_perm_scale; pk[0].ld = H / 32; pk[0].batch = 1; pk[0].rows = R; pk[0].kb = H / 32; pk[0].dst = xs_p;
+    pk[1].src_tab = reinterpret_cast<const uint8_t* const*>(tab + 2 * E); pk[1].ld = H / 32;
+    pk[1].batch = E; pk[1].rows = 2 * F; pk[1].kb = H / 32; pk[1].dst = wgu_p;
+    pk[2].src_tab = reinterpret_cast<const uint8_t* const*>(tab + 3 * E); pk[2].ld = F / 32;
+    pk[2].batch = E; pk[2].rows = H; pk[2].kb = F / 32; pk[2].dst = wd_p;
+    st = launch_scale_pack_batch(pk, 3, s);   // one launch for the three
     if (st != MGE_OK) return st;
   }
 
@@ -557,12 +551,20 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
   // packed scales of every MX operand (the GEMMs read one dword per row and K slice)
   uint32_t *dyr_p = nullptr, *wdc_p = nullptr, *dyc_p = nullptr, *hc_p = nullptr;
   uint32_t *dgr_p = nullptr, *wguc_p = nullptr, *dgc_p = nullptr, *xc_p = nullptr;
+  // the scale packs available at one point of the call go out as one launch
+  ScalePackParams packs[SP_MAXD];
+  int npacks = 0;
   auto pack = [&](const uint8_t* src, const uint8_t* const* src_tab, int batch, int rows, int kb,
                   const int32_t* kb_valid, uint32_t* dst) {
     ScalePackParams q{};
     q.src = src; q.src_tab = src_tab; q.ld = kb; q.batch = batch; q.rows = rows; q.kb = kb;
     q.kb_valid = kb_valid; q.dst = dst;
-    return launch_scale_pack(q, s);
+    packs[npacks++] = q;
+  };
+  auto flush_packs = [&]() {
+    const mge_status r = launch_scale_pack_batch(packs, npacks, s);
+    npacks = 0;
+    return r;
   };
   const int32_t* rows_written = a->group_offsets + E;   // column forms from epilogues end here
   if (mx) {
@@ -574,12 +576,13 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
     wguc_p = static_cast<uint32_t*>(ws.take(packed_bytes(E, H, F2 / 32)));
     dgc_p = static_cast<uint32_t*>(ws.take(packed_bytes(1, F2, R / 32)));
     xc_p = static_cast<uint32_t*>(ws.take(packed_bytes(1, H, R / 32)));
-    st = pack(dyrs, nullptr, 1, R, H / 32, nullptr, dyr_p);
-    if (st == MGE_OK) st = pack(nullptr, reinterpret_cast<const uint8_t* const*>(tab + 2 * E), E, F, H / 32, nullptr, wdc_p);
-    if (st == MGE_OK) st = pack(dycs, nullptr, 1, H, R / 32, nullptr, dyc_p);
-    if (st == MGE_OK) st = pack(a->h_col_scale, nullptr, 1, F, R / 32, rows_written, hc_p);
-    if (st == MGE_OK) st = pack(nullptr, reinterpret_cast<const uint8_t* const*>(tab + 3 * E), E, H, F2 / 32, nullptr, wguc_p);
-    if (st == MGE_OK) st = pack(a->x_col_scale, nullptr, 1, H, R / 32, nullptr, xc_p);
+    pack(dyrs, nullptr, 1, R, H / 32, nullptr, dyr_p);
+    pack(nullptr, reinterpret_cast<const uint8_t* const*>(tab + 2 * E), E, F, H / 32, nullptr, wdc_p);
+    pack(dycs, nullptr, 1, H, R / 32, nullptr, dyc_p);
+    pack(a->h_col_scale, nullptr, 1, F, R / 32, rows_written, hc_p);
+    pack(nullptr, reinterpret_cast<const uint8_t* const*>(tab + 3 * E), E, H, F2 / 32, nullptr, wguc_p);
+    pack(a->x_col_scale, nullptr, 1, H, R / 32, nullptr, xc_p);
+    st = flush_packs();
     if (st != MGE_OK) return st;
   }
   // b2: dh = dY W_down (fp32), then the SwiGLU backward with the saved G, U and p:
@@ -609,8 +612,9 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
     if (st != MGE_OK) return st;
   }
   if (mx) {
-    st = pack(dgrs, nullptr, 1, R, F2 / 32, nullptr, dgr_p);
-    if (st == MGE_OK) st = pack(dgcs, nullptr, 1, F2, R / 32, nullptr, dgc_p);
+    pack(dgrs, nullptr, 1, R, F2 / 32, nullptr, dgr_p);
+    pack(dgcs, nullptr, 1, F2, R / 32, nullptr, dgc_p);
+    st = flush_packs();
     if (st != MGE_OK) return st;
   }
   // b3: d_prob[t][i] = the row sum of the assignment's permuted row

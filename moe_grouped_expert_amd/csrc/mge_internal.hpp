@@ -48,6 +48,8 @@ struct ScalePackParams {
   uint32_t* dst;                  // [batch][ceil(kb/4)][rows]
 };
 mge_status launch_scale_pack(const ScalePackParams& p, hipStream_t s);
+constexpr int SP_MAXD = 8;   // scale packs per batched launch
+mge_status launch_scale_pack_batch(const ScalePackParams* list, int n, hipStream_t s);
 inline int64_t scale_pack_dwords(int rows, int kb) { return int64_t(rows) * ((kb + 3) / 4); }
 
 // ------------------------------------------------------------ routing / permutation

@@ -125,16 +125,31 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileParams p) {
 // ---------------------------------------------------------------- scale packing
 // A 64-row x 64-byte tile of a scale matrix goes through LDS: rows are read with
 // consecutive threads on consecutive bytes, the packed dwords are written with
-// consecutive threads on consecutive rows.
+// consecutive threads on consecutive rows.  One launch packs up to SP_MAXD matrices:
+// the flat grid walks the tiles of matrix 0 (all its batches), then of matrix 1, ...
 constexpr int SP_ROWS = 64;
 constexpr int SP_BYTES = 64;
 
-__global__ __launch_bounds__(256) void scale_pack_kernel(ScalePackParams p) {
+struct ScalePackBatch {
+  ScalePackParams d[SP_MAXD];
+  int start[SP_MAXD + 1];   // first flat tile of matrix j
+  int n;
+};
+
+__global__ __launch_bounds__(256) void scale_pack_kernel(ScalePackBatch B) {
   __shared__ uint8_t tile[SP_ROWS][SP_BYTES + 4];
+  const int blk = blockIdx.x;
+  int jd = 0;
+  while (jd + 1 < B.n && B.start[jd + 1] <= blk) ++jd;
+  const ScalePackParams& p = B.d[jd];
+  const int tx_n = (p.kb + SP_BYTES - 1) / SP_BYTES;
+  const int ty_n = (p.rows + SP_ROWS - 1) / SP_ROWS;
+  const int local = blk - B.start[jd];
+  const int b = local / (tx_n * ty_n);
+  const int rem = local - b * tx_n * ty_n;
+  const int c0 = (rem % tx_n) * SP_BYTES;
+  const int r0 = (rem / tx_n) * SP_ROWS;
   const int tid = threadIdx.x;
-  const int c0 = blockIdx.x * SP_BYTES;
-  const int r0 = blockIdx.y * SP_ROWS;
-  const int b = blockIdx.z;
   const uint8_t* src = p.src_tab ? p.src_tab[b] : p.src + int64_t(b) * p.src_bstride;
   const int kb_lim = p.kb_valid ? min(p.kb, p.kb_valid[0] / 32) : p.kb;
   for (int i = tid; i < SP_ROWS * SP_BYTES; i += 256) {
@@ -158,13 +173,29 @@ __global__ __launch_bounds__(256) void scale_pack_kernel(ScalePackParams p) {
   }
 }
 
-mge_status launch_scale_pack(const ScalePackParams& p, hipStream_t s) {
-  if (p.rows <= 0 || p.kb <= 0 || p.batch <= 0) return MGE_OK;
-  dim3 grid((p.kb + SP_BYTES - 1) / SP_BYTES, (p.rows + SP_ROWS - 1) / SP_ROWS, p.batch);
+mge_status launch_scale_pack_batch(const ScalePackParams* list, int n, hipStream_t s) {
+  MGE_REQUIRE(n >= 0 && n <= SP_MAXD, "at most %d scale packs per launch (got %d)", SP_MAXD, n);
+  ScalePackBatch B{};
+  int total = 0;
+  B.n = 0;
+  for (int i = 0; i < n; ++i) {
+    const ScalePackParams& p = list[i];
+    if (p.rows <= 0 || p.kb <= 0 || p.batch <= 0) continue;
+    const int64_t tiles = int64_t((p.kb + SP_BYTES - 1) / SP_BYTES) * ((p.rows + SP_ROWS - 1) / SP_ROWS) * p.batch;
+    MGE_REQUIRE(total + tiles < (int64_t(1) << 31), "scale pack grid too large");
+    B.d[B.n] = p;
+    B.start[B.n] = total;
+    total += int(tiles);
+    ++B.n;
+  }
+  B.start[B.n] = total;
+  if (total == 0) return MGE_OK;
   ProfScope prof(s, "scale_pack");
-  hipLaunchKernelGGL(scale_pack_kernel, grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL(scale_pack_kernel, dim3(total), dim3(256), 0, s, B);
   return hip_check("scale_pack_kernel");
 }
+
+mge_status launch_scale_pack(const ScalePackParams& p, hipStream_t s) { return launch_scale_pack_batch(&p, 1, s); }
 
 mge_status launch_quant_tile(const QuantTileParams& p, bool mx, hipStream_t s) {
   if (p.R <= 0 || p.C <= 0 || p.batch <= 0) return MGE_OK;
