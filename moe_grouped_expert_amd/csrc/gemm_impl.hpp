@@ -629,38 +629,63 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
           if (fb0 >= F) return;
           const int f = fb0 + l32;
           auto lrow = [&](int r) { return rb + 8 * (r >> 2) + 4 * hi + (r & 3); };
+          // Neighbouring lanes (columns c, c+1) swap one value by DPP so that a lane holds
+          // one row x two columns instead of two rows x one column: bf16 pairs then leave
+          // as dword stores (even lane: row r, odd lane: row r + 1, columns c & ~1, +1).
+          const bool odd = (l32 & 1) != 0;
+          const int fpair = f & ~1;
+          auto pair2 = [&](float v0, float v1) {
+            const float send = odd ? v0 : v1;
+            const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xf, 0xf, false));
+            return bf16x2(odd ? recv : v0, odd ? v1 : recv);
+          };
           float h[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float G = acc_read(acc[mi][j][r]);
-            const float U = acc_read(acc[mi][j + hb][r]);
+          for (int r = 0; r < 16; r += 2) {
+            const float G0 = acc_read(acc[mi][j][r]), G1 = acc_read(acc[mi][j][r + 1]);
+            const float U0 = acc_read(acc[mi][j + hb][r]), U1 = acc_read(acc[mi][j + hb][r + 1]);
             if (train) {
-              const int o = (lrow(r) * F2 + f) * 2;
-              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(G), rGU, o, 0, 0);
-              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(U), rGU, o + 2 * F, 0, 0);
+              const int o = ((lrow(r) + (odd ? 1 : 0)) * F2 + fpair) * 2;
+              __builtin_amdgcn_raw_buffer_store_b32(pair2(G0, G1), rGU, o, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(pair2(U0, U1), rGU, o + 2 * F, 0, 0);
             }
-            h[r] = pr[r] * (G * __builtin_amdgcn_rcpf(1.f + __expf(-G))) * U;
+            h[r] = pr[r] * (G0 * __builtin_amdgcn_rcpf(1.f + __expf(-G0))) * U0;
+            h[r + 1] = pr[r + 1] * (G1 * __builtin_amdgcn_rcpf(1.f + __expf(-G1))) * U1;
           }
           if constexpr (MX) {
             // row form: one scale per (row, 32-column block), shared by the half-wave
             uint32_t sc = 0;
+            float inv[16];
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-              const uint32_t s0 = mx_scale_byte(max_half_wave(fabsf(h[r])));
-              const uint32_t s1 = mx_scale_byte(max_half_wave(fabsf(h[r + 1])));
-              const uint32_t c = e4m3x2(h[r] * mx_inv_scale(s0), h[r + 1] * mx_inv_scale(s1));
-              __builtin_amdgcn_raw_buffer_store_b8(uint8_t(c), rH, lrow(r) * F + f, 0, 0);
-              __builtin_amdgcn_raw_buffer_store_b8(uint8_t(c >> 8), rH, lrow(r + 1) * F + f, 0, 0);
-              sc = l32 == r ? s0 : sc;
-              sc = l32 == r + 1 ? s1 : sc;
+            for (int r = 0; r < 16; ++r) {
+              const uint32_t sr = mx_scale_byte(max_half_wave(fabsf(h[r])));
+              inv[r] = mx_inv_scale(sr);
+              sc = l32 == r ? sr : sc;
+            }
+            // codes of 4 consecutive rows: a lane holds its column's 4 codes (bytes =
+            // rows); a 4 x 4 byte transpose inside each quad of lanes (16-bit halves with
+            // the lane 2 apart, then bytes with the lane 1 apart) leaves row (l32 % 4) of
+            // the quad's 4 columns in the lane: one dword store per lane and 4 rows
+            const bool lo2 = (l32 & 2) == 0;
+            const uint32_t sel = odd ? 0x03070105u : 0x06020400u;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              uint32_t v = e4m3x4(h[4 * g] * inv[4 * g], h[4 * g + 1] * inv[4 * g + 1], h[4 * g + 2] * inv[4 * g + 2],
+                                  h[4 * g + 3] * inv[4 * g + 3]);
+              const uint32_t x = uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x4E, 0xf, 0xf, false));
+              v = lo2 ? ((v & 0xffffu) | (x << 16)) : ((x >> 16) | (v & 0xffff0000u));
+              const uint32_t y = uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0xB1, 0xf, 0xf, false));
+              v = __builtin_amdgcn_perm(y, v, sel);
+              __builtin_amdgcn_raw_buffer_store_b32(v, rH, lrow(4 * g + (l32 & 3)) * F + fb0 + (l32 & ~3), 0, 0);
             }
             // lane l32 < 16 writes the scale of its row l32
             const uint32_t so = l32 < 16 ? uint32_t(lrow(l32) * (F / 32) + fb0 / 32) : kInvalid;
             __builtin_amdgcn_raw_buffer_store_b8(uint8_t(sc), rHs, so, 0, 0);
           } else {
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(h[r]), rH, (lrow(r) * F + f) * 2, 0, 0);
+            for (int r = 0; r < 16; r += 2)
+              __builtin_amdgcn_raw_buffer_store_b32(pair2(h[r], h[r + 1]), rH, ((lrow(r) + (odd ? 1 : 0)) * F + fpair) * 2,
+                                                    0, 0);
           }
           if (train) {
             // column form of column f, rows [rb, rb + 32): after the half-wave swaps,
