@@ -4,7 +4,8 @@
 // One workgroup owns a 64-row x 128-column tile.  Row form: each thread quantizes
 // the 32-value block it loaded itself (no LDS).  Column form: the tile is staged in
 // LDS and each thread quantizes 32 consecutive rows of one column, writing the
-// transposed, K-contiguous layout the weight-gradient GEMMs read.  The bf16 variant
+// transposed, K-contiguous layout the weight-gradient GEMMs read; the two lanes of a
+// column are neighbours, so its 64 rows leave as one 64-byte piece of one store.  The bf16 variant
 // of the same kernel writes a plain (gathered) copy and the bf16 transpose.
 // HBM-bound: 2 B read + (1 + 1/32) B written per element and orientation.
 #include "mge_common.hpp"
@@ -15,10 +16,12 @@ namespace mge {
 constexpr int QT_ROWS = 64;
 constexpr int QT_COLS = 128;
 constexpr int QT_LDS_STRIDE = QT_COLS + 8;   // bf16 elements per LDS row
+constexpr int QT_GRP = 32;                   // extra bf16 per 32-row group (column reads of both groups on distinct banks)
+__device__ __forceinline__ int qt_at(int row, int col) { return row * QT_LDS_STRIDE + (row >> 5) * QT_GRP + col; }
 
 template <bool MX>
 __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileParams p) {
-  __shared__ uint16_t tile[QT_ROWS * QT_LDS_STRIDE];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[QT_ROWS * QT_LDS_STRIDE + (QT_ROWS / 32) * QT_GRP];
   const int tid = threadIdx.x;
   const int c0 = blockIdx.x * QT_COLS;
   const int r0 = blockIdx.y * QT_ROWS;
@@ -82,18 +85,18 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileParams p) {
 
   // ---- column form: stage the tile, then thread -> (column tid%128, rows (tid/128)*32..+32)
   {
-    uint4* t4 = reinterpret_cast<uint4*>(tile + rl * QT_LDS_STRIDE + cl);
+    uint4* t4 = reinterpret_cast<uint4*>(tile + qt_at(rl, cl));
     t4[0] = v[0]; t4[1] = v[1]; t4[2] = v[2]; t4[3] = v[3];
   }
   __syncthreads();
-  const int cc = tid & 127;
-  const int rb = tid >> 7;
+  const int cc = tid >> 1;
+  const int rb = tid & 1;
   const int col = c0 + cc;
   const int rowb = r0 + rb * 32;
   if (col >= p.C || rowb >= p.Rp) return;
   float f[32];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) f[j] = bf16_to_f32(tile[(rb * 32 + j) * QT_LDS_STRIDE + cc]);
+  for (int j = 0; j < 32; ++j) f[j] = bf16_to_f32(tile[qt_at(rb * 32 + j, cc)]);
   const int64_t ocol = int64_t(b) * p.C + col;
   if (MX) {
     float amax = 0.f;
@@ -114,8 +117,7 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileParams p) {
     uint32_t out[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      out[i] = uint32_t(tile[(rb * 32 + 2 * i) * QT_LDS_STRIDE + cc]) |
-               (uint32_t(tile[(rb * 32 + 2 * i + 1) * QT_LDS_STRIDE + cc]) << 16);
+      out[i] = uint32_t(tile[qt_at(rb * 32 + 2 * i, cc)]) | (uint32_t(tile[qt_at(rb * 32 + 2 * i + 1, cc)]) << 16);
     uint4* dst = reinterpret_cast<uint4*>(p.col_bf16 + ocol * p.Rp + rowb);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);

@@ -13,9 +13,11 @@
 // needs many waves in flight).  In a sub-tile, thread t takes row t/2 and the 32-column
 // block t%2: it reads its dh (fp32), G and U (bf16) with 16-byte loads, quantizes its
 // dG and dU row blocks in registers and adds to its share of the row's d_prob.  The
-// column form goes through LDS one array at a time (dG, then dU): the 128 x 64 values
-// are stored with a row stride of 65 floats, so that both the row-wise stores and the
-// column-wise reads (thread t: column t%64, rows 32*(t/64)..+31) hit 64 distinct banks.
+// column form goes through LDS one array at a time (dG, then dU).  There, thread t takes
+// column t/4 and rows 32*(t%4)..+31, so the 4 lanes of a column write its 128 rows as
+// one 128-byte piece of one store instruction.  The 128 x 64 values are stored with a
+// row stride of 65 floats plus 16 floats per 32-row group, so that both the row-wise
+// stores and the column-wise reads hit 64 distinct banks.
 // d_prob leaves as one partial sum per (row, column group), summed in a fixed order by
 // the d_prob reduction.  HBM-bound: 12 B per (row, column) at MXFP8 (4 dh + 4 G,U read,
 // 2 + 2 codes written).
@@ -28,6 +30,8 @@ constexpr int SB_ROWS = 128;                 // rows of a workgroup tile
 constexpr int SB_COLS = 256;                 // ffn columns of a workgroup tile
 constexpr int SB_SUB = 64;                   // columns of a sub-tile (one LDS round)
 constexpr int SB_LD = SB_SUB + 1;            // LDS row stride in floats
+constexpr int SB_GRP = 16;                   // extra floats per 32-row group
+__device__ __forceinline__ int sb_at(int row, int col) { return row * SB_LD + (row >> 5) * SB_GRP + col; }
 
 int swiglu_bwd_nparts(int F) { return (F + SB_COLS - 1) / SB_COLS; }
 
@@ -58,7 +62,7 @@ __device__ __forceinline__ void store_bf16x32(const float* v, uint16_t* dst16) {
 
 template <bool MX>
 __global__ __launch_bounds__(256, 4) void swiglu_bwd_kernel(SwigluBwdParams p) {
-  __shared__ float sv[SB_ROWS * SB_LD];
+  __shared__ float sv[SB_ROWS * SB_LD + (SB_ROWS / 32) * SB_GRP];
   const int tid = threadIdx.x;
   const int r0 = blockIdx.x * SB_ROWS;
   const int cg = blockIdx.y;                 // column group
@@ -70,7 +74,7 @@ __global__ __launch_bounds__(256, 4) void swiglu_bwd_kernel(SwigluBwdParams p) {
   const bool rok = rin && p.perm_src[row] >= 0;
   const float pr = rok ? p.prob[row] : 0.f;
   // column-wise mapping
-  const int c = tid & (SB_SUB - 1), rb = tid >> 6;
+  const int c = tid >> 2, rb = tid & 3;
   const int rr = r0 + rb * 32;               // first row of this thread's column block
   float dps = 0.f;
 
@@ -128,13 +132,13 @@ __global__ __launch_bounds__(256, 4) void swiglu_bwd_kernel(SwigluBwdParams p) {
       const float* src = h == 0 ? dg : du;
       __syncthreads();                       // the previous readers of sv are done
 #pragma unroll
-      for (int j = 0; j < 32; ++j) sv[rl * SB_LD + hh * 32 + j] = src[j];
+      for (int j = 0; j < 32; ++j) sv[sb_at(rl, hh * 32 + j)] = src[j];
       __syncthreads();
       const int fc = f0 + c;
       if (fc < F && rr < p.R) {              // R is a multiple of 32: the block's rows exist
         float v[32];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) v[i] = sv[(rb * 32 + i) * SB_LD + c];
+        for (int i = 0; i < 32; ++i) v[i] = sv[sb_at(rb * 32 + i, c)];
         const int64_t col = int64_t(h) * F + fc;
         if constexpr (MX)
           store_mx32(v, p.col_codes + col * p.Rp + rr, p.col_scales + col * (p.Rp / 32) + rr / 32);
