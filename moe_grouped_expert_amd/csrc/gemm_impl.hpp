@@ -61,7 +61,7 @@ constexpr int G_WNB = 4;   // 32-col MFMA blocks per wave (N)
 constexpr int G_BM = G_WAVES_M * G_WMB * 32;
 constexpr int G_BN = G_WAVES_N * G_WNB * 32;
 constexpr int G_BKB = 128;                    // K bytes per slice: one whole 128-byte line per operand row
-constexpr int G_STAGES = 2;                   // LDS stages: one slice in flight while the other is multiplied
+constexpr int G_STAGES = 2;                   // LDS stages, each refilled once its slice is in registers
 constexpr int G_THREADS = 64 * G_WAVES_M * G_WAVES_N;
 constexpr int G_STAGE_BYTES = (G_BM + G_BN) * G_BKB;   // 64 KB
 constexpr int G_MAXE = 256;
@@ -143,6 +143,20 @@ __device__ __forceinline__ void acc_settle() {
 // s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory and `lgkm`
 // LDS/scalar operations are outstanding (export counter not waited on).
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 0xf) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
+
+// Workgroup barriers of the K loop.  __syncthreads() would also wait for every
+// outstanding vector-memory operation (its fence), including the LDS DMAs that are meant
+// to stay in flight across the barrier; these wait only for what they name.  The asm
+// "memory" clobber keeps the compiler from moving LDS reads across them.
+// lds_barrier: this wave's LDS reads have completed, then all waves meet.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// vm_barrier<N>: at most N of this wave's vector-memory operations (the newest, as they
+// complete in order) and no LDS read still outstanding, then all waves meet.
+template <int N>
+__device__ __forceinline__ void vm_barrier() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(N, 0));
+  asm volatile("s_barrier" ::: "memory");
+}
 
 // 16 bytes per lane from buffer offset `voff` straight into LDS at lds_addr + 16*lane
 // (buffer_load_dwordx4 ... lds; M0 holds the wave's LDS destination).  Written as asm
@@ -426,7 +440,9 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
   };
 
   Tile cur = decode(vid);
-  bool cur_issued = false;   // slice 0 of `cur` already on its way into stage 0
+  // next-tile slices issued before the epilogue (see there)
+  constexpr int G_PREFETCH = OUT == OUT_F32_ACC ? 0 : 1;
+  int cur_issued = 0;   // slices of `cur` (from 0) already on their way into their stages
   for (int tile = vid; tile < total; tile += nwg) {
     rederive_lane();
     const Tile nxt = decode(tile + nwg);
@@ -448,13 +464,12 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
 
     // MX: in K step s (elements 64s..64s+63 of the slice's 128-element group) lane hi
     // scales K block 2s + hi: byte 2s + hi of the group's dword, shifted down to byte 0
-    // (op_sel 0)
-    // The next slice's 16 operand DMAs go out two after each of the first 8 MFMAs of the
-    // slice: issued back to back before the MFMAs they hold the in-order wave at the
-    // memory pipeline, spread over the whole slice the last ones have too little time
-    // left to land (measured on MI355X, both slower).
-    auto mfma_step = [&](int s, const frag_t* af, const frag_t* bfr, const uint32_t* sa, const uint32_t* sb,
-                         const SliceDma& nx) {
+    // (op_sel 0).
+    // With a slice `nx` (the DMA form), step s issues that slice's 16 operand DMAs two
+    // after each of its first 8 MFMAs: issued back to back before the MFMAs they hold the
+    // in-order wave at the memory pipeline (measured on MI355X, slower).
+    auto mfma_step = [&](auto with_dma, int s, const frag_t* af, const frag_t* bfr, const uint32_t* sa,
+                         const uint32_t* sb, const SliceDma& nx) {
       const int sh = 8 * (2 * s + hi);
 #pragma unroll
       for (int mi = 0; mi < G_WMB; ++mi)
@@ -468,28 +483,40 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
           }
           const int q = mi * G_WNB + ni;
-          if (s == 0 && q < 8) {
-            __builtin_amdgcn_sched_barrier(0);
-            dma_operand(nx, 2 * q);
-            dma_operand(nx, 2 * q + 1);
-            __builtin_amdgcn_sched_barrier(0);
+          if constexpr (decltype(with_dma)::value) {
+            if (q < 8) {
+              __builtin_amdgcn_sched_barrier(0);
+              dma_operand(nx, 2 * q);
+              dma_operand(nx, 2 * q + 1);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
         }
     };
+    constexpr std::true_type kDma{};
+    constexpr std::false_type kNoDma{};
 
-    // ---- K loop: G_STAGES LDS stages; slice kt+1 streams in while slice kt is multiplied
-    if (!cur_issued) {
-      __syncthreads();   // LDS stages are free
-#pragma unroll
-      for (int q = 0; q < G_STAGES - 1; ++q) issue_slice(cur, q, q);
+    // ---- K loop over two LDS stages.  A wave reads every fragment and scale of slice kt
+    // into registers at the top of iteration kt; those reads have landed by the end of the
+    // first half of the K steps (the LDS needs about as long to serve them as the MFMAs of
+    // that half take).  From there on the stage is dead, so once every wave has passed
+    // that point it is refilled with slice kt+2.  A slice thus has one and a half
+    // iterations to arrive instead of one, with the same LDS.  The two slices past the
+    // tile's last are issued too, with every lane out of range (they land as zeros and
+    // touch no memory), so that every iteration waits on the same count.
+    if (cur_issued == 0 && nkt > 0) {
+      lds_barrier();   // no wave still reads a stage
+      issue_slice(cur, 0, 0);
+      issue_slice(cur, 1, 1);
+      vm_barrier<DMA_PER_SLICE>();   // slice 0 resident, slice 1 may be on its way
+    } else if (cur_issued == 1) {
+      issue_slice(cur, 1, 1);
+      vm_barrier<DMA_PER_SLICE>();   // slice 0 and the epilogue's stores done
+    } else {
+      vm_barrier<0>();               // prefetched slices 0, 1 and the epilogue's stores
     }
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm((G_STAGES - 2) * DMA_PER_SLICE, 0));   // slice 0 resident
-    __syncthreads();
     for (int kt = 0; kt < nkt; ++kt) {
       const int stage = kt & (G_STAGES - 1);
-      const SliceDma nx = prep_slice(cur, kt + G_STAGES - 1, (kt + G_STAGES - 1) & (G_STAGES - 1));
-      dma_scale(nx);
-      __builtin_amdgcn_sched_barrier(0);
       const uint8_t* sA = smem + stage * G_STAGE_BYTES;
       const uint8_t* sB = sA + G_BM * G_BKB;
       uint32_t sa[G_WMB], sb[G_WNB];
@@ -506,31 +533,36 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
           sb[ni] = *reinterpret_cast<const uint32_t*>(sS + 2048 + (r >> 7) * 1024 + (r & 127) * 4);
         }
       }
-      frag_t af[2][G_WMB], bfr[2][G_WNB];
-      read_frags(sA, sB, 0, af[0], bfr[0]);
+      frag_t af[NSTEP][G_WMB], bfr[NSTEP][G_WNB];
 #pragma unroll
-      for (int s = 0; s < NSTEP; ++s) {
-        if (s + 1 < NSTEP) read_frags(sA, sB, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
-        mfma_step(s, af[s & 1], bfr[s & 1], sa, sb, nx);
-      }
+      for (int s = 0; s < NSTEP; ++s) read_frags(sA, sB, s, af[s], bfr[s]);
+      const SliceDma nx = prep_slice(cur, kt + G_STAGES, stage);
+#pragma unroll
+      for (int s = 0; s < NSTEP / 2; ++s) mfma_step(kNoDma, s, af[s], bfr[s], sa, sb, nx);
       __builtin_amdgcn_sched_barrier(0);
-      // slice kt+1 resident and every wave done with stage kt before it is refilled
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm((G_STAGES - 2) * DMA_PER_SLICE, 0));
-      __syncthreads();
+      lds_barrier();   // every wave is done with this stage
+      dma_scale(nx);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_step(kDma, NSTEP / 2, af[NSTEP / 2], bfr[NSTEP / 2], sa, sb, nx);
+#pragma unroll
+      for (int s = NSTEP / 2 + 1; s < NSTEP; ++s) mfma_step(kNoDma, s, af[s], bfr[s], sa, sb, nx);
+      __builtin_amdgcn_sched_barrier(0);
+      vm_barrier<DMA_PER_SLICE>();   // slice kt+1 resident (kt+2 still on its way)
     }
     __builtin_amdgcn_s_waitcnt(0);   // the past-the-end (all-zero) slices have landed
     acc_settle();                    // the last MFMA results are readable
     rederive_lane();
-    // all stages are free: start the next tile's first slices now so their latency hides
-    // behind the epilogue (which uses no stage memory).  Not when the epilogue reads the
-    // output back: those loads would queue behind the slices.
-    cur_issued = false;
-    {
-      if (nxt.valid && nxt.nkt > 0 && OUT != OUT_F32_ACC) {
-#pragma unroll
-        for (int q = 0; q < G_STAGES - 1; ++q) issue_slice(nxt, q, q);
-        cur_issued = true;
-      }
+    // both stages are free (the loop ends on a barrier): start the next tile's first
+    // slice now so that its latency hides behind the epilogue (which uses no stage
+    // memory); slice 1 follows at the top of the next tile (one or two slices ahead
+    // measure the same on MI355X, and one leaves more of the 63 vector-memory operations
+    // a wave may have outstanding to the epilogue's stores).  None when the epilogue
+    // reads the output back: those loads would queue behind the slice.
+    cur_issued = 0;
+    if (nxt.valid && nxt.nkt > 0 && G_PREFETCH > 0) {
+      issue_slice(nxt, 0, 0);
+      if constexpr (G_PREFETCH > 1) issue_slice(nxt, 1, 1);
+      cur_issued = G_PREFETCH;
     }
 
     // ---------------------------------------------------------------- epilogues
