@@ -61,6 +61,9 @@ constexpr int G_WNB = 4;   // 32-col MFMA blocks per wave (N)
 constexpr int G_BM = G_WAVES_M * G_WMB * 32;
 constexpr int G_BN = G_WAVES_N * G_WNB * 32;
 constexpr int G_BKB = 128;                    // K bytes per slice: one whole 128-byte line per operand row
+#ifndef G_BAR_AT32
+#define G_BAR_AT32 8   // a slice's stage is released after this many 32nds of its MFMAs
+#endif
 constexpr int G_STAGES = 2;                   // LDS stages, each refilled once its slice is in registers
 constexpr int G_THREADS = 64 * G_WAVES_M * G_WAVES_N;
 constexpr int G_STAGE_BYTES = (G_BM + G_BN) * G_BKB;   // 64 KB
@@ -462,39 +465,48 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
-    // MX: in K step s (elements 64s..64s+63 of the slice's 128-element group) lane hi
-    // scales K block 2s + hi: byte 2s + hi of the group's dword, shifted down to byte 0
-    // (op_sel 0).
-    // With a slice `nx` (the DMA form), step s issues that slice's 16 operand DMAs two
-    // after each of its first 8 MFMAs: issued back to back before the MFMAs they hold the
-    // in-order wave at the memory pipeline (measured on MI355X, slower).
-    auto mfma_step = [&](auto with_dma, int s, const frag_t* af, const frag_t* bfr, const uint32_t* sa,
-                         const uint32_t* sb, const SliceDma& nx) {
-      const int sh = 8 * (2 * s + hi);
-#pragma unroll
-      for (int mi = 0; mi < G_WMB; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < G_WNB; ++ni) {
-          if constexpr (MX) {
-            const int xa = int(sa[mi] >> sh);
-            const int xb = int(sb[ni] >> sh);
-            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0, xa, 0, xb);
-          } else {
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
-          }
-          const int q = mi * G_WNB + ni;
-          if constexpr (decltype(with_dma)::value) {
-            if (q < 8) {
-              __builtin_amdgcn_sched_barrier(0);
-              dma_operand(nx, 2 * q);
-              dma_operand(nx, 2 * q + 1);
-              __builtin_amdgcn_sched_barrier(0);
-            }
+    // The MFMAs of one slice, K step by K step (MX: in K step s, elements 64s..64s+63 of
+    // the slice's 128-element group, lane hi scales K block 2s + hi: byte 2s + hi of the
+    // group's dword, shifted down to byte 0, op_sel 0).  Before MFMA BAR_AT every wave
+    // has its fragments (lds_barrier), so the stage is refilled from there on: the scale
+    // DMA first, then the 16 operand DMAs spread evenly over the remaining MFMAs.  A
+    // CU's texture-address path moves about 54 bytes per clock, so a slice's DMAs need
+    // well over half of the slice's MFMA time; packed closer they fill its queue and
+    // stall the issuing wave (measured on MI355X).
+    constexpr int NMFMA = NSTEP * G_WMB * G_WNB;
+    constexpr int BAR_AT = NMFMA * G_BAR_AT32 / 32;
+    auto mfma_slice = [&](frag_t (*af)[G_WMB], frag_t (*bfr)[G_WNB], const uint32_t* sa, const uint32_t* sb,
+                          const SliceDma& nx) {
+      static_for<0, NMFMA>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int s = i / (G_WMB * G_WNB);
+        constexpr int mi = (i % (G_WMB * G_WNB)) / G_WNB;
+        constexpr int ni = i % G_WNB;
+        if constexpr (i == BAR_AT) {
+          __builtin_amdgcn_sched_barrier(0);
+          lds_barrier();   // every wave is done with this stage
+          dma_scale(nx);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (MX) {
+          const int sh = 8 * (2 * s + hi);
+          const int xa = int(sa[mi] >> sh);
+          const int xb = int(sb[ni] >> sh);
+          acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[s][mi], bfr[s][ni], acc[mi][ni], 0, 0, 0, xa, 0, xb);
+        } else {
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s][mi], bfr[s][ni], acc[mi][ni], 0, 0, 0);
+        }
+        if constexpr (i >= BAR_AT) {
+          constexpr int n = NMFMA - BAR_AT;
+          constexpr int d0 = 16 * (i - BAR_AT) / n, d1 = 16 * (i - BAR_AT + 1) / n;
+          if constexpr (d1 > d0) {
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<d0, d1>([&](auto dc) { dma_operand(nx, decltype(dc)::value); });
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
+      });
     };
-    constexpr std::true_type kDma{};
-    constexpr std::false_type kNoDma{};
 
     // ---- K loop over two LDS stages.  A wave reads every fragment and scale of slice kt
     // into registers at the top of iteration kt; those reads have landed by the end of the
@@ -537,15 +549,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s) read_frags(sA, sB, s, af[s], bfr[s]);
       const SliceDma nx = prep_slice(cur, kt + G_STAGES, stage);
-#pragma unroll
-      for (int s = 0; s < NSTEP / 2; ++s) mfma_step(kNoDma, s, af[s], bfr[s], sa, sb, nx);
-      __builtin_amdgcn_sched_barrier(0);
-      lds_barrier();   // every wave is done with this stage
-      dma_scale(nx);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_step(kDma, NSTEP / 2, af[NSTEP / 2], bfr[NSTEP / 2], sa, sb, nx);
-#pragma unroll
-      for (int s = NSTEP / 2 + 1; s < NSTEP; ++s) mfma_step(kNoDma, s, af[s], bfr[s], sa, sb, nx);
+      mfma_slice(af, bfr, sa, sb, nx);
       __builtin_amdgcn_sched_barrier(0);
       vm_barrier<DMA_PER_SLICE>();   // slice kt+1 resident (kt+2 still on its way)
     }
