@@ -125,12 +125,14 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileParams p) {
 }
 
 // ---------------------------------------------------------------- scale packing
-// A 64-row x 64-byte tile of a scale matrix goes through LDS: rows are read with
-// consecutive threads on consecutive bytes, the packed dwords are written with
-// consecutive threads on consecutive rows.  One launch packs up to SP_MAXD matrices:
-// the flat grid walks the tiles of matrix 0 (all its batches), then of matrix 1, ...
+// A 64-row x 64-byte tile of a scale matrix goes through LDS: thread t reads 16 bytes of
+// row t/4 (one 16-byte load where the batch's base and row stride allow it, else byte
+// loads), the packed dwords leave with consecutive threads on consecutive rows.  One
+// launch packs up to SP_MAXD matrices: the flat grid walks the tiles of matrix 0 (all its
+// batches), then of matrix 1, ...
 constexpr int SP_ROWS = 64;
 constexpr int SP_BYTES = 64;
+constexpr int SP_LD = SP_BYTES + 4;   // LDS row stride in bytes: 17 dwords, so the dword reads of 64 rows hit 64 banks
 
 struct ScalePackBatch {
   ScalePackParams d[SP_MAXD];
@@ -139,7 +141,7 @@ struct ScalePackBatch {
 };
 
 __global__ __launch_bounds__(256) void scale_pack_kernel(ScalePackBatch B) {
-  __shared__ uint8_t tile[SP_ROWS][SP_BYTES + 4];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[SP_ROWS * SP_LD];
   const int blk = blockIdx.x;
   int jd = 0;
   while (jd + 1 < B.n && B.start[jd + 1] <= blk) ++jd;
@@ -154,24 +156,39 @@ __global__ __launch_bounds__(256) void scale_pack_kernel(ScalePackBatch B) {
   const int tid = threadIdx.x;
   const uint8_t* src = p.src_tab ? p.src_tab[b] : p.src + int64_t(b) * p.src_bstride;
   const int kb_lim = p.kb_valid ? min(p.kb, p.kb_valid[0] / 32) : p.kb;
-  for (int i = tid; i < SP_ROWS * SP_BYTES; i += 256) {
-    const int rr = i / SP_BYTES, cc = i % SP_BYTES;
+  {
+    const int rr = tid >> 2, cc = (tid & 3) * 16;
     const int r = r0 + rr, c = c0 + cc;
-    uint8_t v = 127;
-    if (r < p.rows && c < kb_lim) v = src[int64_t(r) * p.ld + c];
-    tile[rr][cc] = v;
+    uint32_t w[4];
+    const bool vec = ((reinterpret_cast<uintptr_t>(src) | uintptr_t(p.ld)) & 15) == 0;   // uniform
+    if (vec && r < p.rows && c + 16 <= kb_lim) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src + int64_t(r) * p.ld + c);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int cb = c + 4 * q + k;
+          const uint32_t byte = (r < p.rows && cb < kb_lim) ? src[int64_t(r) * p.ld + cb] : 127u;
+          x |= byte << (8 * k);
+        }
+        w[q] = x;
+      }
+    }
+    uint32_t* t32 = reinterpret_cast<uint32_t*>(tile + rr * SP_LD + cc);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) t32[q] = w[q];
   }
   __syncthreads();
   const int kb4 = (p.kb + 3) / 4;
   uint32_t* dst = p.dst + int64_t(b) * kb4 * p.rows;
+#pragma unroll
   for (int i = tid; i < SP_ROWS * (SP_BYTES / 4); i += 256) {
     const int jj = i / SP_ROWS, rr = i % SP_ROWS;
     const int j = c0 / 4 + jj, r = r0 + rr;
-    if (r < p.rows && j < kb4) {
-      const uint32_t w = uint32_t(tile[rr][4 * jj]) | (uint32_t(tile[rr][4 * jj + 1]) << 8) |
-                         (uint32_t(tile[rr][4 * jj + 2]) << 16) | (uint32_t(tile[rr][4 * jj + 3]) << 24);
-      dst[int64_t(j) * p.rows + r] = w;
-    }
+    if (r < p.rows && j < kb4) dst[int64_t(j) * p.rows + r] = *reinterpret_cast<const uint32_t*>(tile + rr * SP_LD + 4 * jj);
   }
 }
 
