@@ -690,14 +690,8 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
           }
           if constexpr (MX) {
             // row form: one scale per (row, 32-column block), shared by the half-wave
-            uint32_t sc = 0;
             float inv[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const uint32_t sr = mx_scale_byte(max_half_wave(fabsf(h[r])));
-              inv[r] = mx_inv_scale(sr);
-              sc = l32 == r ? sr : sc;
-            }
+            const uint32_t sc = row_block_inv16(h, l32, inv);   // sc: row l32 / 2
             // codes of 4 consecutive rows: a lane holds its column's 4 codes (bytes =
             // rows); a 4 x 4 byte transpose inside each quad of lanes (16-bit halves with
             // the lane 2 apart, then bytes with the lane 1 apart) leaves row (l32 % 4) of
@@ -714,8 +708,8 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
               v = __builtin_amdgcn_perm(y, v, sel);
               __builtin_amdgcn_raw_buffer_store_b32(v, rH, lrow(4 * g + (l32 & 3)) * F + fb0 + (l32 & ~3), 0, 0);
             }
-            // lane l32 < 16 writes the scale of its row l32
-            const uint32_t so = l32 < 16 ? uint32_t(lrow(l32) * (F / 32) + fb0 / 32) : kInvalid;
+            // the even lanes write the scale of their row l32 / 2
+            const uint32_t so = (l32 & 1) == 0 ? uint32_t(lrow(l32 >> 1) * (F / 32) + fb0 / 32) : kInvalid;
             __builtin_amdgcn_raw_buffer_store_b8(uint8_t(sc), rHs, so, 0, 0);
           } else {
 #pragma unroll

@@ -68,18 +68,6 @@ __device__ __forceinline__ uint32_t e4m3_rne(float w) {
   return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(w), 0.f, 0, false)) & 0xffu;
 }
 
-// Max over the 32 lanes of each half-wave, returned in every lane: DPP exchanges
-// within 16-lane rows (xor 1, xor 2, mirror in 8, mirror in 16), then a swizzle that
-// swaps the two 16-lane rows of each half.  Needs all 64 lanes active.
-__device__ __forceinline__ float max_half_wave(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false)));    // quad_perm 1,0,3,2
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false)));    // quad_perm 2,3,0,1
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, false)));   // row_half_mirror
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xf, 0xf, false)));   // row_mirror
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));                // swap 16-lane rows
-  return v;
-}
-
 // v_permlane32_swap_b32: lanes 32..63 of a trade places with lanes 0..31 of b.  Returns
 // the new (a, b): lane i < 32 then holds (a[i], a[i + 32]) and lane i + 32 holds
 // (b[i], b[i + 32]).
@@ -89,6 +77,71 @@ struct U32Pair {
 __device__ __forceinline__ U32Pair permlane32_swap(uint32_t a, uint32_t b) {
   const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
   return U32Pair{uint32_t(r[0]), uint32_t(r[1])};
+}
+
+// v_permlane16_swap_b32: lanes 16..31 of a trade places with lanes 0..15 of b (and
+// lanes 48..63 of a with lanes 32..47 of b).  Returns the new (a, b): a lane in rows 0, 2
+// then holds (its a, the a of the lane 16 above), a lane in rows 1, 3 (the b of the lane
+// 16 below, its b) (measured on MI355X).
+__device__ __forceinline__ U32Pair permlane16_swap(uint32_t a, uint32_t b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  return U32Pair{uint32_t(r[0]), uint32_t(r[1])};
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Row blocks of a 32-column tile held column-wise: in each half-wave, lane c (= l32)
+// holds v[0..15], the values of 16 rows in column c.  Computes, for each of the 16 rows,
+// the E8M0 scale of its 32 values (their amax over the half-wave) and returns in inv[r]
+// the reciprocal scale of row r in every lane, and in the result the scale byte of row
+// l32 / 2.  A reduce-scatter (each exchange halves the rows a lane keeps: 16-lane swap,
+// lane ^ 8 by row_ror:8, mirror in 8, lane ^ 2, lane ^ 1) leaves the amax of row l32 / 2
+// in lanes 2r, 2r + 1; the mirrored all-gather returns the 16 reciprocals: about 70
+// instructions for the 16 rows instead of five exchanges per row.  Needs all 64 lanes.
+__device__ __forceinline__ uint32_t row_block_inv16(const float* v, int l32, float* inv) {
+  const bool b4 = (l32 & 16) != 0, b3 = (l32 & 8) != 0, b2 = (l32 & 4) != 0, b1 = (l32 & 2) != 0;
+  // m1[i]: row i + 8*b4, amax over lanes c, c ^ 16
+  float m1[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const U32Pair x = permlane16_swap(__float_as_uint(fabsf(v[i])), __float_as_uint(fabsf(v[i + 8])));
+    m1[i] = fmaxf(__uint_as_float(x.a), __uint_as_float(x.b));
+  }
+  // m2[i]: row i + 4*b3 + 8*b4 (partner: lane ^ 8)
+  float m2[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m2[i] = fmaxf(b3 ? m1[i + 4] : m1[i], dpp_f<0x128>(b3 ? m1[i] : m1[i + 4]));
+  // m3[i]: row i + 2*b2 + 4*b3 + 8*b4 (partner: lane 7 - c within 8; same b3, b4)
+  float m3[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) m3[i] = fmaxf(b2 ? m2[i + 2] : m2[i], dpp_f<0x141>(b2 ? m2[i] : m2[i + 2]));
+  // m4: row b1 + 2*b2 + 4*b3 + 8*b4 = l32 / 2 (partner: lane ^ 2); then lane ^ 1 holds the same row
+  float m4 = fmaxf(b1 ? m3[1] : m3[0], dpp_f<0x4E>(b1 ? m3[0] : m3[1]));
+  m4 = fmaxf(m4, dpp_f<0xB1>(m4));
+  const uint32_t sc = mx_scale_byte(m4);
+  const float g1 = mx_inv_scale(sc);
+  // all-gather, the same exchanges in reverse
+  const float r2 = dpp_f<0x4E>(g1);
+  const float g2[2] = {b1 ? r2 : g1, b1 ? g1 : r2};                      // rows t + 2*b2 + 4*b3 + 8*b4
+  const float r40 = dpp_f<0x141>(g2[0]), r41 = dpp_f<0x141>(g2[1]);
+  const float g4[4] = {b2 ? r40 : g2[0], b2 ? r41 : g2[1], b2 ? g2[0] : r40, b2 ? g2[1] : r41};   // rows u + 4*b3 + 8*b4
+  float g8[8];                                                            // rows w + 8*b4
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const float r = dpp_f<0x128>(g4[t]);
+    g8[t] = b3 ? r : g4[t];
+    g8[t + 4] = b3 ? g4[t] : r;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {   // every lane: a = row i, b = row i + 8
+    const U32Pair x = permlane16_swap(__float_as_uint(g8[i]), __float_as_uint(g8[i]));
+    inv[i] = __uint_as_float(x.a);
+    inv[i + 8] = __uint_as_float(x.b);
+  }
+  return sc;
 }
 
 // max of v over lanes i and i ^ 32
