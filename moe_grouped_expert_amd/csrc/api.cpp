@@ -339,14 +339,12 @@ mge_status grouped_mlp_fwd(const mge_fwd_args* a, void* stream) {
     else h = ws.take(size_t(R) * a->F * 2);
   }
   const int E = a->E;
-  st = launch_upload_ptrs(reinterpret_cast<const void* const*>(a->w_gate_up), E, tab, s);
-  if (st != MGE_OK) return st;
-  st = launch_upload_ptrs(reinterpret_cast<const void* const*>(a->w_down), E, tab + E, s);
-  if (st != MGE_OK) return st;
-  if (mx) {
-    st = launch_upload_ptrs(reinterpret_cast<const void* const*>(a->w_gate_up_scale), E, tab + 2 * E, s);
-    if (st != MGE_OK) return st;
-    st = launch_upload_ptrs(reinterpret_cast<const void* const*>(a->w_down_scale), E, tab + 3 * E, s);
+  {
+    const void* const* tabs[4] = {reinterpret_cast<const void* const*>(a->w_gate_up),
+                                  reinterpret_cast<const void* const*>(a->w_down),
+                                  mx ? reinterpret_cast<const void* const*>(a->w_gate_up_scale) : nullptr,
+                                  mx ? reinterpret_cast<const void* const*>(a->w_down_scale) : nullptr};
+    st = launch_upload_tables(tabs, 4, E, tab, s);
     if (st != MGE_OK) return st;
   }
   const int64_t rows_bound = int64_t(a->T) * a->k;
@@ -527,13 +525,15 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
     wd_k = wd_t.data();
     wgu_k = wgu_t.data();
   }
-  st = launch_upload_ptrs(wd_k, E, tab, s);
-  if (st == MGE_OK) st = launch_upload_ptrs(wgu_k, E, tab + E, s);
-  if (st == MGE_OK && mx) st = launch_upload_ptrs(reinterpret_cast<const void* const*>(a->w_down_scale), E, tab + 2 * E, s);
-  if (st == MGE_OK && mx) st = launch_upload_ptrs(reinterpret_cast<const void* const*>(a->w_gate_up_scale), E, tab + 3 * E, s);
-  if (st == MGE_OK) st = launch_upload_ptrs(reinterpret_cast<const void* const*>(a->dw_down), E, tab + 4 * E, s);
-  if (st == MGE_OK) st = launch_upload_ptrs(reinterpret_cast<const void* const*>(a->dw_gate_up), E, tab + 5 * E, s);
-  if (st != MGE_OK) return st;
+  {
+    const void* const* tabs[6] = {wd_k, wgu_k,
+                                  mx ? reinterpret_cast<const void* const*>(a->w_down_scale) : nullptr,
+                                  mx ? reinterpret_cast<const void* const*>(a->w_gate_up_scale) : nullptr,
+                                  reinterpret_cast<const void* const*>(a->dw_down),
+                                  reinterpret_cast<const void* const*>(a->dw_gate_up)};
+    st = launch_upload_tables(tabs, 6, E, tab, s);
+    if (st != MGE_OK) return st;
+  }
 
   // b1: dy gathered by perm_src, row form (along H) and column form (along tokens)
   {

@@ -108,28 +108,40 @@ mge_status launch_dprob_reduce(int T, int k, int nparts, const float* partial, c
 }
 
 // Per-expert pointer tables travel in the kernel arguments (captured at launch) and
-// land in the workspace, so host arrays may be reused as soon as the call returns.
-constexpr int UP_CHUNK = 64;
+// land in the workspace, so host arrays may be reused as soon as the call returns.  One
+// launch carries up to UP_CHUNK entries of several tables.
+constexpr int UP_CHUNK = 128;
 struct UploadChunk {
   void** dst;
   int n;
+  int idx[UP_CHUNK];          // slot in dst
   const void* p[UP_CHUNK];
 };
 
 __global__ void upload_ptrs_kernel(UploadChunk c) {
   int i = threadIdx.x;
-  if (i < c.n) c.dst[i] = const_cast<void*>(c.p[i]);
+  if (i < c.n) c.dst[c.idx[i]] = const_cast<void*>(c.p[i]);
 }
 
-mge_status launch_upload_ptrs(const void* const* host_ptrs, int n, void** dev_table, hipStream_t s) {
-  for (int base = 0; base < n; base += UP_CHUNK) {
-    UploadChunk c;
-    c.dst = dev_table + base;
-    c.n = (n - base) < UP_CHUNK ? (n - base) : UP_CHUNK;
-    for (int i = 0; i < c.n; ++i) c.p[i] = host_ptrs[base + i];
+mge_status launch_upload_tables(const void* const* const* tables, int ntab, int n, void** dev_table, hipStream_t s) {
+  UploadChunk c;
+  c.dst = dev_table;
+  c.n = 0;
+  auto flush = [&]() {
+    if (c.n == 0) return;
     ProfScope prof(s, "upload_ptrs");
     hipLaunchKernelGGL(upload_ptrs_kernel, dim3(1), dim3(UP_CHUNK), 0, s, c);
+    c.n = 0;
+  };
+  for (int t = 0; t < ntab; ++t) {
+    if (!tables[t]) continue;
+    for (int i = 0; i < n; ++i) {
+      c.idx[c.n] = t * n + i;
+      c.p[c.n] = tables[t][i];
+      if (++c.n == UP_CHUNK) flush();
+    }
   }
+  flush();
   return hip_check("upload_ptrs_kernel");
 }
 

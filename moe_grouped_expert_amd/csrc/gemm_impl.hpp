@@ -149,10 +149,8 @@ constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 0xf) | ((vm >> 4) << 
 
 // Workgroup barriers of the K loop.  __syncthreads() would also wait for every
 // outstanding vector-memory operation (its fence), including the LDS DMAs that are meant
-// to stay in flight across the barrier; these wait only for what they name.  The asm
-// "memory" clobber keeps the compiler from moving LDS reads across them.
-// lds_barrier: this wave's LDS reads have completed, then all waves meet.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// to stay in flight across the barrier; these wait only for what they name (lds_barrier
+// is in mge_common.hpp).
 // vm_barrier<N>: at most N of this wave's vector-memory operations (the newest, as they
 // complete in order) and no LDS read still outstanding, then all waves meet.
 template <int N>
@@ -628,7 +626,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
       // row, so rows past it are dropped by the hardware range check; 32-row blocks past
       // the group and 32-column blocks past F are skipped whole (wave-uniform).
       s_prob[tid] = my_prob;
-      __syncthreads();
+      lds_barrier();   // (the next tile's first slice stays in flight)
       constexpr int hb = G_WNB / 2;
       const int F = p.F;
       const int F2 = 2 * F;

@@ -88,6 +88,12 @@ __device__ __forceinline__ U32Pair permlane16_swap(uint32_t a, uint32_t b) {
   return U32Pair{uint32_t(r[0]), uint32_t(r[1])};
 }
 
+// Workgroup barrier for LDS data: this wave's LDS accesses have completed, then all waves
+// meet.  Unlike __syncthreads(), whose fence also waits for every outstanding global
+// load and store, it lets stores (and loads meant to stay in flight) continue across the
+// barrier; the asm "memory" clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));

@@ -93,7 +93,9 @@ mge_status launch_swiglu_bwd(const SwigluBwdParams& p, bool mx, hipStream_t s);
 
 mge_status launch_dprob_reduce(int T, int k, int nparts, const float* partial, const int32_t* perm_pos,
                                float* d_prob, hipStream_t s);
-mge_status launch_upload_ptrs(const void* const* host_ptrs, int n, void** dev_table, hipStream_t s);
+// tables[t] (n host pointers each; null tables are skipped) -> dev_table[t * n + i], in as
+// few launches as the kernel argument space allows
+mge_status launch_upload_tables(const void* const* const* tables, int ntab, int n, void** dev_table, hipStream_t s);
 
 // ------------------------------------------------------------ grouped GEMM
 enum GemmMode { RAGGED_M = 0, RAGGED_K = 1 };

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileParams p) {
     uint4* t4 = reinterpret_cast<uint4*>(tile + qt_at(rl, cl));
     t4[0] = v[0]; t4[1] = v[1]; t4[2] = v[2]; t4[3] = v[3];
   }
-  __syncthreads();
+  lds_barrier();   // the tile is in LDS (the row-form stores need not have landed)
   const int cc = tid >> 1;
   const int rb = tid & 1;
   const int col = c0 + cc;
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(256) void scale_pack_kernel(ScalePackBatch B) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) t32[q] = w[q];
   }
-  __syncthreads();
+  lds_barrier();
   const int kb4 = (p.kb + 3) / 4;
   uint32_t* dst = p.dst + int64_t(b) * kb4 * p.rows;
 #pragma unroll

@@ -130,10 +130,10 @@ __global__ __launch_bounds__(256, 4) void swiglu_bwd_kernel(SwigluBwdParams p) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const float* src = h == 0 ? dg : du;
-      __syncthreads();                       // the previous readers of sv are done
+      lds_barrier();                         // the previous readers of sv are done
 #pragma unroll
       for (int j = 0; j < 32; ++j) sv[sb_at(rl, hh * 32 + j)] = src[j];
-      __syncthreads();
+      lds_barrier();                         // (stores in flight may stay so)
       const int fc = f0 + c;
       if (fc < F && rr < p.R) {              // R is a multiple of 32: the block's rows exist
         float v[32];
