@@ -94,6 +94,16 @@ __device__ __forceinline__ U32Pair permlane16_swap(uint32_t a, uint32_t b) {
 // barrier; the asm "memory" clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// The scale bytes of the 4 lanes of a quad, lane 4q + i in byte i (every lane of the quad
+// gets the dword; all four lanes must be active)
+__device__ __forceinline__ uint32_t quad_bytes(uint32_t s) {
+  const uint32_t s0 = uint32_t(__builtin_amdgcn_mov_dpp(int(s), 0x00, 0xf, 0xf, false));   // quad_perm 0,0,0,0
+  const uint32_t s1 = uint32_t(__builtin_amdgcn_mov_dpp(int(s), 0x55, 0xf, 0xf, false));   // 1,1,1,1
+  const uint32_t s2 = uint32_t(__builtin_amdgcn_mov_dpp(int(s), 0xAA, 0xf, 0xf, false));   // 2,2,2,2
+  const uint32_t s3 = uint32_t(__builtin_amdgcn_mov_dpp(int(s), 0xFF, 0xf, 0xf, false));   // 3,3,3,3
+  return (s0 & 0xffu) | ((s1 & 0xffu) << 8) | ((s2 & 0xffu) << 16) | (s3 << 24);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));

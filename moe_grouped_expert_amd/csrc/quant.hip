@@ -47,16 +47,6 @@ __device__ __forceinline__ uint32_t quant32(const uint32_t* w, uint32_t* out) {
   return s;
 }
 
-// The scale bytes of the 4 lanes of a quad, lane 4q + i in byte i (every lane of the quad
-// gets the dword; all four lanes must be active)
-__device__ __forceinline__ uint32_t quad_bytes(uint32_t s) {
-  const uint32_t s0 = uint32_t(__builtin_amdgcn_mov_dpp(int(s), 0x00, 0xf, 0xf, false));   // quad_perm 0,0,0,0
-  const uint32_t s1 = uint32_t(__builtin_amdgcn_mov_dpp(int(s), 0x55, 0xf, 0xf, false));   // 1,1,1,1
-  const uint32_t s2 = uint32_t(__builtin_amdgcn_mov_dpp(int(s), 0xAA, 0xf, 0xf, false));   // 2,2,2,2
-  const uint32_t s3 = uint32_t(__builtin_amdgcn_mov_dpp(int(s), 0xFF, 0xf, 0xf, false));   // 3,3,3,3
-  return (s0 & 0xffu) | ((s1 & 0xffu) << 8) | ((s2 & 0xffu) << 16) | (s3 << 24);
-}
-
 template <bool MX>
 __global__ __launch_bounds__(QT_THREADS) void quant_tile_kernel(QuantTileParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[QT_ROWS * QT_LDS_STRIDE + (QT_ROWS / 32) * QT_GRP];
