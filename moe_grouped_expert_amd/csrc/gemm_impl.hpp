@@ -663,15 +663,19 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
           if (fb0 >= F) return;
           const int f = fb0 + l32;
           auto lrow = [&](int r) { return rb + 8 * (r >> 2) + 4 * hi + (r & 3); };
-          // Neighbouring lanes (columns c, c+1) swap one value by DPP so that a lane holds
-          // one row x two columns instead of two rows x one column: bf16 pairs then leave
-          // as dword stores (even lane: row r, odd lane: row r + 1, columns c & ~1, +1).
+          // Neighbouring lanes (columns c, c+1) trade halves so that a lane holds one row x
+          // two columns instead of two rows x one column: bf16 pairs then leave as dword
+          // stores (even lane: row r, odd lane: row r + 1, columns c & ~1, +1).  A lane
+          // packs its rows (r, r + 1) as one dword, reads its neighbour's by DPP and picks
+          // the halves with one byte permute (even: own low, neighbour's low; odd:
+          // neighbour's high, own high).
           const bool odd = (l32 & 1) != 0;
           const int fpair = f & ~1;
+          const uint32_t psel = odd ? 0x03020706u : 0x05040100u;
           auto pair2 = [&](float v0, float v1) {
-            const float send = odd ? v0 : v1;
-            const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xf, 0xf, false));
-            return bf16x2(odd ? recv : v0, odd ? v1 : recv);
+            const uint32_t own = bf16x2(v0, v1);
+            const uint32_t nb = uint32_t(__builtin_amdgcn_mov_dpp(int(own), 0xB1, 0xf, 0xf, false));
+            return __builtin_amdgcn_perm(nb, own, psel);
           };
           float h[16];
 #pragma unroll
