@@ -218,8 +218,9 @@ mge_status grouped_mlp_fwd(const mge_fwd_args* args, void* stream);
  * moe_route_permute.  BF16: the weights are the bf16 masters (w_gate_up[e] [2F][H],
  * w_down[e] [H][F]); h_col/x_col are the bf16 transposes.
  * Outputs: dx_perm bf16 [R][H] (valid rows), dw_gate_up[e] [2F][H] and dw_down[e]
- * [H][F] (fp32; accumulate != 0 adds to them instead of overwriting; experts with no
- * tokens get zeros), d_prob f32 [T][k].  The intermediates (dY row/col, dGU row/col)
+ * [H][F], fp32 (dw_bf16 = 0, the default) or bf16 (dw_bf16 = 1: rounded to nearest even
+ * from the fp32 sums); accumulate != 0 adds to fp32 outputs instead of overwriting and is
+ * rejected with bf16 ones; experts with no tokens get zeros; d_prob f32 [T][k].  The intermediates (dY row/col, dGU row/col)
  * go to the optional buffers when given, else to the workspace; dh (fp32 [R][F]) and
  * the d_prob partial sums (one per row and 256-column group of F, summed in a fixed
  * order) always live in the workspace.
@@ -241,8 +242,8 @@ typedef struct mge_bwd_args {
   const void* const* w_down;             /* [host] E: MXFP8 col codes [F][H] / BF16 masters [H][F] */
   const uint8_t* const* w_down_scale;    /* [host] E: [F][H/32] (MXFP8) */
   uint16_t* dx_perm;                     /* [R][H] bf16 */
-  float* const* dw_gate_up;              /* [host] E pointers, [2F][H] f32 */
-  float* const* dw_down;                 /* [host] E pointers, [H][F] f32 */
+  void* const* dw_gate_up;               /* [host] E pointers, [2F][H] f32 (bf16 with dw_bf16) */
+  void* const* dw_down;                  /* [host] E pointers, [H][F] f32 (bf16 with dw_bf16) */
   float* d_prob;                         /* [T][k] */
   int32_t accumulate;
   /* optional intermediates (NULL -> workspace) */
@@ -252,6 +253,9 @@ typedef struct mge_bwd_args {
   void* dgu_col; uint8_t* dgu_col_scale; /* [2F][R] */
   void* workspace;
   size_t workspace_bytes;
+  /* added after the first version of the struct: a struct_size that ends before it
+     means 0 */
+  int32_t dw_bf16;                       /* 0: dW in fp32; 1: dW in bf16 (no accumulate) */
 } mge_bwd_args;
 
 size_t mge_bwd_workspace_bytes(const mge_bwd_args* args);

@@ -63,7 +63,7 @@ class BwdArgs(C.Structure):
                 ("accumulate", i32),
                 ("dy_row", vp), ("dy_row_scale", vp), ("dy_col", vp), ("dy_col_scale", vp),
                 ("dgu_row", vp), ("dgu_row_scale", vp), ("dgu_col", vp), ("dgu_col_scale", vp),
-                ("workspace", vp), ("workspace_bytes", C.c_size_t)]
+                ("workspace", vp), ("workspace_bytes", C.c_size_t), ("dw_bf16", i32)]
 
 
 class CombineArgs(C.Structure):
@@ -349,8 +349,11 @@ class BwdOut:
 
 def grouped_mlp_bwd(dy: torch.Tensor, rt: RouteOut, fw: FwdOut, w_gate_up_k, w_down_k, w_gate_up_k_scale=None,
                     w_down_k_scale=None, accumulate: bool = False, keep_intermediates: bool = False,
-                    out: Optional[BwdOut] = None) -> BwdOut:
-    """Backward of the grouped MLP.  Weights: MXFP8 column forms, or the bf16 masters."""
+                    out: Optional[BwdOut] = None, dw_dtype: str = "f32") -> BwdOut:
+    """Backward of the grouped MLP.  Weights: MXFP8 column forms, or the bf16 masters.
+    dw_dtype: "f32" (default) or "bf16" (the fp32 sums rounded to nearest even; no accumulate)."""
+    if dw_dtype not in ("f32", "bf16"):
+        raise ValueError(f"dw_dtype must be 'f32' or 'bf16', not {dw_dtype!r}")
     E, H, R, T, k = rt.E, rt.H, rt.R, rt.T, rt.k
     mx = rt.prec == "mxfp8"
     wg = _split(w_gate_up_k, E)
@@ -359,9 +362,10 @@ def grouped_mlp_bwd(dy: torch.Tensor, rt: RouteOut, fw: FwdOut, w_gate_up_k, w_d
     dev = dy.device
     if out is None:
         f32 = dict(device=dev, dtype=torch.float32)
+        dwt = dict(device=dev, dtype=torch.float32 if dw_dtype == "f32" else torch.bfloat16)
         o = BwdOut(dx_perm=torch.empty((R, H), device=dev, dtype=torch.bfloat16),
-                   dw_gate_up=[torch.empty((2 * F, H), **f32) for _ in range(E)],
-                   dw_down=[torch.empty((H, F), **f32) for _ in range(E)],
+                   dw_gate_up=[torch.empty((2 * F, H), **dwt) for _ in range(E)],
+                   dw_down=[torch.empty((H, F), **dwt) for _ in range(E)],
                    d_prob=torch.empty((T, k), **f32))
         if keep_intermediates:
             cd = torch.uint8 if mx else torch.bfloat16
@@ -394,6 +398,7 @@ def grouped_mlp_bwd(dy: torch.Tensor, rt: RouteOut, fw: FwdOut, w_gate_up_k, w_d
         a.w_gate_up_scale, a.w_down_scale = C.cast(keep[4], vp), C.cast(keep[5], vp)
     a.dx_perm, a.d_prob = _ptr(o.dx_perm), _ptr(o.d_prob)
     a.accumulate = 1 if accumulate else 0
+    a.dw_bf16 = 1 if dw_dtype == "bf16" else 0
     a.dy_row, a.dy_row_scale, a.dy_col, a.dy_col_scale = _ptr(o.dy_row), _ptr(o.dy_row_scale), _ptr(o.dy_col), _ptr(o.dy_col_scale)
     a.dgu_row, a.dgu_row_scale = _ptr(o.dgu_row), _ptr(o.dgu_row_scale)
     a.dgu_col, a.dgu_col_scale = _ptr(o.dgu_col), _ptr(o.dgu_col_scale)

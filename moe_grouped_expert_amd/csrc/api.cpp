@@ -1,6 +1,7 @@
 // C ABI entry points: argument checks, workspace carving and the launch sequence of
 // each call.  Every check runs before the first launch; nothing here synchronizes
 // except mge_check_device_errors.
+#include <cstddef>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -445,7 +446,13 @@ size_t mge_bwd_workspace_bytes(const mge_bwd_args* a) {
 mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
   g_err[0] = 0;
   MGE_REQUIRE(a != nullptr, "args is NULL");
-  MGE_REQUIRE(a->struct_size == sizeof(mge_bwd_args), "struct_size mismatch");
+  // the first version of the struct ended before dw_bf16
+  MGE_REQUIRE(a->struct_size == sizeof(mge_bwd_args) || a->struct_size == offsetof(mge_bwd_args, dw_bf16),
+              "struct_size mismatch");
+  const bool dw_bf16 = a->struct_size == sizeof(mge_bwd_args) && a->dw_bf16 != 0;
+  MGE_REQUIRE(a->struct_size < sizeof(mge_bwd_args) || a->dw_bf16 == 0 || a->dw_bf16 == 1,
+              "dw_bf16 must be 0 or 1 (got %d)", a->dw_bf16);
+  MGE_REQUIRE(!(dw_bf16 && a->accumulate), "accumulate needs fp32 dW outputs");
   mge_status st = check_mlp_dims(a->prec, a->E, a->H, a->F, a->T, a->k, a->align);
   if (st != MGE_OK) return st;
   const bool mx = a->prec == MGE_PREC_MXFP8;
@@ -627,7 +634,7 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
     g.A = static_cast<const uint8_t*>(dyc); g.lda = int64_t(R) * elem; g.Asp = dyc_p; g.asp_ld = H; g.asp_bytes = packed_exact(1, H, R / 32);
     g.B = static_cast<const uint8_t*>(a->h_col); g.ldb = int64_t(R) * elem; g.Bsp = hc_p; g.bsp_ld = F; g.bsp_bytes = packed_exact(1, F, R / 32);
     g.M = H; g.N = F;
-    g.out_dtype = MGE_DTYPE_F32; g.Ct = reinterpret_cast<void* const*>(tab + 4 * E); g.ldc = F;
+    g.out_dtype = dw_bf16 ? MGE_DTYPE_BF16 : MGE_DTYPE_F32; g.Ct = reinterpret_cast<void* const*>(tab + 4 * E); g.ldc = F;
     g.accumulate = a->accumulate;
     g.tiles_upper = gemm_tiles_upper(g, rows_bound);
     g.role = GEMM_DW_DOWN;
@@ -657,7 +664,7 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
     g.A = static_cast<const uint8_t*>(dgc); g.lda = int64_t(R) * elem; g.Asp = dgc_p; g.asp_ld = F2; g.asp_bytes = packed_exact(1, F2, R / 32);
     g.B = static_cast<const uint8_t*>(a->x_col); g.ldb = int64_t(R) * elem; g.Bsp = xc_p; g.bsp_ld = H; g.bsp_bytes = packed_exact(1, H, R / 32);
     g.M = F2; g.N = H;
-    g.out_dtype = MGE_DTYPE_F32; g.Ct = reinterpret_cast<void* const*>(tab + 5 * E); g.ldc = H;
+    g.out_dtype = dw_bf16 ? MGE_DTYPE_BF16 : MGE_DTYPE_F32; g.Ct = reinterpret_cast<void* const*>(tab + 5 * E); g.ldc = H;
     g.accumulate = a->accumulate;
     g.tiles_upper = gemm_tiles_upper(g, rows_bound);
     g.role = GEMM_DW_GATEUP;

@@ -17,11 +17,13 @@ MGE_GEMM_KERNEL(gemm_dw_down_bf16, EPI_STORE, RAGGED_K, OUT_F32)
 MGE_GEMM_KERNEL(gemm_dw_down_acc_bf16, EPI_STORE, RAGGED_K, OUT_F32_ACC)
 MGE_GEMM_KERNEL(gemm_dw_gateup_bf16, EPI_STORE, RAGGED_K, OUT_F32)
 MGE_GEMM_KERNEL(gemm_dw_gateup_acc_bf16, EPI_STORE, RAGGED_K, OUT_F32_ACC)
+MGE_GEMM_KERNEL(gemm_dw_down_bf16out_bf16, EPI_STORE, RAGGED_K, OUT_BF16)
+MGE_GEMM_KERNEL(gemm_dw_gateup_bf16out_bf16, EPI_STORE, RAGGED_K, OUT_BF16)
 
 #undef MGE_GEMM_KERNEL
 
 // Kernel of a role; the output dtype and the accumulate flag were checked by
-// launch_gemm (DOWN: bf16 or f32; DH, DW: f32; DX: bf16).
+// launch_gemm (DOWN, DW: bf16 or f32, accumulate only f32; DH: f32; DX: bf16).
 mge_status launch_gemm_bf16(const GemmParams& p, hipStream_t s) {
   const bool f32 = p.out_dtype == MGE_DTYPE_F32;
   switch (p.role) {
@@ -32,9 +34,11 @@ mge_status launch_gemm_bf16(const GemmParams& p, hipStream_t s) {
     case GEMM_DH: return launch_gemm_kernel(gemm_dh_bf16, "gemm_dh_bf16", p, s);
     case GEMM_DX: return launch_gemm_kernel(gemm_dx_bf16, "gemm_dx_bf16", p, s);
     case GEMM_DW_DOWN:
+      if (!f32) return launch_gemm_kernel(gemm_dw_down_bf16out_bf16, "gemm_dw_down_bf16", p, s);
       return p.accumulate ? launch_gemm_kernel(gemm_dw_down_acc_bf16, "gemm_dw_down_bf16", p, s)
                           : launch_gemm_kernel(gemm_dw_down_bf16, "gemm_dw_down_bf16", p, s);
     case GEMM_DW_GATEUP:
+      if (!f32) return launch_gemm_kernel(gemm_dw_gateup_bf16out_bf16, "gemm_dw_gateup_bf16", p, s);
       return p.accumulate ? launch_gemm_kernel(gemm_dw_gateup_acc_bf16, "gemm_dw_gateup_bf16", p, s)
                           : launch_gemm_kernel(gemm_dw_gateup_bf16, "gemm_dw_gateup_bf16", p, s);
   }

@@ -24,10 +24,10 @@ mge_status launch_gemm(const GemmParams& p, int prec, hipStream_t s) {
     return MGE_ERR_INVALID_ARG;
   }
   if (p.role != GEMM_GATEUP) {
-    const bool ok = p.role == GEMM_DOWN ? (p.out_dtype == MGE_DTYPE_BF16 || p.out_dtype == MGE_DTYPE_F32)
+    const bool ok = (p.role == GEMM_DOWN || k_mode) ? (p.out_dtype == MGE_DTYPE_BF16 || p.out_dtype == MGE_DTYPE_F32)
                     : p.role == GEMM_DX ? p.out_dtype == MGE_DTYPE_BF16
                                         : p.out_dtype == MGE_DTYPE_F32;
-    if (!ok || (p.accumulate && !k_mode)) {
+    if (!ok || (p.accumulate && (!k_mode || p.out_dtype != MGE_DTYPE_F32))) {
       set_error("GEMM role %d: output dtype %d / accumulate %d not supported", p.role, p.out_dtype, p.accumulate);
       return MGE_ERR_INVALID_ARG;
     }

@@ -8,6 +8,9 @@
 * The backward's accumulate flag: a second call with accumulate adds the same
   gradient again, so dW must be exactly twice the first call's (x + x is exact in
   fp32), and experts without tokens keep whatever their buffers held.
+* bf16 weight gradients: the same K loop as the fp32 ones with a rounding epilogue, so
+  they must equal the fp32 call's dW rounded to nearest even, bit for bit; accumulate
+  with bf16 outputs is rejected.
 """
 import numpy as np
 import pytest
@@ -136,3 +139,34 @@ def test_bwd_accumulate(m, prec):
         else:
             assert torch.equal(b2.dw_gate_up[e], 2.0 * first_gu[e]), e
             assert torch.equal(b2.dw_down[e], 2.0 * first_d[e]), e
+
+
+@pytest.mark.parametrize("prec", ["bf16", "mxfp8"])
+def test_bwd_bf16_dw(m, prec):
+    from tests.gpu_helpers import Inputs, say
+    w = synth.custom(140, T=400, E=5, H=128, F=160, k=2, prec=prec)
+    say("[gpu] backward bf16 dW", prec)
+    l = synth.logits(w)
+    l[:, 3] = -1e30                  # expert 3 gets no tokens
+    inp = Inputs(w, logits=l)
+    g = m.moe_route_permute(inp.g_logits, inp.g_x, w.k, align=32, prec=prec, want_col=True)
+    if prec == "mxfp8":
+        wq = m.mxfp8_quantize(inp.g_wgu, "both")
+        dq = m.mxfp8_quantize(inp.g_wd, "both")
+        f = m.grouped_mlp_fwd(g, wq[0], dq[0], wq[1], dq[1], train=True)
+        bw = (wq[2], dq[2], wq[3], dq[3])
+    else:
+        f = m.grouped_mlp_fwd(g, inp.g_wgu, inp.g_wd, train=True)
+        bw = (inp.g_wgu, inp.g_wd)
+    b32 = m.grouped_mlp_bwd(inp.g_dy, g, f, *bw)
+    b16 = m.grouped_mlp_bwd(inp.g_dy, g, f, *bw, dw_dtype="bf16")
+    torch.cuda.synchronize()
+    for e in range(w.E):
+        assert b16.dw_gate_up[e].dtype == torch.bfloat16 and b16.dw_down[e].dtype == torch.bfloat16
+        assert torch.equal(b16.dw_gate_up[e], b32.dw_gate_up[e].to(torch.bfloat16)), e
+        assert torch.equal(b16.dw_down[e], b32.dw_down[e].to(torch.bfloat16)), e
+    assert not torch.any(b16.dw_gate_up[3]) and not torch.any(b16.dw_down[3])
+    valid = g.perm_src >= 0          # dx_perm defines the valid rows only
+    assert torch.equal(b16.dx_perm[valid], b32.dx_perm[valid]) and torch.equal(b16.d_prob, b32.d_prob)
+    with pytest.raises(m.MgeError):
+        m.grouped_mlp_bwd(inp.g_dy, g, f, *bw, accumulate=True, out=b16, dw_dtype="bf16")
