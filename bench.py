@@ -135,11 +135,6 @@ def kernel_work(name, w, R):
         # averaged per launch: bf16 read, row and (training) column forms written
         forms = 2 if w.backward else 1
         return "byte", 1.5 * E * H * F * (2.0 + forms * mxb)
-    if name in ("swiglu_bwd_mx", "swiglu_bwd_bf16"):
-        # per real (row, ffn column): dh f32 and G, U bf16 read; dG, dU written in row
-        # and column forms (MXFP8 codes + scale share, or bf16)
-        out = 2 * 2 * (mxb if name.endswith("_mx") else 2.0)
-        return "byte", float(M) * F * (4.0 + 4.0 + out) + 8.0 * R
     if name == "combine":
         return "byte", 2.0 * k * T * H + 2.0 * T * H + 4.0 * T * k
     if name in ("route_topk", "route_scatter"):

@@ -221,9 +221,9 @@ mge_status grouped_mlp_fwd(const mge_fwd_args* args, void* stream);
  * [H][F], fp32 (dw_bf16 = 0, the default) or bf16 (dw_bf16 = 1: rounded to nearest even
  * from the fp32 sums); accumulate != 0 adds to fp32 outputs instead of overwriting and is
  * rejected with bf16 ones; experts with no tokens get zeros; d_prob f32 [T][k].  The intermediates (dY row/col, dGU row/col)
- * go to the optional buffers when given, else to the workspace; dh (fp32 [R][F]) and
- * the d_prob partial sums (one per row and 256-column group of F, summed in a fixed
- * order) always live in the workspace.
+ * go to the optional buffers when given, else to the workspace; dh never leaves the dh
+ * GEMM (the SwiGLU backward is its epilogue), and the d_prob partial sums (one per row
+ * and 128-column span of F, summed in a fixed order) always live in the workspace.
  * ---------------------------------------------------------------------------- */
 typedef struct mge_bwd_args {
   uint32_t struct_size;

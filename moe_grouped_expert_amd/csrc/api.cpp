@@ -418,8 +418,7 @@ static size_t bwd_ws(const mge_bwd_args* a, int R) {
   const bool mx = a->prec == MGE_PREC_MXFP8;
   const size_t H = a->H, F = a->F, E = a->E, F2 = 2 * F;
   size_t n = up256(6 * E * sizeof(void*));
-  n += up256(size_t(R) * swiglu_bwd_nparts(int(F)) * sizeof(float));   // d_prob partials per permuted row
-  n += up256(size_t(R) * F * sizeof(float));             // dh (fp32)
+  n += up256(size_t(R) * dh_swiglu_nparts(int(F)) * sizeof(float));   // d_prob partials per permuted row
   auto mat = [&](size_t rows, size_t cols) {
     return mx ? up256(rows * cols) + up256(rows * (cols / 32)) : up256(rows * cols * 2);
   };
@@ -490,9 +489,8 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
   const int elem = mx ? 1 : 2;
   Carve ws(a->workspace);
   void** tab = static_cast<void**>(ws.take(6 * size_t(E) * sizeof(void*)));
-  const int nparts = swiglu_bwd_nparts(a->F);
+  const int nparts = dh_swiglu_nparts(a->F);
   float* dprob_part = static_cast<float*>(ws.take(size_t(R) * nparts * sizeof(float)));
-  float* dh = static_cast<float*>(ws.take(size_t(R) * F * sizeof(float)));
   auto mat = [&](void* given, uint8_t* given_s, size_t rows, size_t cols, void** c, uint8_t** sc) {
     if (given) { *c = given; *sc = given_s; return; }
     if (mx) { *c = ws.take(rows * cols); *sc = static_cast<uint8_t*>(ws.take(rows * (cols / 32))); }
@@ -592,8 +590,8 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
     st = flush_packs();
     if (st != MGE_OK) return st;
   }
-  // b2: dh = dY W_down (fp32), then the SwiGLU backward with the saved G, U and p:
-  // dGU in row and column forms and the d_prob row sums
+  // b2: dh = dY W_down, with the SwiGLU backward as the GEMM's epilogue (the saved G, U
+  // and p): dGU in row and column forms and the d_prob partial row sums
   {
     GemmParams g{};
     g.mode = RAGGED_M; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
@@ -602,25 +600,25 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
     g.Bsp = wdc_p; g.bsp_ld = F; g.bsp_estride = scale_pack_dwords(F, H / 32);
     g.bsp_bytes = packed_exact(E, F, H / 32);
     g.ldb = int64_t(H) * elem;
-    g.N = F; g.K = H; g.F = F;
-    g.out_dtype = MGE_DTYPE_F32; g.C = dh; g.ldc = F;
+    g.N = F; g.K = H; g.F = F; g.Rp = R;
+    g.out_dtype = MGE_DTYPE_F32;
+    g.prob = a->prob_perm;
+    g.gu_in = a->saved_gu;
+    if (mx) {
+      g.dgu_row_codes = static_cast<uint8_t*>(dgr); g.dgu_row_scales = dgrs;
+      g.dgu_col_codes = static_cast<uint8_t*>(dgc); g.dgu_col_scales = dgcs;
+    } else {
+      g.dgu_row_bf16 = static_cast<uint16_t*>(dgr); g.dgu_col_bf16 = static_cast<uint16_t*>(dgc);
+    }
+    g.dprob_part = dprob_part; g.dprob_nparts = nparts;
     g.tiles_upper = gemm_tiles_upper(g, rows_bound);
     g.role = GEMM_DH;
     st = launch_gemm(g, a->prec, s);
     if (st != MGE_OK) return st;
-    SwigluBwdParams q{};
-    q.R = R; q.F = F; q.Rp = R;
-    q.dh = dh; q.gu = a->saved_gu; q.prob = a->prob_perm; q.perm_src = a->perm_src;
-    if (mx) { q.row_codes = static_cast<uint8_t*>(dgr); q.row_scales = dgrs; q.col_codes = static_cast<uint8_t*>(dgc); q.col_scales = dgcs; }
-    else { q.row_bf16 = static_cast<uint16_t*>(dgr); q.col_bf16 = static_cast<uint16_t*>(dgc); }
-    q.dprob_part = dprob_part;
-    q.nparts = nparts;
-    st = launch_swiglu_bwd(q, mx, s);
-    if (st != MGE_OK) return st;
   }
   if (mx) {
     pack(dgrs, nullptr, 1, R, F2 / 32, nullptr, dgr_p);
-    pack(dgcs, nullptr, 1, F2, R / 32, nullptr, dgc_p);
+    pack(dgcs, nullptr, 1, F2, R / 32, rows_written, dgc_p);
     st = flush_packs();
     if (st != MGE_OK) return st;
   }

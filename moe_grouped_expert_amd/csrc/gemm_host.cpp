@@ -23,10 +23,19 @@ mge_status launch_gemm(const GemmParams& p, int prec, hipStream_t s) {
     set_error("GEMM role %d does not match mode %d", p.role, p.mode);
     return MGE_ERR_INVALID_ARG;
   }
-  if (p.role != GEMM_GATEUP) {
+  if (p.role == GEMM_DH) {
+    // SwiGLU-backward epilogue: N is F; a wave's 128 rows of [G U] and [dG dU] are
+    // addressed with 32-bit offsets
+    if (p.gu_in == nullptr || p.N != p.F || int64_t(p.F) * 4 * 2 * G_BM >= (int64_t(1) << 31) || p.F % 32 != 0 ||
+        p.Rp % 32 != 0 || p.prob == nullptr || p.dprob_part == nullptr || p.dprob_nparts != dh_swiglu_nparts(p.F) ||
+        (prec == MGE_PREC_MXFP8 ? (!p.dgu_row_codes || !p.dgu_row_scales || !p.dgu_col_codes || !p.dgu_col_scales)
+                                : (!p.dgu_row_bf16 || !p.dgu_col_bf16))) {
+      set_error("dh GEMM with the SwiGLU-backward epilogue: inconsistent parameters (F %d, N %d)", p.F, p.N);
+      return MGE_ERR_INVALID_ARG;
+    }
+  } else if (p.role != GEMM_GATEUP) {
     const bool ok = (p.role == GEMM_DOWN || k_mode) ? (p.out_dtype == MGE_DTYPE_BF16 || p.out_dtype == MGE_DTYPE_F32)
-                    : p.role == GEMM_DX ? p.out_dtype == MGE_DTYPE_BF16
-                                        : p.out_dtype == MGE_DTYPE_F32;
+                                                    : p.out_dtype == MGE_DTYPE_BF16;   // DX
     if (!ok || (p.accumulate && (!k_mode || p.out_dtype != MGE_DTYPE_F32))) {
       set_error("GEMM role %d: output dtype %d / accumulate %d not supported", p.role, p.out_dtype, p.accumulate);
       return MGE_ERR_INVALID_ARG;

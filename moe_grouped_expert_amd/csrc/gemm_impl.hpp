@@ -19,10 +19,11 @@
 //          byte chosen by op_sel.
 //   BF16:  v_mfma_f32_32x32x16_bf16
 // Operands stream HBM -> LDS directly (buffer_load ... lds, no register staging) in
-// 64-byte K slices (64 FP8 or 32 BF16 elements) through a ring of 4 LDS stages, three
-// slices in flight while one is multiplied.  LDS rows are 64 bytes with the 16-byte
-// chunks XOR-swizzled by row so the MFMA fragment reads spread over the 64 banks.  The
-// MX scales of a slice ride along into LDS (packed: one dword = 4 blocks of a row).
+// 128-byte K slices (128 FP8 or 64 BF16 elements) through 2 LDS stages of 64 KB; a
+// stage is refilled as soon as every wave has read its fragments, so a slice has one
+// and a half iterations to arrive.  LDS rows are 128 bytes with the 16-byte chunks
+// XOR-swizzled by row so the MFMA fragment reads spread over the 64 banks.  The MX
+// scales of a slice ride along into LDS (packed: one dword = 4 blocks of a row).
 // A persistent grid walks the tiles (expert-major, then bands of 8 M-tiles walked across
 // N with M fastest, so that the 32 tiles an XCD runs at once are an 8 x 4 block sharing
 // A and B tiles in its L2); virtual workgroup ids are remapped so
@@ -40,6 +41,9 @@
 //                   one 32-column block) or rounded to bf16; training also stores G, U
 //                   (bf16) and the column form of h (blocks of 32 rows: 16 in a lane,
 //                   16 in its partner lane 32 apart)
+//   EPI_SWIGLU_BWD  dh = dY W_down stays in the accumulators; G, U of the same rows and
+//                   columns come in by LDS DMA, and dG, dU (row and column forms, as
+//                   above) and the d_prob partial row sums leave
 #pragma once
 
 #include "mge_common.hpp"
@@ -442,7 +446,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
 
   Tile cur = decode(vid);
   // next-tile slices issued before the epilogue (see there)
-  constexpr int G_PREFETCH = OUT == OUT_F32_ACC ? 0 : 1;
+  constexpr int G_PREFETCH = (OUT == OUT_F32_ACC || EPI == EPI_SWIGLU_BWD) ? 0 : 1;
   int cur_issued = 0;   // slices of `cur` (from 0) already on their way into their stages
   for (int tile = vid; tile < total; tile += nwg) {
     rederive_lane();
@@ -451,7 +455,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
     // SwiGLU: the probability of tile row tid, loaded now so that its latency hides
     // behind the K loop (it is staged in LDS for the epilogue)
     float my_prob = 0.f;
-    if constexpr (EPI == EPI_SWIGLU) {
+    if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD) {
       if (m0 + tid < m_valid) my_prob = p.prob[off + m0 + tid];
     }
 
@@ -754,6 +758,169 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
           __builtin_amdgcn_sched_barrier(0);   // one block at a time (register peak)
         });
       });
+    } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+      // dh = dY W_down sits in the accumulators: lane (hi, l32) of block (mi, ni) holds ffn
+      // column fw0 + 32 ni + l32 of span rows 32 mi + 8 (r/4) + 4 hi + r%4.  Per 32-row
+      // block, G and U of the wave's 32 rows x 128 columns come into this wave's share of
+      // the (now idle) stage memory by LDS DMA, two buffers so that block mi + 1 streams in
+      // while mi is processed.  Then dU = dh p silu(G), dG = dh p U silu'(G) and the row
+      // sums of dh silu(G) U (d_prob), with dG (columns f) and dU (columns F + f) written in
+      // row form (32-column blocks: the half-wave reduce-scatter of the forward) and column
+      // form (32-row blocks: 16 rows in a lane, 16 in the lane 32 apart), MXFP8 or bf16.
+      s_prob[tid] = my_prob;
+      lds_barrier();
+      const int F = p.F, F2 = 2 * F;
+      int vr = m_valid - wrow0;                         // valid rows of the wave's span
+      vr = uniform(vr < 0 ? 0 : (vr > G_WMB * 32 ? G_WMB * 32 : vr));
+      const int64_t grow0 = int64_t(off) + wrow0;       // permuted row of span row 0
+      const int fw0 = nt * G_BN + wn * (G_WNB * 32);    // the wave's first ffn column
+      // staging: per buffer G then U, each 8 DMA blocks of 4 rows x 256 bytes, 1088 bytes
+      // apart (rows 4 apart, read by the two half-waves, then fall 16 banks apart)
+      constexpr int GS = 1088, GA = 8 * GS, GB = 2 * GA;
+      static_assert(G_WAVES_M * G_WAVES_N * 2 * GB <= G_DYN_LDS, "G/U staging exceeds the stage memory");
+      const uint32_t wl = lds_base + uint32_t(wave * 2 * GB);
+      const uint8_t* wsm = smem + wave * 2 * GB;
+      const i32x4 rIn = make_rsrc_n(reinterpret_cast<const uint8_t*>(p.gu_in + grow0 * F2), uint32_t(vr) * uint32_t(F2) * 2u);
+      // DMA instruction j of a block: lane L brings row 4j + L/16, columns fw0 + 8 (L%16) ..+7
+      const uint32_t dl = uint32_t(lane >> 4) * uint32_t(F2) * 2u + uint32_t(fw0 + (lane & 15) * 8) * 2u;
+      auto issue_gu = [&](int mi, int buf) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t o = uint32_t(mi * 32 + 4 * j) * uint32_t(F2) * 2u + dl;
+          dma16(rIn, wl + uint32_t(buf * GB + j * GS), o);                      // G
+          dma16(rIn, wl + uint32_t(buf * GB + GA + j * GS), o + uint32_t(F) * 2u);   // U
+        }
+      };
+      auto rsrc = [](const void* base, uint32_t bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kRsrcFlags);
+      };
+      __amdgpu_buffer_rsrc_t rR, rRs;
+      if constexpr (MX) {
+        rR = rsrc(p.dgu_row_codes + grow0 * F2, uint32_t(vr) * F2);
+        rRs = rsrc(p.dgu_row_scales + grow0 * (F2 / 32), uint32_t(vr) * (F2 / 32));
+      } else {
+        rR = rsrc(p.dgu_row_bf16 + grow0 * F2, uint32_t(vr) * F2 * 2);
+        rRs = rR;
+      }
+      const bool odd = (l32 & 1) != 0;
+      const uint32_t psel = odd ? 0x03020706u : 0x05040100u;
+      auto pair2 = [&](float v0, float v1) {
+        const uint32_t own = bf16x2(v0, v1);
+        const uint32_t nb = uint32_t(__builtin_amdgcn_mov_dpp(int(own), 0xB1, 0xf, 0xf, false));
+        return __builtin_amdgcn_perm(nb, own, psel);
+      };
+      if (vr > 0) {                                      // wave-uniform
+      issue_gu(0, 0);
+      issue_gu(1, 1);
+      static_for<0, G_WMB>([&](auto mic) {
+        constexpr int mi = decltype(mic)::value;
+        constexpr int buf = mi & 1;
+        // block mi's G, U have landed (block mi + 1's, the newest 16 operations, may still
+        // be on their way); asm with a memory clobber, so that no LDS read moves above it
+        if constexpr (mi + 1 < G_WMB) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const int rb = mi * 32;                          // block row within the span
+        if (wrow0 + rb < m_valid) {                      // wave-uniform
+          auto lrow = [&](int r) { return rb + 8 * (r >> 2) + 4 * hi + (r & 3); };
+          float pr[16];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 q = *reinterpret_cast<const float4*>(&s_prob[wm * G_WMB * 32 + rb + 8 * g + 4 * hi]);
+            pr[4 * g] = q.x; pr[4 * g + 1] = q.y; pr[4 * g + 2] = q.z; pr[4 * g + 3] = q.w;
+          }
+          float dps[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dps[r] = 0.f;
+          const uint8_t* gs = wsm + buf * GB;
+          static_for<0, G_WNB>([&](auto nic) {
+            constexpr int ni = decltype(nic)::value;
+            const int fb0 = fw0 + ni * 32;                 // first column of the block
+            if (fb0 >= F) return;                          // wave-uniform
+            float dg[16], du[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int rr = 8 * (r >> 2) + 4 * hi + (r & 3);
+              const int lo = (rr >> 2) * GS + (rr & 3) * 256 + (ni * 32 + l32) * 2;
+              const float G = __uint_as_float(uint32_t(*reinterpret_cast<const uint16_t*>(gs + lo)) << 16);
+              const float U = __uint_as_float(uint32_t(*reinterpret_cast<const uint16_t*>(gs + GA + lo)) << 16);
+              const float dh = acc_read(acc[mi][ni][r]);
+              const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-G));
+              const float sl = G * sg;
+              dps[r] += dh * sl * U;
+              du[r] = dh * pr[r] * sl;
+              dg[r] = dh * pr[r] * U * sg * (1.f + G * (1.f - sg));
+            }
+            // both arrays: h = 0 -> dG at column fb0 + l32, h = 1 -> dU at F + fb0 + l32
+            static_for<0, 2>([&](auto hc) {
+              constexpr int h = decltype(hc)::value;
+              const float* v = h == 0 ? dg : du;
+              const int cb = h * F + fb0;                    // first [dG dU] column of the block
+              if constexpr (MX) {
+                float inv[16];
+                const uint32_t sc = row_block_inv16(v, l32, inv);   // sc: row l32 / 2
+                const bool lo2 = (l32 & 2) == 0;
+                const uint32_t sel = odd ? 0x03070105u : 0x06020400u;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                  uint32_t w = e4m3x4(v[4 * g] * inv[4 * g], v[4 * g + 1] * inv[4 * g + 1], v[4 * g + 2] * inv[4 * g + 2],
+                                      v[4 * g + 3] * inv[4 * g + 3]);
+                  const uint32_t x = uint32_t(__builtin_amdgcn_mov_dpp(int(w), 0x4E, 0xf, 0xf, false));
+                  w = lo2 ? ((w & 0xffffu) | (x << 16)) : ((x >> 16) | (w & 0xffff0000u));
+                  const uint32_t y = uint32_t(__builtin_amdgcn_mov_dpp(int(w), 0xB1, 0xf, 0xf, false));
+                  w = __builtin_amdgcn_perm(y, w, sel);
+                  __builtin_amdgcn_raw_buffer_store_b32(w, rR, lrow(4 * g + (l32 & 3)) * F2 + cb + (l32 & ~3), 0, 0);
+                }
+                const uint32_t so = (l32 & 1) == 0 ? uint32_t(lrow(l32 >> 1) * (F2 / 32) + cb / 32) : kInvalid;
+                __builtin_amdgcn_raw_buffer_store_b8(uint8_t(sc), rRs, so, 0, 0);
+                // column form of column cb + l32, rows [rb, rb + 32)
+                const int64_t cbase = int64_t(cb + l32) * p.Rp + grow0 + rb + 16 * hi;
+                float cmax = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) cmax = fmaxf(cmax, fabsf(v[r]));
+                cmax = max_xor32(cmax);
+                const uint32_t s = mx_scale_byte(cmax);
+                const float ic = mx_inv_scale(s);
+                uint32_t c[4];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) c[g] = e4m3x4(v[4 * g] * ic, v[4 * g + 1] * ic, v[4 * g + 2] * ic, v[4 * g + 3] * ic);
+                const U32Pair x02 = permlane32_swap(c[0], c[2]);
+                const U32Pair x13 = permlane32_swap(c[1], c[3]);
+                *reinterpret_cast<uint4*>(p.dgu_col_codes + cbase) = make_uint4(x02.a, x02.b, x13.a, x13.b);
+                if (hi == 0) p.dgu_col_scales[int64_t(cb + l32) * (p.Rp / 32) + (grow0 + rb) / 32] = uint8_t(s);
+              } else {
+                const int cpair = (cb + l32) & ~1;
+#pragma unroll
+                for (int r = 0; r < 16; r += 2)
+                  __builtin_amdgcn_raw_buffer_store_b32(pair2(v[r], v[r + 1]), rR,
+                                                        ((lrow(r) + (odd ? 1 : 0)) * F2 + cpair) * 2, 0, 0);
+                const int64_t cbase = int64_t(cb + l32) * p.Rp + grow0 + rb + 16 * hi;
+                uint32_t c[8];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                  c[2 * g] = bf16x2(v[4 * g], v[4 * g + 1]);
+                  c[2 * g + 1] = bf16x2(v[4 * g + 2], v[4 * g + 3]);
+                }
+                const U32Pair a0 = permlane32_swap(c[0], c[4]), a1 = permlane32_swap(c[1], c[5]);
+                const U32Pair b0 = permlane32_swap(c[2], c[6]), b1 = permlane32_swap(c[3], c[7]);
+                uint4* dst = reinterpret_cast<uint4*>(p.dgu_col_bf16 + cbase);
+                dst[0] = make_uint4(a0.a, a1.a, a0.b, a1.b);
+                dst[1] = make_uint4(b0.a, b1.a, b0.b, b1.b);
+              }
+            });
+            __builtin_amdgcn_sched_barrier(0);   // one block at a time (register peak)
+          });
+          // d_prob partial of each row over the wave's 128 columns: lanes 2k, 2k + 1 hold row k
+          const float ps = row_block_sum16(dps, l32);
+          if ((l32 & 1) == 0 && wrow0 + lrow(l32 >> 1) < m_valid)
+            p.dprob_part[(grow0 + lrow(l32 >> 1)) * p.dprob_nparts + nt * 2 + wn] = ps;
+        }
+        // the buffer takes block mi + 2 once this wave's reads of it have completed
+        if constexpr (mi + 2 < G_WMB) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          issue_gu(mi + 2, buf);
+        }
+      });
+      }
     }
     cur = nxt;
   }

@@ -160,6 +160,27 @@ __device__ __forceinline__ uint32_t row_block_inv16(const float* v, int l32, flo
   return sc;
 }
 
+// The row sums of the same layout (v[r]: row r, one column per lane of the half-wave):
+// the reduce-scatter half of row_block_inv16 with sums, in a fixed order; returns the sum
+// of row l32 / 2 (in lanes 2r and 2r + 1).
+__device__ __forceinline__ float row_block_sum16(const float* v, int l32) {
+  const bool b4 = (l32 & 16) != 0, b3 = (l32 & 8) != 0, b2 = (l32 & 4) != 0, b1 = (l32 & 2) != 0;
+  float m1[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const U32Pair x = permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 8]));
+    m1[i] = __uint_as_float(x.a) + __uint_as_float(x.b);
+  }
+  float m2[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m2[i] = (b3 ? m1[i + 4] : m1[i]) + dpp_f<0x128>(b3 ? m1[i] : m1[i + 4]);
+  float m3[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) m3[i] = (b2 ? m2[i + 2] : m2[i]) + dpp_f<0x141>(b2 ? m2[i] : m2[i + 2]);
+  const float m4 = (b1 ? m3[1] : m3[0]) + dpp_f<0x4E>(b1 ? m3[0] : m3[1]);
+  return m4 + dpp_f<0xB1>(m4);
+}
+
 // max of v over lanes i and i ^ 32
 __device__ __forceinline__ float max_xor32(float v) {
   const U32Pair r = permlane32_swap(__float_as_uint(v), __float_as_uint(v));

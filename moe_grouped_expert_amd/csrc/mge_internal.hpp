@@ -73,24 +73,9 @@ mge_status launch_route(const RouteParams& p, hipStream_t s);
 // ------------------------------------------------------------ combine / reductions
 mge_status launch_combine(int T, int k, int H, int in_dtype, int out_dtype, const void* in,
                           const int32_t* perm_pos, const float* weights, void* out, hipStream_t s);
-// ------------------------------------------------------------ SwiGLU backward (elementwise)
-struct SwigluBwdParams {
-  int R, F, Rp;                          // permuted rows, ffn width, rows of the column form
-  const float* dh;                       // [R][F] fp32 (dY W_down)
-  const uint16_t* gu;                    // saved [R][2F] bf16 (G then U)
-  const float* prob;                     // prob_perm [R]
-  const int32_t* perm_src;               // [R], -1 on padding rows
-  uint8_t* row_codes; uint8_t* row_scales;  // MX dGU row [R][2F], [R][2F/32]
-  uint16_t* row_bf16;                    // bf16 dGU row [R][2F]
-  uint8_t* col_codes; uint8_t* col_scales;  // MX dGU column [2F][Rp], [2F][Rp/32]
-  uint16_t* col_bf16;                    // bf16 dGU transpose [2F][Rp]
-  // [R][nparts]: sum of dh * silu(G) * U over ffn column group j (256 columns) of row m
-  float* dprob_part;
-  int nparts;                            // swiglu_bwd_nparts(F)
-};
-int swiglu_bwd_nparts(int F);
-mge_status launch_swiglu_bwd(const SwigluBwdParams& p, bool mx, hipStream_t s);
-
+// d_prob partials per row written by the dh GEMM's SwiGLU-backward epilogue (one per
+// 128-column span of F: two per 256-column tile)
+inline int dh_swiglu_nparts(int F) { return 2 * ((F + 255) / 256); }
 mge_status launch_dprob_reduce(int T, int k, int nparts, const float* partial, const int32_t* perm_pos,
                                float* d_prob, hipStream_t s);
 // tables[t] (n host pointers each; null tables are skipped) -> dev_table[t * n + i], in as
@@ -99,7 +84,7 @@ mge_status launch_upload_tables(const void* const* const* tables, int ntab, int 
 
 // ------------------------------------------------------------ grouped GEMM
 enum GemmMode { RAGGED_M = 0, RAGGED_K = 1 };
-enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1 };
+enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_BWD = 2 };
 // What a plain-store epilogue writes (a kernel template parameter, so that each kernel
 // carries one store path): none (SwiGLU), bf16, f32, or f32 added to the output.
 enum OutForm { OUT_NONE = 0, OUT_BF16 = 1, OUT_F32 = 2, OUT_F32_ACC = 3 };
@@ -107,7 +92,7 @@ enum OutForm { OUT_NONE = 0, OUT_BF16 = 1, OUT_F32 = 2, OUT_F32_ACC = 3 };
 enum GemmRole {
   GEMM_GATEUP = 0,      // [G U] = X W_gate_up^T, SwiGLU x p epilogue       (RAGGED_M)
   GEMM_DOWN = 1,        // Y = h W_down^T                                   (RAGGED_M)
-  GEMM_DH = 2,          // dh = dY W_down (fp32; the SwiGLU backward runs after it)  (RAGGED_M)
+  GEMM_DH = 2,          // dh = dY W_down, SwiGLU-backward epilogue           (RAGGED_M)
   GEMM_DX = 3,          // dX = dGU W_gate_up                               (RAGGED_M)
   GEMM_DW_DOWN = 4,     // dW_down = dY^T h                                 (RAGGED_K)
   GEMM_DW_GATEUP = 5    // dW_gate_up = dGU^T X                             (RAGGED_K)
@@ -148,6 +133,12 @@ struct GemmParams {
   uint8_t* hc_codes; uint8_t* hc_scales;   // MX h column [F][Rp], [F][Rp/32] (training)
   uint16_t* hc_bf16;                       // bf16 h transpose [F][Rp] (training)
   int Rp;
+  // SwiGLU-backward epilogue (dh GEMM, N = F): G, U from gu_in; dG (columns f) and dU
+  // (columns F + f) of [dG dU] in row and column forms; d_prob partial sums
+  const uint16_t* gu_in;                                                  // saved [R][2F] bf16
+  uint8_t* dgu_row_codes; uint8_t* dgu_row_scales; uint16_t* dgu_row_bf16; // [R][2F], [R][2F/32]
+  uint8_t* dgu_col_codes; uint8_t* dgu_col_scales; uint16_t* dgu_col_bf16; // [2F][Rp], [2F][Rp/32]
+  float* dprob_part; int dprob_nparts;   // [R][nparts]: one sum per (row, 128-column span of F)
   int tiles_upper;                         // host bound on the number of tiles (grid sizing)
 };
 
