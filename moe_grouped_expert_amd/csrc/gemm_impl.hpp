@@ -81,7 +81,8 @@ constexpr uint32_t kInvalid = 0x80000000u;   // OR-ed into an offset: the lane r
 // Cache-policy operand of the buffer builtins: non-temporal (gfx950's nt bit).  Used for
 // output streams that no workgroup of the same kernel reads again, so that they do not
 // evict the operand lines other workgroups of the XCD are about to share from its L2
-// (weight-gradient GEMMs, 256 KB of fp32 per tile: 7% faster on MI355X).
+// (weight-gradient GEMMs, 256 KB of fp32 per tile: 7% faster on MI355X).  Only for
+// whole-line stores: partial lines with the hint measured slower.
 constexpr int kNonTemporal = 2;
 
 static_assert(G_THREADS == 256, "loader assumes 256 threads");
@@ -176,6 +177,15 @@ __device__ __forceinline__ void vm_barrier() {
 // reads it.
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_addr), "v"(voff),
+               "s"(rsrc)
+               : "memory", "m0");
+}
+
+// The same with the non-temporal hint, for data read once (the SwiGLU backward's G and
+// U): it keeps that stream from evicting the K loop's shared operand lines from L2
+// (dh GEMM 3% faster on MI355X).  Partial-line stores with the hint measured slower.
+__device__ __forceinline__ void dma16_nt(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds" ::"s"(lds_addr), "v"(voff),
                "s"(rsrc)
                : "memory", "m0");
 }
@@ -793,8 +803,8 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const uint32_t o = uint32_t(mi * 32 + 4 * j) * uint32_t(F2) * 2u + dl;
-          dma16(rIn, wl + uint32_t(buf * GB + j * GS), o);                      // G
-          dma16(rIn, wl + uint32_t(buf * GB + GA + j * GS), o + uint32_t(F) * 2u);   // U
+          dma16_nt(rIn, wl + uint32_t(buf * GB + j * GS), o);                      // G
+          dma16_nt(rIn, wl + uint32_t(buf * GB + GA + j * GS), o + uint32_t(F) * 2u);   // U
         }
       };
       auto rsrc = [](const void* base, uint32_t bytes) {
