@@ -20,7 +20,8 @@ Sources followed (titles of the pages this is written from):
 
 Modules:
   oracle.mx     — E4M3 / E8M0 encode-decode and block quantization (row / column).
-  oracle.route  — top-k routing, split_sizes, group offsets, stable permutation.
+  oracle.route  — top-k routing, split_sizes, group offsets, stable permutation,
+                  and the router backward (d_logits from d_prob).
   oracle.mlp    — per-token (O-slow) and grouped (O-grouped) forward, backward,
                   and the MXFP8 pipeline stages fed with given quantized operands.
   oracle.metrics— relative Frobenius error.

@@ -93,3 +93,28 @@ def prob_permuted(topk_prob, perm_pos, R: int) -> np.ndarray:
         for i in range(k):
             pp[perm_pos[t, i]] = topk_prob[t, i]
     return pp
+
+
+def router_bwd(topk_idx, topk_prob, d_prob, E: int) -> np.ndarray:
+    """Gradient of the routing probabilities with respect to the router logits.
+
+    The probabilities of a token's k slots are the softmax of the selected logits
+    z_i = l[idx_i] (the reading of [P1] intro / [P4] GroupedLinear used by ``route``),
+    so the chain rule through that softmax gives, with s = sum_j p_j * d_p_j,
+        d_z_i = p_i * (d_p_i - s),
+    and each d_z_i is added to the logit it was gathered from: d_l[t][idx_i] += d_z_i.
+    Logits that no slot selected get 0: the renormalised probabilities do not depend on
+    them.  Indices outside [0, E) contribute nothing.  Returns fp64 [T][E].
+    """
+    idx = np.asarray(topk_idx)
+    p = np.asarray(topk_prob, dtype=np.float64)
+    dp = np.asarray(d_prob, dtype=np.float64)
+    T, k = idx.shape
+    out = np.zeros((T, E), dtype=np.float64)
+    for t in range(T):
+        s = sum(p[t, j] * dp[t, j] for j in range(k))
+        for i in range(k):
+            e = int(idx[t, i])
+            if 0 <= e < E:
+                out[t, e] += p[t, i] * (dp[t, i] - s)
+    return out

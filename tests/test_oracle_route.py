@@ -6,7 +6,10 @@
   E logits renormalised over the selected k (a different formula, same value);
 * split_sizes equal np.bincount and sum to T*k; offsets are multiples of ALIGN;
 * permutation: a bijection on assignments, rows increase within a group, padding is
-  -1, and for ALIGN = 1 it equals np.argsort(expert_of_assignment, kind="stable").
+  -1, and for ALIGN = 1 it equals np.argsort(expert_of_assignment, kind="stable");
+* router backward: central differences of the oracle's own forward routing (selection
+  held fixed), of softmax(l[idx]) with a repeated index, and the invariants (rows sum
+  to 0, zeros off the selection, k = 1 and a constant d_prob give 0).
 """
 import numpy as np
 import pytest
@@ -111,3 +114,77 @@ def test_prob_permuted():
     perm_src, perm_pos = rt.permutation(idx, 2, 1)
     pp = rt.prob_permuted(p, perm_pos, len(perm_src))
     np.testing.assert_allclose(pp[:4], [0.3, 0.6, 0.7, 0.4])
+
+
+# ---------------------------------------------------------------- router backward
+def _fd_token(fwd, l_row, dp_row, h):
+    """Central differences of L(l) = <fwd(l), dp> for one token, one logit at a time."""
+    g = np.zeros_like(l_row)
+    for e in range(l_row.shape[0]):
+        lp, lm = l_row.copy(), l_row.copy()
+        lp[e] += h
+        lm[e] -= h
+        g[e] = (np.dot(fwd(lp), dp_row) - np.dot(fwd(lm), dp_row)) / (2 * h)
+    return g
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (8, 4), (16, 3), (4, 4)])
+def test_router_bwd_matches_finite_differences_of_route(E, k):
+    """d_logits against numerical derivatives of the oracle's own forward routing:
+    the selection and slot order stay fixed under the perturbation (all logits of a
+    token are kept > 1e-3 apart, far above the step)."""
+    rng = np.random.default_rng(100 + E * k)
+    T, h = 24, 1e-6
+    l = rng.standard_normal((T, E))
+    for t in range(T):
+        while np.min(np.diff(np.sort(l[t]))) < 1e-3:
+            l[t] = rng.standard_normal(E)
+    idx, p = rt.route(l, k)
+    dp = rng.standard_normal((T, k))
+    got = rt.router_bwd(idx, p, dp, E)
+    for t in range(T):
+        sel = idx[t].copy()
+        fwd = lambda lr: rt.route(lr[None, :], k)[1][0]
+        g = _fd_token(fwd, l[t], dp[t], h)
+        np.testing.assert_array_equal(rt.route(l[t][None, :], k)[0][0], sel)
+        np.testing.assert_allclose(got[t], g, rtol=0, atol=1e-7)
+
+
+def test_router_bwd_duplicate_slots_sum():
+    """Two slots gathering the same logit: the gradient is the sum over both, as the
+    numerical derivative of softmax(l[idx]) (a forward written here) shows."""
+    rng = np.random.default_rng(7)
+    E, T = 6, 10
+    l = rng.standard_normal((T, E))
+    idx = np.array([[2, 2, 5], [0, 1, 0]] * 5, np.int32)
+
+    def fwd_for(t):
+        def f(lr):
+            z = lr[idx[t]]
+            ez = np.exp(z - z.max())
+            return ez / ez.sum()
+        return f
+
+    p = np.stack([fwd_for(t)(l[t]) for t in range(T)])
+    dp = rng.standard_normal((T, 3))
+    got = rt.router_bwd(idx, p, dp, E)
+    for t in range(T):
+        np.testing.assert_allclose(got[t], _fd_token(fwd_for(t), l[t], dp[t], 1e-6), rtol=0, atol=1e-7)
+
+
+def test_router_bwd_invariants():
+    """Shift invariance of the softmax (each row sums to 0), zeros off the selection,
+    k = 1 and a constant d_prob give no gradient."""
+    rng = np.random.default_rng(3)
+    T, E, k = 40, 8, 3
+    l = rng.standard_normal((T, E))
+    idx, p = rt.route(l, k)
+    dp = rng.standard_normal((T, k))
+    g = rt.router_bwd(idx, p, dp, E)
+    np.testing.assert_allclose(g.sum(axis=1), 0.0, atol=1e-15)
+    for t in range(T):
+        off = np.setdiff1d(np.arange(E), idx[t])
+        assert np.all(g[t, off] == 0.0)
+    i1, p1 = rt.route(l, 1)
+    assert np.all(rt.router_bwd(i1, p1, rng.standard_normal((T, 1)), E) == 0.0)
+    assert np.abs(rt.router_bwd(idx, p, np.full((T, k), 0.37), E)).max() < 1e-16
