@@ -8,7 +8,8 @@ stage in the library's HIP kernels through the C ABI:
   weights (row and column forms, as every training step re-quantizes them) ->
   grouped_mlp_fwd (gate-up GEMM + SwiGLU x prob + quantize-h epilogue, down GEMM) ->
   unpermute_combine -> grouped_mlp_bwd (dy permute + quantize, dh GEMM + SwiGLU
-  backward, d_prob, dW_down, dX, dW_gate_up) -> unpermute_combine of dx.
+  backward, d_prob, dW_down, dX, dW_gate_up) -> unpermute_combine of dx ->
+  moe_router_bwd (d_logits from d_prob).
 
 Default workload: the Mixtral-8x7B-shaped expert layer (8 experts, hidden 4096,
 ffn 14336, top-2) training step in MXFP8 with 16-bit master weights, 8192 tokens.
@@ -84,7 +85,7 @@ class Step:
         self.g = None
         self.wq = self.dq = None
         self.f = self.b = None
-        self.y = self.dx = None
+        self.y = self.dx = self.dl = None
 
     def __call__(self):
         m, w, inp = self.m, self.w, self.inp
@@ -107,6 +108,7 @@ class Step:
             else:
                 self.b = m.grouped_mlp_bwd(inp["dy"], self.g, self.f, inp["wgu"], inp["wd"], out=self.b)
             self.dx = m.unpermute_combine(self.b.dx_perm, self.g.perm_pos, out=self.dx)
+            self.dl = m.moe_router_bwd(self.g.topk_idx, self.g.topk_prob, self.b.d_prob, w.E, out=self.dl)
 
 
 # ------------------------------------------------------------------------------ per-kernel work
@@ -137,6 +139,9 @@ def kernel_work(name, w, R):
         return "byte", 1.5 * E * H * F * (2.0 + forms * mxb)
     if name == "combine":
         return "byte", 2.0 * k * T * H + 2.0 * T * H + 4.0 * T * k
+    if name == "router_bwd":
+        # indices, probabilities and d_prob read once, d_logits written
+        return "byte", 12.0 * T * k + 4.0 * T * E
     if name in ("route_topk", "route_scatter"):
         return "byte", 4.0 * T * E + 8.0 * T * k if name == "route_topk" else 4.0 * T * k * 4
     return None

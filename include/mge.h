@@ -15,6 +15,7 @@
  *   grouped_mlp_bwd     dy permute (+quantize), dh GEMM with fused SwiGLU backward and
  *                       d_prob, dW_down, dX and dW_gate_up grouped GEMMs
  *   unpermute_combine   out[t] = sum over the k slots of in[perm_pos[t][i]]
+ * and the router backward (moe_router_bwd: d_logits from d_prob).
  *
  * Sources: "NVIDIA Shows an Efficient MoE Training Path for Biological Foundation
  * Models" (sections "Grouped experts instead of a Python loop" and "Memory and
@@ -278,6 +279,35 @@ typedef struct mge_combine_args {
 } mge_combine_args;
 
 mge_status unpermute_combine(const mge_combine_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * moe_router_bwd — gradient of the routing probabilities with respect to the router
+ * logits, the step upstream of grouped_mlp_bwd's d_prob.  moe_route_permute gives
+ * token t's k slots the softmax of its selected logits (z_i = logits[t][topk_idx[t][i]]),
+ * so with s_t = sum_j topk_prob[t][j] * d_prob[t][j] (fp32, slot order):
+ *   d_logits[t][e] = sum over the slots i with topk_idx[t][i] == e of
+ *                    topk_prob[t][i] * (d_prob[t][i] - s_t)
+ * and 0 for the experts no slot selected (the renormalised probabilities do not depend
+ * on their logits).  Sources: the routing of "NVIDIA Shows an Efficient MoE Training
+ * Path for Biological Foundation Models" (introduction: each token goes to a few
+ * experts, its output weighted by the routing probability) and the chain rule through
+ * that softmax.
+ * Layout: topk_idx int32 [T][k], topk_prob and d_prob fp32 [T][k] (as moe_route_permute
+ * and grouped_mlp_bwd write them), d_logits fp32 [T][E], every element written.
+ * Indices outside [0, E) take part in s_t but add to no output.  T = 0 is a no-op.
+ * Errors: MGE_ERR_INVALID_ARG for a NULL pointer (T > 0), E outside [1, 256] or k
+ * outside [1, min(E, 8)].
+ * ---------------------------------------------------------------------------- */
+typedef struct mge_router_bwd_args {
+  uint32_t struct_size;
+  int32_t T, E, k;
+  const int32_t* topk_idx;               /* [T][k] */
+  const float* topk_prob;                /* [T][k] */
+  const float* d_prob;                   /* [T][k] */
+  float* d_logits;                       /* [T][E] */
+} mge_router_bwd_args;
+
+mge_status moe_router_bwd(const mge_router_bwd_args* args, void* stream);
 
 /* ------------------------------------------------------------------------------ helpers */
 const char* mge_status_string(mge_status s);

@@ -71,10 +71,15 @@ class CombineArgs(C.Structure):
                 ("in_", vp), ("perm_pos", vp), ("weights", vp), ("out", vp)]
 
 
+class RouterBwdArgs(C.Structure):
+    _fields_ = [("struct_size", u32), ("T", i32), ("E", i32), ("k", i32), ("topk_idx", vp), ("topk_prob", vp),
+                ("d_prob", vp), ("d_logits", vp)]
+
+
 _LIB = None
 EXPORTS = ["mge_perm_rows", "mge_route_workspace_bytes", "moe_route_permute", "mxfp8_quantize",
            "mge_fwd_workspace_bytes", "grouped_mlp_fwd", "mge_bwd_workspace_bytes", "grouped_mlp_bwd",
-           "unpermute_combine", "mge_status_string", "mge_last_error", "mge_check_device_errors", "mge_version",
+           "unpermute_combine", "moe_router_bwd", "mge_status_string", "mge_last_error", "mge_check_device_errors", "mge_version",
            "mge_profile_start", "mge_profile_stop"]
 
 
@@ -99,7 +104,7 @@ def lib():
         L.mge_bwd_workspace_bytes.argtypes = [C.POINTER(BwdArgs)]
         for name, st in (("moe_route_permute", RouteArgs), ("mxfp8_quantize", QuantArgs),
                          ("grouped_mlp_fwd", FwdArgs), ("grouped_mlp_bwd", BwdArgs),
-                         ("unpermute_combine", CombineArgs)):
+                         ("unpermute_combine", CombineArgs), ("moe_router_bwd", RouterBwdArgs)):
             f = getattr(L, name)
             f.restype = C.c_int
             f.argtypes = [C.POINTER(st), vp]
@@ -443,4 +448,21 @@ def unpermute_combine(inp: torch.Tensor, perm_pos: torch.Tensor, weights: Option
     a.out_dtype = DTYPE["bf16"] if out.dtype == torch.bfloat16 else DTYPE["f32"]
     a.in_, a.perm_pos, a.weights, a.out = _ptr(inp), _ptr(perm_pos), _ptr(weights), _ptr(out)
     _check(lib().unpermute_combine(C.byref(a), _stream(dev)), "unpermute_combine")
+    return out
+
+
+# ------------------------------------------------------------------------------ router backward
+
+def moe_router_bwd(topk_idx: torch.Tensor, topk_prob: torch.Tensor, d_prob: torch.Tensor, E: int,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """d_logits fp32 [T][E] from the slots' indices, probabilities and d_prob ([T][k] each)."""
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    if out is None:
+        out = torch.empty((T, E), device=dev, dtype=torch.float32)
+    a = RouterBwdArgs()
+    a.struct_size = C.sizeof(RouterBwdArgs)
+    a.T, a.E, a.k = T, E, k
+    a.topk_idx, a.topk_prob, a.d_prob, a.d_logits = _ptr(topk_idx), _ptr(topk_prob), _ptr(d_prob), _ptr(out)
+    _check(lib().moe_router_bwd(C.byref(a), _stream(dev)), "moe_router_bwd")
     return out

@@ -687,6 +687,19 @@ mge_status unpermute_combine(const mge_combine_args* a, void* stream) {
                         static_cast<hipStream_t>(stream));
 }
 
+mge_status moe_router_bwd(const mge_router_bwd_args* a, void* stream) {
+  g_err[0] = 0;
+  MGE_REQUIRE(a != nullptr, "args is NULL");
+  MGE_REQUIRE(a->struct_size == sizeof(mge_router_bwd_args), "struct_size mismatch");
+  MGE_REQUIRE(a->T >= 0, "T must be >= 0 (got %d)", a->T);
+  MGE_REQUIRE(a->E >= 1 && a->E <= 256, "E must be in [1, 256] (got %d)", a->E);
+  MGE_REQUIRE(a->k >= 1 && a->k <= 8 && a->k <= a->E, "k must be in [1, min(E, 8)] (got k=%d, E=%d)", a->k, a->E);
+  if (a->T == 0) return MGE_OK;
+  MGE_REQUIRE(a->topk_idx && a->topk_prob && a->d_prob && a->d_logits, "topk_idx / topk_prob / d_prob / d_logits NULL");
+  return launch_router_bwd(a->T, a->E, a->k, a->topk_idx, a->topk_prob, a->d_prob, a->d_logits,
+                           static_cast<hipStream_t>(stream));
+}
+
 mge_status mge_check_device_errors(void* route_workspace, void* stream) {
   g_err[0] = 0;
   MGE_REQUIRE(route_workspace != nullptr, "workspace is NULL");

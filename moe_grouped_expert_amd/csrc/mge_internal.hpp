@@ -69,6 +69,8 @@ struct RouteParams {
   int R;
 };
 mge_status launch_route(const RouteParams& p, hipStream_t s);
+mge_status launch_router_bwd(int T, int E, int k, const int32_t* idx, const float* prob, const float* dprob,
+                             float* dlogits, hipStream_t s);
 
 // ------------------------------------------------------------ combine / reductions
 mge_status launch_combine(int T, int k, int H, int in_dtype, int out_dtype, const void* in,

@@ -14,6 +14,7 @@
 //                          rank.  Writes perm_src / perm_pos / prob_perm and marks the
 //                          padding rows.
 // Being a counting sort over (t, i) order, the result is unique: bit-exact indices.
+//   router_bwd_kernel      the backward of the top-k softmax: d_logits from d_prob
 #include <math.h>
 
 #include "mge_common.hpp"
@@ -204,6 +205,39 @@ __global__ __launch_bounds__(RT_THREADS) void route_scatter_kernel(RouteParams p
       p.prob_perm[r] = 0.f;
     }
   }
+}
+
+// Router backward.  The k slot probabilities of token t are the softmax of its selected
+// logits z_i = l[t][idx_i], so with s_t = sum_j p_j d_p_j the gradient of slot i is
+// p_i (d_p_i - s_t), added into d_logits[t][idx_i]; logits no slot selected get 0.  One
+// thread per output element (t, e), so the [T][E] rows leave as whole lines; the
+// threads of a token re-read its k slots from cache.  s_t is summed in slot order with
+// fused multiply-adds; slots with an index outside [0, E) match no e.
+__global__ void router_bwd_kernel(int T, int E, int k, const int32_t* __restrict__ idx, const float* __restrict__ prob,
+                                  const float* __restrict__ dprob, float* __restrict__ dlogits) {
+  const int64_t g = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (g >= int64_t(T) * E) return;
+  const int t = int(g / E);
+  const int e = int(g - int64_t(t) * E);
+  const int32_t* it = idx + int64_t(t) * k;
+  const float* pt = prob + int64_t(t) * k;
+  const float* dt = dprob + int64_t(t) * k;
+  float s = 0.f;
+  for (int j = 0; j < k; ++j) s = fmaf(pt[j], dt[j], s);
+  float d = 0.f;
+  for (int i = 0; i < k; ++i)
+    if (it[i] == e) d += pt[i] * (dt[i] - s);
+  dlogits[g] = d;
+}
+
+mge_status launch_router_bwd(int T, int E, int k, const int32_t* idx, const float* prob, const float* dprob,
+                             float* dlogits, hipStream_t s) {
+  const int64_t n = int64_t(T) * E;
+  if (n == 0) return MGE_OK;
+  ProfScope prof(s, "router_bwd");
+  hipLaunchKernelGGL(router_bwd_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, T, E, k, idx, prob, dprob,
+                     dlogits);
+  return hip_check("router_bwd_kernel");
 }
 
 mge_status launch_route(const RouteParams& p, hipStream_t s) {

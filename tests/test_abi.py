@@ -132,3 +132,25 @@ def test_fwd_bwd_combine_reject():
 def test_check_device_errors_rejects_null():
     L = b.lib()
     assert L.mge_check_device_errors(None, None) == b.MGE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("fields,msg", [
+    (dict(T=-1, E=8, k=2), "T must"),
+    (dict(T=4, E=0, k=1), "E must"),
+    (dict(T=4, E=257, k=2), "E must"),
+    (dict(T=4, E=4, k=5), "k must"),
+    (dict(T=4, E=16, k=9), "k must"),
+    (dict(T=4, E=8, k=2), "NULL"),
+])
+def test_router_bwd_rejects(fields, msg):
+    r, err = _call("moe_router_bwd", b.RouterBwdArgs, **fields)
+    assert r == b.MGE_ERR_INVALID_ARG and msg in err, err
+
+
+def test_router_bwd_empty_and_struct_size():
+    # T = 0 is a no-op even with NULL pointers; a wrong struct_size is rejected first
+    r, err = _call("moe_router_bwd", b.RouterBwdArgs, T=0, E=8, k=2)
+    assert r == b.MGE_OK, err
+    a = b.RouterBwdArgs()
+    a.struct_size = C.sizeof(b.RouterBwdArgs) + 4
+    assert b.lib().moe_router_bwd(C.byref(a), None) == b.MGE_ERR_INVALID_ARG
