@@ -47,7 +47,16 @@ WORKLOADS = {
     "fwd_bf16": (1, False),
     "fwd_mxfp8": (2, False),
     "fwd_mxfp8_skew": (3, False),
+    # one rank's share of an expert-parallel layer (its local experts, its received rows)
+    "fwd_mxfp8_ep8": (5, False),
+    "fwd_mxfp8_ep4": (6, False),
+    "train_mxfp8_ep8": (7, True),
 }
+
+# How the forward runs its grouped projections: one grouped launch per projection over
+# every expert ("grouped", the method), or one launch per expert and projection with
+# the same kernels ("expert_loop", the per-expert loop the grouped call replaces).
+VARIANTS = ("grouped", "expert_loop")
 
 
 def log(*a):
@@ -73,29 +82,97 @@ def make_inputs(w, dev):
     return dict(logits=logits, x=x, wgu=wgu, wd=wd, dy=dy)
 
 
+def make_ep_share_inputs(m, w, dev):
+    """Inputs of rank 0 of an expert-parallel layer with w.ep ranks of w.T tokens each.
+
+    The w.ep * w.T tokens are routed over all E experts with the library's router (set-up,
+    outside the timed steps); rank 0 holds experts 0 .. E/ep - 1 and receives every
+    assignment routed to them, in the order (source token, slot), with its expert index
+    (local = global here) and its routing probability: what an all-to-all-v of the
+    dispatching ranks' permuted rows delivers.  The received rows of x (and of dy for the
+    training step) are drawn fresh, N(0, 1) like the tokens they stand for.  Returns the
+    inputs and the rank's local problem as a workload: T = rows received, k = 1."""
+    import dataclasses
+
+    import torch
+
+    import synth
+    e_loc = w.E // w.ep
+    logits = torch.from_numpy(synth.logits(w)).to(dev)
+    g = m.moe_route_permute(logits, None, w.k, align=32)
+    mask = g.topk_idx < e_loc
+    idx = g.topk_idx[mask].to(torch.int32).reshape(-1, 1).contiguous()
+    prob = g.topk_prob[mask].to(torch.float32).reshape(-1, 1).contiguous()
+    n = int(idx.shape[0])
+    wl = dataclasses.replace(w, T=n, E=e_loc, k=1, extra={})
+    x = synth.torch_normal_bf16((n, w.H), 1.0, 1000 * w.cfg_id + synth.TID_X, dev)
+    wg = synth.torch_normal_bf16((e_loc, w.F, w.H), w.weight_std, 1000 * w.cfg_id + synth.TID_WGATE, dev)
+    wu = synth.torch_normal_bf16((e_loc, w.F, w.H), w.weight_std, 1000 * w.cfg_id + synth.TID_WUP, dev)
+    wgu = torch.cat([wg, wu], dim=1).contiguous()
+    del wg, wu
+    wd = synth.torch_normal_bf16((e_loc, w.H, w.F), w.weight_std, 1000 * w.cfg_id + synth.TID_WDOWN, dev)
+    dy = synth.torch_normal_bf16((n, w.H), 1.0, 1000 * w.cfg_id + synth.TID_DY, dev) if w.backward else None
+    return dict(logits=None, idx=idx, prob=prob, x=x, wgu=wgu, wd=wd, dy=dy), wl
+
+
 # ------------------------------------------------------------------------------ step
 
 class Step:
     """The hot path with every output buffer allocated once (allocation stays outside
-    the timed region; the library itself never allocates)."""
+    the timed region; the library itself never allocates).
 
-    def __init__(self, m, w, inp, train):
+    With inputs from make_ep_share_inputs the step is one expert-parallel rank's: the
+    received rows are permuted by their given local expert and probability (k = 1), and
+    the router's backward stays with the dispatching ranks.  variant "expert_loop" runs
+    the forward as one single-group grouped_mlp_fwd per expert (inference only)."""
+
+    def __init__(self, m, w, inp, train, variant="grouped"):
         self.m, self.w, self.inp, self.train = m, w, inp, train
+        self.variant = variant
         self.prec = w.prec
+        self.given = inp.get("idx") is not None
         self.g = None
         self.wq = self.dq = None
         self.f = self.b = None
         self.y = self.dx = self.dl = None
+        self.groups = None
+
+    def _fwd_expert_loop(self):
+        """E launches of each projection: expert e's group alone, as a one-expert call
+        whose sizes and offsets are the e-th entries of the device arrays (nothing is
+        read back to the host) over the shared permuted buffers (T = R rows, k = 1,
+        align = 1, so the call's row count is R)."""
+        import dataclasses
+
+        m, g = self.m, self.g
+        if self.groups is None:
+            self.groups = [dataclasses.replace(g, E=1, T=g.R, k=1, align=1, split_sizes=g.split_sizes[e:e + 1],
+                                               group_offsets=g.group_offsets[e:e + 2]) for e in range(g.E)]
+        mx = self.prec == "mxfp8"
+        for e, ge in enumerate(self.groups):
+            if mx:
+                self.f = m.grouped_mlp_fwd(ge, self.wq[0][e:e + 1], self.dq[0][e:e + 1], self.wq[1][e:e + 1],
+                                           self.dq[1][e:e + 1], out=self.f)
+            else:
+                self.f = m.grouped_mlp_fwd(ge, self.inp["wgu"][e:e + 1], self.inp["wd"][e:e + 1], out=self.f)
+        return self.f
 
     def __call__(self):
         m, w, inp = self.m, self.w, self.inp
         mx = self.prec == "mxfp8"
-        self.g = m.moe_route_permute(inp["logits"], inp["x"], w.k, align=32, prec=self.prec, want_col=self.train,
-                                     out=self.g)
+        if self.given:
+            self.g = m.moe_route_permute(None, inp["x"], 1, E=w.E, align=32, prec=self.prec, want_col=self.train,
+                                         topk_idx=inp["idx"], topk_prob=inp["prob"], out=self.g)
+        else:
+            self.g = m.moe_route_permute(inp["logits"], inp["x"], w.k, align=32, prec=self.prec,
+                                         want_col=self.train, out=self.g)
         if mx:
             orient = "both" if self.train else "row"
             self.wq = m.mxfp8_quantize(inp["wgu"], orient, out=self.wq)
             self.dq = m.mxfp8_quantize(inp["wd"], orient, out=self.dq)
+        if self.variant == "expert_loop":
+            self._fwd_expert_loop()
+        elif mx:
             self.f = m.grouped_mlp_fwd(self.g, self.wq[0], self.dq[0], self.wq[1], self.dq[1], train=self.train,
                                        out=self.f)
         else:
@@ -108,7 +185,8 @@ class Step:
             else:
                 self.b = m.grouped_mlp_bwd(inp["dy"], self.g, self.f, inp["wgu"], inp["wd"], out=self.b)
             self.dx = m.unpermute_combine(self.b.dx_perm, self.g.perm_pos, out=self.dx)
-            self.dl = m.moe_router_bwd(self.g.topk_idx, self.g.topk_prob, self.b.d_prob, w.E, out=self.dl)
+            if not self.given:
+                self.dl = m.moe_router_bwd(self.g.topk_idx, self.g.topk_prob, self.b.d_prob, w.E, out=self.dl)
 
 
 # ------------------------------------------------------------------------------ per-kernel work
@@ -360,6 +438,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="train_mxfp8", choices=sorted(WORKLOADS))
+    ap.add_argument("--variant", default="grouped", choices=VARIANTS,
+                    help="grouped projections (default) or the per-expert launch loop (forward workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=32, help="assignments in the CPU oracle sample")
     ap.add_argument("--cpu-fcols", type=int, default=None, help="ffn columns in the CPU oracle sample (default: all)")
@@ -391,10 +471,19 @@ def main():
     dev = torch.device("cuda:0")
     wid, train = WORKLOADS[args.workload]
     w = synth.WORKLOADS[wid]
-    log(f"[bench] workload {w.name}: T={w.T} E={w.E} H={w.H} F={w.F} k={w.k} prec={w.prec} train={train}")
-    inp = make_inputs(w, dev)
+    if args.variant == "expert_loop" and train:
+        print("the expert_loop variant runs forward workloads only", file=sys.stderr)
+        sys.exit(2)
+    log(f"[bench] workload {w.name}: T={w.T} E={w.E} H={w.H} F={w.F} k={w.k} prec={w.prec} train={train} "
+        f"ep={w.ep} variant={args.variant}")
+    wg = w   # the workload as named; w becomes the problem this GPU runs
+    if w.ep > 1:
+        inp, w = make_ep_share_inputs(m, w, dev)
+        log(f"[bench] rank 0 of {wg.ep}: experts 0..{w.E - 1}, {w.T} received rows")
+    else:
+        inp = make_inputs(w, dev)
     torch.cuda.synchronize()
-    step = Step(m, w, inp, train)
+    step = Step(m, w, inp, train, args.variant)
     for i in range(args.warmup):
         step()
         torch.cuda.synchronize()
@@ -427,14 +516,14 @@ def main():
         ach = wk[1] / (dk["avg_ms"] * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_TFLOPS[w.prec],
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS[w.prec], 4),
-                "traffic": traffic_for(dom, args.workload), "avg_launch_ms": dk["avg_ms"],
+                "traffic": traffic_for(dom, args.workload) if args.variant == "grouped" else None, "avg_launch_ms": dk["avg_ms"],
                 "algorithmic_flop_per_launch": wk[1]}
     else:
         nb = wk[1] if wk else None
         ach = nb / (dk["avg_ms"] * 1e-3) / 1e9 if nb else None
         roof = {"kernel": dom, "bound": "hbm", "achieved": ach and round(ach, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": ach and round(ach / PEAK_HBM_GBS, 4),
-                "traffic": traffic_for(dom, args.workload), "avg_launch_ms": dk["avg_ms"]}
+                "traffic": traffic_for(dom, args.workload) if args.variant == "grouped" else None, "avg_launch_ms": dk["avg_ms"]}
     gemm_ms = sum(v["avg_ms"] * v["launches_per_step"] for k, v in kernels.items() if k.startswith("gemm_"))
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -442,7 +531,7 @@ def main():
         "vs_baseline": None, "dtype": w.prec, "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "E": w.E, "H": w.H, "F": w.F, "k": w.k, "prec": w.prec,
                    "passes": "fwd+bwd" if train else "fwd", "align": 32, "split_sizes": sizes,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "variant": args.variant},
         "tokens_per_s": round(tok_s, 1),
         "algorithmic_tflop_per_step": round(flops / 1e12, 4),
         "gemm_only": {"ms_per_step": round(gemm_ms, 4),
@@ -451,9 +540,13 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
+    if wg.ep > 1:
+        out["config"].update(ep_rank_share={"ep": wg.ep, "tokens_per_rank": wg.T, "experts": wg.E,
+                                            "top_k": wg.k, "local_experts": w.E, "rows_received": w.T})
+        out["rows_per_s"] = out.pop("tokens_per_s")   # received rows (assignments), k = 1 locally
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows, args.cpu_fcols)
+        out["cpu_baseline"] = cpu_baseline(wg, args.cpu_rows, args.cpu_fcols)
     print(json.dumps(out), flush=True)
 
 

@@ -49,6 +49,16 @@ class Workload:
     def M(self) -> int:
         return self.T * self.k
 
+    @property
+    def ep(self) -> int:
+        """Expert-parallel degree of a one-rank share (1: the whole layer on one GPU)."""
+        return int(self.extra.get("ep", 1))
+
+    @property
+    def T_route(self) -> int:
+        """Tokens the router sees: T per rank times the expert-parallel degree."""
+        return self.T * self.ep
+
     def flops_fwd(self) -> float:
         # gate-up 4*M*H*F, down 2*M*H*F
         return 6.0 * self.M * self.H * self.F
@@ -65,6 +75,14 @@ WORKLOADS = {
     3: Workload(3, "mixtral_mxfp8_fwd_zipf_skew", T=32768, E=8, H=4096, F=14336, k=2, prec="mxfp8",
                 backward=False, skew=True),
     4: Workload(4, "mixtral_mxfp8_train_step", T=8192, E=8, H=4096, F=14336, k=2, prec="mxfp8", backward=True),
+    # One rank's share under expert parallelism: ep ranks of T tokens each are routed over
+    # the 8 experts; rank 0 holds experts 0 .. 8/ep - 1 and receives their assignments.
+    5: Workload(5, "mixtral_mxfp8_fwd_ep8_rank_share", T=16384, E=8, H=4096, F=14336, k=2, prec="mxfp8",
+                backward=False, extra={"ep": 8}),
+    6: Workload(6, "mixtral_mxfp8_fwd_ep4_rank_share", T=16384, E=8, H=4096, F=14336, k=2, prec="mxfp8",
+                backward=False, extra={"ep": 4}),
+    7: Workload(7, "mixtral_mxfp8_train_step_ep8_rank_share", T=8192, E=8, H=4096, F=14336, k=2, prec="mxfp8",
+                backward=True, extra={"ep": 8}),
 }
 
 
@@ -89,8 +107,8 @@ def skew_bias(E: int) -> np.ndarray:
 
 
 def logits(w: Workload, bias: np.ndarray | None = None) -> np.ndarray:
-    """Router logits fp32 [T][E]; the skewed workload adds its per-expert bias."""
-    z = rng(w.cfg_id, TID_LOGITS).standard_normal((w.T, w.E), dtype=np.float32)
+    """Router logits fp32 [T_route][E]; the skewed workload adds its per-expert bias."""
+    z = rng(w.cfg_id, TID_LOGITS).standard_normal((w.T_route, w.E), dtype=np.float32)
     if w.skew:
         b = skew_bias(w.E) if bias is None else bias.astype(np.float32)
         z = (z + b[None, :]).astype(np.float32)
