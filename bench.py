@@ -53,10 +53,13 @@ WORKLOADS = {
     "train_mxfp8_ep8": (7, True),
 }
 
-# How the forward runs its grouped projections: one grouped launch per projection over
-# every expert ("grouped", the method), or one launch per expert and projection with
-# the same kernels ("expert_loop", the per-expert loop the grouped call replaces).
-VARIANTS = ("grouped", "expert_loop")
+# How the forward runs: one grouped launch per projection over every expert with the
+# SwiGLU x prob (+ quantize) fused into the gate-up epilogue ("grouped", the method);
+# one launch per expert and projection with the same kernels ("expert_loop", the
+# per-expert loop the grouped call replaces); or grouped launches without the fusion,
+# [G U] through HBM in bf16, a standalone SwiGLU x prob and a standalone quantize of h
+# ("unfused", what the fused operation replaces).
+VARIANTS = ("grouped", "expert_loop", "unfused")
 
 
 def log(*a):
@@ -124,11 +127,14 @@ class Step:
     With inputs from make_ep_share_inputs the step is one expert-parallel rank's: the
     received rows are permuted by their given local expert and probability (k = 1), and
     the router's backward stays with the dispatching ranks.  variant "expert_loop" runs
-    the forward as one single-group grouped_mlp_fwd per expert (inference only)."""
+    the forward as one single-group grouped_mlp_fwd per expert, "unfused" as
+    grouped_mlp_fwd_unfused (both inference only; keep_intermediates keeps the unfused
+    call's [G U] and bf16 h in their own buffers instead of the workspace)."""
 
     def __init__(self, m, w, inp, train, variant="grouped"):
         self.m, self.w, self.inp, self.train = m, w, inp, train
         self.variant = variant
+        self.keep_intermediates = False
         self.prec = w.prec
         self.given = inp.get("idx") is not None
         self.g = None
@@ -172,6 +178,13 @@ class Step:
             self.dq = m.mxfp8_quantize(inp["wd"], orient, out=self.dq)
         if self.variant == "expert_loop":
             self._fwd_expert_loop()
+        elif self.variant == "unfused":
+            if mx:
+                self.f = m.grouped_mlp_fwd_unfused(self.g, self.wq[0], self.dq[0], self.wq[1], self.dq[1],
+                                                   keep_intermediates=self.keep_intermediates, out=self.f)
+            else:
+                self.f = m.grouped_mlp_fwd_unfused(self.g, inp["wgu"], inp["wd"],
+                                                   keep_intermediates=self.keep_intermediates, out=self.f)
         elif mx:
             self.f = m.grouped_mlp_fwd(self.g, self.wq[0], self.dq[0], self.wq[1], self.dq[1], train=self.train,
                                        out=self.f)
@@ -198,7 +211,7 @@ def kernel_work(name, w, R):
     kernels: bytes that must cross HBM once (inputs read, outputs written)."""
     M, H, F, T, k, E = w.M, w.H, w.F, w.T, w.k, w.E
     mhf = float(M) * H * F
-    gemm = {"gemm_gateup_swiglu": 4 * mhf, "gemm_down": 2 * mhf, "gemm_dh": 2 * mhf,
+    gemm = {"gemm_gateup_swiglu": 4 * mhf, "gemm_gateup_store": 4 * mhf, "gemm_down": 2 * mhf, "gemm_dh": 2 * mhf,
             "gemm_dx": 4 * mhf, "gemm_dw_down": 2 * mhf, "gemm_dw_gateup": 4 * mhf}
     for key, v in gemm.items():
         if name.startswith(key + "_"):
@@ -215,6 +228,11 @@ def kernel_work(name, w, R):
         # averaged per launch: bf16 read, row and (training) column forms written
         forms = 2 if w.backward else 1
         return "byte", 1.5 * E * H * F * (2.0 + forms * mxb)
+    if name == "swiglu_prob":
+        # unfused forward: [G U] bf16 read, h bf16 written, p read (valid rows)
+        return "byte", 6.0 * M * F + 4.0 * M
+    if name == "quant_h_mx":
+        return "byte", M * F * (2.0 + mxb)
     if name == "combine":
         return "byte", 2.0 * k * T * H + 2.0 * T * H + 4.0 * T * k
     if name == "router_bwd":
@@ -471,8 +489,8 @@ def main():
     dev = torch.device("cuda:0")
     wid, train = WORKLOADS[args.workload]
     w = synth.WORKLOADS[wid]
-    if args.variant == "expert_loop" and train:
-        print("the expert_loop variant runs forward workloads only", file=sys.stderr)
+    if args.variant != "grouped" and train:
+        print(f"the {args.variant} variant runs forward workloads only", file=sys.stderr)
         sys.exit(2)
     log(f"[bench] workload {w.name}: T={w.T} E={w.E} H={w.H} F={w.F} k={w.k} prec={w.prec} train={train} "
         f"ep={w.ep} variant={args.variant}")

@@ -203,6 +203,39 @@ size_t mge_fwd_workspace_bytes(const mge_fwd_args* args);
 mge_status grouped_mlp_fwd(const mge_fwd_args* args, void* stream);
 
 /* ------------------------------------------------------------------------------
+ * grouped_mlp_fwd_unfused — the same forward (inference only) without the fusion:
+ * the structure the pages' fused GroupedLinear -> ScaledSwiGLU -> GroupedLinear
+ * replaces ("Accelerating MoE Training ..." "How it works"; the ai4snews report,
+ * paragraph on the Sequential fusion; the BioNeMo recipe report, "Quantization
+ * Overhead"), kept to measure what the fusion saves:
+ *   1. grouped gate-up GEMM, [G U] written to HBM in bf16 ([R][2F], gate columns
+ *      0..F-1, up columns F..2F-1);
+ *   2. a standalone SwiGLU x prob kernel: h = p * silu(G) * U in fp32 from the bf16
+ *      G, U, rounded to bf16 ([R][F]; rows with p = 0 get 0);
+ *   3. MXFP8 only: a standalone quantize of that bf16 h along F (the row form
+ *      mxfp8_quantize writes) into h / h_scale;
+ *   4. the grouped down GEMM, as in grouped_mlp_fwd.
+ * fwd: grouped_mlp_fwd's arguments; saved_gu, h_col and h_col_scale must be NULL.
+ * Its workspace fields carry this call's workspace.
+ * gu: optional [R][2F] bf16 output of step 1 (NULL: in the workspace).
+ * h_bf16: MXFP8 only, optional [R][F] bf16 output of step 2 (NULL: in the
+ * workspace); in BF16 step 2 writes fwd.h (or the workspace) directly.
+ * Rows outside the groups: gu untouched, h_bf16 and h zero (MXFP8 codes 0, scales
+ * 0 for an all-zero block), y_perm untouched.
+ * Errors: those of grouped_mlp_fwd; MGE_ERR_INVALID_ARG for training buffers or a
+ * misaligned gu / h_bf16.
+ * ---------------------------------------------------------------------------- */
+typedef struct mge_fwd_unfused_args {
+  uint32_t struct_size;
+  mge_fwd_args fwd;
+  uint16_t* gu;                          /* optional [R][2F] bf16 */
+  uint16_t* h_bf16;                      /* optional [R][F] bf16 (MXFP8) */
+} mge_fwd_unfused_args;
+
+size_t mge_fwd_unfused_workspace_bytes(const mge_fwd_unfused_args* args);
+mge_status grouped_mlp_fwd_unfused(const mge_fwd_unfused_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------
  * grouped_mlp_bwd — the matching backward of grouped_mlp_fwd, for L = <dy, y> with
  * y = unpermute_combine(y_perm):
  *   dY = dy gathered by perm_src; dh = dY W_down (K = H)

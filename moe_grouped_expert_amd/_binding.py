@@ -53,6 +53,10 @@ class FwdArgs(C.Structure):
                 ("workspace_bytes", C.c_size_t)]
 
 
+class FwdUnfusedArgs(C.Structure):
+    _fields_ = [("struct_size", u32), ("fwd", FwdArgs), ("gu", vp), ("h_bf16", vp)]
+
+
 class BwdArgs(C.Structure):
     _fields_ = [("struct_size", u32), ("prec", i32), ("E", i32), ("H", i32), ("F", i32), ("T", i32),
                 ("k", i32), ("align", i32),
@@ -78,7 +82,8 @@ class RouterBwdArgs(C.Structure):
 
 _LIB = None
 EXPORTS = ["mge_perm_rows", "mge_route_workspace_bytes", "moe_route_permute", "mxfp8_quantize",
-           "mge_fwd_workspace_bytes", "grouped_mlp_fwd", "mge_bwd_workspace_bytes", "grouped_mlp_bwd",
+           "mge_fwd_workspace_bytes", "grouped_mlp_fwd", "mge_fwd_unfused_workspace_bytes", "grouped_mlp_fwd_unfused",
+           "mge_bwd_workspace_bytes", "grouped_mlp_bwd",
            "unpermute_combine", "moe_router_bwd", "mge_status_string", "mge_last_error", "mge_check_device_errors", "mge_version",
            "mge_profile_start", "mge_profile_stop"]
 
@@ -100,10 +105,13 @@ def lib():
         L.mge_route_workspace_bytes.argtypes = [i32, i32]
         L.mge_fwd_workspace_bytes.restype = C.c_size_t
         L.mge_fwd_workspace_bytes.argtypes = [C.POINTER(FwdArgs)]
+        L.mge_fwd_unfused_workspace_bytes.restype = C.c_size_t
+        L.mge_fwd_unfused_workspace_bytes.argtypes = [C.POINTER(FwdUnfusedArgs)]
         L.mge_bwd_workspace_bytes.restype = C.c_size_t
         L.mge_bwd_workspace_bytes.argtypes = [C.POINTER(BwdArgs)]
         for name, st in (("moe_route_permute", RouteArgs), ("mxfp8_quantize", QuantArgs),
-                         ("grouped_mlp_fwd", FwdArgs), ("grouped_mlp_bwd", BwdArgs),
+                         ("grouped_mlp_fwd", FwdArgs), ("grouped_mlp_fwd_unfused", FwdUnfusedArgs),
+                         ("grouped_mlp_bwd", BwdArgs),
                          ("unpermute_combine", CombineArgs), ("moe_router_bwd", RouterBwdArgs)):
             f = getattr(L, name)
             f.restype = C.c_int
@@ -283,6 +291,8 @@ class FwdOut:
     h_col: Optional[torch.Tensor] = None
     h_col_scale: Optional[torch.Tensor] = None
     workspace: Optional[torch.Tensor] = None
+    gu: Optional[torch.Tensor] = None          # unfused forward: [G U] bf16 (kept on request)
+    h_bf16: Optional[torch.Tensor] = None      # unfused MXFP8 forward: h before its quantize
 
 
 def _split(w, E):
@@ -291,9 +301,10 @@ def _split(w, E):
     return list(w)
 
 
-def grouped_mlp_fwd(rt: RouteOut, w_gate_up, w_down, w_gate_up_scale=None, w_down_scale=None,
-                    y_dtype: str = "bf16", train: bool = False, out: Optional[FwdOut] = None) -> FwdOut:
-    """Grouped gate-up GEMM -> SwiGLU x prob (+ quantize) -> grouped down GEMM."""
+def _fwd_args(rt: RouteOut, w_gate_up, w_down, w_gate_up_scale, w_down_scale, y_dtype: str, train: bool,
+              out: Optional[FwdOut]):
+    """Outputs (allocated unless given) and the filled mge_fwd_args; `keep` holds the
+    host pointer arrays alive while the call runs."""
     E, H, R = rt.E, rt.H, rt.R
     wg = _split(w_gate_up, E)
     wd = _split(w_down, E)
@@ -325,11 +336,41 @@ def grouped_mlp_fwd(rt: RouteOut, w_gate_up, w_down, w_gate_up_scale=None, w_dow
     a.y_dtype = DTYPE[y_dtype]
     a.y_perm, a.h, a.h_scale = _ptr(o.y_perm), _ptr(o.h), _ptr(o.h_scale)
     a.saved_gu, a.h_col, a.h_col_scale = _ptr(o.saved_gu), _ptr(o.h_col), _ptr(o.h_col_scale)
+    return o, a, keep, F, dev
+
+
+def grouped_mlp_fwd(rt: RouteOut, w_gate_up, w_down, w_gate_up_scale=None, w_down_scale=None,
+                    y_dtype: str = "bf16", train: bool = False, out: Optional[FwdOut] = None) -> FwdOut:
+    """Grouped gate-up GEMM -> SwiGLU x prob (+ quantize) -> grouped down GEMM."""
+    o, a, keep, F, dev = _fwd_args(rt, w_gate_up, w_down, w_gate_up_scale, w_down_scale, y_dtype, train, out)
     if o.workspace is None:
         o.workspace = torch.empty(max(int(lib().mge_fwd_workspace_bytes(C.byref(a))), 256), device=dev,
                                   dtype=torch.uint8)
     a.workspace, a.workspace_bytes = _ptr(o.workspace), o.workspace.numel()
     _check(lib().grouped_mlp_fwd(C.byref(a), _stream(dev)), "grouped_mlp_fwd")
+    return o
+
+
+def grouped_mlp_fwd_unfused(rt: RouteOut, w_gate_up, w_down, w_gate_up_scale=None, w_down_scale=None,
+                            y_dtype: str = "bf16", keep_intermediates: bool = False,
+                            out: Optional[FwdOut] = None) -> FwdOut:
+    """The forward without the fusion (inference): [G U] to HBM in bf16, a standalone
+    SwiGLU x prob, (MXFP8) a standalone quantize of h, the grouped down GEMM.  With
+    keep_intermediates, out.gu ([R][2F] bf16) and (MXFP8) out.h_bf16 ([R][F]) are kept."""
+    o, a, keep, F, dev = _fwd_args(rt, w_gate_up, w_down, w_gate_up_scale, w_down_scale, y_dtype, False, out)
+    u = FwdUnfusedArgs()
+    u.struct_size = C.sizeof(FwdUnfusedArgs)
+    if keep_intermediates and o.gu is None:
+        o.gu = torch.empty((rt.R, 2 * F), device=dev, dtype=torch.bfloat16)
+        if rt.prec == "mxfp8":
+            o.h_bf16 = torch.empty((rt.R, F), device=dev, dtype=torch.bfloat16)
+    u.gu, u.h_bf16 = _ptr(o.gu), _ptr(o.h_bf16)
+    u.fwd = a
+    if o.workspace is None:
+        o.workspace = torch.empty(max(int(lib().mge_fwd_unfused_workspace_bytes(C.byref(u))), 256), device=dev,
+                                  dtype=torch.uint8)
+    u.fwd.workspace, u.fwd.workspace_bytes = _ptr(o.workspace), o.workspace.numel()
+    _check(lib().grouped_mlp_fwd_unfused(C.byref(u), _stream(dev)), "grouped_mlp_fwd_unfused")
     return o
 
 

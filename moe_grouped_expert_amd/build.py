@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmge.so")
-SOURCES = ["api.cpp", "route.hip", "quant.hip", "gemm_host.cpp", "gemm_mx.hip", "gemm_bf16.hip", "combine.hip"]
+SOURCES = ["api.cpp", "route.hip", "quant.hip", "gemm_host.cpp", "gemm_mx.hip", "gemm_bf16.hip", "combine.hip", "swiglu.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -292,14 +292,31 @@ static mge_status check_offsets(int R, int H, int F, int elem) {
   return MGE_OK;
 }
 
+// The unfused forward's extra buffers: [G U] bf16, and in MXFP8 the bf16 h before its
+// quantize pass (in BF16 h itself is the bf16 h, counted by fwd_ws).
+static size_t fwd_unfused_extra(const mge_fwd_unfused_args* u, int R) {
+  const mge_fwd_args* a = &u->fwd;
+  size_t n = 0;
+  if (!u->gu) n += up256(size_t(R) * 2 * a->F * 2);
+  if (a->prec == MGE_PREC_MXFP8 && !u->h_bf16) n += up256(size_t(R) * a->F * 2);
+  return n;
+}
+
 size_t mge_fwd_workspace_bytes(const mge_fwd_args* a) {
   if (!a || a->E < 1 || a->T < 0 || a->k < 1 || a->align < 1) return 0;
   return fwd_ws(a, int(mge_perm_rows(a->T, a->k, a->E, a->align)));
 }
 
-mge_status grouped_mlp_fwd(const mge_fwd_args* a, void* stream) {
-  g_err[0] = 0;
-  MGE_REQUIRE(a != nullptr, "args is NULL");
+size_t mge_fwd_unfused_workspace_bytes(const mge_fwd_unfused_args* u) {
+  if (!u) return 0;
+  const mge_fwd_args* a = &u->fwd;
+  if (a->E < 1 || a->T < 0 || a->k < 1 || a->align < 1) return 0;
+  const int R = int(mge_perm_rows(a->T, a->k, a->E, a->align));
+  return fwd_ws(a, R) + fwd_unfused_extra(u, R);
+}
+
+// The forward, fused (u == NULL) or unfused (u != NULL, a == &u->fwd).
+static mge_status fwd_impl(const mge_fwd_args* a, const mge_fwd_unfused_args* u, void* stream) {
   MGE_REQUIRE(a->struct_size == sizeof(mge_fwd_args), "struct_size mismatch");
   mge_status st = check_mlp_dims(a->prec, a->E, a->H, a->F, a->T, a->k, a->align);
   if (st != MGE_OK) return st;
@@ -323,8 +340,12 @@ mge_status grouped_mlp_fwd(const mge_fwd_args* a, void* stream) {
     MGE_REQUIRE(!mx || a->h_col_scale, "h_col_scale is NULL");
     MGE_REQUIRE(a->align % 32 == 0, "training (column form of h) needs align %% 32 == 0 (got %d)", a->align);
   }
+  if (u) {
+    MGE_REQUIRE(!train && !a->h_col && !a->h_col_scale, "the unfused forward is inference only (saved_gu, h_col NULL)");
+    MGE_REQUIRE((!u->gu || aligned16(u->gu)) && (!u->h_bf16 || aligned16(u->h_bf16)), "gu / h_bf16 misaligned");
+  }
   const int R = int(mge_perm_rows(a->T, a->k, a->E, a->align));
-  const size_t need = fwd_ws(a, R);
+  const size_t need = fwd_ws(a, R) + (u ? fwd_unfused_extra(u, R) : 0);
   if (!a->workspace || a->workspace_bytes < need) {
     set_error("forward workspace needs %zu bytes (got %zu)", need, a->workspace_bytes);
     return MGE_ERR_WORKSPACE;
@@ -338,6 +359,12 @@ mge_status grouped_mlp_fwd(const mge_fwd_args* a, void* stream) {
   if (!h) {
     if (mx) { h = ws.take(size_t(R) * a->F); hs = static_cast<uint8_t*>(ws.take(size_t(R) * (a->F / 32))); }
     else h = ws.take(size_t(R) * a->F * 2);
+  }
+  uint16_t* gu = nullptr;     // unfused: [G U] bf16 and (MXFP8) the bf16 h
+  uint16_t* hb = nullptr;
+  if (u) {
+    gu = u->gu ? u->gu : static_cast<uint16_t*>(ws.take(size_t(R) * 2 * a->F * 2));
+    hb = !mx ? static_cast<uint16_t*>(h) : u->h_bf16 ? u->h_bf16 : static_cast<uint16_t*>(ws.take(size_t(R) * a->F * 2));
   }
   const int E = a->E;
   {
@@ -387,10 +414,30 @@ mge_status grouped_mlp_fwd(const mge_fwd_args* a, void* stream) {
     else g.hc_bf16 = static_cast<uint16_t*>(a->h_col);
   }
   g.Rp = R;
-  g.tiles_upper = gemm_tiles_upper(g, rows_bound);
-  g.role = GEMM_GATEUP;
-  st = launch_gemm(g, a->prec, s);
-  if (st != MGE_OK) return st;
+  if (!u) {
+    g.tiles_upper = gemm_tiles_upper(g, rows_bound);
+    g.role = GEMM_GATEUP;
+    st = launch_gemm(g, a->prec, s);
+    if (st != MGE_OK) return st;
+  } else {
+    // [G U] to HBM in bf16, then SwiGLU x p, then (MXFP8) the quantize of h
+    g.h_codes = nullptr; g.h_scales = nullptr; g.h_bf16 = nullptr;
+    g.out_dtype = MGE_DTYPE_BF16; g.C = gu; g.ldc = 2 * int64_t(F);
+    g.tiles_upper = gemm_tiles_upper(g, rows_bound);
+    g.role = GEMM_GATEUP_STORE;
+    st = launch_gemm(g, a->prec, s);
+    if (st != MGE_OK) return st;
+    st = launch_swiglu_prob(R, F, gu, a->prob_perm, hb, s);
+    if (st != MGE_OK) return st;
+    if (mx) {
+      QuantTileParams q{};
+      q.in = hb; q.in_batch_stride = int64_t(R) * F; q.in_row_stride = F;
+      q.batch = 1; q.R = R; q.C = F; q.Rp = R;
+      q.row_codes = static_cast<uint8_t*>(h); q.row_scales = hs;
+      st = launch_quant_tile(q, true, s, "quant_h_mx");
+      if (st != MGE_OK) return st;
+    }
+  }
   if (mx) {
     ScalePackParams q{};
     q.src = hs; q.ld = F / 32; q.batch = 1; q.rows = R; q.kb = F / 32; q.dst = hs_p;
@@ -411,6 +458,19 @@ mge_status grouped_mlp_fwd(const mge_fwd_args* a, void* stream) {
   d.tiles_upper = gemm_tiles_upper(d, rows_bound);
   d.role = GEMM_DOWN;
   return launch_gemm(d, a->prec, s);
+}
+
+mge_status grouped_mlp_fwd(const mge_fwd_args* a, void* stream) {
+  g_err[0] = 0;
+  MGE_REQUIRE(a != nullptr, "args is NULL");
+  return fwd_impl(a, nullptr, stream);
+}
+
+mge_status grouped_mlp_fwd_unfused(const mge_fwd_unfused_args* u, void* stream) {
+  g_err[0] = 0;
+  MGE_REQUIRE(u != nullptr, "args is NULL");
+  MGE_REQUIRE(u->struct_size == sizeof(mge_fwd_unfused_args), "struct_size mismatch");
+  return fwd_impl(&u->fwd, u, stream);
 }
 
 // ------------------------------------------------------------------ backward

@@ -13,6 +13,7 @@ MGE_GEMM_KERNEL(gemm_down_bf16, EPI_STORE, RAGGED_M, OUT_BF16)
 MGE_GEMM_KERNEL(gemm_down_f32_bf16, EPI_STORE, RAGGED_M, OUT_F32)
 MGE_GEMM_KERNEL(gemm_dh_swiglu_bf16, EPI_SWIGLU_BWD, RAGGED_M, OUT_NONE)
 MGE_GEMM_KERNEL(gemm_dx_bf16, EPI_STORE, RAGGED_M, OUT_BF16)
+MGE_GEMM_KERNEL(gemm_gateup_store_bf16, EPI_STORE, RAGGED_M, OUT_BF16)
 MGE_GEMM_KERNEL(gemm_dw_down_bf16, EPI_STORE, RAGGED_K, OUT_F32)
 MGE_GEMM_KERNEL(gemm_dw_down_acc_bf16, EPI_STORE, RAGGED_K, OUT_F32_ACC)
 MGE_GEMM_KERNEL(gemm_dw_gateup_bf16, EPI_STORE, RAGGED_K, OUT_F32)
@@ -24,7 +25,7 @@ MGE_GEMM_KERNEL(gemm_dw_gateup_bf16out_bf16, EPI_STORE, RAGGED_K, OUT_BF16)
 
 // Kernel of a role; the output dtype and the accumulate flag were checked by
 // launch_gemm (DOWN, DW: bf16 or f32, accumulate only f32; DH: the SwiGLU-backward
-// epilogue's outputs; DX: bf16).
+// epilogue's outputs; DX, GATEUP_STORE: bf16).
 mge_status launch_gemm_bf16(const GemmParams& p, hipStream_t s) {
   const bool f32 = p.out_dtype == MGE_DTYPE_F32;
   switch (p.role) {
@@ -34,6 +35,7 @@ mge_status launch_gemm_bf16(const GemmParams& p, hipStream_t s) {
                  : launch_gemm_kernel(gemm_down_bf16, "gemm_down_bf16", p, s);
     case GEMM_DH: return launch_gemm_kernel(gemm_dh_swiglu_bf16, "gemm_dh_swiglu_bf16", p, s);
     case GEMM_DX: return launch_gemm_kernel(gemm_dx_bf16, "gemm_dx_bf16", p, s);
+    case GEMM_GATEUP_STORE: return launch_gemm_kernel(gemm_gateup_store_bf16, "gemm_gateup_store_bf16", p, s);
     case GEMM_DW_DOWN:
       if (!f32) return launch_gemm_kernel(gemm_dw_down_bf16out_bf16, "gemm_dw_down_bf16", p, s);
       return p.accumulate ? launch_gemm_kernel(gemm_dw_down_acc_bf16, "gemm_dw_down_bf16", p, s)

@@ -33,7 +33,8 @@ struct QuantTileParams {
   uint8_t* col_codes;  uint8_t* col_scales;  // MX column form [b][C][Rp], [b][C][Rp/32]
   uint16_t* col_bf16;                        // bf16 transpose [b][C][Rp]
 };
-mge_status launch_quant_tile(const QuantTileParams& p, bool mx, hipStream_t s);
+// timing_name: the launch's name for per-kernel timing (NULL: by form)
+mge_status launch_quant_tile(const QuantTileParams& p, bool mx, hipStream_t s, const char* timing_name = nullptr);
 
 // E8M0 scales [rows][kb] (kb bytes per row, row stride ld bytes) -> the packed layout
 // the GEMM reads: dst[b][j][r] = bytes 4j..4j+3 of row r as one dword (j < ceil(kb/4)).
@@ -75,6 +76,9 @@ mge_status launch_router_bwd(int T, int E, int k, const int32_t* idx, const floa
 // ------------------------------------------------------------ combine / reductions
 mge_status launch_combine(int T, int k, int H, int in_dtype, int out_dtype, const void* in,
                           const int32_t* perm_pos, const float* weights, void* out, hipStream_t s);
+// h = p * silu(G) * U from the bf16 [G U] rows (stride 2F) into bf16 h [R][F] (the
+// unfused forward's standalone SwiGLU x prob; rows with p = 0 get 0)
+mge_status launch_swiglu_prob(int R, int F, const uint16_t* gu, const float* prob, uint16_t* h, hipStream_t s);
 // d_prob partials per row written by the dh GEMM's SwiGLU-backward epilogue (one per
 // 128-column span of F: two per 256-column tile)
 inline int dh_swiglu_nparts(int F) { return 2 * ((F + 255) / 256); }
@@ -97,7 +101,8 @@ enum GemmRole {
   GEMM_DH = 2,          // dh = dY W_down, SwiGLU-backward epilogue           (RAGGED_M)
   GEMM_DX = 3,          // dX = dGU W_gate_up                               (RAGGED_M)
   GEMM_DW_DOWN = 4,     // dW_down = dY^T h                                 (RAGGED_K)
-  GEMM_DW_GATEUP = 5    // dW_gate_up = dGU^T X                             (RAGGED_K)
+  GEMM_DW_GATEUP = 5,   // dW_gate_up = dGU^T X                             (RAGGED_K)
+  GEMM_GATEUP_STORE = 6 // [G U] = X W_gate_up^T stored in bf16 (unfused)  (RAGGED_M)
 };
 
 struct GemmParams {

@@ -231,11 +231,12 @@ mge_status launch_scale_pack_batch(const ScalePackParams* list, int n, hipStream
 
 mge_status launch_scale_pack(const ScalePackParams& p, hipStream_t s) { return launch_scale_pack_batch(&p, 1, s); }
 
-mge_status launch_quant_tile(const QuantTileParams& p, bool mx, hipStream_t s) {
+mge_status launch_quant_tile(const QuantTileParams& p, bool mx, hipStream_t s, const char* timing_name) {
   if (p.R <= 0 || p.C <= 0 || p.batch <= 0) return MGE_OK;
   int rows_cover = p.Rp > p.R ? p.Rp : p.R;
   dim3 grid((p.C + QT_COLS - 1) / QT_COLS, (rows_cover + QT_ROWS - 1) / QT_ROWS, p.batch);
-  const char* name = mx ? (p.gather ? "permute_quant_mx" : "quant_mx") : (p.gather ? "permute_bf16" : "transpose_bf16");
+  const char* name = timing_name ? timing_name
+                     : mx ? (p.gather ? "permute_quant_mx" : "quant_mx") : (p.gather ? "permute_bf16" : "transpose_bf16");
   ProfScope prof(s, name);
   if (mx)
     hipLaunchKernelGGL(quant_tile_kernel<true>, grid, dim3(QT_THREADS), 0, s, p);

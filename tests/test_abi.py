@@ -154,3 +154,41 @@ def test_router_bwd_empty_and_struct_size():
     a = b.RouterBwdArgs()
     a.struct_size = C.sizeof(b.RouterBwdArgs) + 4
     assert b.lib().moe_router_bwd(C.byref(a), None) == b.MGE_ERR_INVALID_ARG
+
+
+def _unfused_args(**fwd_fields):
+    u = b.FwdUnfusedArgs()
+    u.struct_size = C.sizeof(b.FwdUnfusedArgs)
+    u.fwd.struct_size = C.sizeof(b.FwdArgs)
+    for k, v in dict(prec=1, E=4, H=64, F=128, T=8, k=2, align=32, y_dtype=0).items():
+        setattr(u.fwd, k, v)
+    for k, v in fwd_fields.items():
+        setattr(u.fwd, k, v)
+    return u
+
+
+def test_fwd_unfused_rejects_and_workspace():
+    L = b.lib()
+    u = _unfused_args()
+    # workspace: the fused forward's plus [G U] bf16 and the bf16 h (both absent), R = 160 rows
+    R = b.perm_rows(8, 2, 4, 32)
+    fused = L.mge_fwd_workspace_bytes(C.byref(u.fwd))
+    assert L.mge_fwd_unfused_workspace_bytes(C.byref(u)) == fused + R * 2 * 128 * 2 + R * 128 * 2
+    u.gu = 1 << 20
+    assert L.mge_fwd_unfused_workspace_bytes(C.byref(u)) == fused + R * 128 * 2
+    # struct sizes of both levels are checked
+    u = _unfused_args()
+    u.struct_size -= 8
+    assert L.grouped_mlp_fwd_unfused(C.byref(u), None) == b.MGE_ERR_INVALID_ARG
+    u = _unfused_args()
+    u.fwd.struct_size -= 8
+    assert L.grouped_mlp_fwd_unfused(C.byref(u), None) == b.MGE_ERR_INVALID_ARG
+    # inference only: training buffers are rejected before any launch (fake device addresses)
+    ptrs = (C.c_void_p * 4)(*[(i + 1) << 20 for i in range(4)])
+    dev = {n: (i + 8) << 20 for i, n in enumerate(("split_sizes", "group_offsets", "prob_perm", "x_perm",
+                                                     "x_perm_scale", "y_perm"))}
+    u = _unfused_args(w_gate_up=C.cast(ptrs, C.c_void_p), w_down=C.cast(ptrs, C.c_void_p),
+                      w_gate_up_scale=C.cast(ptrs, C.c_void_p), w_down_scale=C.cast(ptrs, C.c_void_p),
+                      saved_gu=1 << 30, h_col=1 << 31, h_col_scale=1 << 32, **dev)
+    assert L.grouped_mlp_fwd_unfused(C.byref(u), None) == b.MGE_ERR_INVALID_ARG
+    assert "inference only" in L.mge_last_error().decode()
