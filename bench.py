@@ -204,18 +204,20 @@ class Step:
 
 # ------------------------------------------------------------------------------ per-kernel work
 
-def kernel_work(name, w, R):
+def kernel_work(name, w, R, launches_per_step=1.0):
     """Algorithmic work of one launch of a library kernel: ("flop", n) or ("byte", n).
 
-    GEMMs: the method's flops on the M = T*k real rows (no padding rows).  HBM-bound
-    kernels: bytes that must cross HBM once (inputs read, outputs written)."""
+    GEMMs: the method's flops on the M = T*k real rows (no padding rows), shared by the
+    step's launches of that GEMM (one grouped launch, or one per expert in the expert
+    loop).  HBM-bound kernels: bytes that must cross HBM once (inputs read, outputs
+    written) per launch."""
     M, H, F, T, k, E = w.M, w.H, w.F, w.T, w.k, w.E
     mhf = float(M) * H * F
     gemm = {"gemm_gateup_swiglu": 4 * mhf, "gemm_gateup_store": 4 * mhf, "gemm_down": 2 * mhf, "gemm_dh": 2 * mhf,
             "gemm_dx": 4 * mhf, "gemm_dw_down": 2 * mhf, "gemm_dw_gateup": 4 * mhf}
     for key, v in gemm.items():
         if name.startswith(key + "_"):
-            return "flop", v
+            return "flop", v / max(launches_per_step, 1.0)
     mxb = 1.0 + 1.0 / 32.0            # bytes per MXFP8 element (code + scale share)
     if name == "permute_quant_mx":
         # x or dy gathered (bf16 read once per token) -> row and (training) column forms
@@ -258,7 +260,7 @@ def summarize_kernels(records, steps, w, R, prec):
         avg = a["total_ms"] / a["launches"]
         d = dict(launches_per_step=a["launches"] / steps, avg_ms=round(avg, 5),
                  share=round(a["total_ms"] / total, 4) if total > 0 else None)
-        wk = kernel_work(name, w, R)
+        wk = kernel_work(name, w, R, a["launches"] / steps)
         if wk is not None:
             kind, n = wk
             if kind == "flop":
@@ -529,7 +531,7 @@ def main():
     kernels, kern_ms = summarize_kernels(records, args.steps, w, R, w.prec)
     dom = next(iter(kernels))
     dk = kernels[dom]
-    wk = kernel_work(dom, w, R)
+    wk = kernel_work(dom, w, R, dk["launches_per_step"])
     if wk and wk[0] == "flop":
         ach = wk[1] / (dk["avg_ms"] * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_TFLOPS[w.prec],
