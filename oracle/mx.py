@@ -15,6 +15,9 @@ and the scale-selection rule come from the OCP MX v1.0 specification [OCP]:
     saturating magnitudes beyond 448 to 448 (the conversion the spec allows
     when clamping is chosen).
 
+FP8 with one scale per tensor (quantize_tensor) applies the same rule with the
+whole tensor as the block.
+
 Readings where the pages are silent (listed in the design notes): floor rule
 with saturation (not the ceil/no-clip rule); -0 encodes as 0x80; partial
 blocks are zero-padded.
@@ -108,6 +111,29 @@ def quantize_cols(v) -> tuple[np.ndarray, np.ndarray]:
     """
     v = np.asarray(v, dtype=np.float64)
     return quantize_rows(np.swapaxes(v, -1, -2))
+
+
+def quantize_tensor(v) -> tuple[np.ndarray, np.uint8]:
+    """FP8 with one scale for the whole tensor: E4M3 codes (same shape as v) and one
+    E8M0 scale byte.
+
+    The pages name FP8 beside MXFP8, both 8-bit, MXFP8 adding a scale per block of 32
+    ([P1] "Memory and quantization overhead"; [P4] paragraph on FP8/MXFP8); they do not
+    say how the FP8 scale is chosen.  Reading: the MX rule above with the whole tensor as
+    the block ("current" scaling from the tensor's own amax, a power-of-two scale):
+    e = floor(log2 amax) - 8 clamped to [-127, 127] (all-zero: -127), codes =
+    RNE(v / 2^e) onto E4M3 with saturation at 448.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    amax = float(np.max(np.abs(v))) if v.size else 0.0
+    e = int(block_scale_exponent(amax))
+    codes = e4m3_encode(v * np.exp2(-float(e)))
+    return codes, np.uint8(e + SCALE_BIAS)
+
+
+def dequantize_tensor(codes, scale) -> np.ndarray:
+    """Inverse of quantize_tensor's encoding: element value * 2^(scale-127)."""
+    return e4m3_decode(codes) * float(e8m0_decode(scale))
 
 
 def dequantize_rows(codes, scales) -> np.ndarray:

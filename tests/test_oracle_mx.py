@@ -195,3 +195,50 @@ def test_mx_matmul_unit_scales_is_matmul():
     got = mx.mx_matmul_nt(qa, sa2, qb, sb)
     np.testing.assert_allclose(got[3], ref[3] + part, rtol=1e-14)
     np.testing.assert_allclose(np.delete(got, 3, 0), np.delete(ref, 3, 0), rtol=1e-14)
+
+
+# ------------------------------------------------------------------------------ FP8, one scale per tensor
+
+def test_tensor_quantize_equals_block_quantize_when_blocks_share_the_amax():
+    """Special case that reduces to the pinned block quantizer: every 32-block holds the
+    tensor's amax, so each block's scale is the tensor's and the codes coincide."""
+    rng = np.random.default_rng(31)
+    for amax in (448.0, 3.0, 2.0 ** -20, 1e30):
+        v = rng.uniform(-amax, amax, size=(12, 96))
+        v[:, ::32] = amax * np.where(rng.random((12, 3)) < 0.5, -1.0, 1.0)
+        q, s = mx.quantize_tensor(v)
+        qb, sb = mx.quantize_rows(v)
+        assert np.all(sb == s)
+        np.testing.assert_array_equal(q, qb)
+
+
+def test_tensor_quantize_brute_force_and_underflow():
+    """Every code is the nearest E4M3 value of v / 2^e (ties to even, saturating), with e
+    fixed by the tensor amax; values far below the amax go subnormal or to zero, which a
+    block scale would have rescued."""
+    rng = np.random.default_rng(32)
+    mag = np.exp2(rng.uniform(-40, 8, size=4000))
+    v = mag * np.where(rng.random(4000) < 0.5, -1.0, 1.0)
+    q, s = mx.quantize_tensor(v)
+    e = int(s) - 127
+    amax = np.max(np.abs(v))
+    assert 256.0 <= amax * 2.0 ** -e < 512.0
+    np.testing.assert_array_equal(q, nearest_code(v * 2.0 ** -e))
+    small = np.abs(v) < 2.0 ** (e - 10)        # below half the smallest subnormal
+    assert small.any() and np.all((q[small] & 0x7F) == 0)
+
+
+def test_tensor_quantize_zero_exact_and_idempotent():
+    q, s = mx.quantize_tensor(np.zeros((4, 64)))
+    assert s == 0 and not q.any()
+    # exactly representable values (E4M3 x 2^e with the tensor's amax in [256, 448] x 2^e) round-trip
+    rng = np.random.default_rng(33)
+    codes = rng.integers(0, 0x7F, size=(8, 64)).astype(np.uint8) | np.where(rng.random((8, 64)) < 0.5, 0x80, 0).astype(np.uint8)
+    codes[0, 0] = 0x7E                          # 448: the amax, scale 2^-3 below
+    v = mx.e4m3_decode(codes) * 2.0 ** -3
+    q, s = mx.quantize_tensor(v)
+    assert s == 127 - 3
+    np.testing.assert_array_equal(mx.dequantize_tensor(q, s), v)
+    q2, s2 = mx.quantize_tensor(mx.dequantize_tensor(q, s))
+    np.testing.assert_array_equal(q2, q)
+    assert s2 == s
