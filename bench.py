@@ -58,8 +58,11 @@ WORKLOADS = {
 # one launch per expert and projection with the same kernels ("expert_loop", the
 # per-expert loop the grouped call replaces); or grouped launches without the fusion,
 # [G U] through HBM in bf16, a standalone SwiGLU x prob and a standalone quantize of h
-# ("unfused", what the fused operation replaces).
-VARIANTS = ("grouped", "expert_loop", "unfused")
+# ("unfused", what the fused operation replaces); or the unfused chain in FP8 with one
+# scale per tensor instead of one per block of 32 ("fp8_tensor": x, each expert's
+# weights and h each take one power-of-two scale from their amax; the GEMMs are the
+# block-scaled ones with every block of a tensor on the same scale).
+VARIANTS = ("grouped", "expert_loop", "unfused", "fp8_tensor")
 
 
 def log(*a):
@@ -142,6 +145,7 @@ class Step:
         self.f = self.b = None
         self.y = self.dx = self.dl = None
         self.groups = None
+        self.ts = {}
 
     def _fwd_expert_loop(self):
         """E launches of each projection: expert e's group alone, as a one-expert call
@@ -163,9 +167,28 @@ class Step:
                 self.f = m.grouped_mlp_fwd(ge, self.inp["wgu"][e:e + 1], self.inp["wd"][e:e + 1], out=self.f)
         return self.f
 
+    def _fwd_fp8_tensor(self):
+        """FP8 with one scale per tensor: the scale of x, of each expert's W_gate_up and
+        W_down, and of h (inside the unfused forward) from their amax, every block of a
+        tensor quantized with it."""
+        m, w, inp, ts = self.m, self.w, self.inp, self.ts
+        ts["x"] = m.tensor_scale(inp["x"], out=ts.get("x"))
+        self.g = m.moe_route_permute(inp["logits"], inp["x"], w.k, align=32, prec="mxfp8", out=self.g,
+                                     x_tensor_scale=ts["x"].scale)
+        ts["wgu"] = m.tensor_scale(inp["wgu"], per_matrix=True, out=ts.get("wgu"))
+        ts["wd"] = m.tensor_scale(inp["wd"], per_matrix=True, out=ts.get("wd"))
+        self.wq = m.mxfp8_quantize(inp["wgu"], "row", out=self.wq, tensor_scale=ts["wgu"].scale)
+        self.dq = m.mxfp8_quantize(inp["wd"], "row", out=self.dq, tensor_scale=ts["wd"].scale)
+        self.f = m.grouped_mlp_fwd_unfused(self.g, self.wq[0], self.dq[0], self.wq[1], self.dq[1], h_per_tensor=True,
+                                           keep_intermediates=self.keep_intermediates, out=self.f)
+        self.y = m.unpermute_combine(self.f.y_perm, self.g.perm_pos, out=self.y)
+
     def __call__(self):
         m, w, inp = self.m, self.w, self.inp
         mx = self.prec == "mxfp8"
+        if self.variant == "fp8_tensor":
+            self._fwd_fp8_tensor()
+            return
         if self.given:
             self.g = m.moe_route_permute(None, inp["x"], 1, E=w.E, align=32, prec=self.prec, want_col=self.train,
                                          topk_idx=inp["idx"], topk_prob=inp["prob"], out=self.g)
@@ -491,6 +514,9 @@ def main():
     dev = torch.device("cuda:0")
     wid, train = WORKLOADS[args.workload]
     w = synth.WORKLOADS[wid]
+    if args.variant == "fp8_tensor" and (wid not in (2, 3)):
+        print("the fp8_tensor variant runs the MXFP8 forward workloads (fwd_mxfp8, fwd_mxfp8_skew)", file=sys.stderr)
+        sys.exit(2)
     if args.variant != "grouped" and train:
         print(f"the {args.variant} variant runs forward workloads only", file=sys.stderr)
         sys.exit(2)
@@ -548,7 +574,8 @@ def main():
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w.prec, "data": "synthetic",
+        "vs_baseline": None, "dtype": "fp8" if args.variant == "fp8_tensor" else w.prec,
+        "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "E": w.E, "H": w.H, "F": w.F, "k": w.k, "prec": w.prec,
                    "passes": "fwd+bwd" if train else "fwd", "align": 32, "split_sizes": sizes,
                    "parallelism": "single GPU", "variant": args.variant},

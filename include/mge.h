@@ -124,6 +124,11 @@ typedef struct mge_route_args {
   uint8_t* x_col_scale;      /* [H][R/32] (MXFP8, MGE_ROUTE_WANT_COL) */
   void* workspace;
   size_t workspace_bytes;
+  /* Added field (a struct_size that ends before it means NULL): optional, MXFP8 only —
+   * one E8M0 scale byte for all of x (FP8 with one scale per tensor, e.g. from
+   * mge_tensor_scale): every block of x_perm / x_col then takes it, and the scale
+   * arrays hold it on every row, padding rows included. */
+  const uint8_t* x_tensor_scale;
 } mge_route_args;
 
 size_t mge_route_workspace_bytes(int32_t T, int32_t E);
@@ -153,9 +158,40 @@ typedef struct mge_quant_args {
   uint8_t* row_scales;
   uint8_t* col_codes;
   uint8_t* col_scales;
+  /* Added field (a struct_size that ends before it means NULL): optional [batch] E8M0
+   * bytes, one per matrix — FP8 with one scale per tensor: every block of matrix b
+   * takes tensor_scale[b] instead of its own, and the scale arrays hold it replicated,
+   * so the block-scaled GEMMs read the result unchanged. */
+  const uint8_t* tensor_scale;
 } mge_quant_args;
 
 mge_status mxfp8_quantize(const mge_quant_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * mge_tensor_scale — the one scale of FP8 with one scale per tensor.  The pages name
+ * FP8 beside MXFP8 (both 8-bit, MXFP8 adding a scale per block of 32: "NVIDIA Shows
+ * an Efficient MoE Training Path ..." section "Memory and quantization overhead"; the
+ * ai4snews report's paragraph on FP8/MXFP8) without the FP8 scale rule; this library
+ * takes the block rule above with the whole tensor as the block: for each of `batch`
+ * bf16 tensors of n elements (tensor b at in + b*batch_stride elements),
+ *   scale[b] = clamp(floor(log2(max |v|)) - 8, -127, 127) + 127   (all-zero: 0).
+ * Feed it to mxfp8_quantize / moe_route_permute as tensor_scale / x_tensor_scale.
+ * Workspace: mge_tensor_scale_workspace_bytes(batch, n).  n = 0 gives scale 0.
+ * Errors: MGE_ERR_INVALID_ARG for NULL in/scale (batch > 0), batch outside [0, 65535],
+ * n < 0 or batch_stride < n (batch > 1).
+ * ---------------------------------------------------------------------------- */
+typedef struct mge_tensor_scale_args {
+  uint32_t struct_size;
+  int32_t batch;
+  int64_t n, batch_stride;
+  const uint16_t* in;
+  uint8_t* scale;                        /* [batch] */
+  void* workspace;
+  size_t workspace_bytes;
+} mge_tensor_scale_args;
+
+size_t mge_tensor_scale_workspace_bytes(int32_t batch, int64_t n);
+mge_status mge_tensor_scale(const mge_tensor_scale_args* args, void* stream);
 
 /* ------------------------------------------------------------------------------
  * grouped_mlp_fwd — GroupedLinear(gate_up) -> ScaledSwiGLU -> GroupedLinear(down)
@@ -213,7 +249,8 @@ mge_status grouped_mlp_fwd(const mge_fwd_args* args, void* stream);
  *   2. a standalone SwiGLU x prob kernel: h = p * silu(G) * U in fp32 from the bf16
  *      G, U, rounded to bf16 ([R][F]; rows with p = 0 get 0);
  *   3. MXFP8 only: a standalone quantize of that bf16 h along F (the row form
- *      mxfp8_quantize writes) into h / h_scale;
+ *      mxfp8_quantize writes) into h / h_scale, by blocks, or with one scale for all
+ *      of h when h_tensor_scale is given;
  *   4. the grouped down GEMM, as in grouped_mlp_fwd.
  * fwd: grouped_mlp_fwd's arguments; saved_gu, h_col and h_col_scale must be NULL.
  * Its workspace fields carry this call's workspace.
@@ -230,6 +267,10 @@ typedef struct mge_fwd_unfused_args {
   mge_fwd_args fwd;
   uint16_t* gu;                          /* optional [R][2F] bf16 */
   uint16_t* h_bf16;                      /* optional [R][F] bf16 (MXFP8) */
+  uint8_t* h_tensor_scale;               /* optional (MXFP8): FP8 with one scale per tensor for h —
+                                            step 3 first takes h's one scale (as mge_tensor_scale
+                                            over [R][F]; padding rows are 0) into this byte, then
+                                            quantizes every block of h with it */
 } mge_fwd_unfused_args;
 
 size_t mge_fwd_unfused_workspace_bytes(const mge_fwd_unfused_args* args);

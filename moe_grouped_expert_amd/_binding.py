@@ -34,13 +34,18 @@ class RouteArgs(C.Structure):
                 ("logits", vp), ("x", vp), ("topk_idx", vp), ("topk_prob", vp), ("split_sizes", vp),
                 ("group_offsets", vp), ("perm_src", vp), ("perm_pos", vp), ("prob_perm", vp),
                 ("x_perm", vp), ("x_perm_scale", vp), ("x_col", vp), ("x_col_scale", vp),
-                ("workspace", vp), ("workspace_bytes", C.c_size_t)]
+                ("workspace", vp), ("workspace_bytes", C.c_size_t), ("x_tensor_scale", vp)]
 
 
 class QuantArgs(C.Structure):
     _fields_ = [("struct_size", u32), ("batch", i32), ("R", i32), ("C", i32),
                 ("in_batch_stride", i64), ("in_row_stride", i64), ("in_", vp), ("orient", u32),
-                ("row_codes", vp), ("row_scales", vp), ("col_codes", vp), ("col_scales", vp)]
+                ("row_codes", vp), ("row_scales", vp), ("col_codes", vp), ("col_scales", vp), ("tensor_scale", vp)]
+
+
+class TensorScaleArgs(C.Structure):
+    _fields_ = [("struct_size", u32), ("batch", i32), ("n", i64), ("batch_stride", i64), ("in_", vp),
+                ("scale", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t)]
 
 
 class FwdArgs(C.Structure):
@@ -54,7 +59,7 @@ class FwdArgs(C.Structure):
 
 
 class FwdUnfusedArgs(C.Structure):
-    _fields_ = [("struct_size", u32), ("fwd", FwdArgs), ("gu", vp), ("h_bf16", vp)]
+    _fields_ = [("struct_size", u32), ("fwd", FwdArgs), ("gu", vp), ("h_bf16", vp), ("h_tensor_scale", vp)]
 
 
 class BwdArgs(C.Structure):
@@ -83,7 +88,7 @@ class RouterBwdArgs(C.Structure):
 _LIB = None
 EXPORTS = ["mge_perm_rows", "mge_route_workspace_bytes", "moe_route_permute", "mxfp8_quantize",
            "mge_fwd_workspace_bytes", "grouped_mlp_fwd", "mge_fwd_unfused_workspace_bytes", "grouped_mlp_fwd_unfused",
-           "mge_bwd_workspace_bytes", "grouped_mlp_bwd",
+           "mge_tensor_scale_workspace_bytes", "mge_tensor_scale", "mge_bwd_workspace_bytes", "grouped_mlp_bwd",
            "unpermute_combine", "moe_router_bwd", "mge_status_string", "mge_last_error", "mge_check_device_errors", "mge_version",
            "mge_profile_start", "mge_profile_stop"]
 
@@ -107,9 +112,12 @@ def lib():
         L.mge_fwd_workspace_bytes.argtypes = [C.POINTER(FwdArgs)]
         L.mge_fwd_unfused_workspace_bytes.restype = C.c_size_t
         L.mge_fwd_unfused_workspace_bytes.argtypes = [C.POINTER(FwdUnfusedArgs)]
+        L.mge_tensor_scale_workspace_bytes.restype = C.c_size_t
+        L.mge_tensor_scale_workspace_bytes.argtypes = [i32, i64]
         L.mge_bwd_workspace_bytes.restype = C.c_size_t
         L.mge_bwd_workspace_bytes.argtypes = [C.POINTER(BwdArgs)]
         for name, st in (("moe_route_permute", RouteArgs), ("mxfp8_quantize", QuantArgs),
+                         ("mge_tensor_scale", TensorScaleArgs),
                          ("grouped_mlp_fwd", FwdArgs), ("grouped_mlp_fwd_unfused", FwdUnfusedArgs),
                          ("grouped_mlp_bwd", BwdArgs),
                          ("unpermute_combine", CombineArgs), ("moe_router_bwd", RouterBwdArgs)):
@@ -188,8 +196,10 @@ class RouteOut:
 def moe_route_permute(logits: Optional[torch.Tensor], x: Optional[torch.Tensor], k: int, E: Optional[int] = None,
                       align: int = 32, prec: str = "bf16", want_col: bool = False,
                       topk_idx: Optional[torch.Tensor] = None, topk_prob: Optional[torch.Tensor] = None,
-                      out: Optional[RouteOut] = None) -> RouteOut:
-    """Top-k routing + stable permutation by expert (+ gather / quantize of x)."""
+                      out: Optional[RouteOut] = None, x_tensor_scale: Optional[torch.Tensor] = None) -> RouteOut:
+    """Top-k routing + stable permutation by expert (+ gather / quantize of x; with
+    x_tensor_scale, a uint8 [1] tensor from tensor_scale(x), every block of x takes that
+    one scale)."""
     given = topk_idx is not None
     ref = logits if logits is not None else topk_idx
     dev = ref.device
@@ -239,6 +249,7 @@ def moe_route_permute(logits: Optional[torch.Tensor], x: Optional[torch.Tensor],
     a.x_perm, a.x_perm_scale = _ptr(o.x_perm), _ptr(o.x_perm_scale)
     a.x_col, a.x_col_scale = _ptr(o.x_col), _ptr(o.x_col_scale)
     a.workspace, a.workspace_bytes = _ptr(o.workspace), o.workspace.numel()
+    a.x_tensor_scale = _ptr(x_tensor_scale)
     _check(lib().moe_route_permute(C.byref(a), _stream(dev)), "moe_route_permute")
     return o
 
@@ -249,8 +260,10 @@ def check_device_errors(route: RouteOut) -> int:
 
 # ------------------------------------------------------------------------------ quantize
 
-def mxfp8_quantize(w: torch.Tensor, orient: str = "row", out=None):
-    """BF16 [..., R, C] -> (row_codes, row_scales, col_codes, col_scales) (absent ones None)."""
+def mxfp8_quantize(w: torch.Tensor, orient: str = "row", out=None, tensor_scale: Optional[torch.Tensor] = None):
+    """BF16 [..., R, C] -> (row_codes, row_scales, col_codes, col_scales) (absent ones None).
+    tensor_scale: optional uint8 [batch] (one scale per matrix, from tensor_scale(w,
+    per_matrix=True)) that every block of its matrix takes instead of its own."""
     assert w.dtype == torch.bfloat16 and w.is_contiguous()
     R, Cc = w.shape[-2], w.shape[-1]
     lead = tuple(w.shape[:-2])
@@ -276,8 +289,37 @@ def mxfp8_quantize(w: torch.Tensor, orient: str = "row", out=None):
     a.in_ = _ptr(w)
     a.orient = (ORIENT_ROW if want_row else 0) | (ORIENT_COL if want_col else 0)
     a.row_codes, a.row_scales, a.col_codes, a.col_scales = _ptr(rc), _ptr(rs), _ptr(cc), _ptr(cs)
+    if tensor_scale is not None:
+        assert tensor_scale.dtype == torch.uint8 and tensor_scale.numel() == batch
+    a.tensor_scale = _ptr(tensor_scale)
     _check(lib().mxfp8_quantize(C.byref(a), _stream(dev)), "mxfp8_quantize")
     return rc, rs, cc, cs
+
+
+@dataclass
+class TensorScaleOut:
+    scale: torch.Tensor        # uint8 [batch]
+    workspace: torch.Tensor
+
+
+def tensor_scale(t: torch.Tensor, per_matrix: bool = False, out: Optional[TensorScaleOut] = None) -> TensorScaleOut:
+    """One E8M0 scale per tensor (FP8 with one scale per tensor): of all of t, or with
+    per_matrix of each t[b] along the leading dimension."""
+    assert t.dtype == torch.bfloat16 and t.is_contiguous()
+    batch = t.shape[0] if per_matrix else 1
+    n = t.numel() // max(batch, 1)
+    dev = t.device
+    if out is None:
+        ws = int(lib().mge_tensor_scale_workspace_bytes(batch, n))
+        out = TensorScaleOut(scale=torch.empty(batch, device=dev, dtype=torch.uint8),
+                             workspace=torch.empty(max(ws, 256), device=dev, dtype=torch.uint8))
+    a = TensorScaleArgs()
+    a.struct_size = C.sizeof(TensorScaleArgs)
+    a.batch, a.n, a.batch_stride = batch, n, n
+    a.in_, a.scale = _ptr(t), _ptr(out.scale)
+    a.workspace, a.workspace_bytes = _ptr(out.workspace), out.workspace.numel()
+    _check(lib().mge_tensor_scale(C.byref(a), _stream(dev)), "mge_tensor_scale")
+    return out
 
 
 # ------------------------------------------------------------------------------ forward
@@ -293,6 +335,7 @@ class FwdOut:
     workspace: Optional[torch.Tensor] = None
     gu: Optional[torch.Tensor] = None          # unfused forward: [G U] bf16 (kept on request)
     h_bf16: Optional[torch.Tensor] = None      # unfused MXFP8 forward: h before its quantize
+    h_tensor_scale: Optional[torch.Tensor] = None  # unfused, one scale for all of h: uint8 [1]
 
 
 def _split(w, E):
@@ -352,14 +395,18 @@ def grouped_mlp_fwd(rt: RouteOut, w_gate_up, w_down, w_gate_up_scale=None, w_dow
 
 
 def grouped_mlp_fwd_unfused(rt: RouteOut, w_gate_up, w_down, w_gate_up_scale=None, w_down_scale=None,
-                            y_dtype: str = "bf16", keep_intermediates: bool = False,
+                            y_dtype: str = "bf16", keep_intermediates: bool = False, h_per_tensor: bool = False,
                             out: Optional[FwdOut] = None) -> FwdOut:
     """The forward without the fusion (inference): [G U] to HBM in bf16, a standalone
     SwiGLU x prob, (MXFP8) a standalone quantize of h, the grouped down GEMM.  With
-    keep_intermediates, out.gu ([R][2F] bf16) and (MXFP8) out.h_bf16 ([R][F]) are kept."""
+    keep_intermediates, out.gu ([R][2F] bf16) and (MXFP8) out.h_bf16 ([R][F]) are kept;
+    with h_per_tensor, h takes one scale for the whole tensor (out.h_tensor_scale)."""
     o, a, keep, F, dev = _fwd_args(rt, w_gate_up, w_down, w_gate_up_scale, w_down_scale, y_dtype, False, out)
     u = FwdUnfusedArgs()
     u.struct_size = C.sizeof(FwdUnfusedArgs)
+    if h_per_tensor and o.h_tensor_scale is None:
+        o.h_tensor_scale = torch.empty(1, device=dev, dtype=torch.uint8)
+    u.h_tensor_scale = _ptr(o.h_tensor_scale)
     if keep_intermediates and o.gu is None:
         o.gu = torch.empty((rt.R, 2 * F), device=dev, dtype=torch.bfloat16)
         if rt.prec == "mxfp8":

@@ -165,8 +165,11 @@ size_t mge_route_workspace_bytes(int32_t T, int32_t E) {
 mge_status moe_route_permute(const mge_route_args* a, void* stream) {
   g_err[0] = 0;
   MGE_REQUIRE(a != nullptr, "args is NULL");
-  MGE_REQUIRE(a->struct_size == sizeof(mge_route_args), "struct_size mismatch (%u vs %zu)", a->struct_size,
-              sizeof(mge_route_args));
+  // the struct may end before its added last field (x_tensor_scale: then NULL)
+  MGE_REQUIRE(a->struct_size == sizeof(mge_route_args) || a->struct_size == offsetof(mge_route_args, x_tensor_scale),
+              "struct_size mismatch (%u vs %zu)", a->struct_size, sizeof(mge_route_args));
+  const uint8_t* x_ts = a->struct_size == sizeof(mge_route_args) ? a->x_tensor_scale : nullptr;
+  MGE_REQUIRE(!x_ts || (a->x && a->prec == MGE_PREC_MXFP8), "x_tensor_scale needs x and prec MXFP8");
   mge_status st = check_common(a->T, a->E, a->k, a->H, a->align);
   if (st != MGE_OK) return st;
   MGE_REQUIRE(a->prec == MGE_PREC_BF16 || a->prec == MGE_PREC_MXFP8, "prec must be BF16 or MXFP8");
@@ -218,6 +221,7 @@ mge_status moe_route_permute(const mge_route_args* a, void* stream) {
   q.in = a->x; q.in_batch_stride = 0; q.in_row_stride = a->H;
   q.gather = a->perm_src;
   q.batch = 1; q.R = R; q.C = a->H; q.Rp = R;
+  q.tensor_scale = x_ts;
   if (a->prec == MGE_PREC_MXFP8) {
     q.row_codes = static_cast<uint8_t*>(a->x_perm);
     q.row_scales = a->x_perm_scale;
@@ -233,7 +237,10 @@ mge_status moe_route_permute(const mge_route_args* a, void* stream) {
 mge_status mxfp8_quantize(const mge_quant_args* a, void* stream) {
   g_err[0] = 0;
   MGE_REQUIRE(a != nullptr, "args is NULL");
-  MGE_REQUIRE(a->struct_size == sizeof(mge_quant_args), "struct_size mismatch");
+  // the struct may end before its added last field (tensor_scale: then NULL)
+  MGE_REQUIRE(a->struct_size == sizeof(mge_quant_args) || a->struct_size == offsetof(mge_quant_args, tensor_scale),
+              "struct_size mismatch");
+  const uint8_t* ts = a->struct_size == sizeof(mge_quant_args) ? a->tensor_scale : nullptr;
   MGE_REQUIRE(a->batch >= 0 && a->R >= 0 && a->C >= 0, "negative size");
   MGE_REQUIRE(a->C % 32 == 0, "C must be a multiple of 32 (got %d)", a->C);
   MGE_REQUIRE(a->orient != 0 && (a->orient & ~3u) == 0, "orient must be ROW, COL or ROW|COL");
@@ -251,7 +258,32 @@ mge_status mxfp8_quantize(const mge_quant_args* a, void* stream) {
   q.batch = a->batch; q.R = a->R; q.C = a->C; q.Rp = (a->R + 31) / 32 * 32;
   if (a->orient & MGE_ORIENT_ROW) { q.row_codes = a->row_codes; q.row_scales = a->row_scales; }
   if (a->orient & MGE_ORIENT_COL) { q.col_codes = a->col_codes; q.col_scales = a->col_scales; }
+  q.tensor_scale = ts;
   return launch_quant_tile(q, true, static_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------------------------ per-tensor scale
+size_t mge_tensor_scale_workspace_bytes(int32_t batch, int64_t n) {
+  if (batch < 0 || n < 0) return 0;
+  return up256(size_t(tensor_scale_parts(n)) * size_t(batch) * sizeof(float));
+}
+
+mge_status mge_tensor_scale(const mge_tensor_scale_args* a, void* stream) {
+  g_err[0] = 0;
+  MGE_REQUIRE(a != nullptr, "args is NULL");
+  MGE_REQUIRE(a->struct_size == sizeof(mge_tensor_scale_args), "struct_size mismatch");
+  MGE_REQUIRE(a->batch >= 0 && a->batch <= 65535, "batch must be in [0, 65535] (got %d)", a->batch);
+  MGE_REQUIRE(a->n >= 0, "n must be >= 0");
+  MGE_REQUIRE(a->batch <= 1 || a->batch_stride >= a->n, "batch_stride must be >= n");
+  if (a->batch == 0) return MGE_OK;
+  MGE_REQUIRE(a->in && a->scale, "in / scale is NULL");
+  const size_t need = mge_tensor_scale_workspace_bytes(a->batch, a->n);
+  if (!a->workspace || a->workspace_bytes < need) {
+    set_error("tensor-scale workspace needs %zu bytes (got %zu)", need, a->workspace_bytes);
+    return MGE_ERR_WORKSPACE;
+  }
+  return launch_tensor_scale(a->in, a->batch, a->n, a->batch_stride, static_cast<float*>(a->workspace), a->scale,
+                             static_cast<hipStream_t>(stream));
 }
 
 // ------------------------------------------------------------------ forward
@@ -299,6 +331,7 @@ static size_t fwd_unfused_extra(const mge_fwd_unfused_args* u, int R) {
   size_t n = 0;
   if (!u->gu) n += up256(size_t(R) * 2 * a->F * 2);
   if (a->prec == MGE_PREC_MXFP8 && !u->h_bf16) n += up256(size_t(R) * a->F * 2);
+  if (u->h_tensor_scale) n += up256(size_t(tensor_scale_parts(int64_t(R) * a->F)) * sizeof(float));
   return n;
 }
 
@@ -343,6 +376,7 @@ static mge_status fwd_impl(const mge_fwd_args* a, const mge_fwd_unfused_args* u,
   if (u) {
     MGE_REQUIRE(!train && !a->h_col && !a->h_col_scale, "the unfused forward is inference only (saved_gu, h_col NULL)");
     MGE_REQUIRE((!u->gu || aligned16(u->gu)) && (!u->h_bf16 || aligned16(u->h_bf16)), "gu / h_bf16 misaligned");
+    MGE_REQUIRE(!u->h_tensor_scale || mx, "h_tensor_scale needs prec MXFP8");
   }
   const int R = int(mge_perm_rows(a->T, a->k, a->E, a->align));
   const size_t need = fwd_ws(a, R) + (u ? fwd_unfused_extra(u, R) : 0);
@@ -366,6 +400,9 @@ static mge_status fwd_impl(const mge_fwd_args* a, const mge_fwd_unfused_args* u,
     gu = u->gu ? u->gu : static_cast<uint16_t*>(ws.take(size_t(R) * 2 * a->F * 2));
     hb = !mx ? static_cast<uint16_t*>(h) : u->h_bf16 ? u->h_bf16 : static_cast<uint16_t*>(ws.take(size_t(R) * a->F * 2));
   }
+  float* h_amax_part = (u && u->h_tensor_scale)
+                           ? static_cast<float*>(ws.take(size_t(tensor_scale_parts(int64_t(R) * a->F)) * sizeof(float)))
+                           : nullptr;
   const int E = a->E;
   {
     const void* const* tabs[4] = {reinterpret_cast<const void* const*>(a->w_gate_up),
@@ -434,6 +471,11 @@ static mge_status fwd_impl(const mge_fwd_args* a, const mge_fwd_unfused_args* u,
       q.in = hb; q.in_batch_stride = int64_t(R) * F; q.in_row_stride = F;
       q.batch = 1; q.R = R; q.C = F; q.Rp = R;
       q.row_codes = static_cast<uint8_t*>(h); q.row_scales = hs;
+      if (u->h_tensor_scale) {   // one scale for all of h: its amax first
+        st = launch_tensor_scale(hb, 1, int64_t(R) * F, 0, h_amax_part, u->h_tensor_scale, s);
+        if (st != MGE_OK) return st;
+        q.tensor_scale = u->h_tensor_scale;
+      }
       st = launch_quant_tile(q, true, s, "quant_h_mx");
       if (st != MGE_OK) return st;
     }

@@ -32,9 +32,17 @@ struct QuantTileParams {
   uint16_t* row_bf16;                        // bf16 row copy [b][R][C]
   uint8_t* col_codes;  uint8_t* col_scales;  // MX column form [b][C][Rp], [b][C][Rp/32]
   uint16_t* col_bf16;                        // bf16 transpose [b][C][Rp]
+  const uint8_t* tensor_scale;               // optional [b]: one E8M0 scale per batch entry for every block
 };
 // timing_name: the launch's name for per-kernel timing (NULL: by form)
 mge_status launch_quant_tile(const QuantTileParams& p, bool mx, hipStream_t s, const char* timing_name = nullptr);
+
+// One E8M0 scale per tensor (FP8 with one scale per tensor): amax of each of `batch`
+// bf16 tensors of n elements (batch stride bstride elements) -> scale[b] by the block
+// rule.  part: tensor_scale_parts(n) * batch floats of workspace.
+int tensor_scale_parts(int64_t n);
+mge_status launch_tensor_scale(const uint16_t* in, int batch, int64_t n, int64_t bstride, float* part,
+                               uint8_t* scale, hipStream_t s);
 
 // E8M0 scales [rows][kb] (kb bytes per row, row stride ld bytes) -> the packed layout
 // the GEMM reads: dst[b][j][r] = bytes 4j..4j+3 of row r as one dword (j < ceil(kb/4)).

@@ -10,6 +10,9 @@
 // 10% slower on MI355X).  Where the layout allows it, the 4 scale bytes a quad of lanes
 // produces go out as one dword (single-byte stores cost another 11%).  The bf16 variant
 // of the same kernel writes a plain (gathered) copy and the bf16 transpose.
+// With a per-tensor scale given (FP8 with one scale per tensor), every block takes that
+// scale instead of its own and the scale arrays hold it replicated, so the block-scaled
+// GEMMs consume such operands unchanged.
 // HBM-bound: 2 B read + (1 + 1/32) B written per element and orientation.
 #include "mge_common.hpp"
 #include "mge_internal.hpp"
@@ -26,15 +29,16 @@ constexpr int QT_GRP = 16;
 __device__ __forceinline__ int qt_at(int row, int col) { return row * QT_LDS_STRIDE + (row >> 5) * QT_GRP + col; }
 
 // One block of 32 bf16 values held as 16 packed pairs (low half first) -> 32 E4M3 codes
-// (8 dwords, element order) and the block's E8M0 scale byte.
-__device__ __forceinline__ uint32_t quant32(const uint32_t* w, uint32_t* out) {
+// (8 dwords, element order) and the block's E8M0 scale byte: from the block's amax, or
+// `given` (a tensor's one scale) when it is not negative.
+__device__ __forceinline__ uint32_t quant32(const uint32_t* w, uint32_t* out, int given) {
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     amax = fmaxf(amax, fabsf(__uint_as_float(w[i] << 16)));
     amax = fmaxf(amax, fabsf(__uint_as_float(w[i] & 0xffff0000u)));
   }
-  const uint32_t s = mx_scale_byte(amax);
+  const uint32_t s = given >= 0 ? uint32_t(given) : mx_scale_byte(amax);
   const float inv = mx_inv_scale(s);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -55,6 +59,7 @@ __global__ __launch_bounds__(QT_THREADS) void quant_tile_kernel(QuantTileParams 
   const int r0 = blockIdx.y * QT_ROWS;
   const int b = blockIdx.z;
   const uint16_t* in = p.in + int64_t(b) * p.in_batch_stride;
+  const int given = p.tensor_scale ? int(p.tensor_scale[b]) : -1;   // uniform
 
   // ---- load: thread -> (row r0 + tid/4, columns c0 + (tid%4)*32 .. +32)
   const int rl = tid >> 2;
@@ -81,7 +86,7 @@ __global__ __launch_bounds__(QT_THREADS) void quant_tile_kernel(QuantTileParams 
     const int64_t ob = int64_t(b) * p.R + r;
     if (MX) {
       uint32_t out[8];
-      const uint32_t s = quant32(reinterpret_cast<const uint32_t*>(v), out);
+      const uint32_t s = quant32(reinterpret_cast<const uint32_t*>(v), out, given);
       uint4* dst = reinterpret_cast<uint4*>(p.row_codes + ob * p.C + c);
       dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
       dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
@@ -120,7 +125,7 @@ __global__ __launch_bounds__(QT_THREADS) void quant_tile_kernel(QuantTileParams 
   const int64_t ocol = int64_t(b) * p.C + col;
   if (MX) {
     uint32_t out[8];
-    const uint32_t s = quant32(hw, out);
+    const uint32_t s = quant32(hw, out, given);
     uint4* dst = reinterpret_cast<uint4*>(p.col_codes + ocol * p.Rp + rowb);
     dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
     dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
@@ -137,6 +142,82 @@ __global__ __launch_bounds__(QT_THREADS) void quant_tile_kernel(QuantTileParams 
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[i] = make_uint4(hw[4 * i], hw[4 * i + 1], hw[4 * i + 2], hw[4 * i + 3]);
   }
+}
+
+// ---------------------------------------------------------------- per-tensor scale
+// FP8 with one scale per tensor: amax over each of `batch` tensors of n bf16 values, then
+// the block rule's E8M0 byte of that amax (the whole tensor as one block).  Two launches,
+// no atomics: each workgroup writes the max of its grid-stride share of a tensor, and one
+// workgroup per tensor reduces those partials.  HBM-bound: 2 B read per element.
+constexpr int TS_THREADS = 256;
+
+__device__ __forceinline__ float ts_block_max(float m, float* red) {
+  m = wave_max_xor(m, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int w = 1; w < TS_THREADS / 64; ++w) m = fmaxf(m, red[w]);
+  return m;
+}
+
+__global__ __launch_bounds__(TS_THREADS) void tensor_amax_kernel(const uint16_t* __restrict__ in, int64_t n,
+                                                                 int64_t bstride, float* __restrict__ part) {
+  __shared__ float red[TS_THREADS / 64];
+  const uint16_t* x = in + int64_t(blockIdx.y) * bstride;
+  const int64_t stride = int64_t(gridDim.x) * TS_THREADS;
+  const int64_t t0 = int64_t(blockIdx.x) * TS_THREADS + threadIdx.x;
+  float m = 0.f;
+  // 16-byte loads where the tensor's base is 16-byte aligned, element loads for the rest
+  const int64_t head = ((16 - (reinterpret_cast<uintptr_t>(x) & 15)) & 15) / 2;
+  const int64_t h = head < n ? head : n;
+  const int64_t nv = (n - h) / 8;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x + h);
+  for (int64_t i = t0; i < nv; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(xv + i);   // read once
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m = fmaxf(m, fabsf(__uint_as_float(u[j] << 16)));
+      m = fmaxf(m, fabsf(__uint_as_float(u[j] & 0xffff0000u)));
+    }
+  }
+  for (int64_t i = t0; i < h; i += stride) m = fmaxf(m, fabsf(bf16_to_f32(x[i])));
+  for (int64_t i = h + nv * 8 + t0; i < n; i += stride) m = fmaxf(m, fabsf(bf16_to_f32(x[i])));
+  m = ts_block_max(m, red);
+  if (threadIdx.x == 0) part[int64_t(blockIdx.y) * gridDim.x + blockIdx.x] = m;
+}
+
+__global__ __launch_bounds__(TS_THREADS) void tensor_scale_kernel(const float* __restrict__ part, int nparts,
+                                                                  uint8_t* __restrict__ scale) {
+  __shared__ float red[TS_THREADS / 64];
+  const float* pb = part + int64_t(blockIdx.x) * nparts;
+  float m = 0.f;
+  for (int i = threadIdx.x; i < nparts; i += TS_THREADS) m = fmaxf(m, pb[i]);
+  m = ts_block_max(m, red);
+  if (threadIdx.x == 0) scale[blockIdx.x] = uint8_t(mx_scale_byte(m));
+}
+
+int tensor_scale_parts(int64_t n) {
+  const int64_t v = (n / 8 + TS_THREADS - 1) / TS_THREADS;
+  return int(v < 1 ? 1 : (v > 1024 ? 1024 : v));
+}
+
+mge_status launch_tensor_scale(const uint16_t* in, int batch, int64_t n, int64_t bstride, float* part,
+                               uint8_t* scale, hipStream_t s) {
+  if (batch <= 0) return MGE_OK;
+  const int nparts = tensor_scale_parts(n);
+  {
+    ProfScope prof(s, "tensor_amax");
+    hipLaunchKernelGGL(tensor_amax_kernel, dim3(nparts, batch), dim3(TS_THREADS), 0, s, in, n, bstride, part);
+    const mge_status st = hip_check("tensor_amax_kernel");
+    if (st != MGE_OK) return st;
+  }
+  ProfScope prof(s, "tensor_scale");
+  hipLaunchKernelGGL(tensor_scale_kernel, dim3(batch), dim3(TS_THREADS), 0, s, part, nparts, scale);
+  return hip_check("tensor_scale_kernel");
 }
 
 // ---------------------------------------------------------------- scale packing

@@ -59,11 +59,39 @@ def _call(fn, st, **fields):
 
 def test_struct_size_checked():
     a = b.RouteArgs()
-    a.struct_size = C.sizeof(b.RouteArgs) - 8
+    a.struct_size = C.sizeof(b.RouteArgs) - 4
     L = b.lib()
     assert L.moe_route_permute(C.byref(a), None) == b.MGE_ERR_INVALID_ARG
     assert "struct_size" in L.mge_last_error().decode()
     assert L.moe_route_permute(None, None) == b.MGE_ERR_INVALID_ARG
+    # a struct that ends before the added last field (x_tensor_scale, tensor_scale) is
+    # accepted and goes on to the next check
+    for fn, st in (("moe_route_permute", b.RouteArgs), ("mxfp8_quantize", b.QuantArgs)):
+        a = st()
+        a.struct_size = C.sizeof(st) - 8
+        if st is b.QuantArgs:
+            a.C = 33
+        assert getattr(L, fn)(C.byref(a), None) == b.MGE_ERR_INVALID_ARG
+        assert "struct_size" not in L.mge_last_error().decode()
+
+
+def test_tensor_scale_rejects_and_workspace():
+    L = b.lib()
+    assert L.mge_tensor_scale_workspace_bytes(1, 8 * 256 * 3000) == 1024 * 4
+    assert L.mge_tensor_scale_workspace_bytes(3, 100) == 256
+    r, err = _call("mge_tensor_scale", b.TensorScaleArgs, batch=70000, n=64)
+    assert r == b.MGE_ERR_INVALID_ARG and "batch" in err
+    r, err = _call("mge_tensor_scale", b.TensorScaleArgs, batch=2, n=64, batch_stride=32)
+    assert r == b.MGE_ERR_INVALID_ARG and "batch_stride" in err
+    r, err = _call("mge_tensor_scale", b.TensorScaleArgs, batch=1, n=64)
+    assert r == b.MGE_ERR_INVALID_ARG and "NULL" in err
+    r, err = _call("mge_tensor_scale", b.TensorScaleArgs, batch=1, n=64, in_=1 << 20, scale=1 << 21)
+    assert r == b.MGE_ERR_WORKSPACE
+    r, err = _call("mge_tensor_scale", b.TensorScaleArgs, batch=0, n=64)
+    assert r == b.MGE_OK
+    # the per-tensor scale of x needs MXFP8
+    r, err = _call("moe_route_permute", b.RouteArgs, T=8, E=4, k=2, H=64, align=32, prec=0, x_tensor_scale=1 << 20)
+    assert r == b.MGE_ERR_INVALID_ARG and "x_tensor_scale" in err
 
 
 @pytest.mark.parametrize("fields,msg", [

@@ -1,0 +1,208 @@
+"""GPU parity of FP8 with one scale per tensor (the format the pages name beside MXFP8)
+against the oracle's quantize_tensor, through the C ABI:
+
+  * mge_tensor_scale: the scale byte of the tensor's amax, bit-exact, over sizes with
+    vector tails, a base that is not 16-byte aligned, all-zero and extreme tensors, and
+    one scale per matrix of a batch;
+  * mxfp8_quantize with tensor_scale: row and column codes bit-exact, every block's scale
+    the tensor's;
+  * moe_route_permute with x_tensor_scale: the permuted x codes bit-exact (padding rows
+    zero codes, the tensor's scale);
+  * the FP8 forward (unfused chain, h with one scale from its amax) stage by stage: [G U]
+    and y_perm within rel_F 2e-3 of the oracle on the GPU's codes, h's scale and codes
+    bit-exact from the GPU's bf16 h; at the Mixtral shape on sampled rows, through
+    bench.Step's fp8_tensor variant.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import mlp, mx
+from oracle.metrics import rel_f
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).to("cuda:0")
+
+
+def _vals(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _npy(t):
+    return t.detach().cpu().numpy()
+
+
+@pytest.mark.parametrize("n,kind", [(1, "normal"), (7, "normal"), (8, "normal"), (1000, "wide"),
+                                    (4096 * 37 + 5, "normal"), (1 << 21, "wide"), (4096, "zero"),
+                                    (300, "tiny"), (300, "huge"), (2049, "spike")])
+def test_tensor_scale_matches_oracle(n, kind):
+    import moe_grouped_expert_amd as m
+
+    rng = np.random.default_rng(n)
+    if kind == "zero":
+        v = np.zeros(n + 3)
+    elif kind == "tiny":
+        v = rng.standard_normal(n + 3) * 1e-39          # bf16 subnormals: the scale clamps at 0
+    elif kind == "huge":
+        v = rng.standard_normal(n + 3) * 1e37
+    elif kind == "wide":
+        v = rng.standard_normal(n + 3) * np.exp2(rng.uniform(-30, 30, n + 3))
+    else:
+        v = rng.standard_normal(n + 3)
+    if kind == "spike":
+        v[n + 2] = -1e4                                  # the amax sits in the unaligned tail
+    g = _bf(v)
+    for off in (0, 3):                                   # base 16-byte aligned, then 6 bytes past
+        t = g[off:off + n]
+        got = int(m.tensor_scale(t).scale.item())
+        _, ref = mx.quantize_tensor(_vals(t))
+        assert got == int(ref), (n, kind, off, got, int(ref))
+
+
+def test_tensor_scale_per_matrix_and_quantize():
+    import moe_grouped_expert_amd as m
+
+    rng = np.random.default_rng(77)
+    E, R, C = 3, 70, 96
+    w = rng.standard_normal((E, R, C)) * np.array([1e-3, 1.0, 300.0])[:, None, None]
+    w[1, 5, 7] = 0.0
+    g = _bf(w)
+    ts = m.tensor_scale(g, per_matrix=True)
+    rc, rs, cc, cs = m.mxfp8_quantize(g, "both", tensor_scale=ts.scale)
+    torch.cuda.synchronize()
+    wv = _vals(g)
+    Rp = (R + 31) // 32 * 32
+    for e in range(E):
+        q, s = mx.quantize_tensor(wv[e])
+        assert int(ts.scale[e]) == int(s)
+        np.testing.assert_array_equal(_npy(rc[e]), q)
+        assert np.all(_npy(rs[e]) == s)
+        np.testing.assert_array_equal(_npy(cc[e])[:, :R], q.T)
+        assert not _npy(cc[e])[:, R:].any()
+        assert np.all(_npy(cs[e]) == s) and _npy(cs[e]).shape == (C, Rp // 32)
+
+
+@pytest.mark.parametrize("want_col", [False, True])
+def test_route_with_x_tensor_scale(want_col):
+    import moe_grouped_expert_amd as m
+    from tests.gpu_helpers import Inputs
+
+    w = synth.custom(1400, T=300, E=4, H=128, F=64, k=2, prec="mxfp8")
+    inp = Inputs(w)
+    ts = m.tensor_scale(inp.g_x)
+    g = m.moe_route_permute(inp.g_logits, inp.g_x, w.k, align=32, prec="mxfp8", want_col=want_col,
+                            x_tensor_scale=ts.scale)
+    torch.cuda.synchronize()
+    q, s = mx.quantize_tensor(inp.x.astype(np.float64))
+    src = _npy(g.perm_src)
+    valid = src >= 0
+    codes = _npy(g.x_perm)
+    np.testing.assert_array_equal(codes[valid], q[src[valid]])
+    assert not codes[~valid].any()
+    assert np.all(_npy(g.x_perm_scale) == s)
+    if want_col:
+        np.testing.assert_array_equal(_npy(g.x_col)[:, valid], q[src[valid]].T)
+        assert not _npy(g.x_col)[:, ~valid].any()
+        assert np.all(_npy(g.x_col_scale) == s)
+
+
+@pytest.mark.parametrize("w,empty", [(synth.custom(1401, T=600, E=4, H=128, F=256, k=2, prec="mxfp8"), ()),
+                                     (synth.custom(1402, T=333, E=5, H=96, F=160, k=2, prec="mxfp8"), (2,))],
+                         ids=["plain", "empty_mid"])
+def test_fp8_tensor_forward_staged(w, empty):
+    import bench
+    import moe_grouped_expert_amd as m
+    from tests.gpu_helpers import Inputs, layout_from_gpu, say
+
+    logits = synth.logits(w)
+    for e in empty:
+        logits[:, e] = np.float32(-1e30)
+    inp = Inputs(w, logits)
+    st = bench.Step(m, w, dict(logits=inp.g_logits, x=inp.g_x, wgu=inp.g_wgu, wd=inp.g_wd, dy=None), train=False,
+                    variant="fp8_tensor")
+    st.keep_intermediates = True
+    st()
+    torch.cuda.synchronize()
+    g, f = st.g, st.f
+    lay = layout_from_gpu(g, w.E, 32)
+    valid = _npy(g.perm_src) >= 0
+    F = w.F
+    # the operands: x and every expert's weights with one scale each, bit-exact
+    qx, sx = mx.quantize_tensor(inp.x.astype(np.float64))
+    np.testing.assert_array_equal(_npy(g.x_perm)[valid], qx[_npy(g.perm_src)[valid]])
+    for e in range(w.E):
+        for wt, qt in ((inp.wgu, st.wq), (inp.wd, st.dq)):
+            q, s = mx.quantize_tensor(wt[e].astype(np.float64))
+            np.testing.assert_array_equal(_npy(qt[0][e]), q)
+            assert np.all(_npy(qt[1][e]) == s)
+    errs = {}
+    GU = mlp.mx_grouped_nt(_npy(g.x_perm), _npy(g.x_perm_scale), [_npy(c) for c in st.wq[0]],
+                           [_npy(c) for c in st.wq[1]], lay)
+    gu = _vals(f.gu)
+    errs["gu"] = rel_f(gu[valid], GU[valid])
+    hb = _vals(f.h_bf16)
+    href = lay.prob_perm[:, None] * mlp.silu(gu[:, :F]) * gu[:, F:]
+    errs["h_bf16"] = rel_f(hb[valid], href[valid])
+    assert not hb[~valid].any()
+    q, s = mx.quantize_tensor(hb)
+    assert int(f.h_tensor_scale.item()) == int(s)
+    np.testing.assert_array_equal(_npy(f.h), q)
+    assert np.all(_npy(f.h_scale) == s)
+    Y = mlp.mx_grouped_nt(q, _npy(f.h_scale), [_npy(c) for c in st.dq[0]], [_npy(c) for c in st.dq[1]], lay)
+    errs["y_perm"] = rel_f(_vals(f.y_perm)[valid], Y[valid])
+    y = lay.combine(_vals(f.y_perm))
+    errs["y"] = rel_f(_vals(st.y), y)
+    say("[gpu] fp8 per-tensor forward", w.name, {k: f"{v:.2e}" for k, v in errs.items()},
+        "scales x/h", int(sx), int(s))
+    for key, v in errs.items():
+        assert v <= 2e-3, (key, v)
+
+
+def test_mixtral_fp8_tensor_forward_sampled():
+    import bench
+    import moe_grouped_expert_amd as m
+    from tests.gpu_helpers import layout_from_gpu, say
+
+    w = synth.WORKLOADS[2]
+    dev = torch.device("cuda:0")
+    say("[gpu] full-size fp8 per-tensor forward: inputs")
+    inp = bench.make_inputs(w, dev)
+    st = bench.Step(m, w, inp, train=False, variant="fp8_tensor")
+    st.keep_intermediates = True
+    st()
+    torch.cuda.synchronize()
+    g, f = st.g, st.f
+    lay = layout_from_gpu(g, w.E, 32)
+    F = w.F
+    # scales of x and of every expert's weights against the oracle (amax over the whole tensor)
+    assert int(st.ts["x"].scale.item()) == int(mx.block_scale_exponent(float(inp["x"].abs().max())) + 127)
+    for e in range(w.E):
+        assert int(st.ts["wgu"].scale[e]) == int(mx.block_scale_exponent(float(inp["wgu"][e].abs().max())) + 127)
+        assert int(st.ts["wd"].scale[e]) == int(mx.block_scale_exponent(float(inp["wd"][e].abs().max())) + 127)
+    assert int(f.h_tensor_scale.item()) == int(mx.block_scale_exponent(float(f.h_bf16.abs().max())) + 127)
+    rng = np.random.default_rng(7171)
+    nonempty = [e for e in range(w.E) if lay.sizes[e] > 0]
+    acc = {"gu": [[], []], "y_perm": [[], []]}
+    hs = int(f.h_tensor_scale.item())
+    for e in sorted({max(nonempty, key=lambda e: lay.sizes[e]), min(nonempty, key=lambda e: lay.sizes[e])}):
+        r = lay.rows(e)
+        rows = np.array(sorted({r.start, r.stop - 1} | set(int(v) for v in rng.integers(r.start, r.stop, 4))))
+        sel = torch.as_tensor(rows, device=dev, dtype=torch.long)
+        xd = mx.dequantize_rows(_npy(g.x_perm.index_select(0, sel)), _npy(g.x_perm_scale.index_select(0, sel)))
+        GU = xd @ mx.dequantize_rows(_npy(st.wq[0][e]), _npy(st.wq[1][e])).T
+        acc["gu"][0].append(_vals(f.gu.index_select(0, sel)))
+        acc["gu"][1].append(GU)
+        hb = _vals(f.h_bf16.index_select(0, sel))
+        codes = mx.e4m3_encode(hb * 2.0 ** -(hs - 127))
+        np.testing.assert_array_equal(_npy(f.h.index_select(0, sel)), codes)
+        Y = mx.dequantize_tensor(codes, np.uint8(hs)) @ mx.dequantize_rows(_npy(st.dq[0][e]), _npy(st.dq[1][e])).T
+        acc["y_perm"][0].append(_vals(f.y_perm.index_select(0, sel)))
+        acc["y_perm"][1].append(Y)
+    res = {k: rel_f(np.concatenate(a), np.concatenate(b)) for k, (a, b) in acc.items()}
+    say("[gpu] full-size fp8 per-tensor", {k: f"{v:.2e}" for k, v in res.items()})
+    for key, v in res.items():
+        assert v <= 2e-3, (key, v)
