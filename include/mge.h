@@ -15,7 +15,10 @@
  *   grouped_mlp_bwd     dy permute (+quantize), dh GEMM with fused SwiGLU backward and
  *                       d_prob, dW_down, dX and dW_gate_up grouped GEMMs
  *   unpermute_combine   out[t] = sum over the k slots of in[perm_pos[t][i]]
- * and the router backward (moe_router_bwd: d_logits from d_prob).
+ * and the router backward (moe_router_bwd: d_logits from d_prob), the forward without
+ * the fusion (grouped_mlp_fwd_unfused, the baseline the fusion is measured against) and
+ * the one scale of FP8 with one scale per tensor (mge_tensor_scale; the quantizers then
+ * take it through their tensor_scale / x_tensor_scale fields).
  *
  * Sources: "NVIDIA Shows an Efficient MoE Training Path for Biological Foundation
  * Models" (sections "Grouped experts instead of a Python loop" and "Memory and
