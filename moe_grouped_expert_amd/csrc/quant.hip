@@ -51,6 +51,27 @@ __device__ __forceinline__ uint32_t quant32(const uint32_t* w, uint32_t* out, in
   return s;
 }
 
+// A quad of lanes q = 0..3 holds bytes [32q, 32q + 32) of a 128-byte piece as out[0..7].
+// Rearranged so that the quad's first store writes bytes [0, 64) and its second bytes
+// [64, 128) (lane q: [16q, 16q + 16), then [64 + 16q, ...)): each store instruction then
+// covers whole 64-byte runs instead of 16-byte pieces spread over the line.
+__device__ __forceinline__ void quad_store128(uint8_t* base, const uint32_t* out) {
+  const bool odd = (threadIdx.x & 1) != 0;
+  uint32_t a[4], b[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t x0 = uint32_t(__builtin_amdgcn_mov_dpp(int(out[j]), 0x50, 0xf, 0xf, false));       // lane q>>1
+    const uint32_t x1 = uint32_t(__builtin_amdgcn_mov_dpp(int(out[4 + j]), 0x50, 0xf, 0xf, false));
+    const uint32_t y0 = uint32_t(__builtin_amdgcn_mov_dpp(int(out[j]), 0xFA, 0xf, 0xf, false));       // lane 2 + (q>>1)
+    const uint32_t y1 = uint32_t(__builtin_amdgcn_mov_dpp(int(out[4 + j]), 0xFA, 0xf, 0xf, false));
+    a[j] = odd ? x1 : x0;
+    b[j] = odd ? y1 : y0;
+  }
+  const int q = threadIdx.x & 3;
+  *reinterpret_cast<uint4*>(base + 16 * q) = make_uint4(a[0], a[1], a[2], a[3]);
+  *reinterpret_cast<uint4*>(base + 64 + 16 * q) = make_uint4(b[0], b[1], b[2], b[3]);
+}
+
 template <bool MX>
 __global__ __launch_bounds__(QT_THREADS) void quant_tile_kernel(QuantTileParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[QT_ROWS * QT_LDS_STRIDE + (QT_ROWS / 32) * QT_GRP];
@@ -87,9 +108,13 @@ __global__ __launch_bounds__(QT_THREADS) void quant_tile_kernel(QuantTileParams 
     if (MX) {
       uint32_t out[8];
       const uint32_t s = quant32(reinterpret_cast<const uint32_t*>(v), out, given);
-      uint4* dst = reinterpret_cast<uint4*>(p.row_codes + ob * p.C + c);
-      dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
-      dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+      if ((p.C & (QT_COLS - 1)) == 0) {   // uniform: the quad's 4 lanes are all here
+        quad_store128(p.row_codes + ob * p.C + c0, out);
+      } else {
+        uint4* dst = reinterpret_cast<uint4*>(p.row_codes + ob * p.C + c);
+        dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+        dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+      }
       uint8_t* rs = p.row_scales + ob * (p.C / 32) + c / 32;
       // uniform: the 4 lanes of the row are all active and the dword is aligned
       if ((p.C & (QT_COLS - 1)) == 0 && (reinterpret_cast<uintptr_t>(p.row_scales) & 3) == 0) {
@@ -126,9 +151,13 @@ __global__ __launch_bounds__(QT_THREADS) void quant_tile_kernel(QuantTileParams 
   if (MX) {
     uint32_t out[8];
     const uint32_t s = quant32(hw, out, given);
-    uint4* dst = reinterpret_cast<uint4*>(p.col_codes + ocol * p.Rp + rowb);
-    dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
-    dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+    if ((p.Rp & (QT_ROWS - 1)) == 0) {   // uniform: the quad's 4 row blocks are all here
+      quad_store128(p.col_codes + ocol * p.Rp + r0, out);
+    } else {
+      uint4* dst = reinterpret_cast<uint4*>(p.col_codes + ocol * p.Rp + rowb);
+      dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+      dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+    }
     uint8_t* cs = p.col_scales + ocol * (p.Rp / 32) + rowb / 32;
     // uniform: the 4 row blocks of every column exist and the dword is aligned
     if ((p.Rp & (QT_ROWS - 1)) == 0 && (reinterpret_cast<uintptr_t>(p.col_scales) & 3) == 0) {
