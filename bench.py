@@ -298,16 +298,34 @@ def summarize_kernels(records, steps, w, R, prec):
 
 # ------------------------------------------------------------------------------ traffic (rocprofv3 counters)
 
-def kernel_source_digest():
-    """Digest of the kernel sources: counter-derived traffic is only reported while the
-    kernels are the ones the counters were taken on."""
+# Sources that build a kernel family: the GEMM kernels are made from these files and from
+# the grouped-GEMM part of mge_internal.hpp (GemmParams); every other kernel is checked
+# against all sources.
+GEMM_SOURCES = ("gemm_impl.hpp", "gemm_mx.hip", "gemm_bf16.hip", "gemm_host.cpp", "mge_common.hpp")
+GEMM_PARAMS_MARK = "// ------------------------------------------------------------ grouped GEMM"
+
+
+def kernel_source_digest(family="all"):
+    """Digest of the sources of a kernel family ("gemm" or "all"): counter-derived traffic
+    is only reported while the kernels are the ones the counters were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "moe_grouped_expert_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".cpp", ".h")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+        if not f.endswith((".hip", ".hpp", ".cpp", ".h")):
+            continue
+        with open(os.path.join(csrc, f), "rb") as fh:
+            text = fh.read()
+        if family == "gemm":
+            if f == "mge_internal.hpp":
+                text = text[text.index(GEMM_PARAMS_MARK.encode()):]
+            elif f not in GEMM_SOURCES:
+                continue
+        h.update(f.encode() + b"\0" + text)
     return h.hexdigest()[:16]
+
+
+def _digest_family(kernel):
+    return "gemm" if kernel.startswith("gemm_") else "all"
 
 
 COPY_CAL_BYTES = 1 << 30   # the plain device-to-device copy the counters are calibrated on
@@ -373,6 +391,7 @@ def summarize_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, workl
         kernels[_short_kernel(name)] = {"dispatches": len(fv), "fetch_bytes": round(fb), "write_bytes": round(wb),
                                         "hbm_bytes_per_launch": round(fb + wb)}
     out = {"source_digest": kernel_source_digest(),
+           "source_digests": {fam: kernel_source_digest(fam) for fam in ("all", "gemm")},
            "calibration": {"copy_bytes": COPY_CAL_BYTES, "fetch_factor": round(f_scale, 5),
                            "write_factor": round(w_scale, 5)},
            "kernels": {workload: kernels}}
@@ -391,7 +410,8 @@ def traffic_for(kernel, workload):
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("source_digest") != kernel_source_digest():
+    fam = _digest_family(kernel)
+    if d.get("source_digests", {}).get(fam) != kernel_source_digest(fam):
         return None
     e = d.get("kernels", {}).get(workload, {}).get(kernel)
     return None if e is None else e.get("hbm_bytes_per_launch")
