@@ -561,14 +561,20 @@ def main():
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    # one event between consecutive steps too (no extra synchronization), for the spread
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps - 1)]
     m.profile_start()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
         step()
+        if i < args.steps - 1:
+            marks[i].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     records = m.profile_stop()
     ms = ev0.elapsed_time(ev1) / args.steps
+    bounds = [ev0] + marks + [ev1]
+    per_step = sorted(bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps))
     log(f"[bench] {args.steps} timed steps: {ms:.3f} ms/step")
 
     flops = w.flops_fwd() + (w.flops_bwd() if train else 0.0)
@@ -604,6 +610,10 @@ def main():
         "gemm_only": {"ms_per_step": round(gemm_ms, 4),
                       "tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms > 0 else None},
         "kernel_ms_per_step": round(kern_ms, 4),
+        "step_ms": {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4),
+                    "max": round(per_step[-1], 4)},
+        "device": {"name": torch.cuda.get_device_name(dev),
+                   "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count},
         "roofline": roof,
         "kernels": kernels,
     }
