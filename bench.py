@@ -47,6 +47,7 @@ WORKLOADS = {
     "fwd_bf16": (1, False),
     "fwd_mxfp8": (2, False),
     "fwd_mxfp8_skew": (3, False),
+    "tiny_bf16": (0, True),    # 4 experts, hidden 64, ffn 128, 256 tokens: latency-bound
     # one rank's share of an expert-parallel layer (its local experts, its received rows)
     "fwd_mxfp8_ep8": (5, False),
     "fwd_mxfp8_ep4": (6, False),
@@ -426,7 +427,8 @@ def cpu_baseline(w, max_rows=32, f_cols=None):
     (their tokens and routing probabilities from the oracle's own routing of the
     workload's logits), the full hidden size and the first `f_cols` of the expert's
     ffn columns (gate, up and down weights restricted to them), through the whole
-    MXFP8 training step (or forward) as the oracle defines it: quantize the weights
+    MXFP8 training step (or forward) as the oracle defines it (BF16 workloads: the grouped
+    definition on the bf16 values): quantize the weights
     (row and column forms), permute and quantize x, gate-up GEMM + SwiGLU x prob,
     quantize h, down GEMM, combine; backward: dy permute/quantize, dh + SwiGLU
     backward, d_prob, dW_down, dX, dW_gate_up.  Rate = the sample's algorithmic flops
@@ -456,6 +458,20 @@ def cpu_baseline(w, max_rows=32, f_cols=None):
     dys = synth.dy(w)[toks] if w.backward else None
     t0 = time.perf_counter()
     lay = mlp.Layout(np.zeros((n, 1), np.int32), p[toks, slots][:, None], 1, 32)
+    if w.prec == "bf16":
+        # the BF16 path: the grouped definition on the bf16 values, no quantization
+        y, saved = mlp.fwd_grouped(xs, wgu0[None], wd0[None], lay, keep=True)
+        flops = 6.0 * n * w.H * fs
+        if w.backward:
+            mlp.bwd_grouped(dys, wgu0[None], wd0[None], lay, saved)
+            flops += 12.0 * n * w.H * fs
+        dt = time.perf_counter() - t0
+        tok = n / w.k * fs / w.F
+        return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                "sample": (f"expert 0 of the {w.name} workload: its first {n} routed assignments, full H={w.H}, "
+                           f"ffn columns 0..{fs - 1} of F={w.F}; whole BF16 "
+                           f"{'training step (fwd+bwd)' if w.backward else 'forward'}; fp64 numpy, {dt:.2f} s wall"),
+                "seconds": round(dt, 3), "tokens_per_s": round(tok / dt, 4)}
     wq = mx.quantize_rows(wgu0)
     dq = mx.quantize_rows(wd0)
     X = lay.gather(xs)

@@ -113,6 +113,29 @@ def quantize_cols(v) -> tuple[np.ndarray, np.ndarray]:
     return quantize_rows(np.swapaxes(v, -1, -2))
 
 
+def pad_segments(v, seg_offsets) -> np.ndarray:
+    """Rows of v [R][C] regrouped so that segment s (rows seg_offsets[s] .. seg_offsets[s+1])
+    starts at a multiple of 32: segment s lands at sum_{j<s} ceil(len_j / 32) * 32 and the
+    rows up to the next segment are zero.  Returns [sum of padded lengths][C]."""
+    v = np.asarray(v, dtype=np.float64)
+    off = np.asarray(seg_offsets, dtype=np.int64)
+    parts = []
+    for s in range(len(off) - 1):
+        seg = v[off[s]:off[s + 1]]
+        n = len(seg)
+        pad = (n + BLOCK - 1) // BLOCK * BLOCK - n
+        parts.append(np.concatenate([seg, np.zeros((pad, v.shape[1]))]) if pad else seg)
+    return np.concatenate(parts) if parts else np.zeros((0, v.shape[1]))
+
+
+def quantize_cols_segmented(v, seg_offsets) -> tuple[np.ndarray, np.ndarray]:
+    """Column form whose 32-row blocks restart at every segment start (the per-expert token
+    blocks of the weight gradients, [P4] paragraph on GroupedLinear: each expert's tokens
+    form their own group): quantize_cols of pad_segments(v), so no block mixes two
+    segments."""
+    return quantize_cols(pad_segments(v, seg_offsets))
+
+
 def quantize_tensor(v) -> tuple[np.ndarray, np.uint8]:
     """FP8 with one scale for the whole tensor: E4M3 codes (same shape as v) and one
     E8M0 scale byte.

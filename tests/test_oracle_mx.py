@@ -242,3 +242,32 @@ def test_tensor_quantize_zero_exact_and_idempotent():
     q2, s2 = mx.quantize_tensor(mx.dequantize_tensor(q, s))
     np.testing.assert_array_equal(q2, q)
     assert s2 == s
+
+
+# ------------------------------------------------------------------------------ segmented column form
+
+def test_segmented_cols_blocks_restart_at_segments():
+    rng = np.random.default_rng(41)
+    v = rng.standard_normal((100, 64)) * np.exp2(rng.integers(-8, 8, size=(100, 1)))
+    off = [0, 7, 7, 40, 72, 100]                 # an empty segment, lengths 7, 33, 32, 28
+    q, s = mx.quantize_cols_segmented(v, off)
+    lens = np.diff(off)
+    padded = (lens + 31) // 32 * 32
+    assert q.shape == (64, padded.sum()) and s.shape == (64, padded.sum() // 32)
+    start = np.concatenate([[0], np.cumsum(padded)])
+    for k in range(len(lens)):
+        if lens[k] == 0:
+            continue
+        # each segment alone, zero-padded to 32 rows: the same codes and scales
+        qk, sk = mx.quantize_cols(v[off[k]:off[k + 1]])
+        np.testing.assert_array_equal(q[:, start[k]:start[k] + qk.shape[1]], qk)
+        np.testing.assert_array_equal(s[:, start[k] // 32:start[k] // 32 + sk.shape[1]], sk)
+
+
+def test_segmented_cols_aligned_segments_equal_plain_cols():
+    rng = np.random.default_rng(42)
+    v = rng.standard_normal((96, 32))
+    q, s = mx.quantize_cols_segmented(v, [0, 32, 96])
+    qp, sp = mx.quantize_cols(v)
+    np.testing.assert_array_equal(q, qp)
+    np.testing.assert_array_equal(s, sp)
