@@ -440,7 +440,7 @@ def cpu_baseline(w, max_rows=32, f_cols=None):
     from oracle import route as rt
 
     cores = len(os.sched_getaffinity(0))
-    l = synth.logits(w)[:4096]
+    l = synth.logits(w)[:max(4096, 2 * max_rows * w.E // w.k)]   # enough tokens to find max_rows for expert 0
     idx, p = rt.route(l, w.k)
     hit = np.argwhere(idx == 0)[:max_rows]
     toks, slots = hit[:, 0], hit[:, 1]
@@ -520,7 +520,8 @@ def main():
     ap.add_argument("--variant", default="grouped", choices=VARIANTS,
                     help="grouped projections (default) or the per-expert launch loop (forward workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=32, help="assignments in the CPU oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=None,
+                    help="assignments in the CPU oracle sample (default: 32 for MXFP8, 4096 for BF16)")
     ap.add_argument("--cpu-fcols", type=int, default=None, help="ffn columns in the CPU oracle sample (default: all)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only the 1 GiB copy the traffic counters are calibrated on")
@@ -639,7 +640,8 @@ def main():
         out["rows_per_s"] = out.pop("tokens_per_s")   # received rows (assignments), k = 1 locally
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(wg, args.cpu_rows, args.cpu_fcols)
+        rows = args.cpu_rows if args.cpu_rows is not None else (4096 if wg.prec == "bf16" else 32)
+        out["cpu_baseline"] = cpu_baseline(wg, rows, args.cpu_fcols)
     print(json.dumps(out), flush=True)
 
 

@@ -166,8 +166,22 @@ typedef struct mge_quant_args {
    * takes tensor_scale[b] instead of its own, and the scale arrays hold it replicated,
    * so the block-scaled GEMMs read the result unchanged. */
   const uint8_t* tensor_scale;
+  /* Added fields (a struct_size that ends before them means no segments): optional
+   * segments along R, for tensors already grouped (e.g. by expert) whose groups do not
+   * start at multiples of 32.  seg_offsets: device int32 [num_segments + 1], non-decreasing
+   * in [0, R] (otherwise undefined but memory-safe results), 1 <= num_segments <= 1024.
+   * Segment s (rows seg_offsets[s] .. seg_offsets[s+1]) is placed at a multiple of 32
+   * rows, padded with zero rows, in Rs = mge_perm_rows(R, 1, num_segments, 32) output
+   * rows: ROW codes [b][Rs][C], scales [b][Rs][C/32]; COL codes [b][C][Rs], scales
+   * [b][C][Rs/32], whose 32-row blocks thus restart at every segment.  Rows past the
+   * padded segments are zero.  workspace: mge_quant_workspace_bytes(args) bytes. */
+  const int32_t* seg_offsets;
+  int32_t num_segments;
+  void* workspace;
+  size_t workspace_bytes;
 } mge_quant_args;
 
+size_t mge_quant_workspace_bytes(const mge_quant_args* args);
 mge_status mxfp8_quantize(const mge_quant_args* args, void* stream);
 
 /* ------------------------------------------------------------------------------

@@ -40,7 +40,8 @@ class RouteArgs(C.Structure):
 class QuantArgs(C.Structure):
     _fields_ = [("struct_size", u32), ("batch", i32), ("R", i32), ("C", i32),
                 ("in_batch_stride", i64), ("in_row_stride", i64), ("in_", vp), ("orient", u32),
-                ("row_codes", vp), ("row_scales", vp), ("col_codes", vp), ("col_scales", vp), ("tensor_scale", vp)]
+                ("row_codes", vp), ("row_scales", vp), ("col_codes", vp), ("col_scales", vp), ("tensor_scale", vp),
+                ("seg_offsets", vp), ("num_segments", i32), ("workspace", vp), ("workspace_bytes", C.c_size_t)]
 
 
 class TensorScaleArgs(C.Structure):
@@ -88,7 +89,8 @@ class RouterBwdArgs(C.Structure):
 _LIB = None
 EXPORTS = ["mge_perm_rows", "mge_route_workspace_bytes", "moe_route_permute", "mxfp8_quantize",
            "mge_fwd_workspace_bytes", "grouped_mlp_fwd", "mge_fwd_unfused_workspace_bytes", "grouped_mlp_fwd_unfused",
-           "mge_tensor_scale_workspace_bytes", "mge_tensor_scale", "mge_bwd_workspace_bytes", "grouped_mlp_bwd",
+           "mge_tensor_scale_workspace_bytes", "mge_tensor_scale", "mge_quant_workspace_bytes",
+           "mge_bwd_workspace_bytes", "grouped_mlp_bwd",
            "unpermute_combine", "moe_router_bwd", "mge_status_string", "mge_last_error", "mge_check_device_errors", "mge_version",
            "mge_profile_start", "mge_profile_stop"]
 
@@ -112,6 +114,8 @@ def lib():
         L.mge_fwd_workspace_bytes.argtypes = [C.POINTER(FwdArgs)]
         L.mge_fwd_unfused_workspace_bytes.restype = C.c_size_t
         L.mge_fwd_unfused_workspace_bytes.argtypes = [C.POINTER(FwdUnfusedArgs)]
+        L.mge_quant_workspace_bytes.restype = C.c_size_t
+        L.mge_quant_workspace_bytes.argtypes = [C.POINTER(QuantArgs)]
         L.mge_tensor_scale_workspace_bytes.restype = C.c_size_t
         L.mge_tensor_scale_workspace_bytes.argtypes = [i32, i64]
         L.mge_bwd_workspace_bytes.restype = C.c_size_t
@@ -260,10 +264,14 @@ def check_device_errors(route: RouteOut) -> int:
 
 # ------------------------------------------------------------------------------ quantize
 
-def mxfp8_quantize(w: torch.Tensor, orient: str = "row", out=None, tensor_scale: Optional[torch.Tensor] = None):
+def mxfp8_quantize(w: torch.Tensor, orient: str = "row", out=None, tensor_scale: Optional[torch.Tensor] = None,
+                   seg_offsets: Optional[torch.Tensor] = None):
     """BF16 [..., R, C] -> (row_codes, row_scales, col_codes, col_scales) (absent ones None).
     tensor_scale: optional uint8 [batch] (one scale per matrix, from tensor_scale(w,
-    per_matrix=True)) that every block of its matrix takes instead of its own."""
+    per_matrix=True)) that every block of its matrix takes instead of its own.
+    seg_offsets: optional int32 [S+1] on the device: segments along R, each placed at a
+    multiple of 32 rows (zero-padded), in perm_rows(R, 1, S, 32) output rows, so that the
+    column form's 32-row blocks restart at every segment."""
     assert w.dtype == torch.bfloat16 and w.is_contiguous()
     R, Cc = w.shape[-2], w.shape[-1]
     lead = tuple(w.shape[:-2])
@@ -271,13 +279,19 @@ def mxfp8_quantize(w: torch.Tensor, orient: str = "row", out=None, tensor_scale:
     for d in lead:
         batch *= d
     Rp = (R + 31) // 32 * 32
+    nseg = 0
+    if seg_offsets is not None:
+        assert seg_offsets.dtype == torch.int32 and seg_offsets.is_contiguous() and seg_offsets.numel() >= 2
+        nseg = seg_offsets.numel() - 1
+        Rp = perm_rows(R, 1, nseg, 32)
+    Rr = Rp if seg_offsets is not None else R   # rows of the row form
     want_row = orient in ("row", "both")
     want_col = orient in ("col", "both")
     dev = w.device
     if out is None:
         u8 = dict(device=dev, dtype=torch.uint8)
-        rc = torch.empty(lead + (R, Cc), **u8) if want_row else None
-        rs = torch.empty(lead + (R, Cc // 32), **u8) if want_row else None
+        rc = torch.empty(lead + (Rr, Cc), **u8) if want_row else None
+        rs = torch.empty(lead + (Rr, Cc // 32), **u8) if want_row else None
         cc = torch.empty(lead + (Cc, Rp), **u8) if want_col else None
         cs = torch.empty(lead + (Cc, Rp // 32), **u8) if want_col else None
     else:
@@ -292,6 +306,11 @@ def mxfp8_quantize(w: torch.Tensor, orient: str = "row", out=None, tensor_scale:
     if tensor_scale is not None:
         assert tensor_scale.dtype == torch.uint8 and tensor_scale.numel() == batch
     a.tensor_scale = _ptr(tensor_scale)
+    ws = None
+    if seg_offsets is not None:
+        a.seg_offsets, a.num_segments = _ptr(seg_offsets), nseg
+        ws = torch.empty(max(int(lib().mge_quant_workspace_bytes(C.byref(a))), 256), device=dev, dtype=torch.uint8)
+        a.workspace, a.workspace_bytes = _ptr(ws), ws.numel()
     _check(lib().mxfp8_quantize(C.byref(a), _stream(dev)), "mxfp8_quantize")
     return rc, rs, cc, cs
 

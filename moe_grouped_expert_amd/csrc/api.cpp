@@ -237,10 +237,21 @@ mge_status moe_route_permute(const mge_route_args* a, void* stream) {
 mge_status mxfp8_quantize(const mge_quant_args* a, void* stream) {
   g_err[0] = 0;
   MGE_REQUIRE(a != nullptr, "args is NULL");
-  // the struct may end before its added last field (tensor_scale: then NULL)
-  MGE_REQUIRE(a->struct_size == sizeof(mge_quant_args) || a->struct_size == offsetof(mge_quant_args, tensor_scale),
+  // the struct may end before its added fields (tensor_scale; the segments): then absent
+  MGE_REQUIRE(a->struct_size == sizeof(mge_quant_args) || a->struct_size == offsetof(mge_quant_args, tensor_scale) ||
+                  a->struct_size == offsetof(mge_quant_args, seg_offsets),
               "struct_size mismatch");
-  const uint8_t* ts = a->struct_size == sizeof(mge_quant_args) ? a->tensor_scale : nullptr;
+  const uint8_t* ts = a->struct_size > offsetof(mge_quant_args, tensor_scale) ? a->tensor_scale : nullptr;
+  const bool seg = a->struct_size == sizeof(mge_quant_args) && a->seg_offsets != nullptr;
+  if (seg) {
+    MGE_REQUIRE(a->num_segments >= 1 && a->num_segments <= SEG_MAX, "num_segments must be in [1, %d] (got %d)",
+                SEG_MAX, a->num_segments);
+    const size_t need = mge_quant_workspace_bytes(a);
+    if (!a->workspace || a->workspace_bytes < need) {
+      set_error("segmented quantize workspace needs %zu bytes (got %zu)", need, a->workspace_bytes);
+      return MGE_ERR_WORKSPACE;
+    }
+  }
   MGE_REQUIRE(a->batch >= 0 && a->R >= 0 && a->C >= 0, "negative size");
   MGE_REQUIRE(a->C % 32 == 0, "C must be a multiple of 32 (got %d)", a->C);
   MGE_REQUIRE(a->orient != 0 && (a->orient & ~3u) == 0, "orient must be ROW, COL or ROW|COL");
@@ -252,14 +263,29 @@ mge_status mxfp8_quantize(const mge_quant_args* a, void* stream) {
     MGE_REQUIRE(a->row_codes && a->row_scales && aligned16(a->row_codes), "row outputs missing or misaligned");
   if (a->orient & MGE_ORIENT_COL)
     MGE_REQUIRE(a->col_codes && a->col_scales && aligned16(a->col_codes), "column outputs missing or misaligned");
-  if (a->batch == 0 || a->R == 0 || a->C == 0) return MGE_OK;
+  if (a->batch == 0 || a->C == 0 || (a->R == 0 && !seg)) return MGE_OK;
+  if (seg) MGE_REQUIRE(a->R < (1 << 30), "R too large for segments");
+  hipStream_t s = static_cast<hipStream_t>(stream);
   QuantTileParams q{};
   q.in = a->in; q.in_batch_stride = a->in_batch_stride; q.in_row_stride = a->in_row_stride;
   q.batch = a->batch; q.R = a->R; q.C = a->C; q.Rp = (a->R + 31) / 32 * 32;
+  if (seg) {   // rows in the padded segment order: gathered through the row map
+    const int Rs = int(mge_perm_rows(a->R, 1, a->num_segments, 32));
+    int32_t* map = static_cast<int32_t*>(a->workspace);
+    const mge_status st = launch_seg_map(a->seg_offsets, a->num_segments, a->R, Rs, map, s);
+    if (st != MGE_OK) return st;
+    q.gather = map;
+    q.R = Rs; q.Rp = Rs;
+  }
   if (a->orient & MGE_ORIENT_ROW) { q.row_codes = a->row_codes; q.row_scales = a->row_scales; }
   if (a->orient & MGE_ORIENT_COL) { q.col_codes = a->col_codes; q.col_scales = a->col_scales; }
   q.tensor_scale = ts;
-  return launch_quant_tile(q, true, static_cast<hipStream_t>(stream));
+  return launch_quant_tile(q, true, s);
+}
+
+size_t mge_quant_workspace_bytes(const mge_quant_args* a) {
+  if (!a || a->struct_size != sizeof(mge_quant_args) || !a->seg_offsets || a->R < 0 || a->num_segments < 1) return 0;
+  return up256(size_t(mge_perm_rows(a->R, 1, a->num_segments, 32)) * sizeof(int32_t));
 }
 
 // ------------------------------------------------------------------ per-tensor scale

@@ -37,6 +37,11 @@ struct QuantTileParams {
 // timing_name: the launch's name for per-kernel timing (NULL: by form)
 mge_status launch_quant_tile(const QuantTileParams& p, bool mx, hipStream_t s, const char* timing_name = nullptr);
 
+// Segmented row map: output row o of the padded order (segment s of input rows
+// [seg[s], seg[s+1]) starting at a multiple of 32) -> input row, or -1; S <= SEG_MAX.
+constexpr int SEG_MAX = 1024;
+mge_status launch_seg_map(const int32_t* seg, int S, int R, int Rp, int32_t* map, hipStream_t s);
+
 // One E8M0 scale per tensor (FP8 with one scale per tensor): amax of each of `batch`
 // bf16 tensors of n elements (batch stride bstride elements) -> scale[b] by the block
 // rule.  part: tensor_scale_parts(n) * batch floats of workspace.

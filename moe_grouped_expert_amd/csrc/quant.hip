@@ -173,6 +173,79 @@ __global__ __launch_bounds__(QT_THREADS) void quant_tile_kernel(QuantTileParams 
   }
 }
 
+// ---------------------------------------------------------------- segmented row map
+// Segments s = input rows [seg[s], seg[s+1]) placed at 32-row multiples: output row o of
+// the padded order -> its input row, or -1 (the zero rows that pad a segment to 32).
+// Every block builds the padded starts in LDS (4 segments per thread, a Hillis-Steele
+// scan of the 256 thread sums), then maps its grid-stride share of the Rp output rows.
+// Offsets are clamped to [0, R] and made non-decreasing, and rows past Rp are not
+// mapped, so malformed offsets give undefined results but stay in bounds.
+constexpr int SEG_THREADS = 256;
+constexpr int SEG_PER_THREAD = SEG_MAX / SEG_THREADS;
+
+__global__ __launch_bounds__(SEG_THREADS) void seg_map_kernel(const int32_t* __restrict__ seg, int S, int R, int Rp,
+                                                              int32_t* __restrict__ map) {
+  __shared__ int32_t pstart[SEG_MAX + 1];
+  __shared__ int32_t istart[SEG_MAX];
+  __shared__ int32_t slen[SEG_MAX];
+  __shared__ int32_t tsum[SEG_THREADS];
+  const int t = threadIdx.x;
+  int padded[SEG_PER_THREAD];
+  int mine = 0;
+#pragma unroll
+  for (int j = 0; j < SEG_PER_THREAD; ++j) {
+    const int s = t * SEG_PER_THREAD + j;
+    padded[j] = 0;
+    if (s < S) {
+      const int a = min(max(seg[s], 0), R);
+      const int b = min(max(seg[s + 1], a), R);
+      istart[s] = a;
+      slen[s] = b - a;
+      padded[j] = (b - a + 31) / 32 * 32;
+      mine += padded[j];
+    }
+  }
+  tsum[t] = mine;
+  __syncthreads();
+  for (int d = 1; d < SEG_THREADS; d <<= 1) {   // inclusive scan of the thread sums
+    const int v = t >= d ? tsum[t - d] : 0;
+    __syncthreads();
+    tsum[t] += v;
+    __syncthreads();
+  }
+  int acc = tsum[t] - mine;
+#pragma unroll
+  for (int j = 0; j < SEG_PER_THREAD; ++j) {
+    const int s = t * SEG_PER_THREAD + j;
+    if (s < S) pstart[s] = acc;
+    acc += padded[j];
+  }
+  if (t == SEG_THREADS - 1) pstart[S] = tsum[t];
+  __syncthreads();
+  for (int o = blockIdx.x * SEG_THREADS + t; o < Rp; o += gridDim.x * SEG_THREADS) {
+    int src = -1;
+    if (o < pstart[S]) {
+      int lo = 0, hi = S - 1;   // the last segment whose padded start is <= o
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pstart[mid] <= o) lo = mid; else hi = mid - 1;
+      }
+      const int i = o - pstart[lo];
+      if (i < slen[lo]) src = istart[lo] + i;
+    }
+    map[o] = src;
+  }
+}
+
+mge_status launch_seg_map(const int32_t* seg, int S, int R, int Rp, int32_t* map, hipStream_t s) {
+  if (Rp <= 0) return MGE_OK;
+  int blocks = (Rp + SEG_THREADS - 1) / SEG_THREADS;
+  if (blocks > 256) blocks = 256;
+  ProfScope prof(s, "seg_map");
+  hipLaunchKernelGGL(seg_map_kernel, dim3(blocks), dim3(SEG_THREADS), 0, s, seg, S, R, Rp, map);
+  return hip_check("seg_map_kernel");
+}
+
 // ---------------------------------------------------------------- per-tensor scale
 // FP8 with one scale per tensor: amax over each of `batch` tensors of n bf16 values, then
 // the block rule's E8M0 byte of that amax (the whole tensor as one block).  Two launches,

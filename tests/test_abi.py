@@ -66,13 +66,40 @@ def test_struct_size_checked():
     assert L.moe_route_permute(None, None) == b.MGE_ERR_INVALID_ARG
     # a struct that ends before the added last field (x_tensor_scale, tensor_scale) is
     # accepted and goes on to the next check
-    for fn, st in (("moe_route_permute", b.RouteArgs), ("mxfp8_quantize", b.QuantArgs)):
+    for fn, st, size in (("moe_route_permute", b.RouteArgs, b.RouteArgs.x_tensor_scale.offset),
+                         ("mxfp8_quantize", b.QuantArgs, b.QuantArgs.tensor_scale.offset),
+                         ("mxfp8_quantize", b.QuantArgs, b.QuantArgs.seg_offsets.offset)):
         a = st()
-        a.struct_size = C.sizeof(st) - 8
+        a.struct_size = size
         if st is b.QuantArgs:
             a.C = 33
         assert getattr(L, fn)(C.byref(a), None) == b.MGE_ERR_INVALID_ARG
         assert "struct_size" not in L.mge_last_error().decode()
+    a = b.QuantArgs()
+    a.struct_size = C.sizeof(b.QuantArgs) - 8
+    assert L.mxfp8_quantize(C.byref(a), None) == b.MGE_ERR_INVALID_ARG
+    assert "struct_size" in L.mge_last_error().decode()
+
+
+def test_quantize_segments_rejects_and_workspace():
+    L = b.lib()
+    base = dict(batch=1, R=100, C=64, in_row_stride=64, in_=1 << 20, orient=b.ORIENT_COL, col_codes=1 << 21,
+                col_scales=1 << 22, seg_offsets=1 << 23)
+    r, err = _call("mxfp8_quantize", b.QuantArgs, num_segments=0, **base)
+    assert r == b.MGE_ERR_INVALID_ARG and "num_segments" in err
+    r, err = _call("mxfp8_quantize", b.QuantArgs, num_segments=1025, **base)
+    assert r == b.MGE_ERR_INVALID_ARG and "num_segments" in err
+    r, err = _call("mxfp8_quantize", b.QuantArgs, num_segments=5, **base)
+    assert r == b.MGE_ERR_WORKSPACE
+    a = b.QuantArgs()
+    a.struct_size = C.sizeof(b.QuantArgs)
+    for k, v in dict(num_segments=5, **base).items():
+        setattr(a, k, v)
+    # the padded rows: R + 31 per segment, rounded up to 32; one int32 row map entry each
+    assert b.perm_rows(100, 1, 5, 32) == 256
+    assert L.mge_quant_workspace_bytes(C.byref(a)) == 256 * 4
+    a.seg_offsets = None
+    assert L.mge_quant_workspace_bytes(C.byref(a)) == 0
 
 
 def test_tensor_scale_rejects_and_workspace():

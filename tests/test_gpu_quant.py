@@ -70,3 +70,34 @@ def test_quantize_shapes_row_col(m, shape):
     qc, sc = mx.quantize_cols(vb)
     np.testing.assert_array_equal(npy(cc), qc)
     np.testing.assert_array_equal(npy(cs), sc)
+
+
+@pytest.mark.parametrize("offsets", [[0, 7, 7, 40, 72, 100], [0, 100], [0, 0, 32, 64, 100, 100], [0, 1, 2, 3, 100]])
+def test_quantize_segments_matches_oracle(offsets):
+    """Segments along R placed at 32-row multiples: row and column codes and scales
+    bit-exact against the oracle's zero-padded segments (empty segments, lengths below,
+    at and above 32, a segment at either end)."""
+    import moe_grouped_expert_amd as m
+
+    rng = np.random.default_rng(len(offsets) * 100 + offsets[1])
+    R, C, B = 100, 96, 2
+    v = rng.standard_normal((B, R, C)) * np.exp2(rng.integers(-6, 6, size=(B, R, 1)))
+    g = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).to("cuda:0")
+    seg = torch.tensor(offsets, dtype=torch.int32, device="cuda:0")
+    rc, rs, cc, cs = m.mxfp8_quantize(g, "both", seg_offsets=seg)
+    torch.cuda.synchronize()
+    Rs = m.perm_rows(R, 1, len(offsets) - 1, 32)
+    assert rc.shape == (B, Rs, C) and cc.shape == (B, C, Rs)
+    vals = g.float().cpu().numpy().astype(np.float64)
+    for b in range(B):
+        padded = mx.pad_segments(vals[b], offsets)
+        full = np.zeros((Rs, C))
+        full[:len(padded)] = padded
+        q, s = mx.quantize_rows(full)
+        np.testing.assert_array_equal(rc[b].cpu().numpy(), q)
+        np.testing.assert_array_equal(rs[b].cpu().numpy(), s)
+        qc, sc = mx.quantize_cols_segmented(vals[b], offsets)
+        n = qc.shape[1]
+        np.testing.assert_array_equal(cc[b].cpu().numpy()[:, :n], qc)
+        np.testing.assert_array_equal(cs[b].cpu().numpy()[:, :n // 32], sc)
+        assert not cc[b].cpu().numpy()[:, n:].any() and not cs[b].cpu().numpy()[:, n // 32:].any()
