@@ -199,7 +199,7 @@ def test_mixtral_forward_sampled(cfg):
     MXFP8 with 32768 tokens and a Zipf-skewed router whose experts 2 and 5 get no
     tokens), through bench.Step: sampled rows of the largest and the smallest non-empty
     expert.  BF16: h and y_perm end to end against fp64 on the same bf16 inputs
-    (rel_F 1e-2).  MXFP8: x codes bit-exact, h from the GPU's x and weight codes and
+    (rel_F 1e-2), and y per token from the per-token definition on sampled tokens.  MXFP8: x codes bit-exact, h from the GPU's x and weight codes and
     y_perm from the GPU's h codes (rel_F 2e-3)."""
     import bench
     import moe_grouped_expert_amd as m
@@ -256,6 +256,22 @@ def test_mixtral_forward_sampled(cfg):
         got["y_perm"][0].append(_bf16_np(_take(f.y_perm, rows)))
         got["y_perm"][1].append(Y)
     errs = {key: rel_f(np.concatenate(a), np.concatenate(ref)) for key, (a, ref) in got.items()}
+    if not mx8:
+        # end to end, per token: the oracle's own routing and the per-token definition
+        # (each slot's expert applied to the token, weighted by its probability) against
+        # the combined bf16 output, on sampled tokens
+        _, p_or = rt.route(synth.logits(w), k)
+        toks = np.sort(rng.choice(w.T, 12, replace=False))
+        y_ref = np.zeros((len(toks), H))
+        for e in sorted(set(int(v) for v in idx[toks].ravel())):
+            wgu_e, wd_e = _bf16_np(inp["wgu"][e])[None], _bf16_np(inp["wd"][e])[None]
+            for i in range(k):
+                hit = np.where(idx[toks, i] == e)[0]
+                if len(hit):
+                    y_ref[hit] += mlp.fwd_per_token(x[toks[hit]], wgu_e, wd_e, np.zeros((len(hit), 1), np.int32),
+                                                    p_or[toks[hit], i][:, None])
+            del wgu_e, wd_e
+        errs["y_per_token"] = rel_f(_bf16_np(_take(step.y, toks)), y_ref)
     say("[gpu] full-size forward", w.name, "experts", experts, "sizes", [int(lay.sizes[e]) for e in experts],
         {kk: f"{v:.2e}" for kk, v in errs.items()})
     tol = TOL if mx8 else 1e-2
