@@ -44,6 +44,8 @@ BF16_CASES = [
     synth.custom(100, T=300, E=3, H=96, F=160, k=2),
     synth.custom(101, T=40, E=1, H=64, F=64, k=1),
     synth.custom(102, T=700, E=6, H=128, F=256, k=3),
+    # the limits: 256 experts, top-8, about 9 assignments per expert and some experts empty
+    synth.custom(104, T=300, E=256, H=64, F=64, k=8),
 ]
 
 
@@ -111,6 +113,8 @@ MX_CASES = [
     synth.custom(201, T=300, E=5, H=96, F=160, k=2, prec="mxfp8"),
     synth.custom(202, T=1100, E=8, H=512, F=384, k=2, prec="mxfp8"),
     synth.custom(203, T=64, E=1, H=128, F=128, k=1, prec="mxfp8"),
+    # many small groups: 64 experts, top-4, about 12 rows each (one partial tile per group)
+    synth.custom(205, T=200, E=64, H=64, F=96, k=4, prec="mxfp8"),
 ]
 
 
