@@ -1,4 +1,4 @@
-"""Bit-exact pins of the quantizers inside the fused GEMM epilogues (MXFP8).
+"""Bit-exact pins of the quantizers inside the fused GEMM epilogues (MXFP8; BF16 roundings too).
 
 The SwiGLU x prob epilogue of the gate-up GEMM quantizes h = p * silu(G) * U from fp32
 registers, and the SwiGLU-backward epilogue of the dh GEMM quantizes dG, dU the same way;
@@ -90,3 +90,54 @@ def test_fused_epilogue_quantizers_bit_exact(T, H, F):
     err = rel_f(b.d_prob.double().cpu().numpy(), lay.to_slots(dp_row))
     say("[gpu] exact epilogue codes: all bit-exact; d_prob rel_F", f"{err:.1e}")
     assert err <= 1e-6
+
+
+def test_fused_epilogues_bf16_bit_exact():
+    """The BF16 path on the same exact-valued inputs: h, its transpose, G, U, dG and dU
+    leave as bf16 roundings (RNE) of exact values, so they equal the oracle's bit for bit."""
+    import moe_grouped_expert_amd as m
+    from tests.gpu_helpers import layout_from_gpu, npy, say
+
+    T, H, F = 200, 64, 96
+    rng = np.random.default_rng(77)
+    say("[gpu] exact epilogue bf16", T, H, F)
+    x, gx = _int_bf16(rng, (T, H), 1, 4)
+    wg, _ = _int_bf16(rng, (1, F, H), 1, 4)
+    wu, _ = _int_bf16(rng, (1, F, H), -4, 4)
+    wgu = np.concatenate([wg, wu], axis=1)
+    gwgu = torch.from_numpy(wgu).to(torch.bfloat16).to("cuda:0")
+    wd, gwd = _int_bf16(rng, (1, H, F), -4, 4)
+    dy, gdy = _int_bf16(rng, (T, H), -4, 4)
+    logits = torch.zeros((T, 1), dtype=torch.float32, device="cuda:0")
+    g = m.moe_route_permute(logits, gx, 1, align=32, prec="bf16", want_col=True)
+    f = m.grouped_mlp_fwd(g, gwgu, gwd, train=True)
+    b = m.grouped_mlp_bwd(gdy, g, f, gwgu, gwd, keep_intermediates=True)
+    torch.cuda.synchronize()
+    lay = layout_from_gpu(g, 1, 32)
+    valid = npy(g.perm_src) >= 0
+    nrow = int(npy(g.group_offsets)[-1])
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).double().numpy()
+
+    def gpu(t):
+        return t.double().cpu().numpy()
+
+    _, sv = mlp.fwd_grouped(x, wgu, wd, lay, keep=True)      # the oracle's grouped forward (p = 1)
+    G, U, h = sv["G"], sv["U"], sv["h"]
+    GU = np.concatenate([G, U], axis=1)
+    assert G[valid].min() >= H and np.abs(h).max() < 2 ** 24
+    np.testing.assert_array_equal(h, np.where(valid[:, None], G * U, 0.0))   # silu(G) = G exactly
+    np.testing.assert_array_equal(gpu(f.saved_gu)[valid], bf(GU)[valid])
+    np.testing.assert_array_equal(gpu(f.h)[valid], bf(h)[valid])
+    np.testing.assert_array_equal(gpu(f.h_col)[:, :nrow], bf(h.T)[:, :nrow])
+    # backward from the GPU's bf16 G, U: dh = dY W_down, dG = dh U, dU = dh G (the backward's
+    # definition with p = 1 and silu'(G) = silu(G) / G = 1 on these inputs)
+    gsv = gpu(f.saved_gu)
+    assert np.all(mlp.dsilu(gsv[valid, :F]) == 1.0) and np.all(mlp.silu(gsv[valid, :F]) == gsv[valid, :F])
+    dh = lay.gather(dy) @ wd[0].astype(np.float64)
+    dGU = np.where(valid[:, None], np.concatenate([dh * gsv[:, F:], dh * gsv[:, :F]], axis=1), 0.0)
+    assert np.abs(dGU).max() < 2 ** 24
+    np.testing.assert_array_equal(gpu(b.dgu_row)[valid], bf(dGU)[valid])
+    np.testing.assert_array_equal(gpu(b.dgu_col)[:, :nrow], bf(dGU.T)[:, :nrow])
+    say("[gpu] exact epilogue bf16: all bit-exact")
