@@ -254,6 +254,10 @@ def kernel_work(name, w, R, launches_per_step=1.0):
         # averaged per launch: bf16 read, row and (training) column forms written
         forms = 2 if w.backward else 1
         return "byte", 1.5 * E * H * F * (2.0 + forms * mxb)
+    if name == "transpose_bf16":
+        # BF16 backward: each expert's W_down [H][F] and W_gate_up [2F][H] transposed
+        # (2 B read + 2 B written per element), two launches per expert: 6*H*F B on average
+        return "byte", 6.0 * H * F
     if name == "swiglu_prob":
         # unfused forward: [G U] bf16 read, h bf16 written, p read (valid rows)
         return "byte", 6.0 * M * F + 4.0 * M

@@ -22,6 +22,8 @@ def test_gemm_work_is_shared_by_the_launches_of_a_step():
     kind, n = bench.kernel_work("swiglu_prob", w, 0)
     assert kind == "byte" and n == 6.0 * w.M * w.F + 4.0 * w.M
     assert bench.kernel_work("tensor_amax", w, 0) is None
+    # the BF16 backward's weight transposes: 2 launches per expert, (4 + 8) H F bytes per expert
+    assert bench.kernel_work("transpose_bf16", w, 0) == ("byte", 6.0 * w.H * w.F)
 
 
 def test_summarize_kernels_per_launch_and_share():
