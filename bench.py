@@ -135,9 +135,10 @@ class Step:
     grouped_mlp_fwd_unfused (both inference only; keep_intermediates keeps the unfused
     call's [G U] and bf16 h in their own buffers instead of the workspace)."""
 
-    def __init__(self, m, w, inp, train, variant="grouped"):
+    def __init__(self, m, w, inp, train, variant="grouped", dw_dtype="f32"):
         self.m, self.w, self.inp, self.train = m, w, inp, train
         self.variant = variant
+        self.dw_dtype = dw_dtype
         self.keep_intermediates = False
         self.prec = w.prec
         self.given = inp.get("idx") is not None
@@ -218,9 +219,10 @@ class Step:
         if self.train:
             if mx:
                 self.b = m.grouped_mlp_bwd(inp["dy"], self.g, self.f, self.wq[2], self.dq[2], self.wq[3], self.dq[3],
-                                           out=self.b)
+                                           out=self.b, dw_dtype=self.dw_dtype)
             else:
-                self.b = m.grouped_mlp_bwd(inp["dy"], self.g, self.f, inp["wgu"], inp["wd"], out=self.b)
+                self.b = m.grouped_mlp_bwd(inp["dy"], self.g, self.f, inp["wgu"], inp["wd"], out=self.b,
+                                           dw_dtype=self.dw_dtype)
             self.dx = m.unpermute_combine(self.b.dx_perm, self.g.perm_pos, out=self.dx)
             if not self.given:
                 self.dl = m.moe_router_bwd(self.g.topk_idx, self.g.topk_prob, self.b.d_prob, w.E, out=self.dl)
@@ -523,6 +525,8 @@ def main():
     ap.add_argument("--workload", default="train_mxfp8", choices=sorted(WORKLOADS))
     ap.add_argument("--variant", default="grouped", choices=VARIANTS,
                     help="grouped projections (default) or the per-expert launch loop (forward workloads)")
+    ap.add_argument("--dw-dtype", default="f32", choices=("f32", "bf16"),
+                    help="weight-gradient output of the training step (default fp32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None,
                     help="assignments in the CPU oracle sample (default: 32 for MXFP8, 4096 for BF16)")
@@ -570,7 +574,7 @@ def main():
     else:
         inp = make_inputs(w, dev)
     torch.cuda.synchronize()
-    step = Step(m, w, inp, train, args.variant)
+    step = Step(m, w, inp, train, args.variant, args.dw_dtype)
     for i in range(args.warmup):
         step()
         torch.cuda.synchronize()
@@ -625,7 +629,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "E": w.E, "H": w.H, "F": w.F, "k": w.k, "prec": w.prec,
                    "passes": "fwd+bwd" if train else "fwd", "align": 32, "split_sizes": sizes,
-                   "parallelism": "single GPU", "variant": args.variant},
+                   "parallelism": "single GPU", "variant": args.variant,
+                   **({"dw_dtype": args.dw_dtype} if train else {})},
         "tokens_per_s": round(tok_s, 1),
         "algorithmic_tflop_per_step": round(flops / 1e12, 4),
         "gemm_only": {"ms_per_step": round(gemm_ms, 4),
