@@ -69,7 +69,7 @@ extern "C" {
 typedef enum mge_status {
   MGE_OK = 0,
   MGE_ERR_INVALID_ARG = 1,   /* bad size, NULL pointer, misaligned pointer */
-  MGE_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement */
+  MGE_ERR_UNSUPPORTED = 2,   /* valid request the library does not implement */
   MGE_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the query says */
   MGE_ERR_HIP = 4,           /* a HIP launch failed (hipGetLastError text in mge_last_error) */
   MGE_ERR_DEVICE_CHECK = 5   /* a kernel flagged bad data (see mge_check_device_errors) */
