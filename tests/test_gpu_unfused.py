@@ -22,9 +22,11 @@ from oracle.metrics import rel_f
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    ("mxfp8", synth.custom(1300, T=600, E=4, H=128, F=256, k=2), ()),
-    ("mxfp8", synth.custom(1301, T=333, E=5, H=96, F=160, k=2), (0, 4)),
-    ("bf16", synth.custom(1302, T=500, E=3, H=64, F=192, k=2), (1,)),
+    ("mxfp8", synth.custom(1300, T=600, E=4, H=128, F=256, k=2), (), 32),
+    ("mxfp8", synth.custom(1301, T=333, E=5, H=96, F=160, k=2), (0, 4), 32),
+    ("bf16", synth.custom(1302, T=500, E=3, H=64, F=192, k=2), (1,), 32),
+    ("mxfp8", synth.custom(1303, T=421, E=6, H=64, F=96, k=2), (3,), 8),    # groups start at multiples of 8
+    ("bf16", synth.custom(1304, T=257, E=3, H=64, F=64, k=1), (), 1),       # unpadded groups
 ]
 
 
@@ -32,8 +34,9 @@ def _np(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("prec,w,empty", CASES, ids=["mx", "mx_empty_ends", "bf16_empty_mid"])
-def test_unfused_forward_staged(prec, w, empty):
+@pytest.mark.parametrize("prec,w,empty,align", CASES,
+                         ids=["mx", "mx_empty_ends", "bf16_empty_mid", "mx_align8", "bf16_align1"])
+def test_unfused_forward_staged(prec, w, empty, align):
     import moe_grouped_expert_amd as m
     from tests.gpu_helpers import Inputs, layout_from_gpu, npy, say
 
@@ -43,7 +46,7 @@ def test_unfused_forward_staged(prec, w, empty):
     inp = Inputs(w, logits)
     say("[gpu] unfused forward", prec, w.name, "empty", empty)
     mx8 = prec == "mxfp8"
-    g = m.moe_route_permute(inp.g_logits, inp.g_x, w.k, align=32, prec=prec)
+    g = m.moe_route_permute(inp.g_logits, inp.g_x, w.k, align=align, prec=prec)
     if mx8:
         wq = m.mxfp8_quantize(inp.g_wgu, "row")
         dq = m.mxfp8_quantize(inp.g_wd, "row")
@@ -53,7 +56,8 @@ def test_unfused_forward_staged(prec, w, empty):
         f = m.grouped_mlp_fwd_unfused(g, inp.g_wgu, inp.g_wd, keep_intermediates=True)
         fused = m.grouped_mlp_fwd(g, inp.g_wgu, inp.g_wd)
     torch.cuda.synchronize()
-    lay = layout_from_gpu(g, w.E, 32)
+    lay = layout_from_gpu(g, w.E, align)
+    np.testing.assert_array_equal(npy(g.group_offsets), lay.off)
     for e in empty:
         assert lay.sizes[e] == 0
     valid = npy(g.perm_src) >= 0
