@@ -152,7 +152,7 @@ mge_status moe_route_permute(const mge_route_args* args, void* stream);
  * ROW quantization of the transpose.
  * Errors: MGE_ERR_INVALID_ARG for a struct_size other than the full size or one that ends
  * before an added field, negative sizes, C % 32 != 0, an unknown orientation, missing or
- * misaligned (16-byte) input / code pointers, strides too small, or num_segments outside
+ * misaligned (16-byte) input (NULL allowed when R = 0) / code pointers, strides too small, or num_segments outside
  * [1, 1024] with seg_offsets; MGE_ERR_WORKSPACE for a missing or short workspace with
  * seg_offsets.  batch, C or (without segments) R = 0 is a no-op.
  * ---------------------------------------------------------------------------- */

@@ -255,7 +255,7 @@ mge_status mxfp8_quantize(const mge_quant_args* a, void* stream) {
   MGE_REQUIRE(a->batch >= 0 && a->R >= 0 && a->C >= 0, "negative size");
   MGE_REQUIRE(a->C % 32 == 0, "C must be a multiple of 32 (got %d)", a->C);
   MGE_REQUIRE(a->orient != 0 && (a->orient & ~3u) == 0, "orient must be ROW, COL or ROW|COL");
-  MGE_REQUIRE(a->in && aligned16(a->in), "in must be non-NULL and 16-byte aligned");
+  MGE_REQUIRE((a->in || a->R == 0 || a->batch == 0) && aligned16(a->in), "in must be non-NULL (R > 0) and 16-byte aligned");
   MGE_REQUIRE(a->in_row_stride >= a->C && a->in_row_stride % 8 == 0, "in_row_stride must be >= C and a multiple of 8");
   MGE_REQUIRE(a->batch <= 1 || (a->in_batch_stride % 8 == 0 && a->in_batch_stride >= int64_t(a->R) * a->in_row_stride),
               "in_batch_stride too small or not a multiple of 8");

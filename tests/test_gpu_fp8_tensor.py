@@ -206,3 +206,41 @@ def test_mixtral_fp8_tensor_forward_sampled():
     say("[gpu] full-size fp8 per-tensor", {k: f"{v:.2e}" for k, v in res.items()})
     for key, v in res.items():
         assert v <= 2e-3, (key, v)
+
+
+def test_tensor_scale_strided_batch_through_the_abi():
+    """batch_stride > n: each tensor is the first n elements of its stride (the rest, which
+    holds the largest values here, must not count)."""
+    import ctypes as C
+
+    import moe_grouped_expert_amd._binding as B
+
+    rng = np.random.default_rng(91)
+    batch, stride, n = 3, 100, 60
+    v = rng.standard_normal((batch, stride)) * np.array([1e-3, 1.0, 7.0])[:, None]
+    v[:, n:] = 1e6
+    g = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).to("cuda:0")
+    out = torch.zeros(batch, dtype=torch.uint8, device="cuda:0")
+    ws = torch.empty(max(int(B.lib().mge_tensor_scale_workspace_bytes(batch, n)), 256), dtype=torch.uint8,
+                     device="cuda:0")
+    a = B.TensorScaleArgs()
+    a.struct_size = C.sizeof(B.TensorScaleArgs)
+    a.batch, a.n, a.batch_stride = batch, n, stride
+    a.in_, a.scale, a.workspace, a.workspace_bytes = g.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel()
+    assert B.lib().mge_tensor_scale(C.byref(a), None) == 0
+    torch.cuda.synchronize()
+    vals = g.float().cpu().numpy().astype(np.float64)
+    for b in range(batch):
+        assert int(out[b]) == int(mx.quantize_tensor(vals[b, :n])[1])
+
+
+def test_quantize_segments_of_an_empty_tensor():
+    """R = 0 with segments: every output row is padding (codes and scales 0)."""
+    import moe_grouped_expert_amd as m
+
+    g = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda:0")
+    seg = torch.zeros(3, dtype=torch.int32, device="cuda:0")
+    rc, rs, cc, cs = m.mxfp8_quantize(g, "both", seg_offsets=seg)
+    torch.cuda.synchronize()
+    assert rc.shape == (m.perm_rows(0, 1, 2, 32), 64)
+    assert not rc.any() and not rs.any() and not cc.any() and not cs.any()
