@@ -473,11 +473,19 @@ def cpu_baseline(w, max_rows=32, f_cols=None):
             flops += 12.0 * n * w.H * fs
         dt = time.perf_counter() - t0
         tok = n / w.k * fs / w.F
-        return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-                "sample": (f"expert 0 of the {w.name} workload: its first {n} routed assignments, full H={w.H}, "
-                           f"ffn columns 0..{fs - 1} of F={w.F}; whole BF16 "
-                           f"{'training step (fwd+bwd)' if w.backward else 'forward'}; fp64 numpy, {dt:.2f} s wall"),
-                "seconds": round(dt, 3), "tokens_per_s": round(tok / dt, 4)}
+        out = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+               "sample": (f"expert 0 of the {w.name} workload: its first {n} routed assignments, full H={w.H}, "
+                          f"ffn columns 0..{fs - 1} of F={w.F}; whole BF16 "
+                          f"{'training step (fwd+bwd)' if w.backward else 'forward'}; fp64 numpy, {dt:.2f} s wall"),
+               "seconds": round(dt, 3), "tokens_per_s": round(tok / dt, 4)}
+        if w.T * w.H * w.F <= 1 << 24:
+            # small workloads: the per-token tier too, the whole forward token by token
+            x_all, l_all = synth.x(w), synth.logits(w)
+            i_all, p_all = rt.route(l_all, w.k)
+            t1 = time.perf_counter()
+            mlp.fwd_per_token(x_all, synth.w_gate_up(w), synth.w_down(w), i_all, p_all)
+            out["per_token_forward_seconds"] = round(time.perf_counter() - t1, 4)
+        return out
     wq = mx.quantize_rows(wgu0)
     dq = mx.quantize_rows(wd0)
     X = lay.gather(xs)
@@ -622,6 +630,13 @@ def main():
                 "unit": "GB/s", "frac": ach and round(ach / PEAK_HBM_GBS, 4),
                 "traffic": traffic_for(dom, args.workload) if args.variant == "grouped" else None, "avg_launch_ms": dk["avg_ms"]}
     gemm_ms = sum(v["avg_ms"] * v["launches_per_step"] for k, v in kernels.items() if k.startswith("gemm_"))
+    # the grouped-MLP calls alone (grouped_mlp_fwd, _unfused, grouped_mlp_bwd): every launch but the routing,
+    # the x permute, the weight quantization, the combines and the router backward
+    # (the one-scale-per-tensor amax passes count with the quantization, outside)
+    outside = ("route_", "router_bwd", "combine", "quant_mx", "permute_", "tensor_", "seg_map")
+    mlp_ms = sum(v["avg_ms"] * v["launches_per_step"] for k, v in kernels.items() if not k.startswith(outside))
+    if train:   # the dy permute-quantize belongs to grouped_mlp_bwd: one of the step's two permute launches
+        mlp_ms += sum(v["avg_ms"] * v["launches_per_step"] for k, v in kernels.items() if k.startswith("permute_")) / 2
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
@@ -635,6 +650,8 @@ def main():
         "algorithmic_tflop_per_step": round(flops / 1e12, 4),
         "gemm_only": {"ms_per_step": round(gemm_ms, 4),
                       "tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms > 0 else None},
+        "grouped_mlp_calls": {"ms_per_step": round(mlp_ms, 4),
+                              "tflops": round(flops / (mlp_ms * 1e-3) / 1e12, 1) if mlp_ms > 0 else None},
         "kernel_ms_per_step": round(kern_ms, 4),
         "step_ms": {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4),
                     "max": round(per_step[-1], 4)},
