@@ -19,7 +19,9 @@ Sources followed (titles of the pages this is written from):
        pages only say "one scale per block of 32 consecutive values").
 
 Modules:
-  oracle.mx     — E4M3 / E8M0 encode-decode and block quantization (row / column).
+  oracle.mx     — E4M3 / E8M0 encode-decode, block quantization (row / column, column
+                  with 32-row blocks restarting at segment starts) and FP8 with one
+                  scale per tensor.
   oracle.route  — top-k routing, split_sizes, group offsets, stable permutation,
                   and the router backward (d_logits from d_prob).
   oracle.mlp    — per-token (O-slow) and grouped (O-grouped) forward, backward,
