@@ -1,8 +1,8 @@
 // Shared device helpers of the gfx950 kernels: bf16 <-> f32, the MXFP8 (E4M3 + E8M0)
 // block encoder, wave-level reductions and launch plumbing.
 //
-// MXFP8 per the OCP Microscaling Formats v1.0 specification (the pages only fix
-// "8-bit values with one scale per block of 32 consecutive values"): the shared
+// MXFP8 per the OCP Microscaling Formats v1.0 specification (the pages fix only 8-bit
+// values sharing one scale per 32 consecutive values): the shared
 // exponent of a block is floor(log2(amax)) - 8 (8 = the largest E4M3 exponent)
 // clamped to the E8M0 range, and each element is v / 2^e rounded to the nearest
 // E4M3 value (ties to even), saturating at 448.

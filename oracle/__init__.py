@@ -16,7 +16,7 @@ Sources followed (titles of the pages this is written from):
        on FP8/MXFP8 and on the Sequential fusion.
   [OCP] OCP Microscaling Formats (MX) v1.0 specification — E4M3 element format,
        E8M0 shared scale, the scale-selection and conversion rules (external; the
-       pages only say "one scale per block of 32 consecutive values").
+       pages fix only one scale per 32 consecutive values).
 
 Modules:
   oracle.mx     — E4M3 / E8M0 encode-decode, block quantization (row / column, column
