@@ -247,3 +247,16 @@ def test_fwd_unfused_rejects_and_workspace():
                       saved_gu=1 << 30, h_col=1 << 31, h_col_scale=1 << 32, **dev)
     assert L.grouped_mlp_fwd_unfused(C.byref(u), None) == b.MGE_ERR_INVALID_ARG
     assert "inference only" in L.mge_last_error().decode()
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """No fallback: without the built library every call raises instead of computing
+    anything another way."""
+    import moe_grouped_expert_amd as m
+
+    monkeypatch.setattr(b, "_LIB", None)
+    monkeypatch.setattr(b, "LIB_PATH", str(tmp_path / "libmge.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        b.lib()
+    with pytest.raises(RuntimeError, match="not built"):
+        m.perm_rows(8, 2, 4, 32)
