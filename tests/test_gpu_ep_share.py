@@ -11,9 +11,10 @@ they are checked for exact equality with the grouped call over all experts:
     row tiles and 32-token scale blocks start at its first row in both calls); their
     weight gradients too in BF16, and in MXFP8 up to the grouping of the token sums
     into 64-token MFMA steps (rel_F 1e-6);
-  * at full size (Mixtral shape, 8 ranks of 16384 tokens, rank 0 holding expert 0) the
-    rank's received rows match the oracle's routing, and sampled rows of h and y_perm
-    match the oracle fed the GPU's codes (rel_F 2e-3).
+  * at full size (Mixtral shape, 8 or 4 ranks of 16384 tokens, rank 0 holding expert 0
+    or experts 0 and 1) the rank's received rows match the oracle's routing, and sampled
+    rows of h and y_perm of every local expert match the oracle fed the GPU's codes
+    (rel_F 2e-3).
 """
 import dataclasses
 
@@ -126,51 +127,114 @@ def test_rank_share_equals_global(prec, train):
                             assert rel_f(g64, r64) <= 1e-6 if np.any(r64) else not np.any(g64)
 
 
-def test_mixtral_ep8_rank_share_forward_sampled():
-    """Rank 0 of 8 (expert 0) at the Mixtral shape: 8 x 16384 tokens routed, the rank's
-    received rows run through bench.Step as bench.py times them."""
+@pytest.mark.parametrize("cfg", [5, 6])
+def test_mixtral_rank_share_forward_sampled(cfg):
+    """Rank 0 of 8 (expert 0) or of 4 (experts 0, 1) at the Mixtral shape: 8 x 16384 or
+    4 x 16384 tokens routed, the rank's received rows run through bench.Step as bench.py
+    times them; sampled rows of every local expert against the oracle."""
     import bench
     import moe_grouped_expert_amd as m
     from tests.gpu_helpers import layout_from_gpu, npy, say
 
-    w = synth.WORKLOADS[5]
-    assert (w.ep, w.T, w.E, w.H, w.F, w.k, w.prec, w.backward) == (8, 16384, 8, 4096, 14336, 2, "mxfp8", False)
+    w = synth.WORKLOADS[cfg]
+    assert (w.T, w.E, w.H, w.F, w.k, w.prec, w.backward) == (16384, 8, 4096, 14336, 2, "mxfp8", False)
     dev = torch.device("cuda:0")
-    say("[gpu] full-size EP=8 rank share: inputs")
+    say("[gpu] full-size rank share: inputs", w.name)
     inp, wl = bench.make_ep_share_inputs(m, w, dev)
+    e_loc = w.E // w.ep
     idx, prob = rt.route(synth.logits(w), w.k)
-    hit = idx == 0
-    assert wl.T == int(hit.sum()) and wl.E == 1 and wl.k == 1
+    hit = idx < e_loc
+    assert wl.T == int(hit.sum()) and wl.E == e_loc and wl.k == 1
+    np.testing.assert_array_equal(npy(inp["idx"])[:, 0], idx[hit])
     np.testing.assert_allclose(npy(inp["prob"])[:, 0], prob[hit], rtol=2e-6, atol=0)
     step = bench.Step(m, wl, inp, train=False)
     step()
     torch.cuda.synchronize()
     g, f = step.g, step.f
-    lay = layout_from_gpu(g, 1, 32)
-    assert int(npy(g.split_sizes)[0]) == wl.T
+    lay = layout_from_gpu(g, e_loc, 32)
+    np.testing.assert_array_equal(npy(g.split_sizes), [int((idx[hit] == e).sum()) for e in range(e_loc)])
     F = w.F
-    rng = np.random.default_rng(5500)
-    r = lay.rows(0)
-    rows = np.array(sorted({r.start, r.stop - 1, min(r.start + 256, r.stop - 1)} |
-                           set(int(v) for v in rng.integers(r.start, r.stop, 5))))
-    sel = torch.as_tensor(rows, device=dev, dtype=torch.long)
+    rng = np.random.default_rng(5500 + cfg)
     perm_src = npy(g.perm_src)
-    x = inp["x"].index_select(0, torch.as_tensor(perm_src[rows], device=dev, dtype=torch.long))
-    q, s = mx.quantize_rows(x.float().cpu().numpy().astype(np.float64))
-    np.testing.assert_array_equal(npy(g.x_perm.index_select(0, sel)), q)
-    np.testing.assert_array_equal(npy(g.x_perm_scale.index_select(0, sel)), s)
-    xd = mx.dequantize_rows(q, s)
-    GU = xd @ mx.dequantize_rows(npy(step.wq[0][0]), npy(step.wq[1][0])).T
-    p = npy(g.prob_perm).astype(np.float64)[rows]
-    h = p[:, None] * mlp.silu(GU[:, :F]) * GU[:, F:]
-    hq, hs = mx.quantize_rows(h)
-    hg = mx.dequantize_rows(npy(f.h.index_select(0, sel)), npy(f.h_scale.index_select(0, sel)))
-    Y = hg @ mx.dequantize_rows(npy(step.dq[0][0]), npy(step.dq[1][0])).T
-    yg = f.y_perm.index_select(0, sel).float().cpu().numpy().astype(np.float64)
-    errs = {"h": rel_f(hg, mx.dequantize_rows(hq, hs)), "y_perm": rel_f(yg, Y)}
-    say("[gpu] EP=8 rank share rows", wl.T, {kk: f"{v:.2e}" for kk, v in errs.items()})
-    for key, v in errs.items():
+    errs = {"h": [[], []], "y_perm": [[], []]}
+    for e in range(e_loc):
+        r = lay.rows(e)
+        rows = np.array(sorted({r.start, r.stop - 1, min(r.start + 256, r.stop - 1)} |
+                               set(int(v) for v in rng.integers(r.start, r.stop, 4))))
+        sel = torch.as_tensor(rows, device=dev, dtype=torch.long)
+        x = inp["x"].index_select(0, torch.as_tensor(perm_src[rows], device=dev, dtype=torch.long))
+        q, s = mx.quantize_rows(x.float().cpu().numpy().astype(np.float64))
+        np.testing.assert_array_equal(npy(g.x_perm.index_select(0, sel)), q)
+        np.testing.assert_array_equal(npy(g.x_perm_scale.index_select(0, sel)), s)
+        GU = mx.dequantize_rows(q, s) @ mx.dequantize_rows(npy(step.wq[0][e]), npy(step.wq[1][e])).T
+        p = npy(g.prob_perm).astype(np.float64)[rows]
+        h = p[:, None] * mlp.silu(GU[:, :F]) * GU[:, F:]
+        hq, hs = mx.quantize_rows(h)
+        hg = mx.dequantize_rows(npy(f.h.index_select(0, sel)), npy(f.h_scale.index_select(0, sel)))
+        errs["h"][0].append(hg)
+        errs["h"][1].append(mx.dequantize_rows(hq, hs))
+        errs["y_perm"][0].append(f.y_perm.index_select(0, sel).float().cpu().numpy().astype(np.float64))
+        errs["y_perm"][1].append(hg @ mx.dequantize_rows(npy(step.dq[0][e]), npy(step.dq[1][e])).T)
+    res = {k: rel_f(np.concatenate(a), np.concatenate(b)) for k, (a, b) in errs.items()}
+    say("[gpu] rank share", w.name, "rows", wl.T, {kk: f"{v:.2e}" for kk, v in res.items()})
+    for key, v in res.items():
         assert v <= 2e-3, (key, v)
+
+
+def test_mixtral_ep8_rank_share_training_sampled():
+    """Rank 0 of 8 (expert 0) at the Mixtral shape, the training step of 8 x 8192 tokens'
+    expert-0 rows as bench.py times it: sampled rows of dx_perm and d_prob from the oracle's
+    dh stage on the GPU's saved G, U (dY and dGU quantized by the oracle: rel_F 5e-3 for
+    dX, a few E4M3 code flips between fp32 and fp64 dGU), and dW_down entries over the whole
+    token span from the oracle's column forms of dY and the GPU's column form of h."""
+    import bench
+    import moe_grouped_expert_amd as m
+    from tests.gpu_helpers import npy, say
+
+    w = synth.WORKLOADS[7]
+    assert (w.ep, w.T, w.E, w.H, w.F, w.k, w.prec, w.backward) == (8, 8192, 8, 4096, 14336, 2, "mxfp8", True)
+    dev = torch.device("cuda:0")
+    say("[gpu] full-size EP=8 training share: inputs")
+    inp, wl = bench.make_ep_share_inputs(m, w, dev)
+    step = bench.Step(m, wl, inp, train=True)
+    step()
+    torch.cuda.synchronize()
+    g, f, b = step.g, step.f, step.b
+    F, H = w.F, w.H
+    off, n = int(npy(g.group_offsets)[0]), int(npy(g.split_sizes)[0])
+    assert off == 0 and n == wl.T
+    perm_src = npy(g.perm_src)
+    rng = np.random.default_rng(7700)
+    rows = np.array(sorted({0, n - 1, 255, 256} | set(int(v) for v in rng.integers(0, n, 4))))
+    sel = torch.as_tensor(rows, device=dev, dtype=torch.long)
+    dy = inp["dy"].index_select(0, torch.as_tensor(perm_src[rows], device=dev, dtype=torch.long))
+    dyq, dys = mx.quantize_rows(dy.float().cpu().numpy().astype(np.float64))
+    dh = mx.dequantize_rows(dyq, dys) @ mx.dequantize_rows(npy(step.dq[2][0]), npy(step.dq[3][0])).T
+    gu = f.saved_gu.index_select(0, sel).float().cpu().numpy().astype(np.float64)
+    G, U = gu[:, :F], gu[:, F:]
+    p = npy(g.prob_perm).astype(np.float64)[rows][:, None]
+    dG = dh * p * U * mlp.dsilu(G)
+    dU = dh * p * mlp.silu(G)
+    gq, gs = mx.quantize_rows(np.concatenate([dG, dU], axis=1))
+    dX = mx.dequantize_rows(gq, gs) @ mx.dequantize_rows(npy(step.wq[2][0]), npy(step.wq[3][0])).T
+    errs = {"dx_perm": rel_f(b.dx_perm.index_select(0, sel).float().cpu().numpy().astype(np.float64), dX),
+            "d_prob": rel_f(npy(b.d_prob)[perm_src[rows], 0].astype(np.float64), np.sum(dh * mlp.silu(G) * U, axis=1))}
+    # dW_down[h][f] = sum over the expert's tokens of dY[t][h] h[t][f], from the column forms
+    hs, fs = rng.integers(0, H, 6), rng.integers(0, F, 6)
+    span = (n + 31) // 32 * 32
+    DYc = np.zeros((span, len(hs)))
+    hs_t = torch.as_tensor(hs, device=dev, dtype=torch.long)
+    fs_t = torch.as_tensor(fs, device=dev, dtype=torch.long)
+    dy_rows = inp["dy"].index_select(0, torch.as_tensor(perm_src[:n], device=dev, dtype=torch.long))
+    DYc[:n] = dy_rows.index_select(1, hs_t).float().cpu().numpy()
+    cq, cs = mx.quantize_cols(DYc)
+    hc = mx.dequantize_rows(npy(f.h_col.index_select(0, fs_t)[:, :span]),
+                            npy(f.h_col_scale.index_select(0, fs_t)[:, :span // 32]))
+    dWd = mx.dequantize_rows(cq, cs) @ hc.T
+    got = b.dw_down[0].index_select(0, hs_t).index_select(1, fs_t)
+    errs["dw_down"] = rel_f(got.double().cpu().numpy(), dWd)
+    say("[gpu] EP=8 training share rows", n, {kk: f"{v:.2e}" for kk, v in errs.items()})
+    assert errs["dx_perm"] <= 5e-3 and errs["d_prob"] <= 2e-3 and errs["dw_down"] <= 2e-3
 
 
 def test_mixtral_expert_loop_equals_grouped():
