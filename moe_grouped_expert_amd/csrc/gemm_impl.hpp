@@ -72,7 +72,7 @@ constexpr int G_STAGES = 2;                   // LDS stages, each refilled once 
 constexpr int G_THREADS = 64 * G_WAVES_M * G_WAVES_N;
 constexpr int G_STAGE_BYTES = (G_BM + G_BN) * G_BKB;   // 64 KB
 constexpr int G_MAXE = 256;
-constexpr int G_GROUP_M = 8;                  // M-tiles per band of the tile raster
+constexpr int G_GROUP_M = 8;                  // M-tiles per band of the tile raster (GemmParams::group_m = 0)
 // Buffer-resource word 3 of the gfx9 family (raw buffer, 32-bit dwords), the record
 // bound, and the offset that lies beyond it (such a lane loads zeros).
 constexpr int kRsrcFlags = 0x00020000;
@@ -274,13 +274,18 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
     t.e = uniform(lo);
     const int local = tile - uniform(s_prefix[t.e]);
     const int mtn = uniform(s_mtiles[t.e]);
-    // grouped raster: bands of G_GROUP_M M-tiles, each band walked across all N-tiles
-    // with M fastest, so that any G_GROUP_M x 4 consecutive tiles (the 32 workgroups of
-    // an XCD) share 8 A tiles and 4 B tiles in that XCD's L2
-    const int band = local / (G_GROUP_M * ntiles);
-    const int within = local - band * G_GROUP_M * ntiles;
-    const int gm = min(G_GROUP_M, mtn - band * G_GROUP_M);
-    const int mt = band * G_GROUP_M + within % gm;
+    // grouped raster: bands of GM = 8 M-tiles, each band walked across all N-tiles with M
+    // fastest, so that the 32 consecutive tiles an XCD runs (an 8 x 4 block) share a few A
+    // and B tiles in that XCD's L2.  With group_m set (ragged M only), an expert's last band
+    // takes a remainder under 4 M-tiles (9 M-tiles walked as one band, not as 8 + a lone 1)
+    constexpr int GM = G_GROUP_M;
+    int nband = (mtn + GM - 1) / GM;
+    if (MODE == RAGGED_M && p.group_m > 0 && nband > 1 && mtn - (nband - 1) * GM < GM / 2) --nband;
+    nband = uniform(nband);
+    const int band = min(local / (GM * ntiles), nband - 1);
+    const int within = local - band * GM * ntiles;
+    const int gm = band == nband - 1 ? mtn - band * GM : GM;
+    const int mt = band * GM + within % gm;
     t.nt = within / gm;
     t.off = ld_uniform(p.offs, t.e);
     t.m_valid = MODE == RAGGED_M ? ld_uniform(p.sizes, t.e) : p.M;

@@ -160,6 +160,7 @@ struct GemmParams {
   uint8_t* dgu_col_codes; uint8_t* dgu_col_scales; uint16_t* dgu_col_bf16; // [2F][Rp], [2F][Rp/32]
   float* dprob_part; int dprob_nparts;   // [R][nparts]: one sum per (row, 128-column span of F)
   int tiles_upper;                         // host bound on the number of tiles (grid sizing)
+  int group_m;                             // 1: a short last raster band joins the one before
 };
 
 // Upper bound of tiles for a RAGGED_M GEMM (host-side, from T*k and E).
