@@ -53,8 +53,10 @@
  *     align a power of two in [1, 256]; column forms (training, backward) need
  *     align % 32 == 0.
  *     T = 0 is a no-op.  NaN/Inf inputs give undefined (but memory-safe) results.
- *   - Calls are thread-safe and re-entrant; each is deterministic (no atomics on
- *     the data path), so two identical calls give bit-identical outputs.
+ *   - Calls are thread-safe and re-entrant; each is deterministic, so two identical
+ *     calls give bit-identical outputs: no floating-point value is accumulated with
+ *     atomics (the only atomics are the integer LDS adds of the routing histogram,
+ *     whose counts do not depend on their order).
  */
 #ifndef MGE_H
 #define MGE_H
@@ -104,7 +106,9 @@ int64_t mge_perm_rows(int32_t T, int32_t k, int32_t E, int32_t align);
  * x_col_scale [H][R/32]); padding rows are zero in every permuted buffer.
  * With MGE_ROUTE_PROB_GIVEN, logits is ignored and topk_idx/topk_prob are read; an
  * index outside [0, E) sets the device error flag (read by mge_check_device_errors)
- * and is clamped.
+ * and is clamped.  A token may name one expert in several slots (given, or after the
+ * clamp): each slot is still its own assignment with its own row, in (t, i) order, so
+ * perm_src is fully defined (every row in [-1, T)).
  * Workspace: mge_route_workspace_bytes(T, E) bytes, 256-byte aligned.
  * ---------------------------------------------------------------------------- */
 typedef struct mge_route_args {
@@ -261,6 +265,31 @@ size_t mge_fwd_workspace_bytes(const mge_fwd_args* args);
 mge_status grouped_mlp_fwd(const mge_fwd_args* args, void* stream);
 
 /* ------------------------------------------------------------------------------
+ * mge_fwd_saved_bytes — sizes of the activations a training forward saves for the
+ * backward.  The fused forward keeps the SwiGLU input and output out of HBM only in
+ * part ("some" intermediates are not materialised: the ai4snews report, paragraph on
+ * the Sequential fusion); this library saves G and U in bf16 (so the backward does
+ * not recompute the gate-up GEMM) and h in column form (the dW_down operand).
+ * For prec, T, k, E, F, align as grouped_mlp_fwd takes them (align % 32 == 0), fills
+ *   rows        R = mge_perm_rows(T, k, E, align)
+ *   saved_gu    bf16 [R][2F]                        (saved_gu)
+ *   h_col       MXFP8 codes [F][R] or bf16 [F][R]   (h_col)
+ *   h_col_scale E8M0 [F][R/32] (MXFP8), 0 for BF16  (h_col_scale)
+ *   total       their sum
+ * in bytes.  out->struct_size must be set by the caller.  Pure host arithmetic: no
+ * device call.  Errors: MGE_ERR_INVALID_ARG for a NULL or mis-sized out, or for
+ * sizes grouped_mlp_fwd's training mode rejects.
+ * ---------------------------------------------------------------------------- */
+typedef struct mge_fwd_saved_sizes {
+  uint32_t struct_size;      /* sizeof(mge_fwd_saved_sizes) */
+  int64_t rows;
+  size_t saved_gu, h_col, h_col_scale, total;
+} mge_fwd_saved_sizes;
+
+mge_status mge_fwd_saved_bytes(int32_t prec, int32_t T, int32_t k, int32_t E, int32_t F, int32_t align,
+                               mge_fwd_saved_sizes* out);
+
+/* ------------------------------------------------------------------------------
  * grouped_mlp_fwd_unfused — the same forward (inference only) without the fusion:
  * the structure the pages' fused GroupedLinear -> ScaledSwiGLU -> GroupedLinear
  * replaces ("Accelerating MoE Training ..." "How it works"; the ai4snews report,
@@ -299,8 +328,10 @@ size_t mge_fwd_unfused_workspace_bytes(const mge_fwd_unfused_args* args);
 mge_status grouped_mlp_fwd_unfused(const mge_fwd_unfused_args* args, void* stream);
 
 /* ------------------------------------------------------------------------------
- * grouped_mlp_bwd — the matching backward of grouped_mlp_fwd, for L = <dy, y> with
- * y = unpermute_combine(y_perm):
+ * grouped_mlp_bwd — the matching backward of grouped_mlp_fwd (the fused forward comes
+ * with a fused backward: "NVIDIA Shows an Efficient MoE Training Path ..." section
+ * "Memory and quantization overhead"; the ai4snews report, paragraph on the Sequential
+ * fusion), for L = <dy, y> with y = unpermute_combine(y_perm):
  *   dY = dy gathered by perm_src; dh = dY W_down (K = H)
  *   d_prob[t][i] = sum_f dh * silu(G) * U        (row perm_pos[t][i])
  *   dU = dh * p * silu(G);  dG = dh * p * U * silu'(G)   (G, U from saved_gu)
@@ -361,8 +392,15 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* args, void* stream);
 /* ------------------------------------------------------------------------------
  * unpermute_combine — out[t][:] = sum_{i<k} w[t][i] * in[perm_pos[t][i]][:]
  * (w = 1 when weights == NULL), summed in fp32 in slot order i = 0..k-1, no atomics.
- * The probability is already applied inside the forward (before the down
- * projection), so the forward's combine is unweighted.
+ * It undoes the gather of every expert's tokens that grouped execution starts with
+ * ("NVIDIA Shows an Efficient MoE Training Path ..." section "Grouped experts instead
+ * of a Python loop"): each token's k expert outputs return to its row and add up.
+ * The probability is already applied inside the forward, in the scaled SwiGLU between
+ * the two grouped linears (the ai4snews report, paragraph on the Sequential fusion),
+ * so the forward's combine is unweighted.
+ * Errors: MGE_ERR_INVALID_ARG for T < 0, k outside [1, 8], H not a positive multiple
+ * of 32, dtypes other than BF16/F32, or a NULL / misaligned (16-byte) in, out or
+ * perm_pos.  Rows of in that no perm_pos entry names are not read.
  * ---------------------------------------------------------------------------- */
 typedef struct mge_combine_args {
   uint32_t struct_size;
@@ -385,9 +423,10 @@ mge_status unpermute_combine(const mge_combine_args* args, void* stream);
  *                    topk_prob[t][i] * (d_prob[t][i] - s_t)
  * and 0 for the experts no slot selected (the renormalised probabilities do not depend
  * on their logits).  Sources: the routing of "NVIDIA Shows an Efficient MoE Training
- * Path for Biological Foundation Models" (introduction: each token goes to a few
- * experts, its output weighted by the routing probability) and the chain rule through
- * that softmax.
+ * Path for Biological Foundation Models" (introduction: each token is sent to only a
+ * few experts), the routing-probability scaling the fused path folds in (the BioNeMo
+ * recipe report, section "Quantization Overhead"; the ai4snews report, paragraph on the
+ * Sequential fusion), and the chain rule through that softmax.
  * Layout: topk_idx int32 [T][k], topk_prob and d_prob fp32 [T][k] (as moe_route_permute
  * and grouped_mlp_bwd write them), d_logits fp32 [T][E], every element written.
  * Indices outside [0, E) take part in s_t but add to no output.  T = 0 is a no-op.

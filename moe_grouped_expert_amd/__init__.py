@@ -7,7 +7,8 @@ outputs with torch.  The library must be built (``python -m
 moe_grouped_expert_amd.build``); without it every call raises.
 """
 from ._binding import (  # noqa: F401
-    BwdOut, FwdOut, MgeError, RouteOut, check_device_errors, grouped_mlp_bwd, grouped_mlp_fwd, grouped_mlp_fwd_unfused,
+    BwdOut, FwdOut, MgeError, RouteOut, check_device_errors, fwd_saved_bytes, grouped_mlp_bwd, grouped_mlp_fwd,
+    grouped_mlp_fwd_unfused,
     lib,
     moe_route_permute, moe_router_bwd, mxfp8_quantize, perm_rows, profile_start, profile_stop, tensor_scale,
     unpermute_combine,

@@ -76,6 +76,11 @@ class BwdArgs(C.Structure):
                 ("workspace", vp), ("workspace_bytes", C.c_size_t), ("dw_bf16", i32)]
 
 
+class FwdSavedSizes(C.Structure):
+    _fields_ = [("struct_size", u32), ("rows", i64), ("saved_gu", C.c_size_t), ("h_col", C.c_size_t),
+                ("h_col_scale", C.c_size_t), ("total", C.c_size_t)]
+
+
 class CombineArgs(C.Structure):
     _fields_ = [("struct_size", u32), ("T", i32), ("k", i32), ("H", i32), ("in_dtype", i32), ("out_dtype", i32),
                 ("in_", vp), ("perm_pos", vp), ("weights", vp), ("out", vp)]
@@ -88,7 +93,7 @@ class RouterBwdArgs(C.Structure):
 
 _LIB = None
 EXPORTS = ["mge_perm_rows", "mge_route_workspace_bytes", "moe_route_permute", "mxfp8_quantize",
-           "mge_fwd_workspace_bytes", "grouped_mlp_fwd", "mge_fwd_unfused_workspace_bytes", "grouped_mlp_fwd_unfused",
+           "mge_fwd_workspace_bytes", "grouped_mlp_fwd", "mge_fwd_saved_bytes", "mge_fwd_unfused_workspace_bytes", "grouped_mlp_fwd_unfused",
            "mge_tensor_scale_workspace_bytes", "mge_tensor_scale", "mge_quant_workspace_bytes",
            "mge_bwd_workspace_bytes", "grouped_mlp_bwd",
            "unpermute_combine", "moe_router_bwd", "mge_status_string", "mge_last_error", "mge_check_device_errors", "mge_version",
@@ -112,6 +117,8 @@ def lib():
         L.mge_route_workspace_bytes.argtypes = [i32, i32]
         L.mge_fwd_workspace_bytes.restype = C.c_size_t
         L.mge_fwd_workspace_bytes.argtypes = [C.POINTER(FwdArgs)]
+        L.mge_fwd_saved_bytes.restype = C.c_int
+        L.mge_fwd_saved_bytes.argtypes = [i32, i32, i32, i32, i32, i32, C.POINTER(FwdSavedSizes)]
         L.mge_fwd_unfused_workspace_bytes.restype = C.c_size_t
         L.mge_fwd_unfused_workspace_bytes.argtypes = [C.POINTER(FwdUnfusedArgs)]
         L.mge_quant_workspace_bytes.restype = C.c_size_t
@@ -343,6 +350,14 @@ def tensor_scale(t: torch.Tensor, per_matrix: bool = False, out: Optional[Tensor
 
 # ------------------------------------------------------------------------------ forward
 
+def fwd_saved_bytes(prec: str, T: int, k: int, E: int, F: int, align: int = 32) -> FwdSavedSizes:
+    """Byte sizes of the activations a training forward saves (mge_fwd_saved_bytes)."""
+    o = FwdSavedSizes()
+    o.struct_size = C.sizeof(FwdSavedSizes)
+    _check(lib().mge_fwd_saved_bytes(PREC[prec], T, k, E, F, align, C.byref(o)), "mge_fwd_saved_bytes")
+    return o
+
+
 @dataclass
 class FwdOut:
     y_perm: torch.Tensor
@@ -379,10 +394,13 @@ def _fwd_args(rt: RouteOut, w_gate_up, w_down, w_gate_up_scale, w_down_scale, y_
         if mx:
             o.h_scale = torch.empty((R, F // 32), device=dev, dtype=torch.uint8)
         if train:
-            o.saved_gu = torch.empty((R, 2 * F), device=dev, dtype=torch.bfloat16)
-            o.h_col = torch.empty((F, R), device=dev, dtype=torch.uint8 if mx else torch.bfloat16)
+            sz = fwd_saved_bytes(rt.prec, rt.T, rt.k, E, F, rt.align)
+            assert sz.rows == R
+            o.saved_gu = torch.empty(sz.saved_gu, device=dev, dtype=torch.uint8).view(torch.bfloat16).view(R, 2 * F)
+            hdt = torch.uint8 if mx else torch.bfloat16
+            o.h_col = torch.empty(sz.h_col, device=dev, dtype=torch.uint8).view(hdt).view(F, R)
             if mx:
-                o.h_col_scale = torch.empty((F, R // 32), device=dev, dtype=torch.uint8)
+                o.h_col_scale = torch.empty(sz.h_col_scale, device=dev, dtype=torch.uint8).view(F, R // 32)
     else:
         o = out
     a = FwdArgs()

@@ -75,9 +75,10 @@ static bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 static size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Gate-up (SwiGLU) GEMM: an expert's M-tile remainder under 4 joins its last raster band.
-// Same-job A/B on the Mixtral-shaped training step: gate-up 1.99 -> 1.95 ms and 3.61 -> 3.28 GB
-// fetched; the same rule on dh fetched 2.75 -> 3.07 GB, and bands of 16 on dW_gate_up
-// 3.03 -> 4.56 GB, for changes within run-to-run noise.
+// Two same-job A/B pairs on the Mixtral-shaped training step: gate-up 1.97 -> 1.93 and
+// 2.02 -> 1.95 ms, with 3.61 -> 3.51 GB fetched per launch; the same rule on dh fetched
+// 2.75 -> 3.07 GB, and bands of 16 on dW_gate_up 3.03 -> 4.56 GB, for time changes within
+// run-to-run noise (so neither is used).
 constexpr int kMergeShortBand = 1;
 
 // Bump allocator over the caller's workspace.
@@ -225,7 +226,7 @@ mge_status moe_route_permute(const mge_route_args* a, void* stream) {
   if (st != MGE_OK || !a->x) return st;
   QuantTileParams q{};
   q.in = a->x; q.in_batch_stride = 0; q.in_row_stride = a->H;
-  q.gather = a->perm_src;
+  q.gather = a->perm_src; q.src_rows = a->T;
   q.batch = 1; q.R = R; q.C = a->H; q.Rp = R;
   q.tensor_scale = x_ts;
   if (a->prec == MGE_PREC_MXFP8) {
@@ -280,7 +281,7 @@ mge_status mxfp8_quantize(const mge_quant_args* a, void* stream) {
     int32_t* map = static_cast<int32_t*>(a->workspace);
     const mge_status st = launch_seg_map(a->seg_offsets, a->num_segments, a->R, Rs, map, s);
     if (st != MGE_OK) return st;
-    q.gather = map;
+    q.gather = map; q.src_rows = a->R;
     q.R = Rs; q.Rp = Rs;
   }
   if (a->orient & MGE_ORIENT_ROW) { q.row_codes = a->row_codes; q.row_scales = a->row_scales; }
@@ -365,6 +366,28 @@ static size_t fwd_unfused_extra(const mge_fwd_unfused_args* u, int R) {
   if (a->prec == MGE_PREC_MXFP8 && !u->h_bf16) n += up256(size_t(R) * a->F * 2);
   if (u->h_tensor_scale) n += up256(size_t(tensor_scale_parts(int64_t(R) * a->F)) * sizeof(float));
   return n;
+}
+
+mge_status mge_fwd_saved_bytes(int32_t prec, int32_t T, int32_t k, int32_t E, int32_t F, int32_t align,
+                               mge_fwd_saved_sizes* out) {
+  g_err[0] = 0;
+  MGE_REQUIRE(out != nullptr, "out is NULL");
+  MGE_REQUIRE(out->struct_size == sizeof(mge_fwd_saved_sizes), "struct_size mismatch");
+  MGE_REQUIRE(prec == MGE_PREC_BF16 || prec == MGE_PREC_MXFP8, "prec must be BF16 or MXFP8");
+  MGE_REQUIRE(T >= 0, "T must be >= 0 (got %d)", T);
+  MGE_REQUIRE(E >= 1 && E <= 256, "E must be in [1, 256] (got %d)", E);
+  MGE_REQUIRE(k >= 1 && k <= 8 && k <= E, "k must be in [1, min(E, 8)] (got k=%d, E=%d)", k, E);
+  MGE_REQUIRE(F >= 32 && F % 32 == 0, "F must be a positive multiple of 32 (got %d)", F);
+  MGE_REQUIRE(pow2(align) && align <= 256 && align % 32 == 0, "training needs align a power of two in [32, 256] (got %d)",
+              align);
+  const size_t R = size_t(mge_perm_rows(T, k, E, align));
+  const bool mx = prec == MGE_PREC_MXFP8;
+  out->rows = int64_t(R);
+  out->saved_gu = R * 2 * size_t(F) * 2;
+  out->h_col = size_t(F) * R * (mx ? 1 : 2);
+  out->h_col_scale = mx ? size_t(F) * (R / 32) : 0;
+  out->total = out->saved_gu + out->h_col + out->h_col_scale;
+  return MGE_OK;
 }
 
 size_t mge_fwd_workspace_bytes(const mge_fwd_args* a) {
@@ -678,7 +701,7 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
   // b1: dy gathered by perm_src, row form (along H) and column form (along tokens)
   {
     QuantTileParams q{};
-    q.in = a->dy; q.in_row_stride = H; q.gather = a->perm_src;
+    q.in = a->dy; q.in_row_stride = H; q.gather = a->perm_src; q.src_rows = a->T;
     q.batch = 1; q.R = R; q.C = H; q.Rp = R;
     if (mx) { q.row_codes = static_cast<uint8_t*>(dyr); q.row_scales = dyrs; q.col_codes = static_cast<uint8_t*>(dyc); q.col_scales = dycs; }
     else { q.row_bf16 = static_cast<uint16_t*>(dyr); q.col_bf16 = static_cast<uint16_t*>(dyc); }

@@ -27,6 +27,7 @@ struct QuantTileParams {
   const uint16_t* in;
   int64_t in_batch_stride, in_row_stride;   // elements
   const int32_t* gather;                    // optional: source row of each output row (-1 = zero row)
+  int64_t src_rows;                         // with gather: rows of `in`; a source row outside [0, src_rows) reads as zero
   int batch, R, C, Rp;                      // output rows R (row form), padded rows Rp (column form)
   uint8_t* row_codes;  uint8_t* row_scales;  // MX row form  [b][R][C], [b][R][C/32]
   uint16_t* row_bf16;                        // bf16 row copy [b][R][C]

@@ -92,7 +92,8 @@ __global__ __launch_bounds__(QT_THREADS) void quant_tile_kernel(QuantTileParams 
   if (r < p.R && c < p.C) {
     int64_t src = r;
     if (p.gather) src = p.gather[r];
-    if (src >= 0) {
+    // a gathered row outside the source rows (only bad data can give one) reads as zero
+    if (src >= 0 && (!p.gather || src < p.src_rows)) {
       const uint4* g = reinterpret_cast<const uint4*>(in + src * p.in_row_stride + c);
       v[0] = g[0]; v[1] = g[1]; v[2] = g[2]; v[3] = g[3];
       have = true;

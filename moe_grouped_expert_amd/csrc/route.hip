@@ -5,11 +5,13 @@
 //   route_clear_kernel     clears the device error flag of this call
 //   route_topk_kernel      one thread per token: top-k of the fp32 logits (ties to the
 //                          lower index), softmax over the selected k, and a per-block
-//                          per-expert count (LDS histogram; counts are order-free)
+//                          per-expert count (LDS histogram built with LDS atomic adds:
+//                          integer counts, so the result does not depend on their order)
 //   route_scan_kernel      per expert, exclusive scan of the block counts -> block
 //                          bases; split_sizes; group_offsets (sizes rounded to align)
 //   route_scatter_kernel   stable rank of every assignment inside its block: within a
-//                          wave by ballot match masks + popcount, across the block's
+//                          wave by ballot match masks + popcount (plus the token's own
+//                          earlier slots with the same expert), across the block's
 //                          waves by per-wave counts in LDS; row = offset + block base +
 //                          rank.  Writes perm_src / perm_pos / prob_perm and marks the
 //                          padding rows.
@@ -153,9 +155,24 @@ __global__ __launch_bounds__(RT_THREADS) void route_scatter_kernel(RouteParams p
   int rank[RT_MAXK], after[RT_MAXK];
 #pragma unroll
   for (int i = 0; i < RT_MAXK; ++i) { rank[i] = 0; after[i] = 0; }
+  // A token may name one expert in several slots (caller-given indices, or an index
+  // clamped into range): its earlier slots with the same expert come first, so the
+  // order stays the stable (t, i) order and every row of the group is written once.
+#pragma unroll
+  for (int i = 0; i < RT_MAXK; ++i) {
+#pragma unroll
+    for (int j = 0; j < RT_MAXK; ++j) {
+      if (i < p.k && j < p.k && ex[j] == ex[i]) {
+        if (j < i) ++rank[i];
+        if (j > i) ++after[i];
+      }
+    }
+  }
   // For each slot j of the other lanes: mask of lanes whose slot-j expert equals my
-  // slot-i expert, assembled bit by bit from ballots.  A token's k experts are
-  // distinct, so the rank of (t, i) counts earlier tokens only.
+  // slot-i expert, assembled bit by bit from ballots; the rank of (t, i) adds the
+  // matching slots of the earlier tokens of the wave.  The last occurrence of an
+  // expert in the wave (no later lane and no later slot of its own token with it)
+  // holds the wave's count of that expert.
   for (int j = 0; j < p.k; ++j) {
     uint64_t m[RT_MAXK];
 #pragma unroll

@@ -139,13 +139,16 @@ def fwd_grouped(x, w_gate_up, w_down, lay: Layout, keep=False):
 
 
 def bwd_grouped(dy, w_gate_up, w_down, lay: Layout, saved):
-    """Grouped backward of L = <dy, y>. Returns dict dx, dw_gate_up, dw_down, d_prob, dX."""
+    """Grouped backward of L = <dy, y>. Returns dict dx, dw_gate_up, dw_down, d_prob, dX
+    and the permuted intermediates dh ([R][F]) and dGU = [dG dU] ([R][2F])."""
     E, F2, H = w_gate_up.shape
     F = F2 // 2
     X, G, U, h = saved["X"], saved["G"], saved["U"], saved["h"]
     dY = lay.gather(dy)
     dX = np.zeros((lay.R, H))
     dp_row = np.zeros(lay.R)
+    dh_all = np.zeros((lay.R, F))
+    dGU_all = np.zeros((lay.R, F2))
     dw_gu = np.zeros((E, F2, H))
     dw_d = np.zeros((E, H, F))
     for e in range(E):
@@ -161,10 +164,13 @@ def bwd_grouped(dy, w_gate_up, w_down, lay: Layout, saved):
         dU = dh * p * s
         dG = dh * p * U[r] * dsilu(G[r])
         dGU = np.concatenate([dG, dU], axis=1)
+        dh_all[r] = dh
+        dGU_all[r] = dGU
         dw_d[e] = dY[r].T @ h[r]
         dw_gu[e] = dGU.T @ X[r]
         dX[r] = dGU @ wgu
-    return dict(dx=lay.combine(dX), dw_gate_up=dw_gu, dw_down=dw_d, d_prob=lay.to_slots(dp_row), dX=dX)
+    return dict(dx=lay.combine(dX), dw_gate_up=dw_gu, dw_down=dw_d, d_prob=lay.to_slots(dp_row), dX=dX,
+                dh=dh_all, dGU=dGU_all)
 
 
 # ----------------------------------------------------------------------------- MXFP8 stages

@@ -1,8 +1,7 @@
 """MXFP8 (E4M3 elements + E8M0 block scales) in fp64 — oracle, test infrastructure only.
 
-What the pages fix: 8-bit elements with one scaling factor per block of 32
-consecutive values ([P1] "Memory and quantization overhead"; [P4] paragraph on
-FP8/MXFP8).  The element format (E4M3), the scale format (E8M0, a power of two)
+What the pages fix: 8-bit elements, with a run of 32 neighbouring elements sharing
+one scale ([P1] "Memory and quantization overhead"; [P4] paragraph on FP8/MXFP8).  The element format (E4M3), the scale format (E8M0, a power of two)
 and the scale-selection rule come from the OCP MX v1.0 specification [OCP]:
 
   * E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits.  Normal values

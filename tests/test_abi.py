@@ -260,3 +260,27 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
         b.lib()
     with pytest.raises(RuntimeError, match="not built"):
         m.perm_rows(8, 2, 4, 32)
+
+
+def test_fwd_saved_bytes():
+    """mge_fwd_saved_bytes is host arithmetic: G, U bf16 [R][2F], h column form [F][R]
+    (+ [F][R/32] scales in MXFP8), R = mge_perm_rows."""
+    R = b.perm_rows(8192, 2, 8, 32)
+    s = b.fwd_saved_bytes("mxfp8", 8192, 2, 8, 14336, 32)
+    assert s.rows == R
+    assert s.saved_gu == R * 2 * 14336 * 2
+    assert s.h_col == 14336 * R and s.h_col_scale == 14336 * (R // 32)
+    assert s.total == s.saved_gu + s.h_col + s.h_col_scale
+    t = b.fwd_saved_bytes("bf16", 256, 2, 4, 128, 32)
+    assert t.h_col == 128 * b.perm_rows(256, 2, 4, 32) * 2 and t.h_col_scale == 0
+    z = b.fwd_saved_bytes("mxfp8", 0, 2, 8, 64, 32)
+    assert z.rows == 256 and z.total == 256 * (4 * 64 + 64 + 2)
+    L = b.lib()
+    o = b.FwdSavedSizes()
+    o.struct_size = C.sizeof(b.FwdSavedSizes)
+    for args in ((1, 10, 2, 8, 48, 32), (1, 10, 2, 8, 64, 8), (2, 10, 2, 8, 64, 32), (1, 10, 9, 8, 64, 32),
+                 (1, -1, 2, 8, 64, 32)):
+        assert L.mge_fwd_saved_bytes(*args, C.byref(o)) == b.MGE_ERR_INVALID_ARG, args
+    o.struct_size = 4
+    assert L.mge_fwd_saved_bytes(1, 10, 2, 8, 64, 32, C.byref(o)) == b.MGE_ERR_INVALID_ARG
+    assert L.mge_fwd_saved_bytes(1, 10, 2, 8, 64, 32, None) == b.MGE_ERR_INVALID_ARG

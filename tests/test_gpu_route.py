@@ -136,3 +136,69 @@ def test_route_deterministic(m):
     b = m.moe_route_permute(l, x, 2, prec="mxfp8", want_col=True)
     for f in ("topk_idx", "topk_prob", "perm_src", "perm_pos", "x_perm", "x_perm_scale", "x_col", "x_col_scale"):
         assert torch.equal(getattr(a, f), getattr(b, f)), f
+
+
+def _repeat_case(T, E, k, seed):
+    """Caller-given top-k with repeated experts inside tokens and a few out-of-range
+    indices (each sets the device flag and is clamped into [0, E))."""
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    idx[::7, :] = idx[::7, :1]                 # every slot of these tokens on one expert
+    bad = idx.copy()
+    bad[3, 0] = E + 5
+    bad[10, k - 1] = -2
+    bad[11, :] = -1                            # clamps to expert 0 in every slot
+    clamped = np.clip(bad, 0, E - 1).astype(np.int32)
+    p = rng.random((T, k)).astype(np.float32)
+    return bad, clamped, p
+
+
+@pytest.mark.parametrize("T,E,k", [(300, 6, 2), (1000, 8, 4), (129, 3, 3), (64, 2, 2)])
+def test_route_given_repeated_experts_maps_only(m, T, E, k):
+    """Maps only (x = NULL): every row of perm_src is written, in [-1, T), and the maps
+    equal the oracle's stable counting sort of the clamped indices."""
+    from tests.gpu_helpers import npy, say
+    say("[gpu] route repeated experts, maps only", T, E, k)
+    bad, clamped, p = _repeat_case(T, E, k, T + E)
+    g = m.moe_route_permute(None, None, k, E=E, align=32, topk_idx=torch.from_numpy(bad).cuda(),
+                            topk_prob=torch.from_numpy(p).cuda())
+    assert m.check_device_errors(g) == 5
+    ps = npy(g.perm_src)
+    assert ps.min() >= -1 and ps.max() < T
+    sizes = rt.split_sizes(clamped, E)
+    np.testing.assert_array_equal(npy(g.split_sizes), sizes)
+    np.testing.assert_array_equal(npy(g.group_offsets), rt.group_offsets(sizes, 32))
+    ops, opp = rt.permutation(clamped, E, 32)
+    np.testing.assert_array_equal(ps, ops)
+    np.testing.assert_array_equal(npy(g.perm_pos), opp)
+    np.testing.assert_array_equal(npy(g.prob_perm), rt.prob_permuted(p.astype(np.float64), opp, len(ops)).astype(np.float32))
+
+
+@pytest.mark.parametrize("prec", ["bf16", "mxfp8"])
+def test_route_given_repeated_experts_with_x(m, prec):
+    """The same inputs with x: the gathered rows (and MXFP8 codes) follow the oracle's
+    permutation (regression test of the repeated-slot rank)."""
+    from tests.gpu_helpers import gpu_bf16, npy, say
+    T, E, k, H = 300, 6, 2, 64
+    say("[gpu] route repeated experts with x", prec)
+    bad, clamped, p = _repeat_case(T, E, k, 77)
+    x = np.random.default_rng(78).standard_normal((T, H)).astype(np.float32)
+    gx = gpu_bf16(x)
+    g = m.moe_route_permute(None, gx, k, E=E, align=32, prec=prec, want_col=True,
+                            topk_idx=torch.from_numpy(bad).cuda(), topk_prob=torch.from_numpy(p).cuda())
+    assert m.check_device_errors(g) == 5
+    ops, _ = rt.permutation(clamped, E, 32)
+    np.testing.assert_array_equal(npy(g.perm_src), ops)
+    xb = gx.float().cpu().numpy().astype(np.float64)
+    X = np.zeros((len(ops), H))
+    X[ops >= 0] = xb[ops[ops >= 0]]
+    if prec == "bf16":
+        np.testing.assert_array_equal(g.x_perm.float().cpu().numpy(), X)
+        np.testing.assert_array_equal(g.x_col.float().cpu().numpy(), X.T)
+    else:
+        q, s = mx.quantize_rows(X)
+        np.testing.assert_array_equal(npy(g.x_perm), q)
+        np.testing.assert_array_equal(npy(g.x_perm_scale), s)
+        qc, sc = mx.quantize_cols(X)
+        np.testing.assert_array_equal(npy(g.x_col), qc)
+        np.testing.assert_array_equal(npy(g.x_col_scale), sc)

@@ -7,7 +7,13 @@
 * empty experts get exactly zero weight gradients;
 * the MXFP8 stages reduce to the exact forward when every operand is representable
   (quantization is then the identity), and the ragged dW stage equals its triple-sum
-  definition on a tiny case.
+  definition on a tiny case;
+* the MXFP8 SwiGLU-backward stage (mx_dh_stage), fed exactly representable dY and
+  W_down column codes, equals the finite-difference-pinned grouped backward's dG, dU
+  and d_prob (G of both signs and near 0, p != 1);
+* the whole MXFP8 forward (mx_fwd_end_to_end) on representable x and weights equals
+  the grouped forward up to the quantization of h, which it applies after the
+  probability scaling.
 """
 import numpy as np
 import pytest
@@ -173,3 +179,80 @@ def test_mx_dw_stage_triple_sum():
             for j in range(NB):
                 ref = sum(Ad[i, m] * Bd[j, m] for m in range(r.start, r.stop))
                 assert abs(got[e, i, j] - ref) <= 1e-12 * (1 + abs(ref))
+
+
+def _col_representable(rng, shape):
+    """[..., R, C] values exactly representable in the column form (blocks of 32 rows)."""
+    v = _representable(rng, shape[:-2] + (shape[-1], shape[-2]))
+    return np.swapaxes(v, -1, -2)
+
+
+def test_mx_dh_stage_equals_grouped_backward_on_representable_operands():
+    rng = np.random.default_rng(31)
+    T, E, H, F, k = 64, 4, 64, 96, 2
+    x = rng.standard_normal((T, H))
+    wgu = rng.standard_normal((E, 2 * F, H)) * 0.3
+    wd = _col_representable(rng, (E, H, F))
+    dy = _representable(rng, (T, H))
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    idx, p = rt.route(l, k)
+    lay = mlp.Layout(idx, p, E, 32)
+    _, saved = mlp.fwd_grouped(x, wgu, wd, lay, keep=True)
+    ref = mlp.bwd_grouped(dy, wgu, wd, lay, saved)
+    G, U = saved["G"], saved["U"]
+    valid = lay.perm_src >= 0
+    # the SwiGLU backward is exercised on both branches of silu' and away from p = 1
+    assert (G[valid] < -1).any() and (G[valid] > 1).any() and (np.abs(G[valid]) < 0.05).any()
+    assert np.all(lay.prob_perm[valid] < 1) and np.ptp(lay.prob_perm[valid]) > 0.3
+    dY = lay.gather(dy)
+    dyq, dys = mx.quantize_rows(dY)
+    np.testing.assert_array_equal(mx.dequantize_rows(dyq, dys), dY)
+    wdc = [mx.quantize_cols(wd[e]) for e in range(E)]
+    for e in range(E):
+        np.testing.assert_array_equal(mx.dequantize_rows(*wdc[e]), wd[e].T)
+    dG, dU, dp_row = mlp.mx_dh_stage(dyq, dys, [a for a, _ in wdc], [b for _, b in wdc], G, U, lay)
+    np.testing.assert_allclose(dG[valid], ref["dGU"][valid, :F], rtol=1e-12, atol=1e-12 * np.abs(ref["dGU"]).max())
+    np.testing.assert_allclose(dU[valid], ref["dGU"][valid, F:], rtol=1e-12, atol=1e-12 * np.abs(ref["dGU"]).max())
+    np.testing.assert_allclose(lay.to_slots(dp_row), ref["d_prob"], rtol=1e-12, atol=1e-12 * np.abs(ref["d_prob"]).max())
+    # dG and dU differ (a swap of the two would fail above), and both are non-trivial
+    assert rel_f(dG[valid], dU[valid]) > 0.5 and np.abs(dG).max() > 0 and np.abs(dU).max() > 0
+
+
+def test_mx_fwd_end_to_end_equals_grouped_up_to_h_quantization():
+    rng = np.random.default_rng(37)
+    T, E, H, F, k = 48, 3, 64, 64, 2
+    x = _representable(rng, (T, H))
+    wgu = _representable(rng, (E, 2 * F, H))
+    wd = _representable(rng, (E, H, F))
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    idx, p = rt.route(l, k)
+    lay = mlp.Layout(idx, p, E, 32)
+    y_ref, keep = mlp.fwd_grouped(x, wgu, wd, lay, keep=True)
+    y, parts = mlp.mx_fwd_end_to_end(x, wgu, wd, lay)
+    # x, W_gate_up and W_down are representable: G, U and h = p * silu(G) * U are exact
+    for name in ("G", "U", "h"):
+        np.testing.assert_allclose(parts[name], keep[name], rtol=1e-13, atol=1e-15)
+    # h is quantized along F after the probability scaling, and only h
+    hq, hs = mx.quantize_rows(keep["h"])
+    np.testing.assert_array_equal(parts["hq"], hq)
+    np.testing.assert_array_equal(parts["hs"], hs)
+    hd = mx.dequantize_rows(hq, hs)
+    Y = np.zeros((lay.R, H))
+    for e in range(E):
+        r = lay.rows(e)
+        Y[r] = hd[r] @ wd[e].T
+    np.testing.assert_allclose(y, lay.combine(Y), rtol=1e-12, atol=1e-12 * np.abs(y).max())
+    # the h quantization is the only difference from the exact forward: E4M3 keeps 3
+    # mantissa bits (relative rounding error <= 2^-4 on normal values)
+    err = rel_f(y, y_ref)
+    assert 0 < err < 2.0 ** -4
+    # the other reading, p * dequantize(quantize(silu(G) * U)), gives a different y on this
+    # input, so the check above tells the two apart
+    pr = lay.prob_perm[:, None]
+    hq2, hs2 = mx.quantize_rows(silu_u := mlp.silu(keep["G"]) * keep["U"])
+    Y2 = np.zeros((lay.R, H))
+    for e in range(E):
+        r = lay.rows(e)
+        Y2[r] = (pr[r] * mx.dequantize_rows(hq2, hs2)[r]) @ wd[e].T
+    assert rel_f(y, lay.combine(Y2)) > 1e-4 and silu_u.shape == keep["h"].shape
+

@@ -108,6 +108,25 @@ def test_empty_experts_and_single_expert():
     np.testing.assert_array_equal(perm_pos, [[32, 0], [33, 1], [2, 34]])
 
 
+def test_permutation_with_repeated_experts_in_a_token():
+    """Caller-given indices may name one expert in several slots of a token: every slot
+    still gets its own row, in (t, i) order.  Pinned by the stable argsort special case
+    (align 1) and by hand on a small case."""
+    idx = np.array([[1, 1], [0, 1], [1, 0], [0, 0]], np.int32)
+    perm_src, perm_pos = rt.permutation(idx, 2, 1)
+    np.testing.assert_array_equal(rt.split_sizes(idx, 2), [4, 4])
+    # expert 0: (1,0) (2,1) (3,0) (3,1); expert 1: (0,0) (0,1) (1,1) (2,0)
+    np.testing.assert_array_equal(perm_pos, [[4, 5], [0, 6], [7, 1], [2, 3]])
+    np.testing.assert_array_equal(perm_src[:8], [1, 2, 3, 3, 0, 0, 1, 2])
+    rng = np.random.default_rng(5)
+    for E, k in ((3, 4), (6, 2), (1, 3)):
+        idx = rng.integers(0, E, size=(200, k)).astype(np.int32)
+        perm_src, perm_pos = rt.permutation(idx, E, 1)
+        order = np.argsort(idx.ravel(), kind="stable")
+        np.testing.assert_array_equal(perm_src[: idx.size], order // k)
+        np.testing.assert_array_equal(perm_pos.ravel()[order], np.arange(idx.size))
+
+
 def test_prob_permuted():
     idx = np.array([[1, 0], [0, 1]], np.int32)
     p = np.array([[0.7, 0.3], [0.6, 0.4]])
