@@ -133,8 +133,9 @@ class Step:
     received rows are permuted by their given local expert and probability (k = 1), and
     the router's backward stays with the dispatching ranks.  variant "expert_loop" runs
     the forward as one single-group grouped_mlp_fwd per expert, "unfused" as
-    grouped_mlp_fwd_unfused (both inference only; keep_intermediates keeps the unfused
-    call's [G U] and bf16 h in their own buffers instead of the workspace)."""
+    grouped_mlp_fwd_unfused (both inference only).  keep_intermediates keeps the unfused
+    call's [G U] and bf16 h, and the backward's dY and dGU codes, in buffers of their own
+    instead of the workspace (the same kernels; the parity tests read them)."""
 
     def __init__(self, m, w, inp, train, variant="grouped", dw_dtype="f32"):
         self.m, self.w, self.inp, self.train = m, w, inp, train
@@ -220,9 +221,11 @@ class Step:
         if self.train:
             if mx:
                 self.b = m.grouped_mlp_bwd(inp["dy"], self.g, self.f, self.wq[2], self.dq[2], self.wq[3], self.dq[3],
-                                           out=self.b, dw_dtype=self.dw_dtype)
+                                           keep_intermediates=self.keep_intermediates, out=self.b,
+                                           dw_dtype=self.dw_dtype)
             else:
-                self.b = m.grouped_mlp_bwd(inp["dy"], self.g, self.f, inp["wgu"], inp["wd"], out=self.b,
+                self.b = m.grouped_mlp_bwd(inp["dy"], self.g, self.f, inp["wgu"], inp["wd"],
+                                           keep_intermediates=self.keep_intermediates, out=self.b,
                                            dw_dtype=self.dw_dtype)
             self.dx = m.unpermute_combine(self.b.dx_perm, self.g.perm_pos, out=self.dx)
             if not self.given:

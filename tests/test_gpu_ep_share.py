@@ -183,10 +183,11 @@ def test_mixtral_rank_share_forward_sampled(cfg):
 
 def test_mixtral_ep8_rank_share_training_sampled():
     """Rank 0 of 8 (expert 0) at the Mixtral shape, the training step of 8 x 8192 tokens'
-    expert-0 rows as bench.py times it: sampled rows of dx_perm and d_prob from the oracle's
-    dh stage on the GPU's saved G, U (dY and dGU quantized by the oracle: rel_F 5e-3 for
-    dX, a few E4M3 code flips between fp32 and fp64 dGU), and dW_down entries over the whole
-    token span from the oracle's column forms of dY and the GPU's column form of h."""
+    expert-0 rows as bench.py times it (the backward keeps its dY and dGU codes in caller
+    buffers, the same kernels): sampled rows of d_prob and of the dGU codes from the
+    oracle's dh stage on the GPU's dY codes and saved G, U; dx_perm rows from the GPU's dGU
+    codes; dW_down entries over the whole token span from the oracle's column forms of dY
+    (bit-exact with the GPU's) and the GPU's column form of h.  rel_F 2e-3 each."""
     import bench
     import moe_grouped_expert_amd as m
     from tests.gpu_helpers import npy, say
@@ -197,6 +198,7 @@ def test_mixtral_ep8_rank_share_training_sampled():
     say("[gpu] full-size EP=8 training share: inputs")
     inp, wl = bench.make_ep_share_inputs(m, w, dev)
     step = bench.Step(m, wl, inp, train=True)
+    step.keep_intermediates = True
     step()
     torch.cuda.synchronize()
     g, f, b = step.g, step.f, step.b
@@ -209,6 +211,8 @@ def test_mixtral_ep8_rank_share_training_sampled():
     sel = torch.as_tensor(rows, device=dev, dtype=torch.long)
     dy = inp["dy"].index_select(0, torch.as_tensor(perm_src[rows], device=dev, dtype=torch.long))
     dyq, dys = mx.quantize_rows(dy.float().cpu().numpy().astype(np.float64))
+    np.testing.assert_array_equal(npy(b.dy_row.index_select(0, sel)), dyq)
+    np.testing.assert_array_equal(npy(b.dy_row_scale.index_select(0, sel)), dys)
     dh = mx.dequantize_rows(dyq, dys) @ mx.dequantize_rows(npy(step.dq[2][0]), npy(step.dq[3][0])).T
     gu = f.saved_gu.index_select(0, sel).float().cpu().numpy().astype(np.float64)
     G, U = gu[:, :F], gu[:, F:]
@@ -216,8 +220,11 @@ def test_mixtral_ep8_rank_share_training_sampled():
     dG = dh * p * U * mlp.dsilu(G)
     dU = dh * p * mlp.silu(G)
     gq, gs = mx.quantize_rows(np.concatenate([dG, dU], axis=1))
-    dX = mx.dequantize_rows(gq, gs) @ mx.dequantize_rows(npy(step.wq[2][0]), npy(step.wq[3][0])).T
-    errs = {"dx_perm": rel_f(b.dx_perm.index_select(0, sel).float().cpu().numpy().astype(np.float64), dX),
+    gq_gpu, gs_gpu = npy(b.dgu_row.index_select(0, sel)), npy(b.dgu_row_scale.index_select(0, sel))
+    flips = float(np.mean(gq_gpu != gq))
+    dX = mx.dequantize_rows(gq_gpu, gs_gpu) @ mx.dequantize_rows(npy(step.wq[2][0]), npy(step.wq[3][0])).T
+    errs = {"dgu_row": rel_f(mx.dequantize_rows(gq_gpu, gs_gpu), mx.dequantize_rows(gq, gs)),
+            "dx_perm": rel_f(b.dx_perm.index_select(0, sel).float().cpu().numpy().astype(np.float64), dX),
             "d_prob": rel_f(npy(b.d_prob)[perm_src[rows], 0].astype(np.float64), np.sum(dh * mlp.silu(G) * U, axis=1))}
     # dW_down[h][f] = sum over the expert's tokens of dY[t][h] h[t][f], from the column forms
     hs, fs = rng.integers(0, H, 6), rng.integers(0, F, 6)
@@ -233,8 +240,10 @@ def test_mixtral_ep8_rank_share_training_sampled():
     dWd = mx.dequantize_rows(cq, cs) @ hc.T
     got = b.dw_down[0].index_select(0, hs_t).index_select(1, fs_t)
     errs["dw_down"] = rel_f(got.double().cpu().numpy(), dWd)
-    say("[gpu] EP=8 training share rows", n, {kk: f"{v:.2e}" for kk, v in errs.items()})
-    assert errs["dx_perm"] <= 5e-3 and errs["d_prob"] <= 2e-3 and errs["dw_down"] <= 2e-3
+    say("[gpu] EP=8 training share rows", n, {kk: f"{v:.2e}" for kk, v in errs.items()}, f"dGU flips {flips:.1e}")
+    for key, v in errs.items():
+        assert v <= 2e-3, (key, v)
+    assert flips <= 2e-3, flips
 
 
 def test_mixtral_expert_loop_equals_grouped():

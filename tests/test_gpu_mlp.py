@@ -21,6 +21,13 @@ pytestmark = pytest.mark.gpu
 
 BF16_TOL = 1e-2
 MX_TOL = 2e-3
+# E4M3 code flips of the quantities the GPU quantizes from its own fp32 values (h in the
+# gate-up epilogue, dG and dU in the dh epilogue) against the oracle's quantization of
+# its fp64 values of the same stage: about 2x the rates measured on MI355X (h
+# 1.4-2.0e-3, dGU 0.8-0.9e-3; the fp32 accumulation of the block-scaled MFMA differs
+# from fp64 by about 1e-4 relative, measured by the f32 down stage below)
+H_FLIP_MAX = 4e-3
+DGU_FLIP_MAX = 2e-3
 
 
 @pytest.fixture(scope="module")
@@ -216,7 +223,7 @@ def test_mxfp8_staged(m, w):
     say("[gpu] staged rel_F", {k: f"{v:.2e}" for k, v in errs.items()}, f"h flips {flips:.1e} dGU flips {flips_dgu:.1e}")
     for k, v in errs.items():
         assert v <= MX_TOL, (k, v)
-    assert flips <= 1e-2 and flips_dgu <= 1e-2
+    assert flips <= H_FLIP_MAX and flips_dgu <= DGU_FLIP_MAX, (flips, flips_dgu)
     # end to end against the unstaged fp64 MXFP8 pipeline (report; loose bound)
     y_e2e, _ = mlp.mx_fwd_end_to_end(inp.x, inp.wgu, inp.wd, lay)
     e2e = rel_f(f64(o["y"]), y_e2e)
@@ -249,3 +256,37 @@ def test_mxfp8_empty_experts_zero_grad(m):
     for e in (1, 5):
         assert not torch.any(o["b"].dw_gate_up[e]) and not torch.any(o["b"].dw_down[e])
     assert torch.any(o["b"].dw_gate_up[0])
+
+
+@pytest.mark.parametrize("w", [MX_CASES[0], MX_CASES[2]], ids=lambda w: w.name)
+def test_mxfp8_down_stage_f32(m, w):
+    """y_perm in fp32 (y_dtype F32): the down GEMM's output without the bf16 rounding,
+    against the oracle's block-scaled product on the GPU's own h and W_down codes.  This
+    measures the accumulation of the block-scaled MFMA itself (fp32 accumulators,
+    K = F); the end-to-end y against the unstaged fp64 MXFP8 pipeline is reported
+    beside it (it carries h's code flips and one bf16 rounding, of y)."""
+    from tests.gpu_helpers import Inputs, f64, layout_from_gpu, npy, say
+    say("[gpu] mxfp8 f32 down stage", w)
+    inp = Inputs(w)
+    o = run_mx(m, inp, y_dtype="f32")
+    g, f = o["g"], o["f"]
+    assert f.y_perm.dtype == torch.float32
+    lay = layout_from_gpu(g, w.E, 32)
+    valid = npy(g.perm_src) >= 0
+    wd_q = [npy(o["dq"][0][e]) for e in range(w.E)]
+    wd_s = [npy(o["dq"][1][e]) for e in range(w.E)]
+    Y = mlp.mx_down_stage(npy(f.h), npy(f.h_scale), wd_q, wd_s, lay)
+    err = rel_f(f64(f.y_perm)[valid], Y[valid])
+    # gate-up: the product before the epilogue is only visible through h; the h codes'
+    # flip rate against the oracle fed the GPU's x and weight codes
+    G, U, h = mlp.mx_gateup_stage(npy(g.x_perm), npy(g.x_perm_scale), [npy(t) for t in o["wq"][0]],
+                                  [npy(t) for t in o["wq"][1]], lay)
+    hq, _ = mx.quantize_rows(h)
+    flips = flip_rate(npy(f.h)[valid], hq[valid])
+    y_e2e, _ = mlp.mx_fwd_end_to_end(inp.x, inp.wgu, inp.wd, lay)
+    e2e = rel_f(f64(o["y"]), y_e2e)
+    say(f"[gpu] f32 y_perm stage rel_F {err:.2e}; h flips {flips:.1e}; end-to-end y rel_F {e2e:.2e}")
+    assert err <= 5e-4, err
+    assert flips <= H_FLIP_MAX
+    assert e2e <= 1e-2, e2e   # reported: h's code flips move y by more than the staged bound
+
