@@ -553,7 +553,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=None,
                     help="assignments in the CPU oracle sample (default: expert 0's whole group for MXFP8, 4096 for BF16)")
     ap.add_argument("--cpu-fcols", type=int, default=None,
-                    help="ffn columns in the CPU oracle sample (default: F/4 for MXFP8, all for BF16)")
+                    help="ffn columns in the CPU oracle sample (default: F/2 for MXFP8, all for BF16)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only the 1 GiB copy the traffic counters are calibrated on")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
@@ -687,11 +687,11 @@ def main():
         out["rows_per_s"] = out.pop("tokens_per_s")   # received rows (assignments), k = 1 locally
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        # MXFP8: expert 0's whole group over a quarter of the ffn columns (about 20 s of fp64
-        # numpy on 8 cores; the weight-slice quantization and the GEMMs both scale with the
+        # MXFP8: expert 0's whole group over half of the ffn columns (about 12 s of fp64 numpy
+        # on 16 host cores; the weight-slice quantization and the GEMMs both scale with the
         # columns, so the mix of the two is that of the whole step)
         rows = args.cpu_rows if args.cpu_rows is not None else (4096 if wg.prec == "bf16" else None)
-        fcols = args.cpu_fcols if args.cpu_fcols is not None else (None if wg.prec == "bf16" else max(32, wg.F // 4))
+        fcols = args.cpu_fcols if args.cpu_fcols is not None else (None if wg.prec == "bf16" else max(32, wg.F // 2))
         out["cpu_baseline"] = cpu_baseline(wg, rows, fcols)
     print(json.dumps(out), flush=True)
 

@@ -11,7 +11,9 @@ groups have exactly the sizes under test:
 BF16: y, dx, dW_gate_up, dW_down and d_prob end to end against fp64 on the same bf16
 inputs (rel_F 1e-2).  MXFP8: staged, each stage against the oracle fed the GPU's own
 quantized operands (rel_F 2e-3; x, dy, weights and the permutation bit-exact; h and dGU
-compared after dequantization with their code flips bounded).  Experts without tokens
+compared after dequantization with their code flips bounded); a bf16-stored stage output
+of under 4096 elements (the single token) whose rel_F exceeds 2e-3 is held element by
+element to one bf16 rounding instead.  Experts without tokens
 get exactly zero weight gradients in both."""
 import numpy as np
 import pytest
@@ -186,8 +188,23 @@ def test_edge_fwd_bwd(m, name, prec):
     dWgu = mlp.mx_dw_stage(npy(b.dgu_col), npy(b.dgu_col_scale), npy(g.x_col), npy(g.x_col_scale), lay)
     errs["dw_gate_up"] = rel_f(np.stack([f64(t) for t in b.dw_gate_up]), dWgu)
     errs["dx"] = rel_f(f64(o["dx"]), lay.combine(np.where(valid[:, None], f64(b.dx_perm), 0.0)))
+    # bf16-stored stage outputs with few elements: (GPU, oracle) pairs for the element bound
+    pairs = dict(G=(gu[valid, :F], G[valid]), U=(gu[valid, F:], U[valid]), y_perm=(f64(f.y_perm)[valid], Y[valid]),
+                 y=(f64(o["y"]), lay.combine(np.where(valid[:, None], f64(f.y_perm), 0.0))),
+                 dx_perm=(f64(b.dx_perm)[valid], dX[valid]),
+                 dx=(f64(o["dx"]), lay.combine(np.where(valid[:, None], f64(b.dx_perm), 0.0))))
+    small = {kk: v for kk, v in pairs.items() if v[1].size < 4096}
     say("[gpu] edge staged rel_F", {kk: f"{v:.2e}" for kk, v in errs.items()}, f"flips h {fl_h:.1e} dGU {fl_g:.1e}")
     for kk, v in errs.items():
+        if v > MX_TOL and kk in small:
+            # under 4096 elements the rel_F of one bf16 rounding (about 1.5e-3 on average)
+            # spreads past 2e-3; such a stage is held element by element to one rounding
+            # (relative 2^-8 at worst) plus the fp32 accumulation (2^-12 relative, 2^-20
+            # of the largest magnitude)
+            got, ref = small[kk]
+            bound = (2.0 ** -8 + 2.0 ** -12) * np.abs(ref) + 2.0 ** -20 * np.abs(ref).max()
+            assert np.all(np.abs(got - ref) <= bound), (kk, v, float(np.max(np.abs(got - ref) / (bound + 1e-300))))
+            continue
         assert v <= MX_TOL, (kk, v)
     # a single token gives too few codes for a rate: at most one flip there
     n_h, n_g = int(valid.sum()) * F, int(valid.sum()) * 2 * F
