@@ -142,6 +142,28 @@ size_t mge_route_workspace_bytes(int32_t T, int32_t E);
 mge_status moe_route_permute(const mge_route_args* args, void* stream);
 
 /* ------------------------------------------------------------------------------
+ * moe_route_permute_noalloc — moe_route_permute for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same computation, kernels and outputs, with its workspace
+ * (the device error flag and the per-block expert counts) in a fixed scratch array
+ * the library holds on every GPU it runs on, 1 MiB per GPU, kept until the process
+ * ends.  The caller still passes every input and output; args->workspace must be
+ * NULL and args->workspace_bytes 0.  Nothing is allocated: no hipMalloc, no hipFree.
+ * Limit: mge_route_workspace_bytes(T, E) <= 1 MiB, i.e. 256 + ceil(T/256)*E*4 bytes
+ * (each part rounded up to 256): about 8.3 M tokens at E = 8, 262 144 at E = 256.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last call's
+ * contents (each call clears the flag and rewrites the counts before reading them):
+ * calls that overlap on one GPU (two streams, two threads) race and must be
+ * serialized by the caller.  The device error flag of an out-of-range given index is
+ * not reported (indices are still clamped); check such inputs with
+ * moe_route_permute and its workspace.
+ * Errors: those of moe_route_permute; MGE_ERR_INVALID_ARG for a workspace given;
+ * MGE_ERR_UNSUPPORTED for T, E beyond the scratch (the message gives the sizes);
+ * MGE_ERR_HIP if the scratch's device address cannot be obtained.
+ * ---------------------------------------------------------------------------- */
+mge_status moe_route_permute_noalloc(const mge_route_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------
  * mxfp8_quantize — BF16 -> MXFP8 (E4M3 + E8M0 per 32), the per-step quantization of
  * the 16-bit master weights.
  *

@@ -92,7 +92,8 @@ class RouterBwdArgs(C.Structure):
 
 
 _LIB = None
-EXPORTS = ["mge_perm_rows", "mge_route_workspace_bytes", "moe_route_permute", "mxfp8_quantize",
+EXPORTS = ["mge_perm_rows", "mge_route_workspace_bytes", "moe_route_permute", "moe_route_permute_noalloc",
+           "mxfp8_quantize",
            "mge_fwd_workspace_bytes", "grouped_mlp_fwd", "mge_fwd_saved_bytes", "mge_fwd_unfused_workspace_bytes", "grouped_mlp_fwd_unfused",
            "mge_tensor_scale_workspace_bytes", "mge_tensor_scale", "mge_quant_workspace_bytes",
            "mge_bwd_workspace_bytes", "grouped_mlp_bwd",
@@ -127,7 +128,8 @@ def lib():
         L.mge_tensor_scale_workspace_bytes.argtypes = [i32, i64]
         L.mge_bwd_workspace_bytes.restype = C.c_size_t
         L.mge_bwd_workspace_bytes.argtypes = [C.POINTER(BwdArgs)]
-        for name, st in (("moe_route_permute", RouteArgs), ("mxfp8_quantize", QuantArgs),
+        for name, st in (("moe_route_permute", RouteArgs), ("moe_route_permute_noalloc", RouteArgs),
+                         ("mxfp8_quantize", QuantArgs),
                          ("mge_tensor_scale", TensorScaleArgs),
                          ("grouped_mlp_fwd", FwdArgs), ("grouped_mlp_fwd_unfused", FwdUnfusedArgs),
                          ("grouped_mlp_bwd", BwdArgs),
@@ -207,10 +209,12 @@ class RouteOut:
 def moe_route_permute(logits: Optional[torch.Tensor], x: Optional[torch.Tensor], k: int, E: Optional[int] = None,
                       align: int = 32, prec: str = "bf16", want_col: bool = False,
                       topk_idx: Optional[torch.Tensor] = None, topk_prob: Optional[torch.Tensor] = None,
-                      out: Optional[RouteOut] = None, x_tensor_scale: Optional[torch.Tensor] = None) -> RouteOut:
+                      out: Optional[RouteOut] = None, x_tensor_scale: Optional[torch.Tensor] = None,
+                      noalloc: bool = False) -> RouteOut:
     """Top-k routing + stable permutation by expert (+ gather / quantize of x; with
     x_tensor_scale, a uint8 [1] tensor from tensor_scale(x), every block of x takes that
-    one scale)."""
+    one scale).  noalloc: call moe_route_permute_noalloc, whose workspace is the library's
+    fixed scratch (no workspace tensor is allocated or passed)."""
     given = topk_idx is not None
     ref = logits if logits is not None else topk_idx
     dev = ref.device
@@ -243,8 +247,9 @@ def moe_route_permute(logits: Optional[torch.Tensor], x: Optional[torch.Tensor],
                 o.x_perm = torch.empty((R, H), device=dev, dtype=torch.bfloat16)
                 if want_col:
                     o.x_col = torch.empty((H, R), device=dev, dtype=torch.bfloat16)
-        nbytes = int(lib().mge_route_workspace_bytes(T, E))
-        o.workspace = torch.empty(max(nbytes, 256), device=dev, dtype=torch.uint8)
+        if not noalloc:
+            nbytes = int(lib().mge_route_workspace_bytes(T, E))
+            o.workspace = torch.empty(max(nbytes, 256), device=dev, dtype=torch.uint8)
     else:
         o = out
     a = RouteArgs()
@@ -259,9 +264,13 @@ def moe_route_permute(logits: Optional[torch.Tensor], x: Optional[torch.Tensor],
     a.perm_src, a.perm_pos, a.prob_perm = _ptr(o.perm_src), _ptr(o.perm_pos), _ptr(o.prob_perm)
     a.x_perm, a.x_perm_scale = _ptr(o.x_perm), _ptr(o.x_perm_scale)
     a.x_col, a.x_col_scale = _ptr(o.x_col), _ptr(o.x_col_scale)
-    a.workspace, a.workspace_bytes = _ptr(o.workspace), o.workspace.numel()
     a.x_tensor_scale = _ptr(x_tensor_scale)
-    _check(lib().moe_route_permute(C.byref(a), _stream(dev)), "moe_route_permute")
+    if noalloc:
+        a.workspace, a.workspace_bytes = None, 0
+        _check(lib().moe_route_permute_noalloc(C.byref(a), _stream(dev)), "moe_route_permute_noalloc")
+    else:
+        a.workspace, a.workspace_bytes = _ptr(o.workspace), o.workspace.numel()
+        _check(lib().moe_route_permute(C.byref(a), _stream(dev)), "moe_route_permute")
     return o
 
 

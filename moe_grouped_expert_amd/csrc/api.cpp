@@ -169,9 +169,9 @@ size_t mge_route_workspace_bytes(int32_t T, int32_t E) {
   return up256(256) + up256(size_t(route_nblk(T)) * E * sizeof(int32_t));
 }
 
-mge_status moe_route_permute(const mge_route_args* a, void* stream) {
-  g_err[0] = 0;
-  MGE_REQUIRE(a != nullptr, "args is NULL");
+// moe_route_permute with the workspace `ws` of `ws_bytes` (the caller's, or the fixed
+// scratch of the no-allocation variant).
+static mge_status route_impl(const mge_route_args* a, void* ws_base, size_t ws_bytes, void* stream) {
   // the struct may end before its added last field (x_tensor_scale: then NULL)
   MGE_REQUIRE(a->struct_size == sizeof(mge_route_args) || a->struct_size == offsetof(mge_route_args, x_tensor_scale),
               "struct_size mismatch (%u vs %zu)", a->struct_size, sizeof(mge_route_args));
@@ -200,14 +200,14 @@ mge_status moe_route_permute(const mge_route_args* a, void* stream) {
     }
   }
   const size_t need = mge_route_workspace_bytes(a->T, a->E);
-  if (!a->workspace || a->workspace_bytes < need) {
-    set_error("route workspace needs %zu bytes (got %zu)", need, a->workspace_bytes);
+  if (!ws_base || ws_bytes < need) {
+    set_error("route workspace needs %zu bytes (got %zu)", need, ws_bytes);
     return MGE_ERR_WORKSPACE;
   }
   if (a->T == 0) return MGE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int R = int(mge_perm_rows(a->T, a->k, a->E, a->align));
-  Carve ws(a->workspace);
+  Carve ws(ws_base);
   RouteParams p{};
   p.T = a->T; p.E = a->E; p.k = a->k; p.align = a->align;
   p.nblk = route_nblk(a->T);
@@ -238,6 +238,34 @@ mge_status moe_route_permute(const mge_route_args* a, void* stream) {
     if (want_col) q.col_bf16 = static_cast<uint16_t*>(a->x_col);
   }
   return launch_quant_tile(q, a->prec == MGE_PREC_MXFP8, s);
+}
+
+mge_status moe_route_permute(const mge_route_args* a, void* stream) {
+  g_err[0] = 0;
+  MGE_REQUIRE(a != nullptr, "args is NULL");
+  return route_impl(a, a->struct_size >= offsetof(mge_route_args, x_tensor_scale) ? a->workspace : nullptr,
+                    a->struct_size >= offsetof(mge_route_args, x_tensor_scale) ? a->workspace_bytes : 0, stream);
+}
+
+mge_status moe_route_permute_noalloc(const mge_route_args* a, void* stream) {
+  g_err[0] = 0;
+  MGE_REQUIRE(a != nullptr, "args is NULL");
+  MGE_REQUIRE(a->struct_size >= offsetof(mge_route_args, x_tensor_scale), "struct_size mismatch");
+  MGE_REQUIRE(a->workspace == nullptr && a->workspace_bytes == 0,
+              "moe_route_permute_noalloc takes no workspace (workspace NULL, workspace_bytes 0)");
+  const mge_status chk = check_common(a->T, a->E, a->k, a->H, a->align);
+  if (chk != MGE_OK) return chk;
+  const size_t need = mge_route_workspace_bytes(a->T, a->E);
+  if (need > kRouteScratchBytes) {
+    set_error("moe_route_permute_noalloc: T=%d, E=%d need %zu bytes of scratch, above its fixed %zu "
+              "(256 + ceil(T/256)*E*4, rounded to 256, must fit); use moe_route_permute with a workspace",
+              a->T, a->E, need, kRouteScratchBytes);
+    return MGE_ERR_UNSUPPORTED;
+  }
+  void* ws = nullptr;
+  const mge_status st = route_scratch(&ws);
+  if (st != MGE_OK) return st;
+  return route_impl(a, ws, kRouteScratchBytes, stream);
 }
 
 // ------------------------------------------------------------------ quantize

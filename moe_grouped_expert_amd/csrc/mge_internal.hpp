@@ -84,6 +84,10 @@ struct RouteParams {
   int R;
 };
 mge_status launch_route(const RouteParams& p, hipStream_t s);
+// moe_route_permute_noalloc's workspace: a fixed device array of kRouteScratchBytes (one
+// per GPU); *ptr = its device address on the current device
+constexpr size_t kRouteScratchBytes = size_t(1) << 20;
+mge_status route_scratch(void** ptr);
 mge_status launch_router_bwd(int T, int E, int k, const int32_t* idx, const float* prob, const float* dprob,
                              float* dlogits, hipStream_t s);
 

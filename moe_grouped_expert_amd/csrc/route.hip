@@ -19,10 +19,46 @@
 //   router_bwd_kernel      the backward of the top-k softmax: d_logits from d_prob
 #include <math.h>
 
+#include <mutex>
+
 #include "mge_common.hpp"
 #include "mge_internal.hpp"
 
 namespace mge {
+
+// ------------------------------------------------------------ fixed scratch
+// The workspace of moe_route_permute_noalloc (the device error flag and the per-block
+// expert counts), for callers that cannot allocate: a file-scope device array, one copy
+// per GPU the library runs on, held until the process ends.  In host code `scratch` only
+// names the symbol; its device address (different on every GPU) comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only that
+// address is ever handed to a kernel.
+static __device__ __align__(256) uint8_t scratch[kRouteScratchBytes];
+
+mge_status route_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* dev_ptr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return hip_check("hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error("device index %d outside the %d the fixed scratch is kept for", dev, kMaxDevices);
+    return MGE_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lk(mu);
+  if (!dev_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      set_error("hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+      return MGE_ERR_HIP;
+    }
+    dev_ptr[dev] = p;
+  }
+  *ptr = dev_ptr[dev];
+  return MGE_OK;
+}
 
 constexpr int RT_THREADS = 256;
 constexpr int RT_WAVES = RT_THREADS / kWave;

@@ -284,3 +284,22 @@ def test_fwd_saved_bytes():
     o.struct_size = 4
     assert L.mge_fwd_saved_bytes(1, 10, 2, 8, 64, 32, C.byref(o)) == b.MGE_ERR_INVALID_ARG
     assert L.mge_fwd_saved_bytes(1, 10, 2, 8, 64, 32, None) == b.MGE_ERR_INVALID_ARG
+
+
+def test_noalloc_route_host_checks():
+    """moe_route_permute_noalloc rejects a workspace and sizes beyond its fixed scratch on
+    the host, before touching the device."""
+    L = b.lib()
+    a = b.RouteArgs()
+    a.struct_size = C.sizeof(b.RouteArgs)
+    a.T, a.E, a.k, a.H, a.align = 300000, 256, 2, 64, 32
+    for f in ("logits", "topk_idx", "topk_prob", "split_sizes", "group_offsets", "perm_src", "perm_pos", "prob_perm"):
+        setattr(a, f, 0x10000)
+    assert L.moe_route_permute_noalloc(C.byref(a), None) == b.MGE_ERR_UNSUPPORTED
+    assert "scratch" in L.mge_last_error().decode()
+    a.workspace, a.workspace_bytes = 0x10000, 1 << 20
+    assert L.moe_route_permute_noalloc(C.byref(a), None) == b.MGE_ERR_INVALID_ARG
+    a.workspace, a.workspace_bytes = None, 0
+    a.T, a.k = 100, 9
+    assert L.moe_route_permute_noalloc(C.byref(a), None) == b.MGE_ERR_INVALID_ARG
+    assert L.moe_route_permute_noalloc(None, None) == b.MGE_ERR_INVALID_ARG
