@@ -171,27 +171,36 @@ class Step:
                 self.f = m.grouped_mlp_fwd(ge, self.inp["wgu"][e:e + 1], self.inp["wd"][e:e + 1], out=self.f)
         return self.f
 
-    def _fwd_fp8_tensor(self):
+    def _fp8_tensor(self):
         """FP8 with one scale per tensor: the scale of x, of each expert's W_gate_up and
         W_down, and of h (inside the unfused forward) from their amax, every block of a
-        tensor quantized with it."""
+        tensor quantized with it.  Training also quantizes the weights' column forms with
+        their scale, saves [G U] and h's column form, and runs the backward with one scale
+        for dY and one for [dG dU]."""
         m, w, inp, ts = self.m, self.w, self.inp, self.ts
         ts["x"] = m.tensor_scale(inp["x"], out=ts.get("x"))
-        self.g = m.moe_route_permute(inp["logits"], inp["x"], w.k, align=32, prec="mxfp8", out=self.g,
-                                     x_tensor_scale=ts["x"].scale)
+        self.g = m.moe_route_permute(inp["logits"], inp["x"], w.k, align=32, prec="mxfp8", want_col=self.train,
+                                     out=self.g, x_tensor_scale=ts["x"].scale)
         ts["wgu"] = m.tensor_scale(inp["wgu"], per_matrix=True, out=ts.get("wgu"))
         ts["wd"] = m.tensor_scale(inp["wd"], per_matrix=True, out=ts.get("wd"))
-        self.wq = m.mxfp8_quantize(inp["wgu"], "row", out=self.wq, tensor_scale=ts["wgu"].scale)
-        self.dq = m.mxfp8_quantize(inp["wd"], "row", out=self.dq, tensor_scale=ts["wd"].scale)
+        orient = "both" if self.train else "row"
+        self.wq = m.mxfp8_quantize(inp["wgu"], orient, out=self.wq, tensor_scale=ts["wgu"].scale)
+        self.dq = m.mxfp8_quantize(inp["wd"], orient, out=self.dq, tensor_scale=ts["wd"].scale)
         self.f = m.grouped_mlp_fwd_unfused(self.g, self.wq[0], self.dq[0], self.wq[1], self.dq[1], h_per_tensor=True,
-                                           keep_intermediates=self.keep_intermediates, out=self.f)
+                                           keep_intermediates=self.keep_intermediates, train=self.train, out=self.f)
         self.y = m.unpermute_combine(self.f.y_perm, self.g.perm_pos, out=self.y)
+        if self.train:
+            self.b = m.grouped_mlp_bwd(inp["dy"], self.g, self.f, self.wq[2], self.dq[2], self.wq[3], self.dq[3],
+                                       keep_intermediates=self.keep_intermediates, out=self.b, dw_dtype=self.dw_dtype,
+                                       per_tensor=True)
+            self.dx = m.unpermute_combine(self.b.dx_perm, self.g.perm_pos, out=self.dx)
+            self.dl = m.moe_router_bwd(self.g.topk_idx, self.g.topk_prob, self.b.d_prob, w.E, out=self.dl)
 
     def __call__(self):
         m, w, inp = self.m, self.w, self.inp
         mx = self.prec == "mxfp8"
         if self.variant == "fp8_tensor":
-            self._fwd_fp8_tensor()
+            self._fp8_tensor()
             return
         if self.given:
             self.g = m.moe_route_permute(None, inp["x"], 1, E=w.E, align=32, prec=self.prec, want_col=self.train,
@@ -268,7 +277,11 @@ def kernel_work(name, w, R, launches_per_step=1.0):
         # unfused forward: [G U] bf16 read, h bf16 written, p read (valid rows)
         return "byte", 6.0 * M * F + 4.0 * M
     if name == "quant_h_mx":
-        return "byte", M * F * (2.0 + mxb)
+        # unfused forward: the bf16 h read, its row form (and, training, column form) written
+        return "byte", M * F * (2.0 + (2 if w.backward else 1) * mxb)
+    if name == "quant_dgu_mx":
+        # FP8 with one scale per tensor: the bf16 [dG dU] read, both forms written
+        return "byte", M * 2.0 * F * (2.0 + 2 * mxb)
     if name == "combine":
         return "byte", 2.0 * k * T * H + 2.0 * T * H + 4.0 * T * k
     if name == "router_bwd":
@@ -582,10 +595,11 @@ def main():
     dev = torch.device("cuda:0")
     wid, train = WORKLOADS[args.workload]
     w = synth.WORKLOADS[wid]
-    if args.variant == "fp8_tensor" and (wid not in (2, 3)):
-        print("the fp8_tensor variant runs the MXFP8 forward workloads (fwd_mxfp8, fwd_mxfp8_skew)", file=sys.stderr)
+    if args.variant == "fp8_tensor" and (wid not in (2, 3, 4)):
+        print("the fp8_tensor variant runs the MXFP8 workloads (fwd_mxfp8, fwd_mxfp8_skew, train_mxfp8)",
+              file=sys.stderr)
         sys.exit(2)
-    if args.variant != "grouped" and train:
+    if args.variant in ("expert_loop", "unfused") and train:
         print(f"the {args.variant} variant runs forward workloads only", file=sys.stderr)
         sys.exit(2)
     log(f"[bench] workload {w.name}: T={w.T} E={w.E} H={w.H} F={w.F} k={w.k} prec={w.prec} train={train} "

@@ -312,7 +312,7 @@ mge_status mge_fwd_saved_bytes(int32_t prec, int32_t T, int32_t k, int32_t E, in
                                mge_fwd_saved_sizes* out);
 
 /* ------------------------------------------------------------------------------
- * grouped_mlp_fwd_unfused — the same forward (inference only) without the fusion:
+ * grouped_mlp_fwd_unfused — the same forward without the fusion:
  * the structure the pages' fused GroupedLinear -> ScaledSwiGLU -> GroupedLinear
  * replaces ("Accelerating MoE Training ..." "How it works"; the ai4snews report,
  * paragraph on the Sequential fusion; the BioNeMo recipe report, "Quantization
@@ -325,15 +325,19 @@ mge_status mge_fwd_saved_bytes(int32_t prec, int32_t T, int32_t k, int32_t E, in
  *      mxfp8_quantize writes) into h / h_scale, by blocks, or with one scale for all
  *      of h when h_tensor_scale is given;
  *   4. the grouped down GEMM, as in grouped_mlp_fwd.
- * fwd: grouped_mlp_fwd's arguments; saved_gu, h_col and h_col_scale must be NULL.
- * Its workspace fields carry this call's workspace.
+ * fwd: grouped_mlp_fwd's arguments.  Its workspace fields carry this call's workspace.
+ * Training (fwd.saved_gu != NULL; align % 32 == 0): step 1 writes [G U] into saved_gu
+ * (the backward's saved G, U; gu must then be NULL or equal to it), and step 3 also
+ * writes the column form of the bf16 h into fwd.h_col (+ h_col_scale), with h's one
+ * scale when h_tensor_scale is given, by blocks of 32 rows otherwise (BF16: the bf16
+ * transpose); it covers all R rows (padding rows zero).
  * gu: optional [R][2F] bf16 output of step 1 (NULL: in the workspace).
  * h_bf16: MXFP8 only, optional [R][F] bf16 output of step 2 (NULL: in the
  * workspace); in BF16 step 2 writes fwd.h (or the workspace) directly.
  * Rows outside the groups: gu untouched, h_bf16 and h zero (MXFP8 codes 0, scales
  * 0 for an all-zero block), y_perm untouched.
- * Errors: those of grouped_mlp_fwd; MGE_ERR_INVALID_ARG for training buffers or a
- * misaligned gu / h_bf16.
+ * Errors: those of grouped_mlp_fwd; MGE_ERR_INVALID_ARG for a misaligned gu / h_bf16,
+ * or a gu other than saved_gu in training.
  * ---------------------------------------------------------------------------- */
 typedef struct mge_fwd_unfused_args {
   uint32_t struct_size;
@@ -406,6 +410,22 @@ typedef struct mge_bwd_args {
   /* added after the first version of the struct: a struct_size that ends before it
      means 0 */
   int32_t dw_bf16;                       /* 0: dW in fp32; 1: dW in bf16 (no accumulate) */
+  /* Added fields (a struct_size that ends before them means NULL): FP8 with one scale per
+   * tensor, MXFP8 only, the two scale pointers together.  dY and [dG dU] then each take
+   * one E8M0 scale from their amax (the rule of mge_tensor_scale), written to these
+   * bytes, and every block of both their forms is quantized with it (the scale arrays hold
+   * it replicated, so the block-scaled GEMMs run unchanged).  A single scale for [dG dU]
+   * needs its amax before any code is written, so the SwiGLU backward then writes
+   * [dG dU] in bf16 ([R][2F], into dgu_bf16 when given, else the workspace; padding rows
+   * zero), a pass takes its amax and a quantize pass writes both forms.  The weights and
+   * the column forms of h and x must come quantized the same way (mxfp8_quantize and
+   * moe_route_permute with a tensor scale; grouped_mlp_fwd_unfused in training).  The
+   * pages name FP8 beside MXFP8 ("NVIDIA Shows an Efficient MoE Training Path ..."
+   * section "Memory and quantization overhead"; the ai4snews report's paragraph on
+   * FP8/MXFP8) and the recipe trains in either. */
+  uint8_t* dy_tensor_scale;              /* [1] written */
+  uint8_t* dgu_tensor_scale;             /* [1] written */
+  uint16_t* dgu_bf16;                    /* optional [R][2F] bf16 (per-tensor mode only) */
 } mge_bwd_args;
 
 size_t mge_bwd_workspace_bytes(const mge_bwd_args* args);

@@ -73,7 +73,8 @@ class BwdArgs(C.Structure):
                 ("accumulate", i32),
                 ("dy_row", vp), ("dy_row_scale", vp), ("dy_col", vp), ("dy_col_scale", vp),
                 ("dgu_row", vp), ("dgu_row_scale", vp), ("dgu_col", vp), ("dgu_col_scale", vp),
-                ("workspace", vp), ("workspace_bytes", C.c_size_t), ("dw_bf16", i32)]
+                ("workspace", vp), ("workspace_bytes", C.c_size_t), ("dw_bf16", i32),
+                ("dy_tensor_scale", vp), ("dgu_tensor_scale", vp), ("dgu_bf16", vp)]
 
 
 class FwdSavedSizes(C.Structure):
@@ -442,20 +443,24 @@ def grouped_mlp_fwd(rt: RouteOut, w_gate_up, w_down, w_gate_up_scale=None, w_dow
 
 def grouped_mlp_fwd_unfused(rt: RouteOut, w_gate_up, w_down, w_gate_up_scale=None, w_down_scale=None,
                             y_dtype: str = "bf16", keep_intermediates: bool = False, h_per_tensor: bool = False,
-                            out: Optional[FwdOut] = None) -> FwdOut:
-    """The forward without the fusion (inference): [G U] to HBM in bf16, a standalone
-    SwiGLU x prob, (MXFP8) a standalone quantize of h, the grouped down GEMM.  With
-    keep_intermediates, out.gu ([R][2F] bf16) and (MXFP8) out.h_bf16 ([R][F]) are kept;
-    with h_per_tensor, h takes one scale for the whole tensor (out.h_tensor_scale)."""
-    o, a, keep, F, dev = _fwd_args(rt, w_gate_up, w_down, w_gate_up_scale, w_down_scale, y_dtype, False, out)
+                            train: bool = False, out: Optional[FwdOut] = None) -> FwdOut:
+    """The forward without the fusion: [G U] to HBM in bf16, a standalone SwiGLU x prob,
+    (MXFP8) a standalone quantize of h, the grouped down GEMM.  With keep_intermediates,
+    out.gu ([R][2F] bf16) and (MXFP8) out.h_bf16 ([R][F]) are kept; with h_per_tensor, h
+    takes one scale for the whole tensor (out.h_tensor_scale).  train: [G U] is written to
+    out.saved_gu (out.gu is the same tensor) and the column form of h to out.h_col."""
+    o, a, keep, F, dev = _fwd_args(rt, w_gate_up, w_down, w_gate_up_scale, w_down_scale, y_dtype, train, out)
     u = FwdUnfusedArgs()
     u.struct_size = C.sizeof(FwdUnfusedArgs)
     if h_per_tensor and o.h_tensor_scale is None:
         o.h_tensor_scale = torch.empty(1, device=dev, dtype=torch.uint8)
     u.h_tensor_scale = _ptr(o.h_tensor_scale)
-    if keep_intermediates and o.gu is None:
-        o.gu = torch.empty((rt.R, 2 * F), device=dev, dtype=torch.bfloat16)
-        if rt.prec == "mxfp8":
+    if train:
+        o.gu = o.saved_gu
+    if keep_intermediates:
+        if o.gu is None:
+            o.gu = torch.empty((rt.R, 2 * F), device=dev, dtype=torch.bfloat16)
+        if rt.prec == "mxfp8" and o.h_bf16 is None:
             o.h_bf16 = torch.empty((rt.R, F), device=dev, dtype=torch.bfloat16)
     u.gu, u.h_bf16 = _ptr(o.gu), _ptr(o.h_bf16)
     u.fwd = a
@@ -484,13 +489,18 @@ class BwdOut:
     dgu_col: Optional[torch.Tensor] = None
     dgu_col_scale: Optional[torch.Tensor] = None
     workspace: Optional[torch.Tensor] = None
+    dy_tensor_scale: Optional[torch.Tensor] = None    # per-tensor mode: uint8 [1] each
+    dgu_tensor_scale: Optional[torch.Tensor] = None
+    dgu_bf16: Optional[torch.Tensor] = None           # per-tensor mode, kept on request: [R][2F] bf16
 
 
 def grouped_mlp_bwd(dy: torch.Tensor, rt: RouteOut, fw: FwdOut, w_gate_up_k, w_down_k, w_gate_up_k_scale=None,
                     w_down_k_scale=None, accumulate: bool = False, keep_intermediates: bool = False,
-                    out: Optional[BwdOut] = None, dw_dtype: str = "f32") -> BwdOut:
+                    out: Optional[BwdOut] = None, dw_dtype: str = "f32", per_tensor: bool = False) -> BwdOut:
     """Backward of the grouped MLP.  Weights: MXFP8 column forms, or the bf16 masters.
-    dw_dtype: "f32" (default) or "bf16" (the fp32 sums rounded to nearest even; no accumulate)."""
+    dw_dtype: "f32" (default) or "bf16" (the fp32 sums rounded to nearest even; no accumulate).
+    per_tensor (MXFP8): FP8 with one scale per tensor for dY and [dG dU] (out.dy_tensor_scale,
+    out.dgu_tensor_scale; with keep_intermediates also the bf16 [dG dU] in out.dgu_bf16)."""
     if dw_dtype not in ("f32", "bf16"):
         raise ValueError(f"dw_dtype must be 'f32' or 'bf16', not {dw_dtype!r}")
     E, H, R, T, k = rt.E, rt.H, rt.R, rt.T, rt.k
@@ -518,6 +528,11 @@ def grouped_mlp_bwd(dy: torch.Tensor, rt: RouteOut, fw: FwdOut, w_gate_up_k, w_d
                 o.dy_col_scale = torch.empty((H, R // 32), **u8)
                 o.dgu_row_scale = torch.empty((R, 2 * F // 32), **u8)
                 o.dgu_col_scale = torch.empty((2 * F, R // 32), **u8)
+            if per_tensor:
+                o.dgu_bf16 = torch.empty((R, 2 * F), device=dev, dtype=torch.bfloat16)
+        if per_tensor:
+            o.dy_tensor_scale = torch.empty(1, device=dev, dtype=torch.uint8)
+            o.dgu_tensor_scale = torch.empty(1, device=dev, dtype=torch.uint8)
     else:
         o = out
     a = BwdArgs()
@@ -541,6 +556,7 @@ def grouped_mlp_bwd(dy: torch.Tensor, rt: RouteOut, fw: FwdOut, w_gate_up_k, w_d
     a.dy_row, a.dy_row_scale, a.dy_col, a.dy_col_scale = _ptr(o.dy_row), _ptr(o.dy_row_scale), _ptr(o.dy_col), _ptr(o.dy_col_scale)
     a.dgu_row, a.dgu_row_scale = _ptr(o.dgu_row), _ptr(o.dgu_row_scale)
     a.dgu_col, a.dgu_col_scale = _ptr(o.dgu_col), _ptr(o.dgu_col_scale)
+    a.dy_tensor_scale, a.dgu_tensor_scale, a.dgu_bf16 = _ptr(o.dy_tensor_scale), _ptr(o.dgu_tensor_scale), _ptr(o.dgu_bf16)
     if o.workspace is None:
         o.workspace = torch.empty(max(int(lib().mge_bwd_workspace_bytes(C.byref(a))), 256), device=dev,
                                   dtype=torch.uint8)

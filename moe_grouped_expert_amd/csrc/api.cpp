@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <vector>
@@ -390,7 +391,7 @@ static mge_status check_offsets(int R, int H, int F, int elem) {
 static size_t fwd_unfused_extra(const mge_fwd_unfused_args* u, int R) {
   const mge_fwd_args* a = &u->fwd;
   size_t n = 0;
-  if (!u->gu) n += up256(size_t(R) * 2 * a->F * 2);
+  if (!u->gu && !a->saved_gu) n += up256(size_t(R) * 2 * a->F * 2);   // training: [G U] is saved_gu
   if (a->prec == MGE_PREC_MXFP8 && !u->h_bf16) n += up256(size_t(R) * a->F * 2);
   if (u->h_tensor_scale) n += up256(size_t(tensor_scale_parts(int64_t(R) * a->F)) * sizeof(float));
   return n;
@@ -457,7 +458,9 @@ static mge_status fwd_impl(const mge_fwd_args* a, const mge_fwd_unfused_args* u,
     MGE_REQUIRE(a->align % 32 == 0, "training (column form of h) needs align %% 32 == 0 (got %d)", a->align);
   }
   if (u) {
-    MGE_REQUIRE(!train && !a->h_col && !a->h_col_scale, "the unfused forward is inference only (saved_gu, h_col NULL)");
+    MGE_REQUIRE(!train || !u->gu || u->gu == a->saved_gu, "training: gu must be NULL or saved_gu ([G U] is saved)");
+    MGE_REQUIRE(train || (!a->h_col && !a->h_col_scale), "h_col / h_col_scale without saved_gu");
+    MGE_REQUIRE(!train || aligned16(a->saved_gu), "saved_gu must be 16-byte aligned");
     MGE_REQUIRE((!u->gu || aligned16(u->gu)) && (!u->h_bf16 || aligned16(u->h_bf16)), "gu / h_bf16 misaligned");
     MGE_REQUIRE(!u->h_tensor_scale || mx, "h_tensor_scale needs prec MXFP8");
   }
@@ -480,7 +483,7 @@ static mge_status fwd_impl(const mge_fwd_args* a, const mge_fwd_unfused_args* u,
   uint16_t* gu = nullptr;     // unfused: [G U] bf16 and (MXFP8) the bf16 h
   uint16_t* hb = nullptr;
   if (u) {
-    gu = u->gu ? u->gu : static_cast<uint16_t*>(ws.take(size_t(R) * 2 * a->F * 2));
+    gu = train ? a->saved_gu : u->gu ? u->gu : static_cast<uint16_t*>(ws.take(size_t(R) * 2 * a->F * 2));
     hb = !mx ? static_cast<uint16_t*>(h) : u->h_bf16 ? u->h_bf16 : static_cast<uint16_t*>(ws.take(size_t(R) * a->F * 2));
   }
   float* h_amax_part = (u && u->h_tensor_scale)
@@ -528,7 +531,7 @@ static mge_status fwd_impl(const mge_fwd_args* a, const mge_fwd_unfused_args* u,
   g.prob = a->prob_perm;
   if (mx) { g.h_codes = static_cast<uint8_t*>(h); g.h_scales = hs; }
   else g.h_bf16 = static_cast<uint16_t*>(h);
-  if (train) {
+  if (train && !u) {
     g.saved_gu = a->saved_gu;
     if (mx) { g.hc_codes = static_cast<uint8_t*>(a->h_col); g.hc_scales = a->h_col_scale; }
     else g.hc_bf16 = static_cast<uint16_t*>(a->h_col);
@@ -555,12 +558,20 @@ static mge_status fwd_impl(const mge_fwd_args* a, const mge_fwd_unfused_args* u,
       q.in = hb; q.in_batch_stride = int64_t(R) * F; q.in_row_stride = F;
       q.batch = 1; q.R = R; q.C = F; q.Rp = R;
       q.row_codes = static_cast<uint8_t*>(h); q.row_scales = hs;
+      if (train) { q.col_codes = static_cast<uint8_t*>(a->h_col); q.col_scales = a->h_col_scale; }
       if (u->h_tensor_scale) {   // one scale for all of h: its amax first
         st = launch_tensor_scale(hb, 1, int64_t(R) * F, 0, h_amax_part, u->h_tensor_scale, s);
         if (st != MGE_OK) return st;
         q.tensor_scale = u->h_tensor_scale;
       }
       st = launch_quant_tile(q, true, s, "quant_h_mx");
+      if (st != MGE_OK) return st;
+    } else if (train) {   // BF16 training: the transpose of h
+      QuantTileParams q{};
+      q.in = hb; q.in_row_stride = F;
+      q.batch = 1; q.R = R; q.C = F; q.Rp = R;
+      q.col_bf16 = static_cast<uint16_t*>(a->h_col);
+      st = launch_quant_tile(q, false, s, "transpose_h_bf16");
       if (st != MGE_OK) return st;
     }
   }
@@ -600,10 +611,32 @@ mge_status grouped_mlp_fwd_unfused(const mge_fwd_unfused_args* u, void* stream) 
 }
 
 // ------------------------------------------------------------------ backward
+// The added per-tensor fields of mge_bwd_args, NULL when the struct ends before them.
+struct BwdTensorScale {
+  uint8_t* dy = nullptr;
+  uint8_t* dgu = nullptr;
+  uint16_t* dgu_bf16 = nullptr;
+};
+static BwdTensorScale bwd_tensor_scale(const mge_bwd_args* a) {
+  BwdTensorScale t;
+  if (a->struct_size == sizeof(mge_bwd_args)) {
+    t.dy = a->dy_tensor_scale;
+    t.dgu = a->dgu_tensor_scale;
+    t.dgu_bf16 = a->dgu_bf16;
+  }
+  return t;
+}
+
 static size_t bwd_ws(const mge_bwd_args* a, int R) {
   const bool mx = a->prec == MGE_PREC_MXFP8;
   const size_t H = a->H, F = a->F, E = a->E, F2 = 2 * F;
   size_t n = up256(6 * E * sizeof(void*));
+  const BwdTensorScale ts = bwd_tensor_scale(a);
+  if (ts.dy) {   // per-tensor scales: the amax partials, and [dG dU] in bf16 unless given
+    const int parts = std::max(tensor_scale_parts(int64_t(a->T) * a->H), tensor_scale_parts(int64_t(R) * F2));
+    n += up256(size_t(parts) * sizeof(float));
+    if (!ts.dgu_bf16) n += up256(size_t(R) * F2 * 2);
+  }
   n += up256(size_t(R) * dh_swiglu_nparts(int(F)) * sizeof(float));   // d_prob partials per permuted row
   auto mat = [&](size_t rows, size_t cols) {
     return mx ? up256(rows * cols) + up256(rows * (cols / 32)) : up256(rows * cols * 2);
@@ -631,12 +664,19 @@ size_t mge_bwd_workspace_bytes(const mge_bwd_args* a) {
 mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
   g_err[0] = 0;
   MGE_REQUIRE(a != nullptr, "args is NULL");
-  // the first version of the struct ended before dw_bf16
-  MGE_REQUIRE(a->struct_size == sizeof(mge_bwd_args) || a->struct_size == offsetof(mge_bwd_args, dw_bf16),
+  // earlier versions of the struct ended before dw_bf16, and before the per-tensor fields
+  MGE_REQUIRE(a->struct_size == sizeof(mge_bwd_args) || a->struct_size == offsetof(mge_bwd_args, dy_tensor_scale) ||
+                  a->struct_size == offsetof(mge_bwd_args, dw_bf16),
               "struct_size mismatch");
-  const bool dw_bf16 = a->struct_size == sizeof(mge_bwd_args) && a->dw_bf16 != 0;
-  MGE_REQUIRE(a->struct_size < sizeof(mge_bwd_args) || a->dw_bf16 == 0 || a->dw_bf16 == 1,
-              "dw_bf16 must be 0 or 1 (got %d)", a->dw_bf16);
+  const bool has_dw_bf16 = a->struct_size > offsetof(mge_bwd_args, dw_bf16);
+  const bool dw_bf16 = has_dw_bf16 && a->dw_bf16 != 0;
+  MGE_REQUIRE(!has_dw_bf16 || a->dw_bf16 == 0 || a->dw_bf16 == 1, "dw_bf16 must be 0 or 1 (got %d)", a->dw_bf16);
+  const BwdTensorScale tsc = bwd_tensor_scale(a);
+  const bool per_tensor = tsc.dy != nullptr;
+  MGE_REQUIRE((tsc.dy == nullptr) == (tsc.dgu == nullptr), "dy_tensor_scale and dgu_tensor_scale go together");
+  MGE_REQUIRE(!per_tensor || a->prec == MGE_PREC_MXFP8, "per-tensor scales need prec MXFP8");
+  MGE_REQUIRE(!tsc.dgu_bf16 || (per_tensor && aligned16(tsc.dgu_bf16)),
+              "dgu_bf16 only with per-tensor scales, 16-byte aligned");
   MGE_REQUIRE(!(dw_bf16 && a->accumulate), "accumulate needs fp32 dW outputs");
   mge_status st = check_mlp_dims(a->prec, a->E, a->H, a->F, a->T, a->k, a->align);
   if (st != MGE_OK) return st;
@@ -682,6 +722,13 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
     if (mx) { *c = ws.take(rows * cols); *sc = static_cast<uint8_t*>(ws.take(rows * (cols / 32))); }
     else { *c = ws.take(rows * cols * 2); *sc = nullptr; }
   };
+  float* ts_part = nullptr;   // per-tensor mode: amax partials, and [dG dU] in bf16
+  uint16_t* dgu_b = nullptr;
+  if (per_tensor) {
+    const int parts = std::max(tensor_scale_parts(int64_t(a->T) * H), tensor_scale_parts(int64_t(R) * F2));
+    ts_part = static_cast<float*>(ws.take(size_t(parts) * sizeof(float)));
+    dgu_b = tsc.dgu_bf16 ? tsc.dgu_bf16 : static_cast<uint16_t*>(ws.take(size_t(R) * F2 * 2));
+  }
   void *dyr, *dyc, *dgr, *dgc;
   uint8_t *dyrs, *dycs, *dgrs, *dgcs;
   mat(a->dy_row, a->dy_row_scale, R, H, &dyr, &dyrs);
@@ -731,6 +778,11 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
     QuantTileParams q{};
     q.in = a->dy; q.in_row_stride = H; q.gather = a->perm_src; q.src_rows = a->T;
     q.batch = 1; q.R = R; q.C = H; q.Rp = R;
+    if (per_tensor) {   // dy's one scale (its amax over [T][H] is the permuted dY's)
+      st = launch_tensor_scale(a->dy, 1, int64_t(a->T) * H, 0, ts_part, tsc.dy, s);
+      if (st != MGE_OK) return st;
+      q.tensor_scale = tsc.dy;
+    }
     if (mx) { q.row_codes = static_cast<uint8_t*>(dyr); q.row_scales = dyrs; q.col_codes = static_cast<uint8_t*>(dyc); q.col_scales = dycs; }
     else { q.row_bf16 = static_cast<uint16_t*>(dyr); q.col_bf16 = static_cast<uint16_t*>(dyc); }
     st = launch_quant_tile(q, mx, s);
@@ -790,7 +842,10 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
     g.out_dtype = MGE_DTYPE_F32;
     g.prob = a->prob_perm;
     g.gu_in = a->saved_gu;
-    if (mx) {
+    if (per_tensor) {   // [dG dU] in bf16, row form only; quantized below with its one scale
+      g.out_dtype = MGE_DTYPE_BF16;
+      g.dgu_row_bf16 = dgu_b;
+    } else if (mx) {
       g.dgu_row_codes = static_cast<uint8_t*>(dgr); g.dgu_row_scales = dgrs;
       g.dgu_col_codes = static_cast<uint8_t*>(dgc); g.dgu_col_scales = dgcs;
     } else {
@@ -800,6 +855,21 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
     g.tiles_upper = gemm_tiles_upper(g, rows_bound);
     g.role = GEMM_DH;
     st = launch_gemm(g, a->prec, s);
+    if (st != MGE_OK) return st;
+  }
+  if (per_tensor) {
+    // padding rows to zero, the one scale of [dG dU], then both forms with it
+    st = launch_zero_pad_rows(R, F2, a->perm_src, dgu_b, s);
+    if (st != MGE_OK) return st;
+    st = launch_tensor_scale(dgu_b, 1, int64_t(R) * F2, 0, ts_part, tsc.dgu, s);
+    if (st != MGE_OK) return st;
+    QuantTileParams q{};
+    q.in = dgu_b; q.in_row_stride = F2;
+    q.batch = 1; q.R = R; q.C = F2; q.Rp = R;
+    q.row_codes = static_cast<uint8_t*>(dgr); q.row_scales = dgrs;
+    q.col_codes = static_cast<uint8_t*>(dgc); q.col_scales = dgcs;
+    q.tensor_scale = tsc.dgu;
+    st = launch_quant_tile(q, true, s, "quant_dgu_mx");
     if (st != MGE_OK) return st;
   }
   if (mx) {

@@ -28,8 +28,9 @@ mge_status launch_gemm(const GemmParams& p, int prec, hipStream_t s) {
     // addressed with 32-bit offsets
     if (p.gu_in == nullptr || p.N != p.F || int64_t(p.F) * 4 * 2 * G_BM >= (int64_t(1) << 31) || p.F % 32 != 0 ||
         p.Rp % 32 != 0 || p.prob == nullptr || p.dprob_part == nullptr || p.dprob_nparts != dh_swiglu_nparts(p.F) ||
-        (prec == MGE_PREC_MXFP8 ? (!p.dgu_row_codes || !p.dgu_row_scales || !p.dgu_col_codes || !p.dgu_col_scales)
-                                : (!p.dgu_row_bf16 || !p.dgu_col_bf16))) {
+        (prec == MGE_PREC_MXFP8 && p.out_dtype != MGE_DTYPE_BF16
+             ? (!p.dgu_row_codes || !p.dgu_row_scales || !p.dgu_col_codes || !p.dgu_col_scales)
+             : (!p.dgu_row_bf16 || (prec != MGE_PREC_MXFP8 && !p.dgu_col_bf16)))) {
       set_error("dh GEMM with the SwiGLU-backward epilogue: inconsistent parameters (F %d, N %d)", p.F, p.N);
       return MGE_ERR_INVALID_ARG;
     }

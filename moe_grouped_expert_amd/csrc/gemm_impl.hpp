@@ -815,8 +815,13 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
       auto rsrc = [](const void* base, uint32_t bytes) {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kRsrcFlags);
       };
+      // outputs in MXFP8 (codes + block scales) or in bf16: the bf16 path of BF16 operands,
+      // and of MX operands with OUT_BF16 (FP8 with one scale per tensor, whose scale needs
+      // all of [dG dU] first); the bf16 column form only when asked for
+      constexpr bool MXO = MX && OUT != OUT_BF16;
+      const bool col_out = MXO || p.dgu_col_bf16 != nullptr;
       __amdgpu_buffer_rsrc_t rR, rRs;
-      if constexpr (MX) {
+      if constexpr (MXO) {
         rR = rsrc(p.dgu_row_codes + grow0 * F2, uint32_t(vr) * F2);
         rRs = rsrc(p.dgu_row_scales + grow0 * (F2 / 32), uint32_t(vr) * (F2 / 32));
       } else {
@@ -876,7 +881,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
               constexpr int h = decltype(hc)::value;
               const float* v = h == 0 ? dg : du;
               const int cb = h * F + fb0;                    // first [dG dU] column of the block
-              if constexpr (MX) {
+              if constexpr (MXO) {
                 float inv[16];
                 const uint32_t sc = row_block_inv16(v, l32, inv);   // sc: row l32 / 2
                 const bool lo2 = (l32 & 2) == 0;
@@ -914,6 +919,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
                 for (int r = 0; r < 16; r += 2)
                   __builtin_amdgcn_raw_buffer_store_b32(pair2(v[r], v[r + 1]), rR,
                                                         ((lrow(r) + (odd ? 1 : 0)) * F2 + cpair) * 2, 0, 0);
+                if (!col_out) return;                       // wave-uniform
                 const int64_t cbase = int64_t(cb + l32) * p.Rp + grow0 + rb + 16 * hi;
                 uint32_t c[8];
 #pragma unroll

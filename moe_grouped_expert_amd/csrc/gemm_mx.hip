@@ -12,6 +12,7 @@ MGE_GEMM_KERNEL(gemm_gateup_swiglu_mx, EPI_SWIGLU, RAGGED_M, OUT_NONE)
 MGE_GEMM_KERNEL(gemm_down_mx, EPI_STORE, RAGGED_M, OUT_BF16)
 MGE_GEMM_KERNEL(gemm_down_f32_mx, EPI_STORE, RAGGED_M, OUT_F32)
 MGE_GEMM_KERNEL(gemm_dh_swiglu_mx, EPI_SWIGLU_BWD, RAGGED_M, OUT_NONE)
+MGE_GEMM_KERNEL(gemm_dh_swiglu_bf16out_mx, EPI_SWIGLU_BWD, RAGGED_M, OUT_BF16)   // [dG dU] in bf16
 MGE_GEMM_KERNEL(gemm_dx_mx, EPI_STORE, RAGGED_M, OUT_BF16)
 MGE_GEMM_KERNEL(gemm_gateup_store_mx, EPI_STORE, RAGGED_M, OUT_BF16)
 MGE_GEMM_KERNEL(gemm_dw_down_mx, EPI_STORE, RAGGED_K, OUT_F32)
@@ -25,7 +26,7 @@ MGE_GEMM_KERNEL(gemm_dw_gateup_bf16out_mx, EPI_STORE, RAGGED_K, OUT_BF16)
 
 // Kernel of a role; the output dtype and the accumulate flag were checked by
 // launch_gemm (DOWN, DW: bf16 or f32, accumulate only f32; DH: the SwiGLU-backward
-// epilogue's outputs; DX, GATEUP_STORE: bf16).
+// epilogue's outputs, MXFP8 or (out_dtype BF16) bf16; DX, GATEUP_STORE: bf16).
 mge_status launch_gemm_mx(const GemmParams& p, hipStream_t s) {
   const bool f32 = p.out_dtype == MGE_DTYPE_F32;
   switch (p.role) {
@@ -33,7 +34,10 @@ mge_status launch_gemm_mx(const GemmParams& p, hipStream_t s) {
     case GEMM_DOWN:
       return f32 ? launch_gemm_kernel(gemm_down_f32_mx, "gemm_down_mx", p, s)
                  : launch_gemm_kernel(gemm_down_mx, "gemm_down_mx", p, s);
-    case GEMM_DH: return launch_gemm_kernel(gemm_dh_swiglu_mx, "gemm_dh_swiglu_mx", p, s);
+    case GEMM_DH:
+      // bf16 [dG dU] (FP8 with one scale per tensor quantizes it afterwards, with its amax)
+      return p.out_dtype == MGE_DTYPE_BF16 ? launch_gemm_kernel(gemm_dh_swiglu_bf16out_mx, "gemm_dh_swiglu_bf16out_mx", p, s)
+                                           : launch_gemm_kernel(gemm_dh_swiglu_mx, "gemm_dh_swiglu_mx", p, s);
     case GEMM_DX: return launch_gemm_kernel(gemm_dx_mx, "gemm_dx_mx", p, s);
     case GEMM_GATEUP_STORE: return launch_gemm_kernel(gemm_gateup_store_mx, "gemm_gateup_store_mx", p, s);
     case GEMM_DW_DOWN:

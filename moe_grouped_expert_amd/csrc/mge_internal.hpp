@@ -97,6 +97,8 @@ mge_status launch_combine(int T, int k, int H, int in_dtype, int out_dtype, cons
 // h = p * silu(G) * U from the bf16 [G U] rows (stride 2F) into bf16 h [R][F] (the
 // unfused forward's standalone SwiGLU x prob; rows with p = 0 get 0)
 mge_status launch_swiglu_prob(int R, int F, const uint16_t* gu, const float* prob, uint16_t* h, hipStream_t s);
+// rows r of a bf16 [R][C] matrix with perm_src[r] < 0 (padding) set to zero (C % 8 == 0)
+mge_status launch_zero_pad_rows(int R, int C, const int32_t* perm_src, uint16_t* m, hipStream_t s);
 // d_prob partials per row written by the dh GEMM's SwiGLU-backward epilogue (one per
 // 128-column span of F: two per 256-column tile)
 inline int dh_swiglu_nparts(int F) { return 2 * ((F + 255) / 256); }

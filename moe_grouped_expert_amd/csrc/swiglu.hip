@@ -56,4 +56,25 @@ mge_status launch_swiglu_prob(int R, int F, const uint16_t* gu, const float* pro
   return hip_check("swiglu_prob_kernel");
 }
 
+// Padding rows of a permuted bf16 [R][C] matrix (perm_src[r] < 0, the rows between and
+// after the expert groups that no GEMM tile writes) set to zero, so that a pass over all
+// R rows (a tensor's amax, the column form's 32-row blocks) reads zeros there.  A
+// workgroup per row, grid-stride; rows of the groups are left untouched (one 4-byte read).
+__global__ __launch_bounds__(SW_THREADS) void zero_pad_rows_kernel(int R, int C, const int32_t* __restrict__ perm_src,
+                                                                   uint16_t* __restrict__ m) {
+  for (int r = blockIdx.x; r < R; r += gridDim.x) {
+    if (perm_src[r] >= 0) continue;   // uniform over the workgroup
+    uint4* row = reinterpret_cast<uint4*>(m + int64_t(r) * C);
+    for (int c = threadIdx.x; c < C / 8; c += SW_THREADS) row[c] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+mge_status launch_zero_pad_rows(int R, int C, const int32_t* perm_src, uint16_t* m, hipStream_t s) {
+  if (R <= 0 || C <= 0) return MGE_OK;
+  const int blocks = R < 4096 ? R : 4096;
+  ProfScope prof(s, "zero_pad_rows");
+  hipLaunchKernelGGL(zero_pad_rows_kernel, dim3(unsigned(blocks)), dim3(SW_THREADS), 0, s, R, C, perm_src, m);
+  return hip_check("zero_pad_rows_kernel");
+}
+
 }  // namespace mge

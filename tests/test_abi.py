@@ -238,15 +238,22 @@ def test_fwd_unfused_rejects_and_workspace():
     u = _unfused_args()
     u.fwd.struct_size -= 8
     assert L.grouped_mlp_fwd_unfused(C.byref(u), None) == b.MGE_ERR_INVALID_ARG
-    # inference only: training buffers are rejected before any launch (fake device addresses)
+    # training: [G U] is written to saved_gu (no workspace for it), and a gu other than
+    # saved_gu, or h_col without saved_gu, is rejected before any launch (fake device addresses)
     ptrs = (C.c_void_p * 4)(*[(i + 1) << 20 for i in range(4)])
     dev = {n: (i + 8) << 20 for i, n in enumerate(("split_sizes", "group_offsets", "prob_perm", "x_perm",
                                                      "x_perm_scale", "y_perm"))}
     u = _unfused_args(w_gate_up=C.cast(ptrs, C.c_void_p), w_down=C.cast(ptrs, C.c_void_p),
                       w_gate_up_scale=C.cast(ptrs, C.c_void_p), w_down_scale=C.cast(ptrs, C.c_void_p),
                       saved_gu=1 << 30, h_col=1 << 31, h_col_scale=1 << 32, **dev)
+    assert L.mge_fwd_unfused_workspace_bytes(C.byref(u)) == L.mge_fwd_workspace_bytes(C.byref(u.fwd)) + R * 128 * 2
+    u.gu = 1 << 20
     assert L.grouped_mlp_fwd_unfused(C.byref(u), None) == b.MGE_ERR_INVALID_ARG
-    assert "inference only" in L.mge_last_error().decode()
+    assert "saved_gu" in L.mge_last_error().decode()
+    u.gu = None
+    u.fwd.saved_gu = None
+    assert L.grouped_mlp_fwd_unfused(C.byref(u), None) == b.MGE_ERR_INVALID_ARG
+    assert "h_col" in L.mge_last_error().decode()
 
 
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):
@@ -303,3 +310,43 @@ def test_noalloc_route_host_checks():
     a.T, a.k = 100, 9
     assert L.moe_route_permute_noalloc(C.byref(a), None) == b.MGE_ERR_INVALID_ARG
     assert L.moe_route_permute_noalloc(None, None) == b.MGE_ERR_INVALID_ARG
+
+
+def test_bwd_per_tensor_fields_checked():
+    """grouped_mlp_bwd's added per-tensor fields: the two scale pointers go together, need
+    MXFP8, and dgu_bf16 needs them; a struct that ends before the fields is accepted."""
+    L = b.lib()
+    ptrs = (C.c_void_p * 4)(*[(i + 1) << 20 for i in range(4)])
+
+    def args(**kw):
+        a = b.BwdArgs()
+        a.struct_size = C.sizeof(b.BwdArgs)
+        a.prec, a.E, a.H, a.F, a.T, a.k, a.align = 1, 4, 64, 64, 8, 2, 32
+        for n in ("dy", "split_sizes", "group_offsets", "perm_src", "perm_pos", "prob_perm", "saved_gu", "h_col",
+                  "h_col_scale", "x_col", "x_col_scale", "dx_perm", "d_prob"):
+            setattr(a, n, 1 << 24)
+        for n in ("w_gate_up", "w_down", "w_gate_up_scale", "w_down_scale", "dw_gate_up", "dw_down"):
+            setattr(a, n, C.cast(ptrs, C.c_void_p))
+        for k_, v in kw.items():
+            setattr(a, k_, v)
+        return a
+
+    a = args(dy_tensor_scale=1 << 25)
+    assert L.grouped_mlp_bwd(C.byref(a), None) == b.MGE_ERR_INVALID_ARG
+    assert "together" in L.mge_last_error().decode()
+    a = args(dy_tensor_scale=1 << 25, dgu_tensor_scale=1 << 26, prec=0)
+    assert L.grouped_mlp_bwd(C.byref(a), None) == b.MGE_ERR_INVALID_ARG
+    a = args(dgu_bf16=1 << 27)
+    assert L.grouped_mlp_bwd(C.byref(a), None) == b.MGE_ERR_INVALID_ARG
+    # per-tensor mode needs more workspace ([dG dU] in bf16, the amax partials) unless dgu_bf16 is given
+    plain = L.mge_bwd_workspace_bytes(C.byref(args()))
+    pt = L.mge_bwd_workspace_bytes(C.byref(args(dy_tensor_scale=1 << 25, dgu_tensor_scale=1 << 26)))
+    R = b.perm_rows(8, 2, 4, 32)
+    assert pt >= plain + R * 2 * 64 * 2
+    given = L.mge_bwd_workspace_bytes(C.byref(args(dy_tensor_scale=1 << 25, dgu_tensor_scale=1 << 26,
+                                                   dgu_bf16=1 << 27)))
+    assert plain < given < pt
+    # the struct before the per-tensor fields: accepted, goes on to the workspace check
+    a = args(dy_tensor_scale=1 << 25)
+    a.struct_size = b.BwdArgs.dy_tensor_scale.offset
+    assert L.grouped_mlp_bwd(C.byref(a), None) == b.MGE_ERR_WORKSPACE

@@ -244,3 +244,98 @@ def test_quantize_segments_of_an_empty_tensor():
     torch.cuda.synchronize()
     assert rc.shape == (m.perm_rows(0, 1, 2, 32), 64)
     assert not rc.any() and not rs.any() and not cc.any() and not cs.any()
+
+
+@pytest.mark.parametrize("w,empty", [(synth.custom(1403, T=500, E=4, H=128, F=192, k=2, prec="mxfp8"), ()),
+                                     (synth.custom(1404, T=300, E=5, H=96, F=128, k=2, prec="mxfp8"), (0, 3))],
+                         ids=["plain", "empty_first_mid"])
+def test_fp8_tensor_training_staged(w, empty):
+    """The FP8 training step with one scale per tensor (bench.Step's fp8_tensor variant,
+    fwd + bwd) stage by stage: every quantized operand's scale and codes bit-exact against
+    the oracle's quantize_tensor of the values the GPU quantized (x, dy, the weights in
+    both forms; h and [dG dU] from the GPU's own bf16 values, both forms); every product
+    within rel_F 2e-3 of the oracle fed the GPU's codes ([G U], y_perm, [dG dU] from the
+    GPU's dY codes and saved G, U, d_prob, dW_down, dX, dW_gate_up); empty experts get
+    zero weight gradients."""
+    import bench
+    import moe_grouped_expert_amd as m
+    from tests.gpu_helpers import Inputs, layout_from_gpu, say
+
+    logits = synth.logits(w)
+    for e in empty:
+        logits[:, e] = np.float32(-1e30)
+    inp = Inputs(w, logits)
+    st = bench.Step(m, w, dict(logits=inp.g_logits, x=inp.g_x, wgu=inp.g_wgu, wd=inp.g_wd, dy=inp.g_dy), train=True,
+                    variant="fp8_tensor")
+    st.keep_intermediates = True
+    st()
+    torch.cuda.synchronize()
+    g, f, b = st.g, st.f, st.b
+    lay = layout_from_gpu(g, w.E, 32)
+    src = _npy(g.perm_src)
+    valid = src >= 0
+    F, E = w.F, w.E
+    lst = lambda t: [_npy(u) for u in t]   # noqa: E731
+    # x: one scale, row and column forms
+    qx, sx = mx.quantize_tensor(inp.x.astype(np.float64))
+    np.testing.assert_array_equal(_npy(g.x_perm)[valid], qx[src[valid]])
+    np.testing.assert_array_equal(_npy(g.x_col)[:, valid], qx[src[valid]].T)
+    assert not _npy(g.x_col)[:, ~valid].any() and np.all(_npy(g.x_col_scale) == sx)
+    # weights: one scale per matrix, both forms
+    for e in range(E):
+        for wt, qt in ((inp.wgu, st.wq), (inp.wd, st.dq)):
+            q, s = mx.quantize_tensor(wt[e].astype(np.float64))
+            np.testing.assert_array_equal(_npy(qt[0][e]), q)
+            np.testing.assert_array_equal(_npy(qt[2][e])[:, :q.shape[0]], q.T)
+            assert np.all(_npy(qt[1][e]) == s) and np.all(_npy(qt[3][e]) == s)
+    errs = {}
+    # forward: [G U] (the saved G, U), h in bf16, h's one scale in both forms, y_perm, y
+    GU = mlp.mx_grouped_nt(_npy(g.x_perm), _npy(g.x_perm_scale), lst(st.wq[0]), lst(st.wq[1]), lay)
+    gu = _vals(f.saved_gu)
+    assert f.gu is f.saved_gu
+    errs["gu"] = rel_f(gu[valid], GU[valid])
+    hb = _vals(f.h_bf16)
+    errs["h_bf16"] = rel_f(hb[valid], (lay.prob_perm[:, None] * mlp.silu(gu[:, :F]) * gu[:, F:])[valid])
+    assert not hb[~valid].any()
+    qh, sh = mx.quantize_tensor(hb)
+    assert int(f.h_tensor_scale.item()) == int(sh)
+    np.testing.assert_array_equal(_npy(f.h), qh)
+    np.testing.assert_array_equal(_npy(f.h_col), qh.T)
+    assert np.all(_npy(f.h_scale) == sh) and np.all(_npy(f.h_col_scale) == sh)
+    Y = mlp.mx_grouped_nt(qh, _npy(f.h_scale), lst(st.dq[0]), lst(st.dq[1]), lay)
+    errs["y_perm"] = rel_f(_vals(f.y_perm)[valid], Y[valid])
+    errs["y"] = rel_f(_vals(st.y), lay.combine(np.where(valid[:, None], _vals(f.y_perm), 0.0)))
+    # backward: dy's one scale (row and column forms of the permuted dY)
+    qd, sd = mx.quantize_tensor(inp.dy.astype(np.float64))
+    assert int(b.dy_tensor_scale.item()) == int(sd)
+    np.testing.assert_array_equal(_npy(b.dy_row)[valid], qd[src[valid]])
+    assert not _npy(b.dy_row)[~valid].any() and np.all(_npy(b.dy_row_scale) == sd)
+    np.testing.assert_array_equal(_npy(b.dy_col)[:, valid], qd[src[valid]].T)
+    assert np.all(_npy(b.dy_col_scale) == sd)
+    # the SwiGLU backward in bf16 from the GPU's dY codes, W_down column codes and saved G, U
+    dG, dU, dp_row = mlp.mx_dh_stage(_npy(b.dy_row), _npy(b.dy_row_scale), lst(st.dq[2]), lst(st.dq[3]),
+                                     gu[:, :F], gu[:, F:], lay)
+    dgb = _vals(b.dgu_bf16)
+    errs["dgu_bf16"] = rel_f(dgb[valid], np.concatenate([dG, dU], axis=1)[valid])
+    assert not dgb[~valid].any()
+    errs["d_prob"] = rel_f(_vals(b.d_prob), lay.to_slots(dp_row))
+    # [dG dU]'s one scale from the GPU's bf16 values, both forms
+    qg, sg = mx.quantize_tensor(dgb)
+    assert int(b.dgu_tensor_scale.item()) == int(sg)
+    np.testing.assert_array_equal(_npy(b.dgu_row), qg)
+    np.testing.assert_array_equal(_npy(b.dgu_col), qg.T)
+    assert np.all(_npy(b.dgu_row_scale) == sg) and np.all(_npy(b.dgu_col_scale) == sg)
+    # the GEMMs on the GPU's codes
+    dWd = mlp.mx_dw_stage(_npy(b.dy_col), _npy(b.dy_col_scale), _npy(f.h_col), _npy(f.h_col_scale), lay)
+    errs["dw_down"] = rel_f(np.stack([_vals(t) for t in b.dw_down]), dWd)
+    dX = mlp.mx_dx_stage(_npy(b.dgu_row), _npy(b.dgu_row_scale), lst(st.wq[2]), lst(st.wq[3]), lay)
+    errs["dx_perm"] = rel_f(_vals(b.dx_perm)[valid], dX[valid])
+    dWgu = mlp.mx_dw_stage(_npy(b.dgu_col), _npy(b.dgu_col_scale), _npy(g.x_col), _npy(g.x_col_scale), lay)
+    errs["dw_gate_up"] = rel_f(np.stack([_vals(t) for t in b.dw_gate_up]), dWgu)
+    errs["dx"] = rel_f(_vals(st.dx), lay.combine(np.where(valid[:, None], _vals(b.dx_perm), 0.0)))
+    for e in empty:
+        assert not torch.any(b.dw_gate_up[e]) and not torch.any(b.dw_down[e])
+    say("[gpu] fp8 per-tensor training", w.name, {k: f"{v:.2e}" for k, v in errs.items()},
+        "scales x/h/dy/dgu", int(sx), int(sh), int(sd), int(sg))
+    for key, v in errs.items():
+        assert v <= 2e-3, (key, v)
