@@ -81,6 +81,12 @@ static size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
 // 2.75 -> 3.07 GB, and bands of 16 on dW_gate_up 3.03 -> 4.56 GB, for time changes within
 // run-to-run noise (so neither is used).
 constexpr int kMergeShortBand = 1;
+// M-tiles per raster band of the weight-gradient GEMMs (the others take 8).  Same-job A/B on
+// the Mixtral-shaped training step, each time over the dX GEMM's of the same run (two runs
+// of bands 1, 2, 4, 8, 16): dW_gate_up (M = 2F, its dGU operand the large one) is fastest
+// with 16 (1.26 -> 1.25 and 1.24; 1, 2, 4: 1.28-1.34), dW_down with 4 (0.62 -> 0.61; 16: 0.69).
+constexpr int kBandDwDown = 4;
+constexpr int kBandDwGateUp = 16;
 
 // Bump allocator over the caller's workspace.
 struct Carve {
@@ -891,6 +897,7 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
     g.out_dtype = dw_bf16 ? MGE_DTYPE_BF16 : MGE_DTYPE_F32; g.Ct = reinterpret_cast<void* const*>(tab + 4 * E); g.ldc = F;
     g.accumulate = a->accumulate;
     g.tiles_upper = gemm_tiles_upper(g, rows_bound);
+    g.band_m = kBandDwDown;
     g.role = GEMM_DW_DOWN;
     st = launch_gemm(g, a->prec, s);
     if (st != MGE_OK) return st;
@@ -921,6 +928,7 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
     g.out_dtype = dw_bf16 ? MGE_DTYPE_BF16 : MGE_DTYPE_F32; g.Ct = reinterpret_cast<void* const*>(tab + 5 * E); g.ldc = H;
     g.accumulate = a->accumulate;
     g.tiles_upper = gemm_tiles_upper(g, rows_bound);
+    g.band_m = kBandDwGateUp;
     g.role = GEMM_DW_GATEUP;
     st = launch_gemm(g, a->prec, s);
   }

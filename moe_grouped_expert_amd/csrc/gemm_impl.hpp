@@ -65,6 +65,9 @@ constexpr int G_WNB = 4;   // 32-col MFMA blocks per wave (N)
 constexpr int G_BM = G_WAVES_M * G_WMB * 32;
 constexpr int G_BN = G_WAVES_N * G_WNB * 32;
 constexpr int G_BKB = 128;                    // K bytes per slice: one whole 128-byte line per operand row
+#ifndef G_EPI_GROUP
+#define G_EPI_GROUP 1   // SwiGLU epilogues: 32 x 32 blocks the scheduler may interleave
+#endif
 #ifndef G_BAR_AT32
 #define G_BAR_AT32 8   // a slice's stage is released after this many 32nds of its MFMAs
 #endif
@@ -278,7 +281,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
     // fastest, so that the 32 consecutive tiles an XCD runs (an 8 x 4 block) share a few A
     // and B tiles in that XCD's L2.  With group_m set (ragged M only), an expert's last band
     // takes a remainder under 4 M-tiles (9 M-tiles walked as one band, not as 8 + a lone 1)
-    constexpr int GM = G_GROUP_M;
+    const int GM = uniform(p.band_m > 0 ? p.band_m : G_GROUP_M);
     int nband = (mtn + GM - 1) / GM;
     if (MODE == RAGGED_M && p.group_m > 0 && nband > 1 && mtn - (nband - 1) * GM < GM / 2) --nband;
     nband = uniform(nband);
@@ -776,7 +779,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
               dst[1] = make_uint4(b0.a, b1.a, b0.b, b1.b);
             }
           }
-          __builtin_amdgcn_sched_barrier(0);   // one block at a time (register peak)
+          if constexpr (G_EPI_GROUP == 1 || (j % G_EPI_GROUP) == G_EPI_GROUP - 1) __builtin_amdgcn_sched_barrier(0);   // blocks in groups (register peak)
         });
       });
     } else if constexpr (EPI == EPI_SWIGLU_BWD) {
@@ -934,7 +937,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
                 dst[1] = make_uint4(b0.a, b1.a, b0.b, b1.b);
               }
             });
-            __builtin_amdgcn_sched_barrier(0);   // one block at a time (register peak)
+            if constexpr (G_EPI_GROUP == 1 || (ni % G_EPI_GROUP) == G_EPI_GROUP - 1) __builtin_amdgcn_sched_barrier(0);   // blocks in groups (register peak)
           });
           // d_prob partial of each row over the wave's 128 columns: lanes 2k, 2k + 1 hold row k
           const float ps = row_block_sum16(dps, l32);

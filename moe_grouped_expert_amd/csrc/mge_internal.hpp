@@ -168,6 +168,7 @@ struct GemmParams {
   float* dprob_part; int dprob_nparts;   // [R][nparts]: one sum per (row, 128-column span of F)
   int tiles_upper;                         // host bound on the number of tiles (grid sizing)
   int group_m;                             // 1: a short last raster band joins the one before
+  int band_m;                              // M-tiles per raster band (0: the default, 8)
 };
 
 // Upper bound of tiles for a RAGGED_M GEMM (host-side, from T*k and E).

@@ -339,3 +339,98 @@ def test_fp8_tensor_training_staged(w, empty):
         "scales x/h/dy/dgu", int(sx), int(sh), int(sd), int(sg))
     for key, v in errs.items():
         assert v <= 2e-3, (key, v)
+
+
+def test_mixtral_fp8_tensor_training_sampled():
+    """The Mixtral-shaped training step (8192 tokens) with one scale per tensor, as bench.py
+    times its fp8_tensor variant: every scale against the oracle's rule on the tensor the
+    GPU quantized (x, dy and the weights from the inputs; h and [dG dU] from the GPU's bf16
+    values), codes bit-exact on sampled rows, and on sampled rows of two experts [G U], h,
+    y_perm, [dG dU] (from the GPU's dY codes and saved G, U), d_prob and dX (from the GPU's
+    [dG dU] codes) within rel_F 2e-3; dW entries over an expert's token span from the
+    GPU's column codes."""
+    import bench
+    import moe_grouped_expert_amd as m
+    from tests.gpu_helpers import layout_from_gpu, say
+
+    w = synth.WORKLOADS[4]
+    dev = torch.device("cuda:0")
+    say("[gpu] full-size fp8 per-tensor training: inputs")
+    inp = bench.make_inputs(w, dev)
+    st = bench.Step(m, w, inp, train=True, variant="fp8_tensor")
+    st.keep_intermediates = True
+    st()
+    torch.cuda.synchronize()
+    g, f, b = st.g, st.f, st.b
+    lay = layout_from_gpu(g, w.E, 32)
+    F, H, E = w.F, w.H, w.E
+    F2 = 2 * F
+    sc = lambda t: int(mx.block_scale_exponent(float(t.abs().max())) + 127)   # noqa: E731
+    assert int(st.ts["x"].scale.item()) == sc(inp["x"])
+    assert int(b.dy_tensor_scale.item()) == sc(inp["dy"])
+    for e in range(E):
+        assert int(st.ts["wgu"].scale[e]) == sc(inp["wgu"][e]) and int(st.ts["wd"].scale[e]) == sc(inp["wd"][e])
+    hs, ds = int(f.h_tensor_scale.item()), int(b.dgu_tensor_scale.item())
+    assert hs == sc(f.h_bf16) and ds == sc(b.dgu_bf16)
+    src = _npy(g.perm_src)
+    prob = _npy(g.prob_perm).astype(np.float64)
+    pp_all = _npy(g.perm_pos)
+    slot = {int(pp_all[t, i]): (t, i) for t in range(w.T) for i in range(w.k)}
+    dpg = _npy(b.d_prob)
+    rng = np.random.default_rng(7272)
+    acc = {key: [[], []] for key in ("gu", "h", "y_perm", "dgu", "d_prob", "dx_perm", "dw_down", "dw_gate_up")}
+
+    def add(key, got, ref):
+        acc[key][0].append(np.asarray(got, np.float64).ravel())
+        acc[key][1].append(np.asarray(ref, np.float64).ravel())
+
+    def take(t, idx, dim=0):
+        return t.index_select(dim, torch.as_tensor(idx, device=dev, dtype=torch.long))
+
+    sx, sdy = int(st.ts["x"].scale.item()), int(b.dy_tensor_scale.item())
+    for e in (0, E - 1):
+        r = lay.rows(e)
+        rows = np.array(sorted({r.start, r.stop - 1} | set(int(v) for v in rng.integers(r.start, r.stop, 4))))
+        toks = src[rows]
+        # codes of x, dy and h, dGU on the sampled rows: the tensor's one scale
+        np.testing.assert_array_equal(_npy(take(g.x_perm, rows)), mx.e4m3_encode(_vals(take(inp["x"], toks)) * 2.0 ** -(sx - 127)))
+        np.testing.assert_array_equal(_npy(take(b.dy_row, rows)), mx.e4m3_encode(_vals(take(inp["dy"], toks)) * 2.0 ** -(sdy - 127)))
+        hb = _vals(take(f.h_bf16, rows))
+        np.testing.assert_array_equal(_npy(take(f.h, rows)), mx.e4m3_encode(hb * 2.0 ** -(hs - 127)))
+        gb = _vals(take(b.dgu_bf16, rows))
+        np.testing.assert_array_equal(_npy(take(b.dgu_row, rows)), mx.e4m3_encode(gb * 2.0 ** -(ds - 127)))
+        # forward products on the GPU's codes
+        xd = mx.dequantize_rows(_npy(take(g.x_perm, rows)), _npy(take(g.x_perm_scale, rows)))
+        GU = xd @ mx.dequantize_rows(_npy(st.wq[0][e]), _npy(st.wq[1][e])).T
+        gu = _vals(take(f.saved_gu, rows))
+        add("gu", gu, GU)
+        add("h", hb, prob[rows][:, None] * mlp.silu(gu[:, :F]) * gu[:, F:])
+        Y = mx.dequantize_tensor(_npy(take(f.h, rows)), np.uint8(hs)) @ mx.dequantize_rows(_npy(st.dq[0][e]), _npy(st.dq[1][e])).T
+        add("y_perm", _vals(take(f.y_perm, rows)), Y)
+        # backward: dh from the GPU's dY codes and W_down column codes, SwiGLU backward on the saved G, U
+        dh = mx.dequantize_tensor(_npy(take(b.dy_row, rows)), np.uint8(sdy)) @ mx.dequantize_rows(_npy(st.dq[2][e]), _npy(st.dq[3][e])).T
+        p = prob[rows][:, None]
+        G, U = gu[:, :F], gu[:, F:]
+        add("dgu", gb, np.concatenate([dh * p * U * mlp.dsilu(G), dh * p * mlp.silu(G)], axis=1))
+        add("d_prob", [float(dpg[slot[int(rr)]]) for rr in rows], np.sum(dh * mlp.silu(G) * U, axis=1))
+        hc = np.unique(np.concatenate([[0, H - 1], rng.integers(0, H, 30)]))
+        wgc = mx.dequantize_rows(_npy(take(st.wq[2][e], hc)), _npy(take(st.wq[3][e], hc)))
+        add("dx_perm", _vals(take(take(b.dx_perm, rows), hc, 1)),
+            mx.dequantize_tensor(_npy(take(b.dgu_row, rows)), np.uint8(ds)) @ wgc.T)
+        # weight gradients over the expert's token span from the GPU's column codes
+        span = lay.kspan(e)
+        sb = slice(span.start // 32, span.stop // 32)
+        hh = np.unique(rng.integers(0, H, 8))
+        ff = np.unique(rng.integers(0, F, 8))
+        dyc = mx.dequantize_rows(_npy(take(b.dy_col, hh)[:, span]), _npy(take(b.dy_col_scale, hh)[:, sb]))
+        hcd = mx.dequantize_rows(_npy(take(f.h_col, ff)[:, span]), _npy(take(f.h_col_scale, ff)[:, sb]))
+        add("dw_down", _npy(take(take(b.dw_down[e], hh), ff, 1)), dyc @ hcd.T)
+        jj = np.unique(np.concatenate([rng.integers(0, F, 4), F + rng.integers(0, F, 4)]))
+        gcd = mx.dequantize_rows(_npy(take(b.dgu_col, jj)[:, span]), _npy(take(b.dgu_col_scale, jj)[:, sb]))
+        xcd = mx.dequantize_rows(_npy(take(g.x_col, hh)[:, span]), _npy(take(g.x_col_scale, hh)[:, sb]))
+        add("dw_gate_up", _npy(take(take(b.dw_gate_up[e], jj), hh, 1)), gcd @ xcd.T)
+    res = {k: rel_f(np.concatenate(a), np.concatenate(r_)) for k, (a, r_) in acc.items()}
+    say("[gpu] full-size fp8 per-tensor training", {k: f"{v:.2e}" for k, v in res.items()},
+        "scales x/h/dy/dgu", sx, hs, sdy, ds)
+    for key, v in res.items():
+        assert v <= 2e-3, (key, v)
