@@ -65,6 +65,9 @@ constexpr int G_WNB = 4;   // 32-col MFMA blocks per wave (N)
 constexpr int G_BM = G_WAVES_M * G_WMB * 32;
 constexpr int G_BN = G_WAVES_N * G_WNB * 32;
 constexpr int G_BKB = 128;                    // K bytes per slice: one whole 128-byte line per operand row
+#ifndef G_TAIL_SPLIT
+#define G_TAIL_SPLIT 1   // plain-store ragged-M GEMMs: the grid's last round as quarter-width items
+#endif
 #ifndef G_EPI_GROUP
 #define G_EPI_GROUP 1   // SwiGLU epilogues: 32 x 32 blocks the scheduler may interleave
 #endif
@@ -201,6 +204,7 @@ struct Tile {
   // operand buffer resources: A starts at the tile's first row and B at its first weight
   // row (SwiGLU: the gate half; the up half is F rows further); the record bounds end at
   // the last valid row, so the hardware range check zeroes rows past the group / N / F
+  int nb;                     // first output column (and B row) of the work item
   const uint8_t* A;
   const uint8_t* B;
   uint32_t arec, brec;
@@ -216,8 +220,17 @@ constexpr int G_SCALE_STAGE = 4096;
 constexpr int G_SCALE_BASE = G_STAGES * G_STAGE_BYTES;
 constexpr int G_DYN_LDS = G_SCALE_BASE + G_STAGES * G_SCALE_STAGE;
 
-template <bool MX, int EPI, int MODE, int OUT>
+// QT = 1: the quarter-width tail kernel of a plain-store ragged-M GEMM.  The tiles past the
+// last whole round of the main launch's grid would run alone on a fraction of the chip;
+// this launch runs each of them as four 256 x 64 work items instead (the main launch leaves
+// them out; both take the same decision from the same tile table).  Every output element is
+// still accumulated by one wave over K in the same order: the results are bit-identical.
+template <bool MX, int EPI, int MODE, int OUT, int QT = 0>
 __device__ __forceinline__ void gemm_body(const GemmParams& p) {
+  static_assert(QT == 0 || (EPI == EPI_STORE && MODE == RAGGED_M), "the quarter-width tail is for plain-store ragged-M GEMMs");
+  constexpr int BW = QT ? G_BN / 4 : G_BN;        // output columns (B rows) of a work item
+  constexpr int WNB = BW / (32 * G_WAVES_N);       // 32-column MFMA blocks per wave
+  constexpr int NOPS = 8 + BW / 32;                // operand DMA instructions per wave and slice (A: 8)
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   // LDS byte address of the dynamic shared block (the low half of its generic address)
   const uint32_t lds_base = uniform(int(uint32_t(reinterpret_cast<uintptr_t>(smem))));
@@ -263,12 +276,35 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
   const int nwg = gridDim.x;
   int vid = blockIdx.x;
   if ((nwg & 7) == 0) vid = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+  // Work items of this launch.  With tail_split the tiles past the main launch's last whole
+  // round go to the tail launch as quarter-width items, when there are at most two rounds of
+  // those (each item streams the whole A slice, so it takes well over a quarter of a tile's
+  // time).  Both launches decide from the same numbers: the tile count and the main grid.
+  int items = total, t_full = total;
+  {
+    const int g = p.grid_main > 0 ? p.grid_main : nwg;
+    const int full = (total / g) * g, tail = total - full;
+    const bool split = p.tail_split != 0 && full > 0 && tail > 0 && tail * 4 <= 2 * g;
+    if constexpr (QT) {
+      t_full = full;
+      items = split ? tail * 4 : 0;
+    } else {
+      items = split ? full : total;
+    }
+    items = uniform(items);
+    t_full = uniform(t_full);
+  }
 
   // every tile quantity is wave-uniform: kept in scalar registers
-  auto decode = [&](int tile) {
+  auto decode = [&](int item) {
     Tile t{};
-    t.valid = tile < total;
+    t.valid = item < items;
     if (!t.valid) return t;
+    int tile = item, quarter = 0;
+    if constexpr (QT) {
+      tile = t_full + item / 4;
+      quarter = item % 4;
+    }
     int lo = 0, hi_ = p.E - 1;
     while (lo < hi_) {
       int mid = (lo + hi_ + 1) >> 1;
@@ -312,11 +348,13 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
     }
     t.arec = uint32_t(rows_left(t.m_valid - t.m0, G_BM)) * uint32_t(p.lda);
     if constexpr (EPI == EPI_SWIGLU) {
-      t.B = bmat + int64_t(t.nt) * (G_BN / 2) * p.ldb;
-      t.brec = uint32_t(rows_left(p.F - t.nt * (G_BN / 2), G_BN / 2)) * uint32_t(p.ldb);
+      t.nb = t.nt * (G_BN / 2);
+      t.B = bmat + int64_t(t.nb) * p.ldb;
+      t.brec = uint32_t(rows_left(p.F - t.nb, G_BN / 2)) * uint32_t(p.ldb);
     } else {
-      t.B = bmat + int64_t(t.nt) * G_BN * p.ldb;
-      t.brec = uint32_t(rows_left(p.N - t.nt * G_BN, G_BN)) * uint32_t(p.ldb);
+      t.nb = t.nt * G_BN + quarter * BW;
+      t.B = bmat + int64_t(t.nb) * p.ldb;
+      t.brec = uint32_t(rows_left(p.N - t.nb, BW)) * uint32_t(p.ldb);
     }
     t.nkt = (t.khi - t.kbase + G_BKB - 1) / G_BKB;
     if constexpr (MX) {
@@ -345,7 +383,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
   // and odd instructions; instruction i adds i*8 rows.
   const int lchunk0 = (lane & 7) ^ (lane >> 4);
   const int arow0 = wave * 64 + (lane >> 3);
-  const int brow0 = (EPI == EPI_SWIGLU ? (wave & 1) * 64 : wave * 64) + (lane >> 3);
+  const int brow0 = (EPI == EPI_SWIGLU ? (wave & 1) * 64 : wave * (BW / 4)) + (lane >> 3);
   const uint32_t a_lane[2] = {uint32_t(arow0) * uint32_t(p.lda) + lchunk0 * 16,
                               uint32_t(arow0) * uint32_t(p.lda) + (lchunk0 ^ 4) * 16};
   const uint32_t b_lane[2] = {uint32_t(brow0) * uint32_t(p.ldb) + lchunk0 * 16,
@@ -356,7 +394,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
   // the last slice every lane is out of range and loads zeros.  prep_slice computes the
   // slice's resources and offsets; dma_operand(i) issues operand instruction i (0..7 A,
   // 8..15 B) so that the K loop can spread them between its MFMAs.
-  constexpr int DMA_PER_SLICE = 16 + (MX ? 1 : 0);   // VMEM operations of one slice
+  constexpr int DMA_PER_SLICE = NOPS + (MX ? 1 : 0);   // VMEM operations of one slice
   struct SliceDma {
     i32x4 rA, rB, rS;
     uint32_t kadd, out0, out1, la, lb, ls, so;
@@ -378,8 +416,10 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
     c.out0 = ((uint32_t(kb0 - t.klo) | uint32_t(t.khi - 1 - kb0)) >> 31) << 31;
     c.out1 = ((uint32_t(kb1 - t.klo) | uint32_t(t.khi - 1 - kb1)) >> 31) << 31;
     c.kadd = uint32_t(kslice);
+    // A: 64 rows per wave (8 instructions of 8 rows); B: BW / 4 rows per wave, stored at
+    // B row wave * BW / 4 of the stage (SwiGLU: waves 0, 1 the gate rows, 2, 3 the up rows)
     c.la = lds_base + stage * G_STAGE_BYTES + wave * 8 * 1024;
-    c.lb = c.la + G_BM * G_BKB;
+    c.lb = lds_base + stage * G_STAGE_BYTES + G_BM * G_BKB + wave * (BW / 4) * G_BKB;
     if constexpr (MX) {
       // wave w brings 128 rows of scale dwords (lanes 0..31, 16 B = 4 rows each):
       // A rows (w&1)*128.. for w < 2, B rows for w >= 2; the dwords of the slice's
@@ -396,14 +436,17 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
         bytes = p.asp_bytes;
       } else {
         int r0;
-        if constexpr (EPI == EPI_SWIGLU) r0 = half == 0 ? t.nt * (G_BN / 2) : p.F + t.nt * (G_BN / 2);
-        else r0 = t.nt * G_BN + half * 128;
+        if constexpr (EPI == EPI_SWIGLU) r0 = half == 0 ? t.nb : p.F + t.nb;
+        else r0 = t.nb + half * 128;
         dw = t.sb_rows + j * p.bsp_ld + r0;
         base = p.Bsp;
         bytes = p.bsp_bytes;
       }
       c.rS = make_rsrc_n(base, bytes);
-      c.so = (slice_ok && lane < 32) ? uint32_t(dw * 4) + lane * 16 : kInvalid;
+      // lanes of 4 rows each: 32 (128 rows), fewer for the B rows of a narrow work item
+      constexpr int kBLanes0 = BW >= 128 ? 32 : BW / 4, kBLanes1 = BW >= 256 ? 32 : (BW > 128 ? (BW - 128) / 4 : 0);
+      const int nlanes = wave < 2 ? 32 : (half == 0 ? kBLanes0 : kBLanes1);
+      c.so = (slice_ok && lane < nlanes) ? uint32_t(dw * 4) + lane * 16 : kInvalid;
       c.ls = lds_base + G_SCALE_BASE + stage * G_SCALE_STAGE + wave * 1024;
     }
     return c;
@@ -419,18 +462,18 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
   auto issue_slice = [&](const Tile& t, int kt, int stage) {
     const SliceDma c = prep_slice(t, kt, stage);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) dma_operand(c, i);
+    for (int i = 0; i < NOPS; ++i) dma_operand(c, i);
     dma_scale(c);
   };
 
-  int brow_tile[G_WNB];
+  int brow_tile[WNB];
 #pragma unroll
-  for (int ni = 0; ni < G_WNB; ++ni) {
+  for (int ni = 0; ni < WNB; ++ni) {
     if constexpr (EPI == EPI_SWIGLU) {
       constexpr int hb = G_WNB / 2;
       brow_tile[ni] = ni < hb ? (wn * hb + ni) * 32 : G_BN / 2 + (wn * hb + ni - hb) * 32;
     } else {
-      brow_tile[ni] = (wn * G_WNB + ni) * 32;
+      brow_tile[ni] = (wn * WNB + ni) * 32;
     }
   }
 
@@ -454,7 +497,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
       }
     }
 #pragma unroll
-    for (int ni = 0; ni < G_WNB; ++ni) {
+    for (int ni = 0; ni < WNB; ++ni) {
       const int row = brow_tile[ni] + l32;
       if constexpr (MX) {
         const int c = 4 * s + hi;
@@ -471,10 +514,10 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
   // next-tile slices issued before the epilogue (see there)
   constexpr int G_PREFETCH = (OUT == OUT_F32_ACC || EPI == EPI_SWIGLU_BWD) ? 0 : 1;
   int cur_issued = 0;   // slices of `cur` (from 0) already on their way into their stages
-  for (int tile = vid; tile < total; tile += nwg) {
+  for (int item = vid; item < items; item += nwg) {
     rederive_lane();
-    const Tile nxt = decode(tile + nwg);
-    const int e = cur.e, nt = cur.nt, off = cur.off, m_valid = cur.m_valid, m0 = cur.m0, nkt = cur.nkt;
+    const Tile nxt = decode(item + nwg);
+    const int e = cur.e, nt = cur.nt, nb = cur.nb, off = cur.off, m_valid = cur.m_valid, m0 = cur.m0, nkt = cur.nkt;
     // SwiGLU: the probability of tile row tid, loaded now so that its latency hides
     // behind the K loop (it is staged in LDS for the epilogue)
     float my_prob = 0.f;
@@ -482,11 +525,11 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
       if (m0 + tid < m_valid) my_prob = p.prob[off + m0 + tid];
     }
 
-    f32x16 acc[G_WMB][G_WNB];
+    f32x16 acc[G_WMB][WNB];
 #pragma unroll
     for (int mi = 0; mi < G_WMB; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < G_WNB; ++ni)
+      for (int ni = 0; ni < WNB; ++ni)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
@@ -498,15 +541,15 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
     // CU's texture-address path moves about 54 bytes per clock, so a slice's DMAs need
     // well over half of the slice's MFMA time; packed closer they fill its queue and
     // stall the issuing wave (measured on MI355X).
-    constexpr int NMFMA = NSTEP * G_WMB * G_WNB;
+    constexpr int NMFMA = NSTEP * G_WMB * WNB;
     constexpr int BAR_AT = NMFMA * G_BAR_AT32 / 32;
-    auto mfma_slice = [&](frag_t (*af)[G_WMB], frag_t (*bfr)[G_WNB], const uint32_t* sa, const uint32_t* sb,
+    auto mfma_slice = [&](frag_t (*af)[G_WMB], frag_t (*bfr)[WNB], const uint32_t* sa, const uint32_t* sb,
                           const SliceDma& nx) {
       static_for<0, NMFMA>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        constexpr int s = i / (G_WMB * G_WNB);
-        constexpr int mi = (i % (G_WMB * G_WNB)) / G_WNB;
-        constexpr int ni = i % G_WNB;
+        constexpr int s = i / (G_WMB * WNB);
+        constexpr int mi = (i % (G_WMB * WNB)) / WNB;
+        constexpr int ni = i % WNB;
         if constexpr (i == BAR_AT) {
           __builtin_amdgcn_sched_barrier(0);
           lds_barrier();   // every wave is done with this stage
@@ -523,7 +566,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
         }
         if constexpr (i >= BAR_AT) {
           constexpr int n = NMFMA - BAR_AT;
-          constexpr int d0 = 16 * (i - BAR_AT) / n, d1 = 16 * (i - BAR_AT + 1) / n;
+          constexpr int d0 = NOPS * (i - BAR_AT) / n, d1 = NOPS * (i - BAR_AT + 1) / n;
           if constexpr (d1 > d0) {
             __builtin_amdgcn_sched_barrier(0);
             static_for<d0, d1>([&](auto dc) { dma_operand(nx, decltype(dc)::value); });
@@ -556,7 +599,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
       const int stage = kt & (G_STAGES - 1);
       const uint8_t* sA = smem + stage * G_STAGE_BYTES;
       const uint8_t* sB = sA + G_BM * G_BKB;
-      uint32_t sa[G_WMB], sb[G_WNB];
+      uint32_t sa[G_WMB], sb[WNB];
       if constexpr (MX) {
         const uint8_t* sS = smem + G_SCALE_BASE + stage * G_SCALE_STAGE;
 #pragma unroll
@@ -565,12 +608,12 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
           sa[mi] = *reinterpret_cast<const uint32_t*>(sS + (r >> 7) * 1024 + (r & 127) * 4);
         }
 #pragma unroll
-        for (int ni = 0; ni < G_WNB; ++ni) {
+        for (int ni = 0; ni < WNB; ++ni) {
           const int r = brow_tile[ni] + l32;
           sb[ni] = *reinterpret_cast<const uint32_t*>(sS + 2048 + (r >> 7) * 1024 + (r & 127) * 4);
         }
       }
-      frag_t af[NSTEP][G_WMB], bfr[NSTEP][G_WNB];
+      frag_t af[NSTEP][G_WMB], bfr[NSTEP][WNB];
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s) read_frags(sA, sB, s, af[s], bfr[s]);
       const SliceDma nx = prep_slice(cur, kt + G_STAGES, stage);
@@ -617,9 +660,9 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
       static_for<0, G_WMB>([&](auto mic) {
         constexpr int mi = decltype(mic)::value;
         if (wrow0 + mi * 32 >= m_valid) return;
-        static_for<0, G_WNB>([&](auto nic) {
+        static_for<0, WNB>([&](auto nic) {
           constexpr int ni = decltype(nic)::value;
-          const int col = nt * G_BN + brow_tile[ni] + l32;
+          const int col = nb + brow_tile[ni] + l32;
           const uint32_t lo = col < p.N ? uint32_t(col) * ESZ + uint32_t(4 * hi) * rowb : kInvalid;
           constexpr int pol = MODE == RAGGED_K ? kNonTemporal : 0;   // gradients: written once
           if constexpr (OUT == OUT_F32_ACC) {
@@ -981,6 +1024,36 @@ static mge_status launch_gemm_kernel(Kern kern, const char* name, const GemmPara
   if (grid <= 0) return MGE_OK;
   ProfScope prof(s, name);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(G_THREADS), G_DYN_LDS, s, p);
+  return hip_check(name);
+}
+
+// A plain-store ragged-M GEMM as two launches: the main kernel over the whole rounds of
+// its grid, then the tail kernel over the rest as quarter-width work items (each kernel
+// finds its share on the device: the tile count depends on the group sizes there).
+template <typename KernMain, typename KernTail>
+static mge_status launch_gemm_split(KernMain kmain, KernTail ktail, const char* name, const GemmParams& p0,
+                                    hipStream_t s) {
+  hipFuncSetAttribute(reinterpret_cast<const void*>(kmain), hipFuncAttributeMaxDynamicSharedMemorySize, G_DYN_LDS);
+  hipFuncSetAttribute(reinterpret_cast<const void*>(ktail), hipFuncAttributeMaxDynamicSharedMemorySize, G_DYN_LDS);
+  const int cus = device_cus();
+  int grid = cus;
+  if (p0.tiles_upper < grid) grid = p0.tiles_upper;
+  if (grid <= 0) return MGE_OK;
+  GemmParams p = p0;
+  p.tail_split = G_TAIL_SPLIT;
+  p.grid_main = grid;
+  {
+    ProfScope prof(s, name);
+    hipLaunchKernelGGL(kmain, dim3(grid), dim3(G_THREADS), G_DYN_LDS, s, p);
+  }
+  mge_status st = hip_check(name);
+  if (st != MGE_OK) return st;
+  // at most two rounds of quarter-width items (the kernel exits at once when there is no tail)
+  const int tail_grid = (p0.tiles_upper < grid ? p0.tiles_upper : grid);
+  {
+    ProfScope prof(s, name);
+    hipLaunchKernelGGL(ktail, dim3(tail_grid), dim3(G_THREADS), G_DYN_LDS, s, p);
+  }
   return hip_check(name);
 }
 

@@ -22,6 +22,16 @@ MGE_GEMM_KERNEL(gemm_dw_gateup_acc_mx, EPI_STORE, RAGGED_K, OUT_F32_ACC)
 MGE_GEMM_KERNEL(gemm_dw_down_bf16out_mx, EPI_STORE, RAGGED_K, OUT_BF16)
 MGE_GEMM_KERNEL(gemm_dw_gateup_bf16out_mx, EPI_STORE, RAGGED_K, OUT_BF16)
 
+// the quarter-width tail launches of the plain-store ragged-M GEMMs (see gemm_body)
+#define MGE_GEMM_TAIL_KERNEL(name, OUT) \
+  __global__ __launch_bounds__(G_THREADS, 1) void name(GemmParams p) { gemm_body<true, EPI_STORE, RAGGED_M, OUT, 1>(p); }
+
+MGE_GEMM_TAIL_KERNEL(gemm_down_tail_mx, OUT_BF16)
+MGE_GEMM_TAIL_KERNEL(gemm_down_f32_tail_mx, OUT_F32)
+MGE_GEMM_TAIL_KERNEL(gemm_dx_tail_mx, OUT_BF16)
+MGE_GEMM_TAIL_KERNEL(gemm_gateup_store_tail_mx, OUT_BF16)
+
+#undef MGE_GEMM_TAIL_KERNEL
 #undef MGE_GEMM_KERNEL
 
 // Kernel of a role; the output dtype and the accumulate flag were checked by
@@ -32,14 +42,15 @@ mge_status launch_gemm_mx(const GemmParams& p, hipStream_t s) {
   switch (p.role) {
     case GEMM_GATEUP: return launch_gemm_kernel(gemm_gateup_swiglu_mx, "gemm_gateup_swiglu_mx", p, s);
     case GEMM_DOWN:
-      return f32 ? launch_gemm_kernel(gemm_down_f32_mx, "gemm_down_mx", p, s)
-                 : launch_gemm_kernel(gemm_down_mx, "gemm_down_mx", p, s);
+      return f32 ? launch_gemm_split(gemm_down_f32_mx, gemm_down_f32_tail_mx, "gemm_down_mx", p, s)
+                 : launch_gemm_split(gemm_down_mx, gemm_down_tail_mx, "gemm_down_mx", p, s);
     case GEMM_DH:
       // bf16 [dG dU] (FP8 with one scale per tensor quantizes it afterwards, with its amax)
       return p.out_dtype == MGE_DTYPE_BF16 ? launch_gemm_kernel(gemm_dh_swiglu_bf16out_mx, "gemm_dh_swiglu_bf16out_mx", p, s)
                                            : launch_gemm_kernel(gemm_dh_swiglu_mx, "gemm_dh_swiglu_mx", p, s);
-    case GEMM_DX: return launch_gemm_kernel(gemm_dx_mx, "gemm_dx_mx", p, s);
-    case GEMM_GATEUP_STORE: return launch_gemm_kernel(gemm_gateup_store_mx, "gemm_gateup_store_mx", p, s);
+    case GEMM_DX: return launch_gemm_split(gemm_dx_mx, gemm_dx_tail_mx, "gemm_dx_mx", p, s);
+    case GEMM_GATEUP_STORE:
+      return launch_gemm_split(gemm_gateup_store_mx, gemm_gateup_store_tail_mx, "gemm_gateup_store_mx", p, s);
     case GEMM_DW_DOWN:
       if (!f32) return launch_gemm_kernel(gemm_dw_down_bf16out_mx, "gemm_dw_down_mx", p, s);
       return p.accumulate ? launch_gemm_kernel(gemm_dw_down_acc_mx, "gemm_dw_down_mx", p, s)

@@ -169,6 +169,8 @@ struct GemmParams {
   int tiles_upper;                         // host bound on the number of tiles (grid sizing)
   int group_m;                             // 1: a short last raster band joins the one before
   int band_m;                              // M-tiles per raster band (0: the default, 8)
+  int tail_split;                          // plain-store ragged M: tiles past the last whole round go to the tail launch
+  int grid_main;                           // workgroups of the main launch (set by the launcher; both launches read it)
 };
 
 // Upper bound of tiles for a RAGGED_M GEMM (host-side, from T*k and E).
