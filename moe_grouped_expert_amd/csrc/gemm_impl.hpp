@@ -769,14 +769,17 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
             // rows); a 4 x 4 byte transpose inside each quad of lanes (16-bit halves with
             // the lane 2 apart, then bytes with the lane 1 apart) leaves row (l32 % 4) of
             // the quad's 4 columns in the lane: one dword store per lane and 4 rows
-            const bool lo2 = (l32 & 2) == 0;
+            // the 16-bit halves (one v_perm_b32, bytes 0-3 of v, 4-7 of x): lanes with
+            // l32 & 2 == 0 keep their low half under the partner's low half, the others take
+            // the partner's high half under their own high half
+            const uint32_t sel16 = (l32 & 2) == 0 ? 0x05040100u : 0x03020706u;
             const uint32_t sel = odd ? 0x03070105u : 0x06020400u;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               uint32_t v = e4m3x4(h[4 * g] * inv[4 * g], h[4 * g + 1] * inv[4 * g + 1], h[4 * g + 2] * inv[4 * g + 2],
                                   h[4 * g + 3] * inv[4 * g + 3]);
               const uint32_t x = uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x4E, 0xf, 0xf, false));
-              v = lo2 ? ((v & 0xffffu) | (x << 16)) : ((x >> 16) | (v & 0xffff0000u));
+              v = __builtin_amdgcn_perm(x, v, sel16);   // low half: own | partner's; high: partner's | own
               const uint32_t y = uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0xB1, 0xf, 0xf, false));
               v = __builtin_amdgcn_perm(y, v, sel);
               __builtin_amdgcn_raw_buffer_store_b32(v, rH, lrow(4 * g + (l32 & 3)) * F + fb0 + (l32 & ~3), 0, 0);
@@ -930,14 +933,14 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
               if constexpr (MXO) {
                 float inv[16];
                 const uint32_t sc = row_block_inv16(v, l32, inv);   // sc: row l32 / 2
-                const bool lo2 = (l32 & 2) == 0;
+                const uint32_t sel16 = (l32 & 2) == 0 ? 0x05040100u : 0x03020706u;   // halves, as in the forward
                 const uint32_t sel = odd ? 0x03070105u : 0x06020400u;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                   uint32_t w = e4m3x4(v[4 * g] * inv[4 * g], v[4 * g + 1] * inv[4 * g + 1], v[4 * g + 2] * inv[4 * g + 2],
                                       v[4 * g + 3] * inv[4 * g + 3]);
                   const uint32_t x = uint32_t(__builtin_amdgcn_mov_dpp(int(w), 0x4E, 0xf, 0xf, false));
-                  w = lo2 ? ((w & 0xffffu) | (x << 16)) : ((x >> 16) | (w & 0xffff0000u));
+                  w = __builtin_amdgcn_perm(x, w, sel16);
                   const uint32_t y = uint32_t(__builtin_amdgcn_mov_dpp(int(w), 0xB1, 0xf, 0xf, false));
                   w = __builtin_amdgcn_perm(y, w, sel);
                   __builtin_amdgcn_raw_buffer_store_b32(w, rR, lrow(4 * g + (l32 & 3)) * F2 + cb + (l32 & ~3), 0, 0);
