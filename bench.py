@@ -322,9 +322,9 @@ def summarize_kernels(records, steps, w, R, prec):
 
 # ------------------------------------------------------------------------------ traffic (rocprofv3 counters)
 
-# Sources that build a kernel family: the GEMM kernels are made from these files and from
-# the grouped-GEMM part of mge_internal.hpp (GemmParams); every other kernel is checked
-# against all sources.
+# Sources that build a kernel family: the GEMM kernels are made from these files, from
+# the grouped-GEMM part of mge_internal.hpp (GemmParams) and from the launch constants of
+# api.cpp (raster bands); every other kernel is checked against all sources.
 GEMM_SOURCES = ("gemm_impl.hpp", "gemm_mx.hip", "gemm_bf16.hip", "gemm_host.cpp", "mge_common.hpp")
 GEMM_PARAMS_MARK = "// ------------------------------------------------------------ grouped GEMM"
 
@@ -342,6 +342,9 @@ def kernel_source_digest(family="all"):
         if family == "gemm":
             if f == "mge_internal.hpp":
                 text = text[text.index(GEMM_PARAMS_MARK.encode()):]
+            elif f == "api.cpp":
+                # the launch settings the host passes the GEMMs (raster bands and the like)
+                text = b"\n".join(l for l in text.split(b"\n") if l.startswith(b"constexpr int k"))
             elif f not in GEMM_SOURCES:
                 continue
         h.update(f.encode() + b"\0" + text)

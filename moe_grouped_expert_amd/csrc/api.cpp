@@ -83,10 +83,11 @@ static size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
 constexpr int kMergeShortBand = 1;
 // M-tiles per raster band of the weight-gradient GEMMs (the others take 8).  Same-job A/B on
 // the Mixtral-shaped training step, each time over the dX GEMM's of the same run (two runs
-// of bands 1, 2, 4, 8, 16): dW_gate_up (M = 2F, its dGU operand the large one) is fastest
-// with 16 (1.26 -> 1.25 and 1.24; 1, 2, 4: 1.28-1.34), dW_down with 4 (0.62 -> 0.61; 16: 0.69).
+// of bands 1, 2, 4, 8, 16): dW_down is fastest with 4 (0.62 -> 0.61; 16: 0.69); dW_gate_up
+// with 16 by about 1% (1.26 -> 1.25 and 1.24; 1, 2, 4: 1.28-1.34) while its counter traffic
+// grows from 3.0 to 4.6 GB per launch, so it keeps 8.
 constexpr int kBandDwDown = 4;
-constexpr int kBandDwGateUp = 16;
+constexpr int kBandDwGateUp = 8;
 
 // Bump allocator over the caller's workspace.
 struct Carve {

@@ -166,7 +166,10 @@ int main() {
     if (mge_fwd_unfused_workspace_bytes(&u) <= need) ++g_fail;           // [G U] and h in the workspace
     EXPECT(grouped_mlp_fwd_unfused(&u, nullptr), MGE_ERR_WORKSPACE);
     u.fwd.saved_gu = static_cast<uint16_t*>(A16); u.fwd.h_col = A16; u.fwd.h_col_scale = static_cast<uint8_t*>(A16);
-    EXPECT(grouped_mlp_fwd_unfused(&u, nullptr), MGE_ERR_INVALID_ARG);   // training buffers rejected
+    EXPECT(grouped_mlp_fwd_unfused(&u, nullptr), MGE_ERR_WORKSPACE);     // training: [G U] is saved_gu
+    { mge_fwd_unfused_args v = u; v.gu = static_cast<uint16_t*>(A16) + 8; EXPECT(grouped_mlp_fwd_unfused(&v, nullptr), MGE_ERR_INVALID_ARG); }
+    { mge_fwd_unfused_args v = u; v.fwd.h_col = nullptr; EXPECT(grouped_mlp_fwd_unfused(&v, nullptr), MGE_ERR_INVALID_ARG); }
+    { mge_fwd_unfused_args v = u; v.fwd.saved_gu = nullptr; EXPECT(grouped_mlp_fwd_unfused(&v, nullptr), MGE_ERR_INVALID_ARG); }
     EXPECT(grouped_mlp_fwd_unfused(nullptr, nullptr), MGE_ERR_INVALID_ARG);
   }
 
