@@ -7,7 +7,11 @@ groups have exactly the sizes under test:
     32-row scale block and the 256-row M-tile, several tiles with a ragged tail;
   * H = F = 32, the smallest sizes the layout allows (one scale block along K);
   * one expert receiving every token at E = 8 (seven empty experts, k = 2);
-  * a single token (T = 1).
+  * a single token (T = 1);
+  * the grid's last round as quarter-width work items: 2 experts of 2176 rows each (every
+    token on both), H = 4096, so the dX and down GEMMs have 2 x 9 x 16 = 288 tiles on 256
+    CUs, and their last 32 tiles (the second expert's last two M-tiles, one of them half
+    full) run as 128 items of 256 x 64 in the tail launch.
 BF16: y, dx, dW_gate_up, dW_down and d_prob end to end against fp64 on the same bf16
 inputs (rel_F 1e-2).  MXFP8: staged, each stage against the oracle fed the GPU's own
 quantized operands (rel_F 2e-3; x, dy, weights and the permutation bit-exact; h and dGU
@@ -62,6 +66,11 @@ def _case(name):
         E, k, H, F, T = 8, 2, 64, 96, 1
         logits = rng.standard_normal((T, E)).astype(np.float32)
         idx = prob = None
+    elif name == "tail_split":
+        E, k, H, F, T = 2, 2, 4096, 256, 2176
+        idx = np.tile(np.array([[0, 1]], np.int32), (T, 1))
+        idx[::2] = idx[::2, ::-1]                                    # either expert in slot 0
+        prob = rng.uniform(0.2, 0.8, (T, k)).astype(np.float32)
     else:
         raise ValueError(name)
     T = idx.shape[0] if idx is not None else logits.shape[0]
@@ -95,13 +104,19 @@ def _run(m, prec, x, wgu, wd, dy, E, k, idx, prob, logits):
     return o
 
 
-CASES = ["sizes", "h32_f32", "one_expert_all_tokens", "one_token"]
+CASES = ["sizes", "h32_f32", "one_expert_all_tokens", "one_token", "tail_split"]
+
+
+def _needs_256_cus(name):
+    if name == "tail_split" and torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the tile arithmetic of this case assumes 256 compute units")
 
 
 @pytest.mark.parametrize("prec", ["bf16", "mxfp8"])
 @pytest.mark.parametrize("name", CASES)
 def test_edge_fwd_bwd(m, name, prec):
     from tests.gpu_helpers import f64, npy, say
+    _needs_256_cus(name)
     x, wgu, wd, dy, E, k, idx, prob, logits = _case(name)
     say("[gpu] edge", name, prec, "T", x.shape[0], "E", E, "k", k, "H", x.shape[1], "F", wd.shape[2])
     o = _run(m, prec, x, wgu, wd, dy, E, k, idx, prob, logits)
@@ -209,3 +224,23 @@ def test_edge_fwd_bwd(m, name, prec):
     # a single token gives too few codes for a rate: at most one flip there
     n_h, n_g = int(valid.sum()) * F, int(valid.sum()) * 2 * F
     assert fl_h <= max(H_FLIP_MAX, 1.0 / n_h) and fl_g <= max(DGU_FLIP_MAX, 1.0 / n_g), (fl_h, fl_g)
+
+
+@pytest.mark.parametrize("prec", ["bf16", "mxfp8"])
+def test_tail_split_rerun_identical(m, prec):
+    """Two runs of the case whose dX and down GEMMs end in the quarter-width tail launch give
+    the same bits: each output element is one wave's K sum in a fixed order, whichever launch
+    computes it."""
+    from tests.gpu_helpers import say
+    _needs_256_cus("tail_split")
+    args = _case("tail_split")
+    say("[gpu] edge tail_split rerun", prec)
+    a = _run(m, prec, *args)
+    b = _run(m, prec, *args)
+    v = a["g"].perm_src >= 0            # padding rows of the permuted outputs are not written
+    assert torch.equal(a["g"].perm_src, b["g"].perm_src)
+    assert torch.equal(a["f"].y_perm[v], b["f"].y_perm[v]) and torch.equal(a["b"].dx_perm[v], b["b"].dx_perm[v])
+    assert torch.equal(a["y"], b["y"]) and torch.equal(a["dx"], b["dx"])
+    assert all(torch.equal(u, v) for u, v in zip(a["b"].dw_gate_up, b["b"].dw_gate_up))
+    assert all(torch.equal(u, v) for u, v in zip(a["b"].dw_down, b["b"].dw_down))
+    assert torch.equal(a["b"].d_prob, b["b"].d_prob)
