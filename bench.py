@@ -565,6 +565,9 @@ def main():
                     help="grouped projections (default) or the per-expert launch loop (forward workloads)")
     ap.add_argument("--dw-dtype", default="f32", choices=("f32", "bf16"),
                     help="weight-gradient output of the training step (default fp32)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the step captured in a HIP graph (the per-kernel breakdown still comes "
+                         "from an eager profiled pass; the eager time is reported beside it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None,
                     help="assignments in the CPU oracle sample (default: expert 0's whole group for MXFP8, 4096 for BF16)")
@@ -623,27 +626,51 @@ def main():
     sizes = step.g.split_sizes.cpu().tolist()
 
     stream = torch.cuda.current_stream(dev)
+    graph = None
+    if args.graph:
+        # the step only launches kernels on the current stream (no allocation, memset, copy
+        # or host synchronization inside the library's calls), so it can be captured whole;
+        # a warm-up on a side stream (default priority) first, as torch's capture expects
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        log("[bench] step captured in a HIP graph")
 
-    def timed_pass(profile):
+    def timed_pass(profile, replay=False):
         """K steps bracketed by synchronizations; one event before, after and between
         consecutive steps (no extra synchronization).  With profile, the library also
-        records an event pair around every kernel launch (per-kernel times)."""
+        records an event pair around every kernel launch (per-kernel times); with replay,
+        each step is a replay of the captured graph."""
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         torch.cuda.synchronize()
         if profile:
             m.profile_start()
         ev[0].record(stream)
         for i in range(args.steps):
-            step()
+            if replay:
+                graph.replay()
+            else:
+                step()
             ev[i + 1].record(stream)
         torch.cuda.synchronize()
         recs = m.profile_stop() if profile else None
         return ev[0].elapsed_time(ev[-1]) / args.steps, sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)), recs
 
-    # the headline: a pass with no per-kernel events; then a profiled pass of the same
-    # steps for the per-kernel breakdown and the roofline of the dominant kernel
-    ms, per_step, _ = timed_pass(False)
-    log(f"[bench] {args.steps} timed steps: {ms:.3f} ms/step")
+    # the headline: a pass with no per-kernel events (graph replays with --graph); then a
+    # profiled eager pass of the same steps for the per-kernel breakdown and the roofline
+    # of the dominant kernel
+    ms, per_step, _ = timed_pass(False, replay=graph is not None)
+    log(f"[bench] {args.steps} timed steps{' (graph replays)' if graph is not None else ''}: {ms:.3f} ms/step")
+    ms_eager = timed_pass(False)[0] if graph is not None else None
     ms_prof, _, records = timed_pass(True)
     log(f"[bench] {args.steps} profiled steps (an event pair per kernel): {ms_prof:.3f} ms/step")
 
@@ -682,6 +709,7 @@ def main():
         "config": {"workload": w.name, "T": w.T, "E": w.E, "H": w.H, "F": w.F, "k": w.k, "prec": w.prec,
                    "passes": "fwd+bwd" if train else "fwd", "align": 32, "split_sizes": sizes,
                    "parallelism": "single GPU", "variant": args.variant,
+                   **({"graph": True} if graph is not None else {}),
                    **({"dw_dtype": args.dw_dtype} if train else {})},
         "tokens_per_s": round(tok_s, 1),
         "algorithmic_tflop_per_step": round(flops / 1e12, 4),
@@ -690,6 +718,7 @@ def main():
         "grouped_mlp_calls": {"ms_per_step": round(mlp_ms, 4),
                               "tflops": round(flops / (mlp_ms * 1e-3) / 1e12, 1) if mlp_ms > 0 else None},
         "kernel_ms_per_step": round(kern_ms, 4),
+        **({"eager_ms_per_step": round(ms_eager, 4)} if ms_eager is not None else {}),
         "profiled_ms_per_step": round(ms_prof, 4),
         "step_ms": {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4),
                     "max": round(per_step[-1], 4)},
