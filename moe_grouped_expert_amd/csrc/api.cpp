@@ -77,9 +77,9 @@ static size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Gate-up (SwiGLU) GEMM: an expert's M-tile remainder under 4 joins its last raster band.
 // Two same-job A/B pairs on the Mixtral-shaped training step: gate-up 1.97 -> 1.93 and
-// 2.02 -> 1.95 ms, with 3.61 -> 3.51 GB fetched per launch; the same rule on dh fetched
-// 2.75 -> 3.07 GB, and bands of 16 on dW_gate_up 3.03 -> 4.56 GB, for time changes within
-// run-to-run noise (so neither is used).
+// 2.02 -> 1.95 ms, with 3.61 -> 3.51 GB fetched per launch.  The same rule on dh fetched
+// 2.75 -> 3.07 GB for a time change within run-to-run noise, so dh does not use it (the
+// weight-gradient GEMMs' band heights are kBandDwDown and kBandDwGateUp below).
 constexpr int kMergeShortBand = 1;
 // M-tiles per raster band of the weight-gradient GEMMs (the others take 8).  Same-job A/B on
 // the Mixtral-shaped training step, each time over the dX GEMM's of the same run (two runs
