@@ -122,6 +122,8 @@ MX_CASES = [
     synth.custom(203, T=64, E=1, H=128, F=128, k=1, prec="mxfp8"),
     # many small groups: 64 experts, top-4, about 12 rows each (one partial tile per group)
     synth.custom(205, T=200, E=64, H=64, F=96, k=4, prec="mxfp8"),
+    # the limits: 256 experts, top-8, about 9 assignments per expert and some experts empty
+    synth.custom(206, T=300, E=256, H=64, F=64, k=8, prec="mxfp8"),
 ]
 
 
