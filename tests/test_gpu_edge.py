@@ -24,16 +24,8 @@ import pytest
 import torch
 
 import synth
-from oracle import mlp, mx
-from oracle import route as rt
-from oracle.metrics import rel_f
 
 pytestmark = pytest.mark.gpu
-
-BF16_TOL = 1e-2
-MX_TOL = 2e-3
-H_FLIP_MAX = 4e-3
-DGU_FLIP_MAX = 2e-3
 
 
 @pytest.fixture(scope="module")
@@ -81,29 +73,6 @@ def _case(name):
     return x, wgu, wd, dy, E, k, idx, prob, logits
 
 
-def _run(m, prec, x, wgu, wd, dy, E, k, idx, prob, logits):
-    from tests.gpu_helpers import gpu_bf16
-    gx, gwgu, gwd, gdy = gpu_bf16(x), gpu_bf16(wgu), gpu_bf16(wd), gpu_bf16(dy)
-    if idx is not None:
-        g = m.moe_route_permute(None, gx, k, E=E, align=32, prec=prec, want_col=True,
-                                topk_idx=torch.from_numpy(idx).cuda(), topk_prob=torch.from_numpy(prob).cuda())
-    else:
-        g = m.moe_route_permute(torch.from_numpy(logits).cuda(), gx, k, align=32, prec=prec, want_col=True)
-    o = dict(g=g)
-    if prec == "mxfp8":
-        wq = m.mxfp8_quantize(gwgu, "both")
-        dq = m.mxfp8_quantize(gwd, "both")
-        f = m.grouped_mlp_fwd(g, wq[0], dq[0], wq[1], dq[1], train=True)
-        b = m.grouped_mlp_bwd(gdy, g, f, wq[2], dq[2], wq[3], dq[3], keep_intermediates=True)
-        o.update(wq=wq, dq=dq)
-    else:
-        f = m.grouped_mlp_fwd(g, gwgu, gwd, train=True)
-        b = m.grouped_mlp_bwd(gdy, g, f, gwgu, gwd)
-    o.update(f=f, b=b, y=m.unpermute_combine(f.y_perm, g.perm_pos), dx=m.unpermute_combine(b.dx_perm, g.perm_pos))
-    torch.cuda.synchronize()
-    return o
-
-
 CASES = ["sizes", "h32_f32", "one_expert_all_tokens", "one_token", "tail_split"]
 
 
@@ -115,128 +84,25 @@ def _needs_256_cus(name):
 @pytest.mark.parametrize("prec", ["bf16", "mxfp8"])
 @pytest.mark.parametrize("name", CASES)
 def test_edge_fwd_bwd(m, name, prec):
-    from tests.gpu_helpers import f64, npy, say
+    from tests.gpu_helpers import check_fwd_bwd, npy, say
     _needs_256_cus(name)
     x, wgu, wd, dy, E, k, idx, prob, logits = _case(name)
     say("[gpu] edge", name, prec, "T", x.shape[0], "E", E, "k", k, "H", x.shape[1], "F", wd.shape[2])
-    o = _run(m, prec, x, wgu, wd, dy, E, k, idx, prob, logits)
-    g, f, b = o["g"], o["f"], o["b"]
-    if idx is None:
-        idx, p = rt.route(logits, k)
-        np.testing.assert_array_equal(npy(g.topk_idx), idx)
-    else:
-        p = prob.astype(np.float64)
-    lay = mlp.Layout(npy(g.topk_idx), npy(g.topk_prob).astype(np.float64), E, 32)
-    np.testing.assert_array_equal(lay.topk_idx, idx)
-    np.testing.assert_array_equal(npy(g.split_sizes), lay.sizes)
-    np.testing.assert_array_equal(npy(g.perm_src), lay.perm_src)
-    np.testing.assert_array_equal(npy(g.perm_pos), lay.perm_pos)
+    o = check_fwd_bwd(m, prec, x, wgu, wd, dy, E, k, idx, prob, logits)
     if name == "sizes":
-        np.testing.assert_array_equal(lay.sizes, [0, 1, 31, 32, 33, 255, 256, 257, 513])
-    empty = [e for e in range(E) if lay.sizes[e] == 0]
-    for e in empty:
-        assert not torch.any(b.dw_gate_up[e]) and not torch.any(b.dw_down[e]), e
-    valid = lay.perm_src >= 0
-    F = wd.shape[2]
-    errs = {}
-    if prec == "bf16":
-        lay_ref = mlp.Layout(idx, p, E, 32)
-        y_ref, saved = mlp.fwd_grouped(x, wgu, wd, lay_ref, keep=True)
-        ref = mlp.bwd_grouped(dy, wgu, wd, lay_ref, saved)
-        errs = dict(y=rel_f(f64(o["y"]), y_ref), dx=rel_f(f64(o["dx"]), ref["dx"]),
-                    dw_gate_up=rel_f(np.stack([f64(t) for t in b.dw_gate_up]), ref["dw_gate_up"]),
-                    dw_down=rel_f(np.stack([f64(t) for t in b.dw_down]), ref["dw_down"]),
-                    d_prob=rel_f(f64(b.d_prob), ref["d_prob"]))
-        say("[gpu] edge rel_F", {kk: f"{v:.2e}" for kk, v in errs.items()})
-        for kk, v in errs.items():
-            assert v <= BF16_TOL, (kk, v)
-        return
-    # MXFP8, staged on the GPU's own codes
-    wq, dq = o["wq"], o["dq"]
-    for e in range(E):
-        q, s = mx.quantize_rows(wgu[e])
-        np.testing.assert_array_equal(npy(wq[0][e]), q)
-        np.testing.assert_array_equal(npy(wq[1][e]), s)
-        q, s = mx.quantize_cols(wd[e])
-        np.testing.assert_array_equal(npy(dq[2][e]), q)
-        np.testing.assert_array_equal(npy(dq[3][e]), s)
-    X = lay.gather(x)
-    q, s = mx.quantize_rows(X)
-    np.testing.assert_array_equal(npy(g.x_perm), q)
-    np.testing.assert_array_equal(npy(g.x_perm_scale), s)
-    q, s = mx.quantize_cols(X)
-    np.testing.assert_array_equal(npy(g.x_col), q)
-    np.testing.assert_array_equal(npy(g.x_col_scale), s)
-    DY = lay.gather(dy)
-    q, s = mx.quantize_rows(DY)
-    np.testing.assert_array_equal(npy(b.dy_row), q)
-    q, s = mx.quantize_cols(DY)
-    np.testing.assert_array_equal(npy(b.dy_col), q)
-    lst = lambda t: [npy(u) for u in t]   # noqa: E731
-    G, U, h = mlp.mx_gateup_stage(npy(g.x_perm), npy(g.x_perm_scale), lst(wq[0]), lst(wq[1]), lay)
-    gu = f64(f.saved_gu)
-    errs["G"] = rel_f(gu[valid, :F], G[valid])
-    errs["U"] = rel_f(gu[valid, F:], U[valid])
-    hq, hs = mx.quantize_rows(h)
-    errs["h"] = rel_f(mx.dequantize_rows(npy(f.h), npy(f.h_scale))[valid], mx.dequantize_rows(hq, hs)[valid])
-    fl_h = float(np.mean(npy(f.h)[valid] != hq[valid]))
-    nrow = int(lay.off[-1])
-    hcq, hcs = mx.quantize_cols(h)
-    errs["h_col"] = rel_f(mx.dequantize_rows(npy(f.h_col), npy(f.h_col_scale))[:, :nrow],
-                          mx.dequantize_rows(hcq, hcs)[:, :nrow])
-    Y = mlp.mx_down_stage(npy(f.h), npy(f.h_scale), lst(dq[0]), lst(dq[1]), lay)
-    errs["y_perm"] = rel_f(f64(f.y_perm)[valid], Y[valid])
-    errs["y"] = rel_f(f64(o["y"]), lay.combine(np.where(valid[:, None], f64(f.y_perm), 0.0)))
-    dG, dU, dp_row = mlp.mx_dh_stage(npy(b.dy_row), npy(b.dy_row_scale), lst(dq[2]), lst(dq[3]), gu[:, :F],
-                                     gu[:, F:], lay)
-    dGU = np.concatenate([dG, dU], axis=1)
-    dGU[~valid] = 0.0
-    q, s = mx.quantize_rows(dGU)
-    errs["dgu_row"] = rel_f(mx.dequantize_rows(npy(b.dgu_row), npy(b.dgu_row_scale))[valid],
-                            mx.dequantize_rows(q, s)[valid])
-    fl_g = float(np.mean(npy(b.dgu_row)[valid] != q[valid]))
-    errs["d_prob"] = rel_f(f64(b.d_prob), lay.to_slots(dp_row))
-    dWd = mlp.mx_dw_stage(npy(b.dy_col), npy(b.dy_col_scale), npy(f.h_col), npy(f.h_col_scale), lay)
-    errs["dw_down"] = rel_f(np.stack([f64(t) for t in b.dw_down]), dWd)
-    dX = mlp.mx_dx_stage(npy(b.dgu_row), npy(b.dgu_row_scale), lst(wq[2]), lst(wq[3]), lay)
-    errs["dx_perm"] = rel_f(f64(b.dx_perm)[valid], dX[valid])
-    dWgu = mlp.mx_dw_stage(npy(b.dgu_col), npy(b.dgu_col_scale), npy(g.x_col), npy(g.x_col_scale), lay)
-    errs["dw_gate_up"] = rel_f(np.stack([f64(t) for t in b.dw_gate_up]), dWgu)
-    errs["dx"] = rel_f(f64(o["dx"]), lay.combine(np.where(valid[:, None], f64(b.dx_perm), 0.0)))
-    # bf16-stored stage outputs with few elements: (GPU, oracle) pairs for the element bound
-    pairs = dict(G=(gu[valid, :F], G[valid]), U=(gu[valid, F:], U[valid]), y_perm=(f64(f.y_perm)[valid], Y[valid]),
-                 y=(f64(o["y"]), lay.combine(np.where(valid[:, None], f64(f.y_perm), 0.0))),
-                 dx_perm=(f64(b.dx_perm)[valid], dX[valid]),
-                 dx=(f64(o["dx"]), lay.combine(np.where(valid[:, None], f64(b.dx_perm), 0.0))))
-    small = {kk: v for kk, v in pairs.items() if v[1].size < 4096}
-    say("[gpu] edge staged rel_F", {kk: f"{v:.2e}" for kk, v in errs.items()}, f"flips h {fl_h:.1e} dGU {fl_g:.1e}")
-    for kk, v in errs.items():
-        if v > MX_TOL and kk in small:
-            # under 4096 elements the rel_F of one bf16 rounding (about 1.5e-3 on average)
-            # spreads past 2e-3; such a stage is held element by element to one rounding
-            # (relative 2^-8 at worst) plus the fp32 accumulation (2^-12 relative, 2^-20
-            # of the largest magnitude)
-            got, ref = small[kk]
-            bound = (2.0 ** -8 + 2.0 ** -12) * np.abs(ref) + 2.0 ** -20 * np.abs(ref).max()
-            assert np.all(np.abs(got - ref) <= bound), (kk, v, float(np.max(np.abs(got - ref) / (bound + 1e-300))))
-            continue
-        assert v <= MX_TOL, (kk, v)
-    # a single token gives too few codes for a rate: at most one flip there
-    n_h, n_g = int(valid.sum()) * F, int(valid.sum()) * 2 * F
-    assert fl_h <= max(H_FLIP_MAX, 1.0 / n_h) and fl_g <= max(DGU_FLIP_MAX, 1.0 / n_g), (fl_h, fl_g)
-
+        np.testing.assert_array_equal(npy(o["g"].split_sizes), [0, 1, 31, 32, 33, 255, 256, 257, 513])
 
 @pytest.mark.parametrize("prec", ["bf16", "mxfp8"])
 def test_tail_split_rerun_identical(m, prec):
     """Two runs of the case whose dX and down GEMMs end in the quarter-width tail launch give
     the same bits: each output element is one wave's K sum in a fixed order, whichever launch
     computes it."""
-    from tests.gpu_helpers import say
+    from tests.gpu_helpers import run_fwd_bwd, say
     _needs_256_cus("tail_split")
     args = _case("tail_split")
     say("[gpu] edge tail_split rerun", prec)
-    a = _run(m, prec, *args)
-    b = _run(m, prec, *args)
+    a = run_fwd_bwd(m, prec, *args)
+    b = run_fwd_bwd(m, prec, *args)
     v = a["g"].perm_src >= 0            # padding rows of the permuted outputs are not written
     assert torch.equal(a["g"].perm_src, b["g"].perm_src)
     assert torch.equal(a["f"].y_perm[v], b["f"].y_perm[v]) and torch.equal(a["b"].dx_perm[v], b["b"].dx_perm[v])
