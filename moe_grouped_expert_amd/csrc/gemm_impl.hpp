@@ -237,6 +237,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
   __shared__ int32_t s_prefix[G_MAXE + 1];
   __shared__ int32_t s_mtiles[G_MAXE];
   __shared__ __attribute__((aligned(16))) float s_prob[G_BM];   // SwiGLU: routing probability of each tile row
+  __shared__ __attribute__((aligned(16))) float s_inv[G_WAVES_M * G_WAVES_N * 32];   // SwiGLU: row-scale broadcast
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -742,6 +743,10 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
           // neighbour's high, own high).
           const bool odd = (l32 & 1) != 0;
           const int fpair = f & ~1;
+          // the lane's share of the MXFP8 offsets (as in the backward's epilogue)
+          const int q2 = l32 >> 1;
+          const int row_lane = (4 * hi + (l32 & 3)) * F + (l32 & ~3);
+          const uint32_t sc_lane = (l32 & 1) == 0 ? uint32_t((8 * (q2 >> 2) + 4 * hi + (q2 & 3)) * (F / 32)) : kInvalid;
           const uint32_t psel = odd ? 0x03020706u : 0x05040100u;
           auto pair2 = [&](float v0, float v1) {
             const uint32_t own = bf16x2(v0, v1);
@@ -764,7 +769,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
           if constexpr (MX) {
             // row form: one scale per (row, 32-column block), shared by the half-wave
             float inv[16];
-            const uint32_t sc = row_block_inv16(h, l32, inv);   // sc: row l32 / 2
+            const uint32_t sc = row_block_inv16(h, l32, inv, s_inv + wave * 32 + hi * 16);   // sc: row l32 / 2
             // codes of 4 consecutive rows: a lane holds its column's 4 codes (bytes =
             // rows); a 4 x 4 byte transpose inside each quad of lanes (16-bit halves with
             // the lane 2 apart, then bytes with the lane 1 apart) leaves row (l32 % 4) of
@@ -782,10 +787,10 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
               v = __builtin_amdgcn_perm(x, v, sel16);   // low half: own | partner's; high: partner's | own
               const uint32_t y = uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0xB1, 0xf, 0xf, false));
               v = __builtin_amdgcn_perm(y, v, sel);
-              __builtin_amdgcn_raw_buffer_store_b32(v, rH, lrow(4 * g + (l32 & 3)) * F + fb0 + (l32 & ~3), 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(v, rH, (rb + 8 * g) * F + fb0 + row_lane, 0, 0);
             }
             // the even lanes write the scale of their row l32 / 2
-            const uint32_t so = (l32 & 1) == 0 ? uint32_t(lrow(l32 >> 1) * (F / 32) + fb0 / 32) : kInvalid;
+            const uint32_t so = sc_lane == kInvalid ? kInvalid : sc_lane + uint32_t(rb * (F / 32) + fb0 / 32);
             __builtin_amdgcn_raw_buffer_store_b8(uint8_t(sc), rHs, so, 0, 0);
           } else {
 #pragma unroll
@@ -796,7 +801,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
           if (train) {
             // column form of column f, rows [rb, rb + 32): after the half-wave swaps,
             // lane hi holds rows 16*hi .. 16*hi + 15 in order
-            const int64_t cbase = int64_t(f) * p.Rp + grow0 + rb + 16 * hi;   // element index
+            const int64_t cbase = int64_t(fb0) * p.Rp + grow0 + rb + (int64_t(l32) * p.Rp + 16 * hi);   // element index
             if constexpr (MX) {
               float cmax = 0.f;
 #pragma unroll
@@ -884,15 +889,27 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
         const uint32_t nb = uint32_t(__builtin_amdgcn_mov_dpp(int(own), 0xB1, 0xf, 0xf, false));
         return __builtin_amdgcn_perm(nb, own, psel);
       };
+      // the lane's share of the MXFP8 output offsets, once per tile (the block's share is
+      // wave-uniform): the row-form dword of rows 4g + (l32 % 4) and columns l32 & ~3, the
+      // scale byte of row l32 / 2 (even lanes), the column form's 16 rows from 16 hi
+      const int q2 = l32 >> 1;
+      const int row_lane = (4 * hi + (l32 & 3)) * F2 + (l32 & ~3);
+      const uint32_t sc_lane = (l32 & 1) == 0 ? uint32_t((8 * (q2 >> 2) + 4 * hi + (q2 & 3)) * (F2 / 32)) : kInvalid;
+      const int64_t col_lane = int64_t(l32) * p.Rp + 16 * hi;
+      const int lds_lane = hi * GS + 2 * l32;            // the lane's G, U element in a staged block
       if (vr > 0) {                                      // wave-uniform
       issue_gu(0, 0);
       issue_gu(1, 1);
-      static_for<0, G_WMB>([&](auto mic) {
-        constexpr int mi = decltype(mic)::value;
-        constexpr int buf = mi & 1;
+      // One 32-row block.  With MXFP8 outputs the blocks run as a loop, not unrolled:
+      // unrolled four times that epilogue was larger than the instruction cache two CUs
+      // share (89 KB of code against 37 KB).  AGPR indexes are compile-time, so block mi's
+      // accumulators are read in a uniform branch per value of mi (folded away when the
+      // blocks are unrolled, as they stay for bf16 outputs, whose loop form spills).
+      auto row_block = [&](const int mi) __attribute__((always_inline)) {
+        const int buf = mi & 1;
         // block mi's G, U have landed (block mi + 1's, the newest 16 operations, may still
         // be on their way); asm with a memory clobber, so that no LDS read moves above it
-        if constexpr (mi + 1 < G_WMB) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        if (mi + 1 < G_WMB) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         const int rb = mi * 32;                          // block row within the span
         if (wrow0 + rb < m_valid) {                      // wave-uniform
@@ -911,19 +928,30 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
             constexpr int ni = decltype(nic)::value;
             const int fb0 = fw0 + ni * 32;                 // first column of the block
             if (fb0 >= F) return;                          // wave-uniform
-            float dg[16], du[16];
+            float dg[16], du[16], dhv[4];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int rr = 8 * (r >> 2) + 4 * hi + (r & 3);
-              const int lo = (rr >> 2) * GS + (rr & 3) * 256 + (ni * 32 + l32) * 2;
+              if ((r & 3) == 0) {                          // four accumulators at a time (register peak)
+                static_for<0, G_WMB>([&](auto mc) {
+                  constexpr int m = decltype(mc)::value;
+                  if (mi == m) {                           // wave-uniform
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) dhv[k] = acc_read(acc[m][ni][r + k]);
+                  }
+                });
+              }
+              // row 8 (r / 4) + 4 hi + r % 4 of the block: 4-row group 2 (r / 4) + hi, row r % 4 in it
+              const int lo = 2 * (r >> 2) * GS + (r & 3) * 256 + ni * 64 + lds_lane;
               const float G = __uint_as_float(uint32_t(*reinterpret_cast<const uint16_t*>(gs + lo)) << 16);
               const float U = __uint_as_float(uint32_t(*reinterpret_cast<const uint16_t*>(gs + GA + lo)) << 16);
-              const float dh = acc_read(acc[mi][ni][r]);
+              const float dh = dhv[r & 3];
               const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-G));
-              const float sl = G * sg;
-              dps[r] += dh * sl * U;
-              du[r] = dh * pr[r] * sl;
-              dg[r] = dh * pr[r] * U * sg * (1.f + G * (1.f - sg));
+              const float sl = G * sg;                       // silu(G)
+              const float t = dh * sl;
+              dps[r] = fmaf(t, U, dps[r]);
+              du[r] = t * pr[r];
+              const float ds = fmaf(sl, 1.f - sg, sg);       // silu'(G) = sg (1 + G (1 - sg))
+              dg[r] = (dh * pr[r]) * (U * ds);
             }
             // both arrays: h = 0 -> dG at column fb0 + l32, h = 1 -> dU at F + fb0 + l32
             static_for<0, 2>([&](auto hc) {
@@ -932,7 +960,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
               const int cb = h * F + fb0;                    // first [dG dU] column of the block
               if constexpr (MXO) {
                 float inv[16];
-                const uint32_t sc = row_block_inv16(v, l32, inv);   // sc: row l32 / 2
+                const uint32_t sc = row_block_inv16(v, l32, inv, s_inv + wave * 32 + hi * 16);   // sc: row l32 / 2
                 const uint32_t sel16 = (l32 & 2) == 0 ? 0x05040100u : 0x03020706u;   // halves, as in the forward
                 const uint32_t sel = odd ? 0x03070105u : 0x06020400u;
 #pragma unroll
@@ -943,12 +971,12 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
                   w = __builtin_amdgcn_perm(x, w, sel16);
                   const uint32_t y = uint32_t(__builtin_amdgcn_mov_dpp(int(w), 0xB1, 0xf, 0xf, false));
                   w = __builtin_amdgcn_perm(y, w, sel);
-                  __builtin_amdgcn_raw_buffer_store_b32(w, rR, lrow(4 * g + (l32 & 3)) * F2 + cb + (l32 & ~3), 0, 0);
+                  __builtin_amdgcn_raw_buffer_store_b32(w, rR, (rb + 8 * g) * F2 + cb + row_lane, 0, 0);
                 }
-                const uint32_t so = (l32 & 1) == 0 ? uint32_t(lrow(l32 >> 1) * (F2 / 32) + cb / 32) : kInvalid;
+                const uint32_t so = sc_lane == kInvalid ? kInvalid : sc_lane + uint32_t(rb * (F2 / 32) + cb / 32);
                 __builtin_amdgcn_raw_buffer_store_b8(uint8_t(sc), rRs, so, 0, 0);
                 // column form of column cb + l32, rows [rb, rb + 32)
-                const int64_t cbase = int64_t(cb + l32) * p.Rp + grow0 + rb + 16 * hi;
+                const int64_t cbase = int64_t(cb) * p.Rp + grow0 + rb + col_lane;
                 float cmax = 0.f;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) cmax = fmaxf(cmax, fabsf(v[r]));
@@ -991,11 +1019,17 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
             p.dprob_part[(grow0 + lrow(l32 >> 1)) * p.dprob_nparts + nt * 2 + wn] = ps;
         }
         // the buffer takes block mi + 2 once this wave's reads of it have completed
-        if constexpr (mi + 2 < G_WMB) {
+        if (mi + 2 < G_WMB) {
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           issue_gu(mi + 2, buf);
         }
-      });
+      };
+      if constexpr (MXO) {
+#pragma clang loop unroll(disable)
+        for (int mi = 0; mi < G_WMB; ++mi) row_block(mi);
+      } else {
+        static_for<0, G_WMB>([&](auto mic) { row_block(decltype(mic)::value); });
+      }
       }
     }
     cur = nxt;

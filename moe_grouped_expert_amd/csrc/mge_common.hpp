@@ -52,20 +52,25 @@ __device__ __forceinline__ float mx_inv_scale(uint32_t s) { return __uint_as_flo
 // beyond 448 become 448.
 __device__ __forceinline__ float e4m3_clamp(float w) { return __builtin_amdgcn_fmed3f(w, -448.f, 448.f); }
 
-// codes of a, b in bytes 0, 1
+// codes of a, b in bytes 0, 1.  The conversion writes one 16-bit half of its destination
+// and keeps the other from its third operand; that half is masked off (or, in e4m3x4,
+// overwritten), so the clamped a itself serves as that operand and no zero is loaded.
 __device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
-  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false)) & 0xffffu;
+  const float ca = e4m3_clamp(a);
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(ca, e4m3_clamp(b), __float_as_int(ca), false)) & 0xffffu;
 }
 
 // codes of a, b, c, d in bytes 0..3
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  int v = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+  const float ca = e4m3_clamp(a);
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(ca, e4m3_clamp(b), __float_as_int(ca), false);
   v = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), v, true);
   return uint32_t(v);
 }
 
 __device__ __forceinline__ uint32_t e4m3_rne(float w) {
-  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(w), 0.f, 0, false)) & 0xffu;
+  const float cw = e4m3_clamp(w);
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(cw, 0.f, __float_as_int(cw), false)) & 0xffu;
 }
 
 // v_permlane32_swap_b32: lanes 32..63 of a trade places with lanes 0..31 of b.  Returns
@@ -109,53 +114,62 @@ __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
+// max(|a|, |b|) of two fp32 bit patterns as one VOP3 max with abs modifiers.  Written as
+// asm because the compiler otherwise canonicalizes each bit-cast operand first (one more
+// max per operand) and clears the sign bits with separate ands; the result for NaN inputs
+// is not defined here.
+__device__ __forceinline__ uint32_t max_abs_bits(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_max_f32_e64 %0, |%1|, |%2|" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_mov_dpp(int(v), CTRL, 0xf, 0xf, true));
+}
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
 // Row blocks of a 32-column tile held column-wise: in each half-wave, lane c (= l32)
 // holds v[0..15], the values of 16 rows in column c.  Computes, for each of the 16 rows,
 // the E8M0 scale of its 32 values (their amax over the half-wave) and returns in inv[r]
 // the reciprocal scale of row r in every lane, and in the result the scale byte of row
 // l32 / 2.  A reduce-scatter (each exchange halves the rows a lane keeps: 16-lane swap,
 // lane ^ 8 by row_ror:8, mirror in 8, lane ^ 2, lane ^ 1) leaves the amax of row l32 / 2
-// in lanes 2r, 2r + 1; the mirrored all-gather returns the 16 reciprocals: about 70
-// instructions for the 16 rows instead of five exchanges per row.  Needs all 64 lanes.
-__device__ __forceinline__ uint32_t row_block_inv16(const float* v, int l32, float* inv) {
-  const bool b4 = (l32 & 16) != 0, b3 = (l32 & 8) != 0, b2 = (l32 & 4) != 0, b1 = (l32 & 2) != 0;
+// in lanes 2r, 2r + 1.  After the first step the values are non-negative, and
+// non-negative fp32 values order as their bit patterns: the later steps are integer maxes,
+// which take the DPP exchange as an operand.  The 16 reciprocals return through `slot`,
+// 16 floats of LDS per half-wave (lanes 2r, 2r + 1 write row r's, every lane reads all
+// 16 back): one wave's LDS accesses are performed in issue order, and the compiler keeps
+// the reads after the write (same array, indexes it cannot tell apart).  Needs all 64
+// lanes.
+__device__ __forceinline__ uint32_t row_block_inv16(const float* v, int l32, float* inv, float* slot) {
+  const bool b3 = (l32 & 8) != 0, b2 = (l32 & 4) != 0, b1 = (l32 & 2) != 0;
   // m1[i]: row i + 8*b4, amax over lanes c, c ^ 16
-  float m1[8];
+  uint32_t m1[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const U32Pair x = permlane16_swap(__float_as_uint(fabsf(v[i])), __float_as_uint(fabsf(v[i + 8])));
-    m1[i] = fmaxf(__uint_as_float(x.a), __uint_as_float(x.b));
+    const U32Pair x = permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 8]));
+    m1[i] = max_abs_bits(x.a, x.b);
   }
   // m2[i]: row i + 4*b3 + 8*b4 (partner: lane ^ 8)
-  float m2[4];
+  uint32_t m2[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) m2[i] = fmaxf(b3 ? m1[i + 4] : m1[i], dpp_f<0x128>(b3 ? m1[i] : m1[i + 4]));
+  for (int i = 0; i < 4; ++i) m2[i] = umax(b3 ? m1[i + 4] : m1[i], dpp_u<0x128>(b3 ? m1[i] : m1[i + 4]));
   // m3[i]: row i + 2*b2 + 4*b3 + 8*b4 (partner: lane 7 - c within 8; same b3, b4)
-  float m3[2];
+  uint32_t m3[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) m3[i] = fmaxf(b2 ? m2[i + 2] : m2[i], dpp_f<0x141>(b2 ? m2[i] : m2[i + 2]));
+  for (int i = 0; i < 2; ++i) m3[i] = umax(b2 ? m2[i + 2] : m2[i], dpp_u<0x141>(b2 ? m2[i] : m2[i + 2]));
   // m4: row b1 + 2*b2 + 4*b3 + 8*b4 = l32 / 2 (partner: lane ^ 2); then lane ^ 1 holds the same row
-  float m4 = fmaxf(b1 ? m3[1] : m3[0], dpp_f<0x4E>(b1 ? m3[0] : m3[1]));
-  m4 = fmaxf(m4, dpp_f<0xB1>(m4));
-  const uint32_t sc = mx_scale_byte(m4);
-  const float g1 = mx_inv_scale(sc);
-  // all-gather, the same exchanges in reverse
-  const float r2 = dpp_f<0x4E>(g1);
-  const float g2[2] = {b1 ? r2 : g1, b1 ? g1 : r2};                      // rows t + 2*b2 + 4*b3 + 8*b4
-  const float r40 = dpp_f<0x141>(g2[0]), r41 = dpp_f<0x141>(g2[1]);
-  const float g4[4] = {b2 ? r40 : g2[0], b2 ? r41 : g2[1], b2 ? g2[0] : r40, b2 ? g2[1] : r41};   // rows u + 4*b3 + 8*b4
-  float g8[8];                                                            // rows w + 8*b4
+  uint32_t m4 = umax(b1 ? m3[1] : m3[0], dpp_u<0x4E>(b1 ? m3[0] : m3[1]));
+  m4 = umax(m4, dpp_u<0xB1>(m4));
+  const uint32_t sc = mx_scale_byte(__uint_as_float(m4));
+  slot[l32 >> 1] = mx_inv_scale(sc);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const float r = dpp_f<0x128>(g4[t]);
-    g8[t] = b3 ? r : g4[t];
-    g8[t + 4] = b3 ? g4[t] : r;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {   // every lane: a = row i, b = row i + 8
-    const U32Pair x = permlane16_swap(__float_as_uint(g8[i]), __float_as_uint(g8[i]));
-    inv[i] = __uint_as_float(x.a);
-    inv[i + 8] = __uint_as_float(x.b);
+  for (int g = 0; g < 4; ++g) {
+    const float4 q = *reinterpret_cast<const float4*>(slot + 4 * g);
+    inv[4 * g] = q.x; inv[4 * g + 1] = q.y; inv[4 * g + 2] = q.z; inv[4 * g + 3] = q.w;
   }
   return sc;
 }
@@ -181,10 +195,10 @@ __device__ __forceinline__ float row_block_sum16(const float* v, int l32) {
   return m4 + dpp_f<0xB1>(m4);
 }
 
-// max of v over lanes i and i ^ 32
+// max of a non-negative v over lanes i and i ^ 32 (an integer max of the bit patterns)
 __device__ __forceinline__ float max_xor32(float v) {
   const U32Pair r = permlane32_swap(__float_as_uint(v), __float_as_uint(v));
-  return fmaxf(__uint_as_float(r.a), __uint_as_float(r.b));
+  return __uint_as_float(umax(r.a, r.b));
 }
 
 __device__ __forceinline__ float wave_max_xor(float v, int lanes) {
