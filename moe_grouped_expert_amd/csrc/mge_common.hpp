@@ -141,9 +141,8 @@ __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b 
 // non-negative fp32 values order as their bit patterns: the later steps are integer maxes,
 // which take the DPP exchange as an operand.  The 16 reciprocals return through `slot`,
 // 16 floats of LDS per half-wave (lanes 2r, 2r + 1 write row r's, every lane reads all
-// 16 back): one wave's LDS accesses are performed in issue order, and the compiler keeps
-// the reads after the write (same array, indexes it cannot tell apart).  Needs all 64
-// lanes.
+// 16 back): one wave's LDS accesses are performed in issue order, and a wave barrier keeps
+// the compiler from moving the reads above the write.  Needs all 64 lanes.
 __device__ __forceinline__ uint32_t row_block_inv16(const float* v, int l32, float* inv, float* slot) {
   const bool b3 = (l32 & 8) != 0, b2 = (l32 & 4) != 0, b1 = (l32 & 2) != 0;
   // m1[i]: row i + 8*b4, amax over lanes c, c ^ 16
@@ -166,6 +165,7 @@ __device__ __forceinline__ uint32_t row_block_inv16(const float* v, int l32, flo
   m4 = umax(m4, dpp_u<0xB1>(m4));
   const uint32_t sc = mx_scale_byte(__uint_as_float(m4));
   slot[l32 >> 1] = mx_inv_scale(sc);
+  __builtin_amdgcn_wave_barrier();   // the other lanes' writes before the reads (no instruction)
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const float4 q = *reinterpret_cast<const float4*>(slot + 4 * g);
