@@ -329,9 +329,44 @@ GEMM_SOURCES = ("gemm_impl.hpp", "gemm_mx.hip", "gemm_bf16.hip", "gemm_host.cpp"
 GEMM_PARAMS_MARK = "// ------------------------------------------------------------ grouped GEMM"
 
 
+def _code_text(text):
+    """C/C++ source bytes without comments, trailing blanks and empty lines: what the
+    compiler sees, so that counters stay attached to a kernel across comment edits."""
+    out, in_block = [], False
+    for line in text.decode("utf-8", "replace").split("\n"):
+        code, i, n = [], 0, len(line)
+        while i < n:
+            if in_block:
+                j = line.find("*/", i)
+                if j < 0:
+                    break
+                in_block, i = False, j + 2
+                continue
+            c = line[i]
+            if c in "\"'":                      # string or character literal, copied whole
+                j = i + 1
+                while j < n and line[j] != c:
+                    j += 2 if line[j] == "\\" else 1
+                code.append(line[i:j + 1])
+                i = j + 1
+                continue
+            if line.startswith("//", i):
+                break
+            if line.startswith("/*", i):
+                in_block, i = True, i + 2
+                continue
+            code.append(c)
+            i += 1
+        kept = "".join(code).rstrip()
+        if kept.strip():
+            out.append(kept)
+    return "\n".join(out).encode()
+
+
 def kernel_source_digest(family="all"):
-    """Digest of the sources of a kernel family ("gemm" or "all"): counter-derived traffic
-    is only reported while the kernels are the ones the counters were taken on."""
+    """Digest of the code of a kernel family ("gemm" or "all"), comments left out:
+    counter-derived traffic is only reported while the kernels are the ones the counters
+    were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "moe_grouped_expert_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
@@ -347,7 +382,7 @@ def kernel_source_digest(family="all"):
                 text = b"\n".join(l for l in text.split(b"\n") if l.startswith(b"constexpr int k"))
             elif f not in GEMM_SOURCES:
                 continue
-        h.update(f.encode() + b"\0" + text)
+        h.update(f.encode() + b"\0" + _code_text(text))
     return h.hexdigest()[:16]
 
 

@@ -29,8 +29,8 @@
 // A and B tiles in its L2); virtual workgroup ids are remapped so
 // that the workgroups of one XCD (hardware dispatches round-robin over the 8 XCDs)
 // take consecutive tiles and share that XCD's L2.  Empty experts own no tiles (RAGGED_M)
-// or produce zero gradients (RAGGED_K).  The next tile's first slices are issued
-// before the epilogue, so their latency hides behind it.
+// or produce zero gradients (RAGGED_K).  Before a plain-store or SwiGLU epilogue the next
+// tile's first slice is issued, so its latency hides behind the epilogue.
 // Epilogues (fp32 accumulators never reach HBM; no per-element branches: stores go
 // through buffer resources whose record bound ends at the last valid row, so the
 // hardware range check drops rows past the group, and columns past N get an offset

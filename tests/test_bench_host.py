@@ -44,19 +44,23 @@ def test_source_digests_by_family(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(root))
     g0, a0 = bench.kernel_source_digest("gemm"), bench.kernel_source_digest("all")
     csrc = root / "moe_grouped_expert_amd" / "csrc"
-    # a change outside the GEMM sources leaves the GEMM digest alone
-    (csrc / "quant.hip").write_text((csrc / "quant.hip").read_text() + "\n// x\n")
+    # comments and blank lines are not code: editing them changes no digest
+    gi = (csrc / "gemm_impl.hpp").read_text()
+    (csrc / "gemm_impl.hpp").write_text("// note\n\n" + gi.replace("\n", "  // c\n", 3) + "\n/* block\n */\n")
+    assert bench.kernel_source_digest("gemm") == g0 and bench.kernel_source_digest("all") == a0
+    # a code change outside the GEMM sources leaves the GEMM digest alone
+    (csrc / "quant.hip").write_text((csrc / "quant.hip").read_text() + "\nstatic int x_;\n")
     assert bench.kernel_source_digest("gemm") == g0 and bench.kernel_source_digest("all") != a0
-    # so does a change to mge_internal.hpp above the grouped-GEMM section
+    # so does one in mge_internal.hpp above the grouped-GEMM section
     txt = (csrc / "mge_internal.hpp").read_text()
     i = txt.index(bench.GEMM_PARAMS_MARK)
-    (csrc / "mge_internal.hpp").write_text(txt[:i] + "// y\n" + txt[i:])
+    (csrc / "mge_internal.hpp").write_text(txt[:i] + "static int y_;\n" + txt[i:])
     assert bench.kernel_source_digest("gemm") == g0
-    # a change inside it, or to a GEMM file, does not
-    (csrc / "mge_internal.hpp").write_text(txt + "\n// z\n")
+    # one inside it, or in a GEMM file, does not
+    (csrc / "mge_internal.hpp").write_text(txt + "\nstatic int z_;\n")
     assert bench.kernel_source_digest("gemm") != g0
     (csrc / "mge_internal.hpp").write_text(txt)
-    (csrc / "gemm_impl.hpp").write_text((csrc / "gemm_impl.hpp").read_text() + "\n")
+    (csrc / "gemm_impl.hpp").write_text(gi + "\nstatic int w_;\n")
     assert bench.kernel_source_digest("gemm") != g0
 
 
@@ -73,6 +77,6 @@ def test_traffic_is_none_once_the_sources_change(tmp_path, monkeypatch):
     assert bench.traffic_for("combine_kernel", "train_mxfp8") == 7
     assert bench.traffic_for("gemm_dx_mx", "fwd_mxfp8") is None
     csrc = root / "moe_grouped_expert_amd" / "csrc"
-    (csrc / "combine.hip").write_text((csrc / "combine.hip").read_text() + "\n")
+    (csrc / "combine.hip").write_text((csrc / "combine.hip").read_text() + "\nstatic int c_;\n")
     assert bench.traffic_for("gemm_dx_mx", "train_mxfp8") == 123
     assert bench.traffic_for("combine_kernel", "train_mxfp8") is None
