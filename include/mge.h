@@ -53,6 +53,12 @@
  *     align a power of two in [1, 256]; column forms (training, backward) need
  *     align % 32 == 0.
  *     T = 0 is a no-op.  NaN/Inf inputs give undefined (but memory-safe) results.
+ *   - The routing maps the grouped calls take are those moe_route_permute wrote for
+ *     the same T, k, E and align.  They stay on the device, where the host cannot
+ *     check them: other split_sizes or group_offsets can make the grouped GEMMs read
+ *     or write outside their buffers.  perm_src and perm_pos are checked where they
+ *     are read: the gathers take a source row outside [0, T) as zeros, and the combine
+ *     and the d_prob reduction skip an entry outside the permuted rows.
  *   - Calls are thread-safe and re-entrant; each is deterministic, so two identical
  *     calls give bit-identical outputs: no floating-point value is accumulated with
  *     atomics (the only atomics are the integer LDS adds of the routing histogram,
@@ -442,16 +448,19 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* args, void* stream);
  * so the forward's combine is unweighted.
  * Errors: MGE_ERR_INVALID_ARG for T < 0, k outside [1, 8], H not a positive multiple
  * of 32, dtypes other than BF16/F32, or a NULL / misaligned (16-byte) in, out or
- * perm_pos.  Rows of in that no perm_pos entry names are not read.
+ * perm_pos, or in_rows < 0.  Rows of in that no perm_pos entry names are not read; an
+ * entry outside [0, in_rows) names no row, and its slot adds nothing (so a caller may
+ * drop a slot by setting its entry to -1).
  * ---------------------------------------------------------------------------- */
 typedef struct mge_combine_args {
   uint32_t struct_size;
   int32_t T, k, H;
   int32_t in_dtype, out_dtype;           /* MGE_DTYPE_* */
-  const void* in;                        /* [R][H] */
+  const void* in;                        /* [in_rows][H] */
   const int32_t* perm_pos;               /* [T][k] */
   const float* weights;                  /* [T][k] or NULL */
   void* out;                             /* [T][H] */
+  int64_t in_rows;                       /* rows of in (R for the permuted buffers) */
 } mge_combine_args;
 
 mge_status unpermute_combine(const mge_combine_args* args, void* stream);

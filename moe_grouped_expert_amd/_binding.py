@@ -84,7 +84,7 @@ class FwdSavedSizes(C.Structure):
 
 class CombineArgs(C.Structure):
     _fields_ = [("struct_size", u32), ("T", i32), ("k", i32), ("H", i32), ("in_dtype", i32), ("out_dtype", i32),
-                ("in_", vp), ("perm_pos", vp), ("weights", vp), ("out", vp)]
+                ("in_", vp), ("perm_pos", vp), ("weights", vp), ("out", vp), ("in_rows", i64)]
 
 
 class RouterBwdArgs(C.Structure):
@@ -179,6 +179,8 @@ def _ptr_array(ts: Sequence[torch.Tensor]):
 
 
 def perm_rows(T: int, k: int, E: int, align: int) -> int:
+    """Rows of the permuted buffers for T tokens, top-k over E experts, groups starting at
+    multiples of `align`: T*k plus the worst-case padding, E*(align-1)."""
     return int(lib().mge_perm_rows(T, k, E, align))
 
 
@@ -276,6 +278,9 @@ def moe_route_permute(logits: Optional[torch.Tensor], x: Optional[torch.Tensor],
 
 
 def check_device_errors(route: RouteOut) -> int:
+    """Synchronise the stream and read the routing call's device flag (set when a given
+    top-k index was out of range and clamped); returns the library status code.  For
+    tests and debugging: it blocks the host."""
     return lib().mge_check_device_errors(_ptr(route.workspace), _stream(route.workspace.device))
 
 
@@ -431,7 +436,11 @@ def _fwd_args(rt: RouteOut, w_gate_up, w_down, w_gate_up_scale, w_down_scale, y_
 
 def grouped_mlp_fwd(rt: RouteOut, w_gate_up, w_down, w_gate_up_scale=None, w_down_scale=None,
                     y_dtype: str = "bf16", train: bool = False, out: Optional[FwdOut] = None) -> FwdOut:
-    """Grouped gate-up GEMM -> SwiGLU x prob (+ quantize) -> grouped down GEMM."""
+    """Grouped gate-up GEMM -> SwiGLU x prob (+ quantize) -> grouped down GEMM over every
+    expert of `rt`, one launch per projection.
+    w_gate_up: [E, 2F, H] (gate rows first), w_down: [E, H, F]; bf16 masters for a BF16
+    route, MXFP8 row codes (with w_*_scale) for an MXFP8 one.  y_dtype "bf16" or "f32".
+    train=True also keeps what the backward needs (G and U in bf16, h's column form)."""
     o, a, keep, F, dev = _fwd_args(rt, w_gate_up, w_down, w_gate_up_scale, w_down_scale, y_dtype, train, out)
     if o.workspace is None:
         o.workspace = torch.empty(max(int(lib().mge_fwd_workspace_bytes(C.byref(a))), 256), device=dev,
@@ -586,6 +595,10 @@ def profile_stop() -> list:
 
 def unpermute_combine(inp: torch.Tensor, perm_pos: torch.Tensor, weights: Optional[torch.Tensor] = None,
                       out_dtype: str = "bf16", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[t] = sum over i of weights[t, i] * inp[perm_pos[t, i]] (unweighted when weights
+    is None), in slot order and fp32, without atomics; a slot whose entry is outside
+    [0, rows of inp), such as -1, adds nothing.  inp: [rows, H] bf16 or f32 (y_perm or
+    dx_perm); out_dtype "bf16" or "f32"."""
     T, k = perm_pos.shape
     H = inp.shape[1]
     dev = inp.device
@@ -597,6 +610,7 @@ def unpermute_combine(inp: torch.Tensor, perm_pos: torch.Tensor, weights: Option
     a.in_dtype = DTYPE["bf16"] if inp.dtype == torch.bfloat16 else DTYPE["f32"]
     a.out_dtype = DTYPE["bf16"] if out.dtype == torch.bfloat16 else DTYPE["f32"]
     a.in_, a.perm_pos, a.weights, a.out = _ptr(inp), _ptr(perm_pos), _ptr(weights), _ptr(out)
+    a.in_rows = inp.shape[0]
     _check(lib().unpermute_combine(C.byref(a), _stream(dev)), "unpermute_combine")
     return out
 

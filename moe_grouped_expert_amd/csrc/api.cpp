@@ -886,7 +886,7 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
     if (st != MGE_OK) return st;
   }
   // b3: d_prob[t][i] = the row sum of the assignment's permuted row
-  st = launch_dprob_reduce(a->T, a->k, nparts, dprob_part, a->perm_pos, a->d_prob, s);
+  st = launch_dprob_reduce(a->T, a->k, nparts, dprob_part, int64_t(R), a->perm_pos, a->d_prob, s);
   if (st != MGE_OK) return st;
   // b4: dW_down[e] = dY_e^T h_e  (K = tokens of e)
   {
@@ -948,8 +948,9 @@ mge_status unpermute_combine(const mge_combine_args* a, void* stream) {
               "dtypes must be BF16 or F32");
   MGE_REQUIRE(a->in && aligned16(a->in) && a->out && aligned16(a->out) && a->perm_pos,
               "in / out / perm_pos NULL or misaligned");
-  return launch_combine(a->T, a->k, a->H, a->in_dtype, a->out_dtype, a->in, a->perm_pos, a->weights, a->out,
-                        static_cast<hipStream_t>(stream));
+  MGE_REQUIRE(a->in_rows >= 0, "in_rows must be >= 0 (got %lld)", (long long)a->in_rows);
+  return launch_combine(a->T, a->k, a->H, a->in_dtype, a->out_dtype, a->in, a->in_rows, a->perm_pos, a->weights,
+                        a->out, static_cast<hipStream_t>(stream));
 }
 
 mge_status moe_router_bwd(const mge_router_bwd_args* a, void* stream) {

@@ -13,16 +13,22 @@ constexpr int CB_THREADS = 256;
 
 template <typename TIn, typename TOut>
 __global__ __launch_bounds__(CB_THREADS) void combine_kernel(int k, int H, const TIn* __restrict__ in,
+                                                             int64_t in_rows,
                                                              const int32_t* __restrict__ perm_pos,
                                                              const float* __restrict__ weights,
                                                              TOut* __restrict__ out) {
   const int t = blockIdx.x;
+  // a slot whose entry names no row of in (outside [0, in_rows), e.g. -1) adds nothing;
+  // the test is uniform over the workgroup (one token)
   int rows[8];
   float w[8];
+  bool use[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
+    use[i] = false;
     if (i < k) {
       rows[i] = perm_pos[int64_t(t) * k + i];
+      use[i] = rows[i] >= 0 && rows[i] < in_rows;
       w[i] = weights ? weights[int64_t(t) * k + i] : 1.0f;
     }
   }
@@ -33,7 +39,7 @@ __global__ __launch_bounds__(CB_THREADS) void combine_kernel(int k, int H, const
     for (int j = 0; j < 8; ++j) acc[j] = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (i < k) {
+      if (use[i]) {
         const TIn* src = in + int64_t(rows[i]) * H + c * 8;
         if constexpr (sizeof(TIn) == 2) {
           uint4 v = *reinterpret_cast<const uint4*>(src);
@@ -66,44 +72,48 @@ __global__ __launch_bounds__(CB_THREADS) void combine_kernel(int k, int H, const
   }
 }
 
-mge_status launch_combine(int T, int k, int H, int in_dtype, int out_dtype, const void* in,
+mge_status launch_combine(int T, int k, int H, int in_dtype, int out_dtype, const void* in, int64_t in_rows,
                           const int32_t* perm_pos, const float* weights, void* out, hipStream_t s) {
   if (T <= 0) return MGE_OK;
   dim3 g(T), b(CB_THREADS);
   ProfScope prof(s, "combine");
   if (in_dtype == MGE_DTYPE_BF16 && out_dtype == MGE_DTYPE_BF16)
-    hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t>), g, b, 0, s, k, H, (const uint16_t*)in, perm_pos,
+    hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t>), g, b, 0, s, k, H, (const uint16_t*)in, in_rows, perm_pos,
                        weights, (uint16_t*)out);
   else if (in_dtype == MGE_DTYPE_BF16)
-    hipLaunchKernelGGL((combine_kernel<uint16_t, float>), g, b, 0, s, k, H, (const uint16_t*)in, perm_pos,
+    hipLaunchKernelGGL((combine_kernel<uint16_t, float>), g, b, 0, s, k, H, (const uint16_t*)in, in_rows, perm_pos,
                        weights, (float*)out);
   else if (out_dtype == MGE_DTYPE_BF16)
-    hipLaunchKernelGGL((combine_kernel<float, uint16_t>), g, b, 0, s, k, H, (const float*)in, perm_pos,
+    hipLaunchKernelGGL((combine_kernel<float, uint16_t>), g, b, 0, s, k, H, (const float*)in, in_rows, perm_pos,
                        weights, (uint16_t*)out);
   else
-    hipLaunchKernelGGL((combine_kernel<float, float>), g, b, 0, s, k, H, (const float*)in, perm_pos, weights,
+    hipLaunchKernelGGL((combine_kernel<float, float>), g, b, 0, s, k, H, (const float*)in, in_rows, perm_pos, weights,
                        (float*)out);
   return hip_check("combine_kernel");
 }
 
-// d_prob[t][i] = sum_j partial[perm_pos[t][i]][j], j ascending (fixed order).
-__global__ void dprob_reduce_kernel(int n, int nparts, const float* __restrict__ partial,
+// d_prob[t][i] = sum_j partial[perm_pos[t][i]][j], j ascending (fixed order); 0 for an
+// entry outside the R permuted rows.
+__global__ void dprob_reduce_kernel(int n, int nparts, const float* __restrict__ partial, int64_t rows,
                                     const int32_t* __restrict__ perm_pos, float* __restrict__ d_prob) {
   int a = blockIdx.x * blockDim.x + threadIdx.x;
   if (a >= n) return;
-  const float* src = partial + int64_t(perm_pos[a]) * nparts;
+  const int32_t pos = perm_pos[a];
   float s = 0.f;
-  for (int j = 0; j < nparts; ++j) s += src[j];
+  if (pos >= 0 && pos < rows) {
+    const float* src = partial + int64_t(pos) * nparts;
+    for (int j = 0; j < nparts; ++j) s += src[j];
+  }
   d_prob[a] = s;
 }
 
-mge_status launch_dprob_reduce(int T, int k, int nparts, const float* partial, const int32_t* perm_pos,
+mge_status launch_dprob_reduce(int T, int k, int nparts, const float* partial, int64_t rows, const int32_t* perm_pos,
                                float* d_prob, hipStream_t s) {
   int n = T * k;
   if (n <= 0) return MGE_OK;
   ProfScope prof(s, "dprob_reduce");
-  hipLaunchKernelGGL(dprob_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, s, n, nparts, partial, perm_pos,
-                     d_prob);
+  hipLaunchKernelGGL(dprob_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, s, n, nparts, partial, rows,
+                     perm_pos, d_prob);
   return hip_check("dprob_reduce_kernel");
 }
 

@@ -92,7 +92,8 @@ mge_status launch_router_bwd(int T, int E, int k, const int32_t* idx, const floa
                              float* dlogits, hipStream_t s);
 
 // ------------------------------------------------------------ combine / reductions
-mge_status launch_combine(int T, int k, int H, int in_dtype, int out_dtype, const void* in,
+// entries of perm_pos outside [0, in_rows) add nothing
+mge_status launch_combine(int T, int k, int H, int in_dtype, int out_dtype, const void* in, int64_t in_rows,
                           const int32_t* perm_pos, const float* weights, void* out, hipStream_t s);
 // h = p * silu(G) * U from the bf16 [G U] rows (stride 2F) into bf16 h [R][F] (the
 // unfused forward's standalone SwiGLU x prob; rows with p = 0 get 0)
@@ -102,7 +103,8 @@ mge_status launch_zero_pad_rows(int R, int C, const int32_t* perm_src, uint16_t*
 // d_prob partials per row written by the dh GEMM's SwiGLU-backward epilogue (one per
 // 128-column span of F: two per 256-column tile)
 inline int dh_swiglu_nparts(int F) { return 2 * ((F + 255) / 256); }
-mge_status launch_dprob_reduce(int T, int k, int nparts, const float* partial, const int32_t* perm_pos,
+// (an entry of perm_pos outside [0, rows) gives 0)
+mge_status launch_dprob_reduce(int T, int k, int nparts, const float* partial, int64_t rows, const int32_t* perm_pos,
                                float* d_prob, hipStream_t s);
 // tables[t] (n host pointers each; null tables are skipped) -> dev_table[t * n + i], in as
 // few launches as the kernel argument space allows

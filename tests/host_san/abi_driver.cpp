@@ -212,6 +212,8 @@ int main() {
     EXPECT(unpermute_combine(&c, nullptr), MGE_ERR_INVALID_ARG);
     c.in_dtype = MGE_DTYPE_BF16; c.out = A8;
     EXPECT(unpermute_combine(&c, nullptr), MGE_ERR_INVALID_ARG);
+    c.out = A16; c.in_rows = -1;
+    EXPECT(unpermute_combine(&c, nullptr), MGE_ERR_INVALID_ARG);
   }
   EXPECT(moe_router_bwd(nullptr, nullptr), MGE_ERR_INVALID_ARG);
   {

@@ -182,6 +182,11 @@ def test_fwd_bwd_combine_reject():
     assert r == b.MGE_ERR_INVALID_ARG
     r, err = _call("unpermute_combine", b.CombineArgs, T=4, k=2, H=64, in_dtype=2)
     assert r == b.MGE_ERR_INVALID_ARG and "dtype" in err
+    # host buffers stand in for device ones: the call fails before any launch
+    buf = (C.c_uint8 * 4096)()
+    addr = (C.addressof(buf) + 15) // 16 * 16
+    r, err = _call("unpermute_combine", b.CombineArgs, T=4, k=2, H=64, in_=addr, out=addr, perm_pos=addr, in_rows=-1)
+    assert r == b.MGE_ERR_INVALID_ARG and "in_rows" in err
 
 
 def test_check_device_errors_rejects_null():
