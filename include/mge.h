@@ -55,10 +55,11 @@
  *     T = 0 is a no-op.  NaN/Inf inputs give undefined (but memory-safe) results.
  *   - The routing maps the grouped calls take are those moe_route_permute wrote for
  *     the same T, k, E and align.  They stay on the device, where the host cannot
- *     check them: other split_sizes or group_offsets can make the grouped GEMMs read
- *     or write outside their buffers.  perm_src and perm_pos are checked where they
- *     are read: the gathers take a source row outside [0, T) as zeros, and the combine
- *     and the d_prob reduction skip an entry outside the permuted rows.
+ *     check them, so the kernels bound what they read through them: the grouped GEMMs
+ *     clamp each group's span into the R permuted rows, the gathers take a source row
+ *     outside [0, T) as zeros, and the combine and the d_prob reduction skip an entry
+ *     outside the permuted rows.  Other maps give wrong results, but no access outside
+ *     the buffers.
  *   - Calls are thread-safe and re-entrant; each is deterministic, so two identical
  *     calls give bit-identical outputs: no floating-point value is accumulated with
  *     atomics (the only atomics are the integer LDS adds of the routing histogram,

@@ -527,7 +527,7 @@ static mge_status fwd_impl(const mge_fwd_args* a, const mge_fwd_unfused_args* u,
   }
 
   GemmParams g{};
-  g.mode = RAGGED_M; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
+  g.mode = RAGGED_M; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets; g.rows = R;
   g.A = static_cast<const uint8_t*>(a->x_perm); g.lda = int64_t(a->H) * elem;
   g.Asp = xs_p; g.asp_ld = R; g.asp_bytes = packed_exact(1, R, H / 32);
   g.Bt = reinterpret_cast<const uint8_t* const*>(tab);
@@ -590,7 +590,7 @@ static mge_status fwd_impl(const mge_fwd_args* a, const mge_fwd_unfused_args* u,
   }
 
   GemmParams d{};
-  d.mode = RAGGED_M; d.E = E; d.sizes = a->split_sizes; d.offs = a->group_offsets;
+  d.mode = RAGGED_M; d.E = E; d.sizes = a->split_sizes; d.offs = a->group_offsets; d.rows = R;
   d.A = static_cast<const uint8_t*>(h); d.lda = int64_t(a->F) * elem;
   d.Asp = hs_p; d.asp_ld = R; d.asp_bytes = packed_exact(1, R, F / 32);
   d.Bt = reinterpret_cast<const uint8_t* const*>(tab + E);
@@ -839,7 +839,7 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
   // and p): dGU in row and column forms and the d_prob partial row sums
   {
     GemmParams g{};
-    g.mode = RAGGED_M; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
+    g.mode = RAGGED_M; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets; g.rows = R;
     g.A = static_cast<const uint8_t*>(dyr); g.lda = int64_t(H) * elem; g.Asp = dyr_p; g.asp_ld = R; g.asp_bytes = packed_exact(1, R, H / 32);
     g.Bt = reinterpret_cast<const uint8_t* const*>(tab);
     g.Bsp = wdc_p; g.bsp_ld = F; g.bsp_estride = scale_pack_dwords(F, H / 32);
@@ -891,7 +891,7 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
   // b4: dW_down[e] = dY_e^T h_e  (K = tokens of e)
   {
     GemmParams g{};
-    g.mode = RAGGED_K; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
+    g.mode = RAGGED_K; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets; g.rows = R;
     g.A = static_cast<const uint8_t*>(dyc); g.lda = int64_t(R) * elem; g.Asp = dyc_p; g.asp_ld = H; g.asp_bytes = packed_exact(1, H, R / 32);
     g.B = static_cast<const uint8_t*>(a->h_col); g.ldb = int64_t(R) * elem; g.Bsp = hc_p; g.bsp_ld = F; g.bsp_bytes = packed_exact(1, F, R / 32);
     g.M = H; g.N = F;
@@ -906,7 +906,7 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
   // b5: dX = dGU W_gate_up  (K = 2F)
   {
     GemmParams g{};
-    g.mode = RAGGED_M; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
+    g.mode = RAGGED_M; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets; g.rows = R;
     g.A = static_cast<const uint8_t*>(dgr); g.lda = int64_t(F2) * elem; g.Asp = dgr_p; g.asp_ld = R; g.asp_bytes = packed_exact(1, R, F2 / 32);
     g.Bt = reinterpret_cast<const uint8_t* const*>(tab + E);
     g.Bsp = wguc_p; g.bsp_ld = H; g.bsp_estride = scale_pack_dwords(H, F2 / 32);
@@ -922,7 +922,7 @@ mge_status grouped_mlp_bwd(const mge_bwd_args* a, void* stream) {
   // b6: dW_gate_up[e] = dGU_e^T X_e  (K = tokens of e)
   {
     GemmParams g{};
-    g.mode = RAGGED_K; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets;
+    g.mode = RAGGED_K; g.E = E; g.sizes = a->split_sizes; g.offs = a->group_offsets; g.rows = R;
     g.A = static_cast<const uint8_t*>(dgc); g.lda = int64_t(R) * elem; g.Asp = dgc_p; g.asp_ld = F2; g.asp_bytes = packed_exact(1, F2, R / 32);
     g.B = static_cast<const uint8_t*>(a->x_col); g.ldb = int64_t(R) * elem; g.Bsp = xc_p; g.bsp_ld = H; g.bsp_bytes = packed_exact(1, H, R / 32);
     g.M = F2; g.N = H;

@@ -262,10 +262,16 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
   const int ncols_per_tile = (EPI == EPI_SWIGLU) ? G_BN / 2 : G_BN;
   const int ncols = (EPI == EPI_SWIGLU) ? p.F : p.N;
   const int ntiles = (ncols + ncols_per_tile - 1) / ncols_per_tile;
+  // A group's span, clamped into the R permuted rows, so that maps other than the routing
+  // call's give wrong results but no access outside the buffers (the host cannot check
+  // device-side maps).
+  auto group_off = [&](int off) { return off < 0 ? 0 : (off > p.rows ? p.rows : off); };
+  auto group_size = [&](int size, int off) { return size < 0 ? 0 : (size > p.rows - off ? p.rows - off : size); };
   if (tid == 0) {
     int acc = 0;
     for (int e = 0; e < p.E; ++e) {
-      int mt = MODE == RAGGED_M ? (p.sizes[e] + G_BM - 1) / G_BM : (p.M + G_BM - 1) / G_BM;
+      int mt = MODE == RAGGED_M ? (group_size(p.sizes[e], group_off(p.offs[e])) + G_BM - 1) / G_BM
+                                : (p.M + G_BM - 1) / G_BM;
       s_prefix[e] = acc;
       s_mtiles[e] = mt;
       acc += mt * ntiles;
@@ -327,8 +333,8 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
     const int gm = band == nband - 1 ? mtn - band * GM : GM;
     const int mt = band * GM + within % gm;
     t.nt = within / gm;
-    t.off = ld_uniform(p.offs, t.e);
-    t.m_valid = MODE == RAGGED_M ? ld_uniform(p.sizes, t.e) : p.M;
+    t.off = uniform(group_off(ld_uniform(p.offs, t.e)));
+    t.m_valid = MODE == RAGGED_M ? uniform(group_size(ld_uniform(p.sizes, t.e), t.off)) : p.M;
     t.m0 = mt * G_BM;
     // K range in bytes.  RAGGED_M: [0, K).  RAGGED_K: the expert's token span
     // [off, off + roundup32(size)) of the column forms; the loop starts at the slice
@@ -340,7 +346,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
       t.A = p.A + (int64_t(t.off) + t.m0) * p.lda;
       bmat = ld_uniform(p.Bt, t.e);
     } else {
-      const int span = ((ld_uniform(p.sizes, t.e) + 31) / 32) * 32;
+      const int span = uniform(group_size(((group_size(ld_uniform(p.sizes, t.e), t.off) + 31) / 32) * 32, t.off));
       t.klo = t.off * ELEM;
       t.khi = (t.off + span) * ELEM;
       t.kbase = span > 0 ? (t.klo / G_BKB) * G_BKB : t.klo;

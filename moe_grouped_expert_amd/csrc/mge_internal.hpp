@@ -133,6 +133,7 @@ struct GemmParams {
   int E;
   const int32_t* sizes;
   const int32_t* offs;
+  int rows;              // R, the permuted rows: every group's span is clamped into [0, R)
   // A: RAGGED_M -> shared [R][K] (row stride lda bytes); RAGGED_K -> shared [M][R] (row stride lda bytes)
   const uint8_t* A;  int64_t lda;
   // B: RAGGED_M -> per-expert table Bt[e] ([N][K], row stride ldb bytes); RAGGED_K -> shared [N][R]
