@@ -53,6 +53,8 @@ WORKLOADS = {
     "fwd_mxfp8_ep8": (5, False),
     "fwd_mxfp8_ep4": (6, False),
     "train_mxfp8_ep8": (7, True),
+    # the same step on one expert (top-1, 16384 rows): the GEMMs as dense ones
+    "train_mxfp8_dense": (8, True),
 }
 
 # How the forward runs: one grouped launch per projection over every expert with the
@@ -770,8 +772,10 @@ def main():
         log("[bench] timing the CPU oracle on a bounded sample")
         # MXFP8: expert 0's whole group over half of the ffn columns (about 12 s of fp64 numpy
         # on 16 host cores; the weight-slice quantization and the GEMMs both scale with the
-        # columns, so the mix of the two is that of the whole step)
-        rows = args.cpu_rows if args.cpu_rows is not None else (4096 if wg.prec == "bf16" else None)
+        # columns, so the mix of the two is that of the whole step); an expert holding more
+        # than 4096 rows on average (the one-expert workload) is sampled by its first 2048
+        big_group = wg.T * wg.k > 4096 * wg.E
+        rows = args.cpu_rows if args.cpu_rows is not None else (4096 if wg.prec == "bf16" else (2048 if big_group else None))
         fcols = args.cpu_fcols if args.cpu_fcols is not None else (None if wg.prec == "bf16" else max(32, wg.F // 2))
         out["cpu_baseline"] = cpu_baseline(wg, rows, fcols)
     print(json.dumps(out), flush=True)

@@ -83,6 +83,9 @@ WORKLOADS = {
                 backward=False, extra={"ep": 4}),
     7: Workload(7, "mixtral_mxfp8_train_step_ep8_rank_share", T=8192, E=8, H=4096, F=14336, k=2, prec="mxfp8",
                 backward=True, extra={"ep": 8}),
+    # The training step's GEMMs as dense ones: one expert, top-1, the same 16384 rows, so
+    # every M-tile shares one weight matrix (the shape of a plain dense FP8 GEMM).
+    8: Workload(8, "mxfp8_train_step_one_expert", T=16384, E=1, H=4096, F=14336, k=1, prec="mxfp8", backward=True),
 }
 
 
